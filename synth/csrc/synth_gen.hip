@@ -1,0 +1,109 @@
+// Seeded synthetic key/value rows on the GPU: the device twin of the numpy
+// generator in synth/host.py. It holds no attention arithmetic; it only
+// draws inputs, bit for bit the same as the host side:
+//   word(key, n)  = SplitMix64 mix of (key + n * 0x9E3779B97F4A7C15)
+//                   (Steele, Lea, Flood, OOPSLA 2014)
+//   z(e)          = (sum of the twelve 16-bit fields of words 3e+1..3e+3 - 6*65536) / 65536
+//   x             = mu + sigma * z   (float64, two roundings, no fused multiply-add)
+//   x            *= mult             (1 or 8, exact)
+//   stored        = float32 (nearest even) or bf16 (nearest even, directly from float64)
+// Element counter of row (b, t, h, j): (((b << 20) | t) * Hkv + h) * d + j.
+//
+// Built with -ffp-contract=off so that mu + sigma * z is never fused.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ull;
+
+__device__ __forceinline__ uint64_t mix64(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+__device__ __forceinline__ double irwin_hall(uint64_t key, uint64_t e) {
+  int64_t total = 0;
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    uint64_t w = mix64(key + (e * 3ull + (uint64_t)(k + 1)) * kGamma);
+    total += (int64_t)(w & 0xFFFFull) + (int64_t)((w >> 16) & 0xFFFFull) +
+             (int64_t)((w >> 32) & 0xFFFFull) + (int64_t)((w >> 48) & 0xFFFFull);
+  }
+  return (double)(total - 6 * 65536) * (1.0 / 65536.0);
+}
+
+__device__ __forceinline__ uint16_t bf16_from_f64(double x) {
+  uint64_t u = (uint64_t)__double_as_longlong(x);
+  uint64_t lsb = (u >> 45) & 1ull;
+  uint64_t r = (u + ((1ull << 44) - 1ull) + lsb) & ~((1ull << 45) - 1ull);
+  float f = (float)__longlong_as_double((long long)r);  // exact: 8 significant bits
+  return (uint16_t)(__float_as_uint(f) >> 16);
+}
+
+__global__ void fill_kv_kernel(void* __restrict__ out, int out_bf16, int B, int n_tok, int t0,
+                               int Hkv, int d, uint64_t key, const double* __restrict__ mu,
+                               const double* __restrict__ sigma, const double* __restrict__ mult) {
+  const uint64_t total = (uint64_t)B * n_tok * Hkv * d;
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (uint64_t)gridDim.x * blockDim.x) {
+    const int j = (int)(i % d);
+    uint64_t r = i / d;
+    const int h = (int)(r % Hkv);
+    r /= Hkv;
+    const int tt = (int)(r % n_tok);
+    const int b = (int)(r / n_tok);
+    const uint64_t t = (uint64_t)(t0 + tt);
+    const uint64_t e = ((((uint64_t)b << 20) | t) * (uint64_t)Hkv + (uint64_t)h) * (uint64_t)d + (uint64_t)j;
+    const double z = irwin_hall(key, e);
+    const int c = h * d + j;
+    const double prod = sigma[c] * z;
+    const double x = (mu[c] + prod) * mult[c];
+    if (out_bf16)
+      static_cast<uint16_t*>(out)[i] = bf16_from_f64(x);
+    else
+      static_cast<float*>(out)[i] = (float)x;
+  }
+}
+
+__global__ void touch_kernel(uint4* __restrict__ buf, uint64_t n, uint32_t salt) {
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (uint64_t)gridDim.x * blockDim.x)
+    buf[i] = make_uint4((uint32_t)i, salt, (uint32_t)(i >> 32), ~salt);
+}
+
+}  // namespace
+
+extern "C" {
+
+// Writes out[B][n_tok][Hkv][d] (float32 if out_bf16 == 0, bf16 bits otherwise)
+// for tokens t0 .. t0+n_tok-1. mu, sigma, mult: device float64 [Hkv][d].
+// Returns 0 or the hipError_t of the launch.
+int synth_fill_kv(void* out, int out_bf16, int B, int n_tok, int t0, int Hkv, int d,
+                  uint64_t key, const double* mu, const double* sigma, const double* mult,
+                  void* stream) {
+  if (!out || !mu || !sigma || !mult || B <= 0 || n_tok <= 0 || Hkv <= 0 || d <= 0 || t0 < 0 ||
+      (int64_t)t0 + n_tok > (1 << 20) || B >= (1 << 11))
+    return -1;
+  const uint64_t total = (uint64_t)B * n_tok * Hkv * d;
+  uint64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(fill_kv_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, out,
+                     out_bf16, B, n_tok, t0, Hkv, d, key, mu, sigma, mult);
+  return (int)hipGetLastError();
+}
+
+// Overwrites `bytes` (multiple of 16) of a scratch buffer, evicting earlier
+// data from the GPU caches between timed calls.
+int synth_touch(void* buf, uint64_t bytes, uint32_t salt, void* stream) {
+  if (!buf || bytes % 16) return -1;
+  const uint64_t n = bytes / 16;
+  uint64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(touch_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                     static_cast<uint4*>(buf), n, salt);
+  return (int)hipGetLastError();
+}
+
+}  // extern "C"
