@@ -1,0 +1,178 @@
+/*
+ * kvlr.h -- C ABI of libkvlr.so: decode attention over a key/value cache
+ * stored as rank-r latents, for AMD Instinct MI355X (gfx950).
+ *
+ * The method (StiefAttention technical summary, "Metodologia:
+ * StiefAttention" > "Mecanismo Central", item 5 "Inferência"; the German
+ * page "Don't be so Stief!", "Technisches Resümee" > "Kernmechanismus" >
+ * "Inferenz"): keys are kept in compressed form K_lat = K P_K and
+ * reconstructed as K_lat P_K^T before attention; values likewise with P_V.
+ * P_K and P_V have orthonormal columns (same section, item 2; item 3: the Q
+ * factor of a QR factorisation). STAR-KV ("Metodologia" section 1,
+ * "Inferenza") truncates the projections per attention head, so every KV
+ * head h carries its own ranks r_k[h], r_v[h].
+ *
+ * The library computes the same quantity in latent order:
+ *   q~ = q P_K[h],  s_t = (K_lat[t] . q~) * scale,  p = softmax(s),
+ *   o  = (sum_t p_t V_lat[t]) P_V[h]^T
+ * which equals softmax(K~ q * scale) V~ by associativity.
+ *
+ * Conventions for every entry point:
+ *  - Every function returns 0 (KVLR_OK) or a negative kvlr_status.
+ *    Argument checks run on the host before any HIP call; on failure nothing
+ *    is launched and no buffer is touched.
+ *  - The caller owns every buffer. The library allocates nothing, keeps no
+ *    pointer after returning and never synchronises: work is enqueued on
+ *    `stream` (a hipStream_t passed as void*; NULL is the null stream) and
+ *    is complete when that stream is.
+ *  - Pointers named "device" must be device memory (or memory the device
+ *    can read/write); descriptor rank arrays are host memory.
+ *  - Calls are re-entrant and thread-safe on disjoint output buffers.
+ *  - Device-resident indices (seq_lens, pos) are trusted preconditions;
+ *    kernels clamp them to [0, capacity] and never access memory out of
+ *    bounds.
+ *  - The library never prints.
+ */
+#ifndef KVLR_H
+#define KVLR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVLR_API __attribute__((visibility("default")))
+
+/* Status codes. */
+typedef enum kvlr_status {
+  KVLR_OK = 0,
+  KVLR_ERR_NULL = -1,      /* a required pointer is NULL */
+  KVLR_ERR_SHAPE = -2,     /* inconsistent shape: Hq % Hkv, head_dim, start + n_tok > capacity ... */
+  KVLR_ERR_RANK = -3,      /* rank outside [1, min(head_dim, 128)] or not a multiple of the
+                              storage granule (16 for bf16 latents, 4 for fp32 latents) */
+  KVLR_ERR_DTYPE = -4,     /* unsupported dtype code */
+  KVLR_ERR_WORKSPACE = -5, /* workspace NULL or smaller than kvlr_decode_workspace_bytes() */
+  KVLR_ERR_HIP = -6,       /* a kernel launch failed (hipGetLastError) */
+  KVLR_ERR_ARG = -7        /* other invalid scalar argument (split_tokens, scale, start) */
+} kvlr_status;
+
+/* Element types. */
+typedef enum kvlr_dtype {
+  KVLR_F32 = 0,  /* IEEE binary32 */
+  KVLR_BF16 = 1  /* bfloat16, stored as the upper 16 bits of binary32; fp32 -> bf16 rounds to nearest even */
+} kvlr_dtype;
+
+/* Shape of one layer's cache.
+ *   batch       B   >= 1
+ *   n_q_heads   Hq  >= 1, a multiple of n_kv_heads, with G = Hq / Hkv <= 16
+ *   n_kv_heads  Hkv in [1, 64]; query head i reads KV head i / G
+ *   head_dim    d   in [32, 256], a multiple of 32
+ *   capacity    T_cap >= 1: rows allocated per (batch row, KV head)
+ *   r_k, r_v    host arrays [Hkv]: ranks of each KV head (uniform per-layer
+ *               ranks repeat one value); 1 <= r <= min(d, 128), a multiple of 16
+ *               for bf16 latents and of 4 for fp32 latents
+ *   in_dtype    dtype of the full-width K/V rows given to compression and append
+ *   latent_dtype dtype of the latent cache
+ *
+ * Latent cache layout (lat_k; lat_v likewise with r_v): with
+ * R = sum_h r_k[h] and R_pre(h) = sum_{h' < h} r_k[h'], element (b, h, t, j)
+ * sits at index  T_cap * (b * R + R_pre(h)) + t * r_k[h] + j.
+ * With uniform ranks this is a contiguous [B][Hkv][T_cap][r] array; each
+ * (b, h) is one contiguous block of T_cap rows of r_k[h] elements.
+ *
+ * Basis layout: P_K is fp32, heads packed back to back, head h a row-major
+ * [d][r_k[h]] block starting at element d * R_pre(h); P_V likewise. */
+typedef struct kvlr_desc {
+  int32_t batch;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t capacity;
+  const int32_t* r_k;
+  const int32_t* r_v;
+  int32_t in_dtype;
+  int32_t latent_dtype;
+} kvlr_desc;
+
+/* Library version as 10000 * major + 100 * minor + patch. */
+KVLR_API int kvlr_version(void);
+
+/* Static message for a status code (never NULL). */
+KVLR_API const char* kvlr_status_string(int status);
+
+/* Validates `desc` and returns, through k_elems / v_elems, the number of
+ * latent elements of lat_k and lat_v: B * T_cap * sum_h r(h). */
+KVLR_API int kvlr_cache_elems(const kvlr_desc* desc, size_t* k_elems, size_t* v_elems);
+
+/* Bytes of decode workspace that kvlr_decode_attn needs for this
+ * descriptor and split length (split_tokens as in kvlr_decode_attn; 0 picks
+ * the library's choice, the same one kvlr_decode_attn makes for 0). */
+KVLR_API int kvlr_decode_workspace_bytes(const kvlr_desc* desc, int32_t split_tokens, size_t* bytes);
+
+/* Splits that kvlr_decode_attn uses per (batch row, KV head) for
+ * split_tokens (0 = library choice), and the tokens per split. */
+KVLR_API int kvlr_decode_plan(const kvlr_desc* desc, int32_t split_tokens, int32_t* n_splits,
+                              int32_t* tokens_per_split);
+
+/* Prefill compression: store the latents of n_tok consecutive tokens.
+ * (StiefAttention technical summary, "Mecanismo Central" item 5: keys are
+ * stored as K P_K; values likewise as V P_V.)
+ *   K, V      device, in_dtype, [B][n_tok][Hkv][d] (the layout a fused k/v
+ *             projection produces), token n of the call is cache row start + n
+ *   start     first cache row written, >= 0, start + n_tok <= capacity
+ *   n_tok     >= 0 (0 is a no-op)
+ *   P_K, P_V  device fp32 packed bases (see kvlr_desc)
+ *   lat_k, lat_v device latent caches (latent_dtype, layout in kvlr_desc);
+ *             rows start .. start+n_tok-1 of every (b, h) are overwritten,
+ *             nothing else is written.
+ * Products accumulate in fp32 (bf16 inputs: MFMA with the basis split into a
+ * high and a low bf16 part); results are rounded to the latent dtype. */
+KVLR_API int kvlr_prefill_compress(const kvlr_desc* desc, const void* K, const void* V, int32_t start,
+                                   int32_t n_tok, const float* P_K, const float* P_V, void* lat_k,
+                                   void* lat_v, void* stream);
+
+/* Append one token per batch row: lat_k[b, h, pos[b], :] = k_new[b, h, :] P_K[h],
+ * the same with v (autoregressive growth of the cache; StiefAttention
+ * technical summary, "Definição do Problema"; storage rule of
+ * "Mecanismo Central" item 5).
+ *   k_new, v_new device, in_dtype, [B][Hkv][d]
+ *   pos       device int32 [B]: row written for batch row b; a row outside
+ *             [0, capacity) is not written. The library never increments it
+ *             and never changes seq_lens: the caller advances both.
+ * fp32 accumulation, rounded to the latent dtype. */
+KVLR_API int kvlr_append(const kvlr_desc* desc, const void* k_new, const void* v_new, const int32_t* pos,
+                         const float* P_K, const float* P_V, void* lat_k, void* lat_v, void* stream);
+
+/* Decode attention over the latent cache for one new query per (batch row,
+ * query head) (StiefAttention technical summary, "Mecanismo Central" item 5;
+ * evaluated in the latent order given at the top of this file).
+ *   q         device fp32 [B][Hq][d]
+ *   P_K, P_V  device fp32 packed bases
+ *   lat_k, lat_v device latent caches
+ *   seq_lens  device int32 [B]: batch row b attends to rows t < seq_lens[b]
+ *             (clamped to [0, capacity]); 0 gives a zero output row
+ *   scale     finite score scale (1/sqrt(d) for standard attention)
+ *   out       device fp32 [B][Hq][d], fully overwritten
+ *   workspace device scratch of at least kvlr_decode_workspace_bytes(desc,
+ *             split_tokens) bytes; contents need no initialisation and are
+ *             garbage afterwards; calls sharing one workspace must be
+ *             ordered on one stream
+ *   split_tokens 0 for the library's choice, or a multiple of 64: tokens
+ *             per split of the sequence (every split yields a partial
+ *             softmax state; a second kernel merges them and back-projects
+ *             with P_V^T)
+ * Scores and the softmax are computed in fp32; bf16 latents are read as
+ * stored and multiplied in fp32 (the key side on MFMA with the query split
+ * into a high and a low bf16 part). */
+KVLR_API int kvlr_decode_attn(const kvlr_desc* desc, const float* q, const float* P_K, const float* P_V,
+                              const void* lat_k, const void* lat_v, const int32_t* seq_lens, float scale,
+                              float* out, void* workspace, size_t workspace_bytes, int32_t split_tokens,
+                              void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVLR_H */

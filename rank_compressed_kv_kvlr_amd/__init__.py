@@ -1,0 +1,256 @@
+"""Python binding of libkvlr: decode attention over a rank-compressed KV cache
+on AMD MI355X (gfx950).
+
+Argument marshalling only. Every step of the computation runs in the HIP
+kernels of ``libkvlr.so`` (see ``include/kvlr.h`` for the ABI); torch is
+used for device memory and the current stream. Importing this module fails
+if the library has not been built (``python -m rank_compressed_kv_kvlr_amd.build``);
+there is no fallback.
+
+Entry points mirror the C ABI:
+
+* ``prefill_compress(desc, K, V, start, P_K, P_V, lat_k, lat_v)`` stores
+  K P_K, V P_V for tokens start .. start + n - 1 (StiefAttention technical
+  summary, "Mecanismo Central" item 5);
+* ``append(desc, k_new, v_new, pos, P_K, P_V, lat_k, lat_v)`` stores one
+  token per batch row at row pos[b];
+* ``decode_attn(desc, q, P_K, P_V, lat_k, lat_v, seq_lens, scale, out, workspace)``
+  computes softmax((K_lat P_K^T) q * scale) (V_lat P_V^T) in latent order.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+__all__ = [
+    "KvlrError", "Desc", "F32", "BF16", "lib", "version", "status_string",
+    "cache_elems", "decode_workspace_bytes", "decode_plan",
+    "prefill_compress", "append", "decode_attn",
+    "alloc_cache", "alloc_workspace", "pack_bases", "head_view",
+]
+
+F32, BF16 = 0, 1
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvlr.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m rank_compressed_kv_kvlr_amd.build`")
+
+
+class _CDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("capacity", ctypes.c_int32),
+                ("r_k", ctypes.POINTER(ctypes.c_int32)), ("r_v", ctypes.POINTER(ctypes.c_int32)),
+                ("in_dtype", ctypes.c_int32), ("latent_dtype", ctypes.c_int32)]
+
+
+lib = ctypes.CDLL(LIB_PATH)
+_P = ctypes.c_void_p
+_D = ctypes.POINTER(_CDesc)
+_SZ = ctypes.POINTER(ctypes.c_size_t)
+_I32P = ctypes.POINTER(ctypes.c_int32)
+lib.kvlr_version.restype = ctypes.c_int
+lib.kvlr_status_string.restype = ctypes.c_char_p
+lib.kvlr_status_string.argtypes = [ctypes.c_int]
+lib.kvlr_cache_elems.argtypes = [_D, _SZ, _SZ]
+lib.kvlr_decode_workspace_bytes.argtypes = [_D, ctypes.c_int32, _SZ]
+lib.kvlr_decode_plan.argtypes = [_D, ctypes.c_int32, _I32P, _I32P]
+lib.kvlr_prefill_compress.argtypes = [_D, _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P]
+lib.kvlr_append.argtypes = [_D, _P, _P, _P, _P, _P, _P, _P, _P]
+lib.kvlr_decode_attn.argtypes = [_D, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, ctypes.c_size_t,
+                                 ctypes.c_int32, _P]
+for _f in ("kvlr_cache_elems", "kvlr_decode_workspace_bytes", "kvlr_decode_plan", "kvlr_prefill_compress",
+           "kvlr_append", "kvlr_decode_attn"):
+    getattr(lib, _f).restype = ctypes.c_int
+
+
+class KvlrError(RuntimeError):
+    def __init__(self, code: int, where: str = ""):
+        self.code = code
+        super().__init__(f"{where}: {status_string(code)} ({code})")
+
+
+def version() -> int:
+    return lib.kvlr_version()
+
+
+def status_string(code: int) -> str:
+    return lib.kvlr_status_string(code).decode()
+
+
+def _check(code: int, where: str):
+    if code != 0:
+        raise KvlrError(code, where)
+
+
+class Desc:
+    """One layer's cache shape (mirrors ``kvlr_desc``); keeps the rank arrays alive."""
+
+    def __init__(self, batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, capacity: int,
+                 r_k, r_v, in_dtype: int = BF16, latent_dtype: int = BF16):
+        rk = np.broadcast_to(np.asarray(r_k, dtype=np.int32), (n_kv_heads,)).copy()
+        rv = np.broadcast_to(np.asarray(r_v, dtype=np.int32), (n_kv_heads,)).copy()
+        self.r_k, self.r_v = rk, rv
+        self.batch, self.n_q_heads, self.n_kv_heads = batch, n_q_heads, n_kv_heads
+        self.head_dim, self.capacity = head_dim, capacity
+        self.in_dtype, self.latent_dtype = in_dtype, latent_dtype
+        self._c = _CDesc(batch, n_q_heads, n_kv_heads, head_dim, capacity,
+                         rk.ctypes.data_as(_I32P), rv.ctypes.data_as(_I32P), in_dtype, latent_dtype)
+
+    @property
+    def ptr(self):
+        return ctypes.byref(self._c)
+
+    @property
+    def G(self):
+        return self.n_q_heads // self.n_kv_heads
+
+    def rank_offsets(self, which: str):
+        r = self.r_k if which == "k" else self.r_v
+        return np.concatenate([[0], np.cumsum(r)]).astype(np.int64)
+
+
+def cache_elems(desc: Desc):
+    k, v = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib.kvlr_cache_elems(desc.ptr, ctypes.byref(k), ctypes.byref(v)), "kvlr_cache_elems")
+    return k.value, v.value
+
+
+def decode_workspace_bytes(desc: Desc, split_tokens: int = 0) -> int:
+    n = ctypes.c_size_t()
+    _check(lib.kvlr_decode_workspace_bytes(desc.ptr, split_tokens, ctypes.byref(n)), "kvlr_decode_workspace_bytes")
+    return n.value
+
+
+def decode_plan(desc: Desc, split_tokens: int = 0):
+    ns, length = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib.kvlr_decode_plan(desc.ptr, split_tokens, ctypes.byref(ns), ctypes.byref(length)), "kvlr_decode_plan")
+    return ns.value, length.value
+
+
+# ---------------------------------------------------------------------------
+# torch-facing helpers (device memory and streams only)
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_of(code: int):
+    torch = _torch()
+    return torch.bfloat16 if code == BF16 else torch.float32
+
+
+def _stream():
+    torch = _torch()
+    return _P(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, name: str, dtype, numel: Optional[int] = None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements, got {t.numel()}")
+    return _P(t.data_ptr())
+
+
+def alloc_cache(desc: Desc, device="cuda"):
+    """Flat latent caches (lat_k, lat_v) in the ABI layout."""
+    torch = _torch()
+    nk, nv = cache_elems(desc)
+    dt = _dtype_of(desc.latent_dtype)
+    return torch.empty(nk, dtype=dt, device=device), torch.empty(nv, dtype=dt, device=device)
+
+
+def alloc_workspace(desc: Desc, split_tokens: int = 0, device="cuda"):
+    torch = _torch()
+    n = decode_workspace_bytes(desc, split_tokens)
+    return torch.empty(max(n, 4) // 4, dtype=torch.float32, device=device)
+
+
+def pack_bases(bases: Sequence, device="cuda"):
+    """Per-head [d][r_h] arrays -> one packed fp32 device tensor."""
+    torch = _torch()
+    flat = np.concatenate([np.ascontiguousarray(b, dtype=np.float32).ravel() for b in bases])
+    return torch.from_numpy(flat).to(device)
+
+
+def head_view(lat, desc: Desc, which: str, b: int, h: int):
+    """View [capacity][r] of the latent rows of (batch row b, KV head h)."""
+    r = int((desc.r_k if which == "k" else desc.r_v)[h])
+    off = desc.rank_offsets(which)
+    R = int(off[-1])
+    start = desc.capacity * (b * R + int(off[h]))
+    return lat[start:start + desc.capacity * r].view(desc.capacity, r)
+
+
+def _basis_numel(desc: Desc, which: str) -> int:
+    return int(desc.head_dim * (desc.r_k if which == "k" else desc.r_v).sum())
+
+
+def prefill_compress(desc: Desc, K, V, start: int, P_K, P_V, lat_k, lat_v):
+    """Store latents of K, V [B][n][Hkv][d] (in_dtype) at cache rows start .. start+n-1."""
+    torch = _torch()
+    n_tok = K.shape[1] if K is not None and K.dim() == 4 else 0
+    shape = (desc.batch, n_tok, desc.n_kv_heads, desc.head_dim)
+    for t, name in ((K, "K"), (V, "V")):
+        if t is None or tuple(t.shape) != shape:
+            raise ValueError(f"{name} must have shape {shape}")
+    nk, nv = cache_elems(desc)
+    ind = _dtype_of(desc.in_dtype)
+    lad = _dtype_of(desc.latent_dtype)
+    args = (_need(K, "K", ind), _need(V, "V", ind), start, n_tok,
+            _need(P_K, "P_K", torch.float32, _basis_numel(desc, "k")),
+            _need(P_V, "P_V", torch.float32, _basis_numel(desc, "v")),
+            _need(lat_k, "lat_k", lad, nk), _need(lat_v, "lat_v", lad, nv))
+    _check(lib.kvlr_prefill_compress(desc.ptr, *args, _stream()), "kvlr_prefill_compress")
+
+
+def append(desc: Desc, k_new, v_new, pos, P_K, P_V, lat_k, lat_v):
+    """Store one token per batch row: k_new, v_new [B][Hkv][d] at row pos[b] (device int32 [B])."""
+    torch = _torch()
+    n = desc.batch * desc.n_kv_heads * desc.head_dim
+    nk, nv = cache_elems(desc)
+    ind = _dtype_of(desc.in_dtype)
+    lad = _dtype_of(desc.latent_dtype)
+    args = (_need(k_new, "k_new", ind, n), _need(v_new, "v_new", ind, n),
+            _need(pos, "pos", torch.int32, desc.batch),
+            _need(P_K, "P_K", torch.float32, _basis_numel(desc, "k")),
+            _need(P_V, "P_V", torch.float32, _basis_numel(desc, "v")),
+            _need(lat_k, "lat_k", lad, nk), _need(lat_v, "lat_v", lad, nv))
+    _check(lib.kvlr_append(desc.ptr, *args, _stream()), "kvlr_append")
+
+
+def decode_attn(desc: Desc, q, P_K, P_V, lat_k, lat_v, seq_lens, scale: Optional[float] = None,
+                out=None, workspace=None, split_tokens: int = 0):
+    """o [B][Hq][d] fp32 for queries q [B][Hq][d] fp32 over rows t < seq_lens[b]."""
+    torch = _torch()
+    if scale is None:
+        scale = 1.0 / math.sqrt(desc.head_dim)
+    nq = desc.batch * desc.n_q_heads * desc.head_dim
+    if out is None:
+        out = torch.empty((desc.batch, desc.n_q_heads, desc.head_dim), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(desc, split_tokens, q.device)
+    nk, nv = cache_elems(desc)
+    lad = _dtype_of(desc.latent_dtype)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    args = (_need(q, "q", torch.float32, nq),
+            _need(P_K, "P_K", torch.float32, _basis_numel(desc, "k")),
+            _need(P_V, "P_V", torch.float32, _basis_numel(desc, "v")),
+            _need(lat_k, "lat_k", lad, nk), _need(lat_v, "lat_v", lad, nv),
+            _need(seq_lens, "seq_lens", torch.int32, desc.batch), ctypes.c_float(scale),
+            _need(out, "out", torch.float32, nq), _need(workspace, "workspace", workspace.dtype),
+            ctypes.c_size_t(ws_bytes), split_tokens)
+    _check(lib.kvlr_decode_attn(desc.ptr, *args, _stream()), "kvlr_decode_attn")
+    return out

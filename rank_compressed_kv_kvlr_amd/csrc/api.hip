@@ -1,0 +1,248 @@
+// Host side of the libkvlr C ABI: argument validation, split planning and
+// kernel launches on the caller's stream. Allocates nothing, keeps no state,
+// never synchronises. Every check runs before the first HIP call.
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "kvlr_internal.hpp"
+
+namespace {
+
+using kvlr::HeadTable;
+
+constexpr int kVersion = 10000;   // 1.0.0
+constexpr int kSplitGranule = kvlr::kTile;
+constexpr long long kTargetWorkgroups = 2048;
+
+bool valid_dtype(int t) { return t == KVLR_F32 || t == KVLR_BF16; }
+
+// Validates the descriptor and fills the per-head tables.
+int check_desc(const kvlr_desc* d, HeadTable* ht, int* Rk, int* Rv, int* rank_bound) {
+  if (!d || !d->r_k || !d->r_v) return KVLR_ERR_NULL;
+  if (!valid_dtype(d->in_dtype) || !valid_dtype(d->latent_dtype)) return KVLR_ERR_DTYPE;
+  if (d->batch < 1 || d->n_kv_heads < 1 || d->n_kv_heads > kvlr::kMaxKvHeads || d->n_q_heads < 1 ||
+      d->n_q_heads % d->n_kv_heads != 0 || d->n_q_heads / d->n_kv_heads > 16 || d->capacity < 1 ||
+      d->head_dim < 32 || d->head_dim > 256 || d->head_dim % 32 != 0)
+    return KVLR_ERR_SHAPE;
+  const int granule = d->latent_dtype == KVLR_BF16 ? 16 : 4;
+  const int rmax = d->head_dim < kvlr::kMaxRank ? d->head_dim : kvlr::kMaxRank;
+  int sk = 0, sv = 0, bound = 0;
+  for (int h = 0; h < d->n_kv_heads; ++h) {
+    const int rk = d->r_k[h], rv = d->r_v[h];
+    if (rk < 1 || rv < 1 || rk > rmax || rv > rmax || rk % granule || rv % granule) return KVLR_ERR_RANK;
+    if (ht) {
+      ht->rk[h] = rk;
+      ht->rv[h] = rv;
+      ht->rk_pre[h] = sk;
+      ht->rv_pre[h] = sv;
+    }
+    sk += rk;
+    sv += rv;
+    bound = rk > bound ? rk : bound;
+    bound = rv > bound ? rv : bound;
+  }
+  // every per-(b, h) block offset T_cap * (b * R + R_pre) must fit comfortably in size_t;
+  // kernels index rows with 32-bit token counts
+  if ((long long)d->capacity * d->batch * (sk > sv ? sk : sv) > (1LL << 46)) return KVLR_ERR_SHAPE;
+  if (Rk) *Rk = sk;
+  if (Rv) *Rv = sv;
+  if (rank_bound) *rank_bound = bound <= 32 ? 32 : bound <= 64 ? 64 : bound <= 96 ? 96 : 128;
+  return KVLR_OK;
+}
+
+int plan_split(const kvlr_desc* d, int32_t split_tokens, int* n_splits, int* split_len) {
+  const int G = d->n_q_heads / d->n_kv_heads;
+  const int groups = (G + kvlr::kHeadsPerWg - 1) / kvlr::kHeadsPerWg;
+  int len;
+  if (split_tokens < 0 || split_tokens % kSplitGranule != 0) return KVLR_ERR_ARG;
+  if (split_tokens > 0) {
+    len = split_tokens;
+  } else {
+    const char* env = getenv("KVLR_SPLIT_TOKENS");   // tuning override
+    long long want = env ? atoll(env) : 0;
+    if (want <= 0 || want % kSplitGranule) {
+      const long long units = (long long)d->batch * d->n_kv_heads * groups;
+      want = (units * d->capacity + kTargetWorkgroups - 1) / kTargetWorkgroups;
+      const long long g4 = (long long)kSplitGranule * kvlr::kWaves;
+      want = (want + g4 - 1) / g4 * g4;   // whole tiles for every wave
+      if (want < g4) want = g4;
+    }
+    len = want > d->capacity ? ((d->capacity + kSplitGranule - 1) / kSplitGranule) * kSplitGranule : (int)want;
+  }
+  const long long ns = ((long long)d->capacity + len - 1) / len;
+  if (ns > 65535) return KVLR_ERR_ARG;   // grid.x limit of the split kernel
+  *n_splits = (int)ns;
+  *split_len = len;
+  return KVLR_OK;
+}
+
+int ws_stride_of(const HeadTable& ht, int Hkv) {
+  int m = 0;
+  for (int h = 0; h < Hkv; ++h) m = ht.rv[h] > m ? ht.rv[h] : m;
+  return (m + 2 + 3) / 4 * 4;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? KVLR_OK : KVLR_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+KVLR_API int kvlr_version(void) { return kVersion; }
+
+KVLR_API const char* kvlr_status_string(int status) {
+  switch (status) {
+    case KVLR_OK: return "ok";
+    case KVLR_ERR_NULL: return "a required pointer is NULL";
+    case KVLR_ERR_SHAPE: return "inconsistent or unsupported shape";
+    case KVLR_ERR_RANK: return "rank out of range or not a multiple of the storage granule";
+    case KVLR_ERR_DTYPE: return "unsupported dtype";
+    case KVLR_ERR_WORKSPACE: return "workspace missing or too small";
+    case KVLR_ERR_HIP: return "HIP launch failed";
+    case KVLR_ERR_ARG: return "invalid scalar argument";
+    default: return "unknown status";
+  }
+}
+
+KVLR_API int kvlr_cache_elems(const kvlr_desc* desc, size_t* k_elems, size_t* v_elems) {
+  int Rk = 0, Rv = 0;
+  const int rc = check_desc(desc, nullptr, &Rk, &Rv, nullptr);
+  if (rc) return rc;
+  if (!k_elems || !v_elems) return KVLR_ERR_NULL;
+  *k_elems = (size_t)desc->batch * desc->capacity * Rk;
+  *v_elems = (size_t)desc->batch * desc->capacity * Rv;
+  return KVLR_OK;
+}
+
+KVLR_API int kvlr_decode_plan(const kvlr_desc* desc, int32_t split_tokens, int32_t* n_splits,
+                              int32_t* tokens_per_split) {
+  int rc = check_desc(desc, nullptr, nullptr, nullptr, nullptr);
+  if (rc) return rc;
+  if (!n_splits || !tokens_per_split) return KVLR_ERR_NULL;
+  int ns = 0, len = 0;
+  rc = plan_split(desc, split_tokens, &ns, &len);
+  if (rc) return rc;
+  *n_splits = ns;
+  *tokens_per_split = len;
+  return KVLR_OK;
+}
+
+KVLR_API int kvlr_decode_workspace_bytes(const kvlr_desc* desc, int32_t split_tokens, size_t* bytes) {
+  HeadTable ht;
+  int rc = check_desc(desc, &ht, nullptr, nullptr, nullptr);
+  if (rc) return rc;
+  if (!bytes) return KVLR_ERR_NULL;
+  int ns = 0, len = 0;
+  rc = plan_split(desc, split_tokens, &ns, &len);
+  if (rc) return rc;
+  *bytes = (size_t)desc->batch * desc->n_q_heads * ns * ws_stride_of(ht, desc->n_kv_heads) * sizeof(float);
+  return KVLR_OK;
+}
+
+KVLR_API int kvlr_prefill_compress(const kvlr_desc* desc, const void* K, const void* V, int32_t start,
+                                   int32_t n_tok, const float* P_K, const float* P_V, void* lat_k,
+                                   void* lat_v, void* stream) {
+  kvlr::CompressParams p;
+  int rc = check_desc(desc, &p.ht, &p.Rk, &p.Rv, nullptr);
+  if (rc) return rc;
+  if (start < 0 || n_tok < 0) return KVLR_ERR_ARG;
+  if ((long long)start + n_tok > desc->capacity) return KVLR_ERR_SHAPE;
+  if (n_tok == 0) return KVLR_OK;
+  if (!K || !V || !P_K || !P_V || !lat_k || !lat_v) return KVLR_ERR_NULL;
+  if ((long long)desc->batch * n_tok * desc->n_kv_heads * desc->head_dim > (1LL << 40)) return KVLR_ERR_SHAPE;
+  p.x_k = K;
+  p.x_v = V;
+  p.pk = P_K;
+  p.pv = P_V;
+  p.lat_k = lat_k;
+  p.lat_v = lat_v;
+  p.B = desc->batch;
+  p.Hkv = desc->n_kv_heads;
+  p.d = desc->head_dim;
+  p.cap = desc->capacity;
+  p.start = start;
+  p.n_tok = n_tok;
+  p.in_bf16 = desc->in_dtype == KVLR_BF16;
+  p.out_bf16 = desc->latent_dtype == KVLR_BF16;
+  return hip_status(kvlr::launch_compress(p, static_cast<hipStream_t>(stream)));
+}
+
+KVLR_API int kvlr_append(const kvlr_desc* desc, const void* k_new, const void* v_new, const int32_t* pos,
+                         const float* P_K, const float* P_V, void* lat_k, void* lat_v, void* stream) {
+  kvlr::AppendParams p;
+  const int rc = check_desc(desc, &p.ht, &p.Rk, &p.Rv, nullptr);
+  if (rc) return rc;
+  if (!k_new || !v_new || !pos || !P_K || !P_V || !lat_k || !lat_v) return KVLR_ERR_NULL;
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.pos = pos;
+  p.pk = P_K;
+  p.pv = P_V;
+  p.lat_k = lat_k;
+  p.lat_v = lat_v;
+  p.B = desc->batch;
+  p.Hkv = desc->n_kv_heads;
+  p.d = desc->head_dim;
+  p.cap = desc->capacity;
+  p.in_bf16 = desc->in_dtype == KVLR_BF16;
+  p.out_bf16 = desc->latent_dtype == KVLR_BF16;
+  return hip_status(kvlr::launch_append(p, static_cast<hipStream_t>(stream)));
+}
+
+KVLR_API int kvlr_decode_attn(const kvlr_desc* desc, const float* q, const float* P_K, const float* P_V,
+                              const void* lat_k, const void* lat_v, const int32_t* seq_lens, float scale,
+                              float* out, void* workspace, size_t workspace_bytes, int32_t split_tokens,
+                              void* stream) {
+  kvlr::DecodeParams p;
+  int rank_bound = 0;
+  int rc = check_desc(desc, &p.ht, &p.Rk, &p.Rv, &rank_bound);
+  if (rc) return rc;
+  if (!q || !P_K || !P_V || !lat_k || !lat_v || !seq_lens || !out) return KVLR_ERR_NULL;
+  if (!isfinite(scale)) return KVLR_ERR_ARG;
+  int ns = 0, len = 0;
+  rc = plan_split(desc, split_tokens, &ns, &len);
+  if (rc) return rc;
+  const int stride = ws_stride_of(p.ht, desc->n_kv_heads);
+  const size_t need = (size_t)desc->batch * desc->n_q_heads * ns * stride * sizeof(float);
+  if (!workspace || workspace_bytes < need) return KVLR_ERR_WORKSPACE;
+
+  const int G = desc->n_q_heads / desc->n_kv_heads;
+  p.q = q;
+  p.pk = P_K;
+  p.lat_k = lat_k;
+  p.lat_v = lat_v;
+  p.seq_lens = seq_lens;
+  p.ws = static_cast<float*>(workspace);
+  p.B = desc->batch;
+  p.Hq = desc->n_q_heads;
+  p.Hkv = desc->n_kv_heads;
+  p.G = G;
+  p.d = desc->head_dim;
+  p.cap = desc->capacity;
+  p.split_len = len;
+  p.n_splits = ns;
+  p.ws_stride = stride;
+  p.n_head_groups = (G + kvlr::kHeadsPerWg - 1) / kvlr::kHeadsPerWg;
+  p.scale_log2 = scale * 1.4426950408889634f;
+
+  kvlr::MergeParams m;
+  m.ws = p.ws;
+  m.pv = P_V;
+  m.out = out;
+  m.B = p.B;
+  m.Hq = p.Hq;
+  m.Hkv = p.Hkv;
+  m.G = G;
+  m.d = p.d;
+  m.n_splits = ns;
+  m.ws_stride = stride;
+  m.ht = p.ht;
+
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  rc = hip_status(kvlr::launch_decode(p, desc->latent_dtype == KVLR_BF16, rank_bound, s));
+  if (rc) return rc;
+  return hip_status(kvlr::launch_merge(m, s));
+}
+
+}  // extern "C"

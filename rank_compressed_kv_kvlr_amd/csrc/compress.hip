@@ -1,0 +1,240 @@
+// Latent storage of keys and values (gfx950): prefill compression and
+// single-token append.
+//
+// Method (StiefAttention technical summary, "Mecanismo Central" item 5):
+// during inference keys are stored compressed as K P_K (values as V P_V);
+// the cache grows by one row per decoded token ("Definição do Problema").
+//
+// Prefill with bf16 inputs is a dense contraction [n_tok x d] . [d x r] per
+// (batch row, KV head) and runs on MFMA (v_mfma_f32_16x16x32_bf16) with the
+// roles swapped so that each lane ends with 4 consecutive latent channels of
+// one token (one 8-byte store): A = P^T (latent channels as rows), B = the
+// token rows (16 tokens as columns, 16 contiguous input bytes per lane).
+// The fp32 basis enters as a high and a low bf16 part (two MFMAs into one
+// fp32 accumulator), so products carry ~16 bits of the basis and the only
+// rounding of note is the final one to the latent dtype. The basis operands
+// are staged once per workgroup in LDS, pre-arranged in operand order.
+//
+// fp32 inputs (and any other combination) use a plain VALU kernel; append
+// uses one workgroup per (batch row, KV head, K or V).
+#include "kvlr_internal.hpp"
+
+namespace kvlr {
+namespace {
+
+constexpr int kCompressWaves = 4;
+constexpr int kTokensPerWave = 64;        // 4 MFMA column tiles of 16 tokens
+constexpr int kWaveIters = 4;             // tiles per wave per workgroup
+constexpr int kTokensPerWg = kCompressWaves * kTokensPerWave * kWaveIters;   // 1024
+
+// LDS budget for the staged basis: (r/16) * (d/32) * 64 lanes * 16 B * 2 = 4 r d bytes.
+constexpr int kStageBytes = 4 * kMaxRank * 256;   // r <= 128, d <= 256
+
+// NKB = d / 32: 32-channel input blocks (one MFMA each per 16 tokens).
+template <bool kOutBf16, int NKB>
+__global__ __launch_bounds__(256) void compress_bf16_mfma(CompressParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint4 stage[];   // [mt][kb][lane] hi, then lo
+  const int kind = blockIdx.y & 1;             // 0 keys, 1 values
+  const int h = blockIdx.y >> 1;
+  const int b = blockIdx.z;
+  const int d = p.d;
+  const int r = kind ? p.ht.rv[h] : p.ht.rk[h];
+  const int r_pre = kind ? p.ht.rv_pre[h] : p.ht.rk_pre[h];
+  const int R = kind ? p.Rv : p.Rk;
+  const float* P = (kind ? p.pv : p.pk) + (size_t)d * r_pre;
+  const uint16_t* X = static_cast<const uint16_t*>(kind ? p.x_v : p.x_k);
+  const int n_mt = r >> 4, dq = d >> 2;
+  constexpr int n_kb = NKB;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n16 = lane & 15, q4 = lane >> 4;
+
+  // ---- stage P^T operands: entry (mt, kb, lane) holds P[q*dq + 8kb + e][16mt + lane%16], e < 8
+  const int n_entries = n_mt * n_kb * 64;
+  uint4* st_hi = stage;
+  uint4* st_lo = stage + n_entries;
+  for (int idx = tid; idx < n_entries; idx += blockDim.x) {
+    const int ln = idx & 63;
+    const int kb = (idx >> 6) % n_kb;
+    const int mt = (idx >> 6) / n_kb;
+    const int col = 16 * mt + (ln & 15);
+    const int row0 = (ln >> 4) * dq + 8 * kb;
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const float x0 = P[(size_t)(row0 + e) * r + col];
+      const float x1 = P[(size_t)(row0 + e + 1) * r + col];
+      const uint16_t h0 = f32_to_bf16_bits(x0), h1 = f32_to_bf16_bits(x1);
+      const uint16_t l0 = f32_to_bf16_bits(x0 - bf16_bits_to_f32(h0));
+      const uint16_t l1 = f32_to_bf16_bits(x1 - bf16_bits_to_f32(h1));
+      hi[e >> 1] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+      lo[e >> 1] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+    }
+    st_hi[idx] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    st_lo[idx] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+  }
+  __syncthreads();
+
+  const size_t row_stride = (size_t)p.Hkv * d;   // elements between consecutive tokens
+  const uint16_t* Xb = X + (size_t)b * p.n_tok * row_stride + (size_t)h * d;
+  const size_t lat_base = (size_t)p.cap * ((size_t)b * R + r_pre);
+  const int tok_wg0 = blockIdx.x * kTokensPerWg;
+
+  for (int it = 0; it < kWaveIters; ++it) {
+    const int tw0 = tok_wg0 + (it * kCompressWaves + wave) * kTokensPerWave;
+    if (tw0 >= p.n_tok) break;
+    // input rows: 4 column tiles of 16 tokens, lane covers d/4 channels
+    uint4 xin[4][NKB];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int t = min(tw0 + 16 * nt + n16, p.n_tok - 1);
+      const uint16_t* row = Xb + (size_t)t * row_stride + q4 * dq;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) xin[nt][kb] = *reinterpret_cast<const uint4*>(row + 8 * kb);
+    }
+    for (int mt = 0; mt < n_mt; ++mt) {
+      f32x4_t acc[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) acc[nt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        {
+          const int e = (mt * n_kb + kb) * 64 + lane;
+          const bf16x8_t ahi = __builtin_bit_cast(bf16x8_t, st_hi[e]);
+          const bf16x8_t alo = __builtin_bit_cast(bf16x8_t, st_lo[e]);
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) {
+            const bf16x8_t xb = __builtin_bit_cast(bf16x8_t, xin[nt][kb]);
+            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, xb, acc[nt], 0, 0, 0);
+            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, xb, acc[nt], 0, 0, 0);
+          }
+        }
+      }
+      // lane holds latent channels 16mt + 4q4 + i (i < 4) of token tw0 + 16nt + n16
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int t = tw0 + 16 * nt + n16;
+        if (t < p.n_tok) {
+          const size_t off = lat_base + (size_t)(p.start + t) * r + 16 * mt + 4 * q4;
+          if (kOutBf16) {
+            const uint32_t w0 = (uint32_t)f32_to_bf16_bits(acc[nt][0]) | ((uint32_t)f32_to_bf16_bits(acc[nt][1]) << 16);
+            const uint32_t w1 = (uint32_t)f32_to_bf16_bits(acc[nt][2]) | ((uint32_t)f32_to_bf16_bits(acc[nt][3]) << 16);
+            uint16_t* dst = static_cast<uint16_t*>(kind ? p.lat_v : p.lat_k) + off;
+            *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
+          } else {
+            float* dst = static_cast<float*>(kind ? p.lat_v : p.lat_k) + off;
+            *reinterpret_cast<float4*>(dst) = make_float4(acc[nt][0], acc[nt][1], acc[nt][2], acc[nt][3]);
+          }
+        }
+      }
+    }
+  }
+}
+
+// Plain VALU compression for fp32 inputs (any latent dtype): one workgroup
+// per (64-token tile, KV head x {K, V}, batch row); the tile is staged in LDS
+// as fp32 and each thread forms latent channels as fp32 dot products.
+constexpr int kValuTile = 64;
+
+__global__ __launch_bounds__(256) void compress_valu(CompressParams p) {
+  extern __shared__ __attribute__((aligned(16))) float xs[];   // [64][d]
+  const int kind = blockIdx.y & 1;
+  const int h = blockIdx.y >> 1;
+  const int b = blockIdx.z;
+  const int d = p.d;
+  const int r = kind ? p.ht.rv[h] : p.ht.rk[h];
+  const int r_pre = kind ? p.ht.rv_pre[h] : p.ht.rk_pre[h];
+  const int R = kind ? p.Rv : p.Rk;
+  const float* P = (kind ? p.pv : p.pk) + (size_t)d * r_pre;
+  const void* X = kind ? p.x_v : p.x_k;
+  const int t0 = blockIdx.x * kValuTile;
+  const int nt = min(kValuTile, p.n_tok - t0);
+  const size_t row_stride = (size_t)p.Hkv * d;
+  for (int idx = threadIdx.x; idx < nt * d; idx += blockDim.x) {
+    const int t = idx / d, i = idx - t * d;
+    const size_t src = ((size_t)b * p.n_tok + t0 + t) * row_stride + (size_t)h * d + i;
+    xs[idx] = p.in_bf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(X)[src]) : static_cast<const float*>(X)[src];
+  }
+  __syncthreads();
+  const size_t lat_base = (size_t)p.cap * ((size_t)b * R + r_pre);
+  for (int idx = threadIdx.x; idx < nt * r; idx += blockDim.x) {
+    const int t = idx / r, j = idx - t * r;
+    const float* x = xs + t * d;
+    float acc = 0.f;
+    for (int i = 0; i < d; ++i) acc = fmaf(x[i], P[(size_t)i * r + j], acc);
+    const size_t off = lat_base + (size_t)(p.start + t0 + t) * r + j;
+    if (p.out_bf16)
+      static_cast<uint16_t*>(kind ? p.lat_v : p.lat_k)[off] = f32_to_bf16_bits(acc);
+    else
+      static_cast<float*>(kind ? p.lat_v : p.lat_k)[off] = acc;
+  }
+}
+
+// Append: one workgroup per (batch row, KV head, K or V).
+__global__ __launch_bounds__(128) void append_kernel(AppendParams p) {
+  __shared__ float xs[256];
+  const int b = blockIdx.x, h = blockIdx.y, kind = blockIdx.z;
+  const int d = p.d;
+  const int pos = p.pos[b];
+  if (pos < 0 || pos >= p.cap) return;   // rows outside the cache are not written
+  const int r = kind ? p.ht.rv[h] : p.ht.rk[h];
+  const int r_pre = kind ? p.ht.rv_pre[h] : p.ht.rk_pre[h];
+  const int R = kind ? p.Rv : p.Rk;
+  const float* P = (kind ? p.pv : p.pk) + (size_t)d * r_pre;
+  const void* X = kind ? p.v_new : p.k_new;
+  const size_t src0 = ((size_t)b * p.Hkv + h) * d;
+  for (int i = threadIdx.x; i < d; i += blockDim.x)
+    xs[i] = p.in_bf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(X)[src0 + i])
+                      : static_cast<const float*>(X)[src0 + i];
+  __syncthreads();
+  const size_t off0 = (size_t)p.cap * ((size_t)b * R + r_pre) + (size_t)pos * r;
+  for (int j = threadIdx.x; j < r; j += blockDim.x) {
+    float acc = 0.f;
+    for (int i = 0; i < d; ++i) acc = fmaf(xs[i], P[(size_t)i * r + j], acc);
+    if (p.out_bf16)
+      static_cast<uint16_t*>(kind ? p.lat_v : p.lat_k)[off0 + j] = f32_to_bf16_bits(acc);
+    else
+      static_cast<float*>(kind ? p.lat_v : p.lat_k)[off0 + j] = acc;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_compress(const CompressParams& p, hipStream_t stream) {
+  if (p.n_tok <= 0) return hipSuccess;
+  int max_r = 0;
+  for (int h = 0; h < p.Hkv; ++h) max_r = max(max_r, max(p.ht.rk[h], p.ht.rv[h]));
+  if (p.in_bf16) {
+    const size_t lds = (size_t)4 * max_r * p.d;   // hi + lo operand tiles
+    const dim3 grid((p.n_tok + kTokensPerWg - 1) / kTokensPerWg, 2 * p.Hkv, p.B);
+#define KVLR_COMPRESS_CASE(NKB)                                                              \
+  case NKB:                                                                                  \
+    if (p.out_bf16)                                                                          \
+      hipLaunchKernelGGL((compress_bf16_mfma<true, NKB>), grid, dim3(256), lds, stream, p);  \
+    else                                                                                     \
+      hipLaunchKernelGGL((compress_bf16_mfma<false, NKB>), grid, dim3(256), lds, stream, p); \
+    break;
+    switch (p.d / 32) {
+      KVLR_COMPRESS_CASE(1)
+      KVLR_COMPRESS_CASE(2)
+      KVLR_COMPRESS_CASE(3)
+      KVLR_COMPRESS_CASE(4)
+      KVLR_COMPRESS_CASE(5)
+      KVLR_COMPRESS_CASE(6)
+      KVLR_COMPRESS_CASE(7)
+      default: KVLR_COMPRESS_CASE(8)
+    }
+#undef KVLR_COMPRESS_CASE
+  } else {
+    const size_t lds = (size_t)kValuTile * p.d * sizeof(float);
+    const dim3 grid((p.n_tok + kValuTile - 1) / kValuTile, 2 * p.Hkv, p.B);
+    hipLaunchKernelGGL(compress_valu, grid, dim3(256), lds, stream, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(append_kernel, dim3(p.B, p.Hkv, 2), dim3(128), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace kvlr

@@ -1,0 +1,132 @@
+// Internal declarations of libkvlr: kernel parameter blocks, launchers and
+// small device helpers shared by the gfx950 kernels. Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kvlr.h"
+
+namespace kvlr {
+
+constexpr int kMaxKvHeads = 64;   // per-head tables travel in the kernel argument block
+constexpr int kMaxRank = 128;     // rank bound of the decode kernels' register tiles
+constexpr int kHeadsPerWg = 4;    // query heads sharing one KV head handled by one workgroup
+constexpr int kTile = 64;         // tokens per wave iteration in decode
+constexpr int kWaves = 4;         // waves per decode workgroup
+
+// Per-KV-head tables: ranks and prefix sums of ranks (latent and basis offsets).
+struct HeadTable {
+  int rk[kMaxKvHeads];
+  int rv[kMaxKvHeads];
+  int rk_pre[kMaxKvHeads];
+  int rv_pre[kMaxKvHeads];
+};
+
+struct DecodeParams {
+  const float* q;        // [B][Hq][d]
+  const float* pk;       // packed [h][d][rk(h)]
+  const void* lat_k;     // latent caches
+  const void* lat_v;
+  const int* seq_lens;   // [B]
+  float* ws;             // partial records [B][Hq][n_splits][ws_stride]
+  int B, Hq, Hkv, G, d, cap;
+  int split_len, n_splits, ws_stride, n_head_groups;
+  int Rk, Rv;            // sum of ranks over heads
+  float scale_log2;      // scale * log2(e): scores live in the base-2 domain
+  HeadTable ht;
+};
+
+struct MergeParams {
+  const float* ws;
+  const float* pv;       // packed [h][d][rv(h)]
+  float* out;            // [B][Hq][d]
+  int B, Hq, Hkv, G, d;
+  int n_splits, ws_stride;
+  HeadTable ht;
+};
+
+struct CompressParams {
+  const void* x_k;       // [B][n_tok][Hkv][d] in_dtype (keys)
+  const void* x_v;       // values
+  const float* pk;
+  const float* pv;
+  void* lat_k;
+  void* lat_v;
+  int B, Hkv, d, cap, start, n_tok;
+  int Rk, Rv;
+  int in_bf16, out_bf16;
+  HeadTable ht;
+};
+
+struct AppendParams {
+  const void* k_new;     // [B][Hkv][d]
+  const void* v_new;
+  const int* pos;        // [B]
+  const float* pk;
+  const float* pv;
+  void* lat_k;
+  void* lat_v;
+  int B, Hkv, d, cap;
+  int Rk, Rv;
+  int in_bf16, out_bf16;
+  HeadTable ht;
+};
+
+// Launchers (return hipGetLastError() of their launches).
+hipError_t launch_decode(const DecodeParams& p, int latent_bf16, int rank_bound, hipStream_t s);
+hipError_t launch_merge(const MergeParams& p, hipStream_t s);
+hipError_t launch_compress(const CompressParams& p, hipStream_t s);
+hipError_t launch_append(const AppendParams& p, hipStream_t s);
+
+// ------------------------------------------------------------------------
+// device helpers
+// ------------------------------------------------------------------------
+typedef short bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+  __bf16 h = static_cast<__bf16>(x);
+  return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// All-reduce over the 16 lanes of a DPP row (max or sum) with row rotations
+// and quad permutations; every lane of the row ends with the result.
+template <bool kMax>
+__device__ __forceinline__ float row16_allreduce(float x) {
+  float y;
+  y = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));  // row_ror:8
+  x = kMax ? fmaxf(x, y) : x + y;
+  y = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xf, 0xf, false));  // row_ror:4
+  x = kMax ? fmaxf(x, y) : x + y;
+  y = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4e, 0xf, 0xf, false));   // quad_perm [2,3,0,1]
+  x = kMax ? fmaxf(x, y) : x + y;
+  y = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xb1, 0xf, 0xf, false));   // quad_perm [1,0,3,2]
+  x = kMax ? fmaxf(x, y) : x + y;
+  return x;
+}
+
+// All-reduce over the 64 lanes of a wave (butterfly through ds_swizzle/bpermute).
+template <bool kMax>
+__device__ __forceinline__ float wave_allreduce(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    float y = __shfl_xor(x, off, 64);
+    x = kMax ? fmaxf(x, y) : x + y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ float readlane_f(float x, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace kvlr

@@ -1,0 +1,137 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+that include/kvlr.h declares, and rejects bad arguments on the host before
+any HIP call (so these calls are safe without a device)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import rank_compressed_kv_kvlr_amd as kv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvlr.h")
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"KVLR_API\s+[\w\s\*]+?\b(kvlr_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("kvlr_prefill_compress", "kvlr_append", "kvlr_decode_attn", "kvlr_cache_elems",
+              "kvlr_decode_workspace_bytes", "kvlr_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(kv.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_status_strings():
+    assert kv.status_string(0) == "ok"
+    for code in range(-7, 0):
+        assert kv.status_string(code) not in ("ok", "unknown status")
+    assert kv.status_string(-99) == "unknown status"
+
+
+def _desc(**kw):
+    base = dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, capacity=1000, r_k=64, r_v=32,
+                in_dtype=kv.BF16, latent_dtype=kv.BF16)
+    base.update(kw)
+    return kv.Desc(**base)
+
+
+def _ws(desc, split=0):
+    n = ctypes.c_size_t()
+    return kv.lib.kvlr_decode_workspace_bytes(desc.ptr, split, ctypes.byref(n)), n.value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_q_heads=7), -2), (dict(n_q_heads=2 * 17), -2), (dict(head_dim=100), -2), (dict(head_dim=512), -2),
+    (dict(capacity=0), -2), (dict(batch=0), -2), (dict(n_kv_heads=65, n_q_heads=65), -2),
+    (dict(r_k=8), -3), (dict(r_v=0), -3), (dict(r_k=144), -3), (dict(r_k=[16, 24]), -3),
+    (dict(head_dim=64, r_k=96), -3), (dict(latent_dtype=kv.F32, r_k=6), -3),
+    (dict(in_dtype=3), -4), (dict(latent_dtype=-1), -4),
+])
+def test_descriptor_validation(kw, code):
+    assert _ws(_desc(**kw))[0] == code
+
+
+def test_fp32_latents_allow_rank_multiple_of_four():
+    assert _ws(_desc(latent_dtype=kv.F32, r_k=12, r_v=4))[0] == 0
+
+
+def test_cache_elems_and_layout():
+    d = _desc(r_k=[16, 48], r_v=[32, 80], capacity=100)
+    nk, nv = kv.cache_elems(d)
+    assert nk == 2 * 100 * 64 and nv == 2 * 100 * 112
+    assert list(d.rank_offsets("v")) == [0, 32, 112]
+
+
+def test_workspace_and_plan():
+    d = _desc(capacity=32768)
+    ns, length = kv.decode_plan(d, 1024)
+    assert (ns, length) == (32, 1024)
+    rc, n = _ws(d, 1024)
+    assert rc == 0 and n == 2 * 8 * 32 * 36 * 4      # stride = round_up(32 + 2, 4)
+    assert kv.lib.kvlr_decode_workspace_bytes(d.ptr, 100, ctypes.byref(ctypes.c_size_t())) == -7
+    assert kv.lib.kvlr_decode_workspace_bytes(d.ptr, -64, ctypes.byref(ctypes.c_size_t())) == -7
+    ns, length = kv.decode_plan(d, 0)
+    assert length % 256 == 0 and ns * length >= 32768
+
+
+def test_null_pointers_rejected():
+    d = _desc()
+    assert kv.lib.kvlr_cache_elems(None, ctypes.byref(ctypes.c_size_t()), ctypes.byref(ctypes.c_size_t())) == -1
+    assert kv.lib.kvlr_decode_attn(d.ptr, None, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE, FAKE,
+                                   1 << 30, 0, None) == -1
+    assert kv.lib.kvlr_append(d.ptr, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None) == -1
+    assert kv.lib.kvlr_prefill_compress(d.ptr, None, FAKE, 0, 10, FAKE, FAKE, FAKE, FAKE, None) == -1
+
+
+def test_prefill_bounds_and_noop():
+    d = _desc(capacity=100)
+    # start + n_tok beyond capacity
+    assert kv.lib.kvlr_prefill_compress(d.ptr, FAKE, FAKE, 90, 11, FAKE, FAKE, FAKE, FAKE, None) == -2
+    assert kv.lib.kvlr_prefill_compress(d.ptr, FAKE, FAKE, -1, 5, FAKE, FAKE, FAKE, FAKE, None) == -7
+    # zero tokens: nothing to do, no launch, even with NULL buffers
+    assert kv.lib.kvlr_prefill_compress(d.ptr, None, None, 5, 0, None, None, None, None, None) == 0
+
+
+def test_decode_workspace_and_scale_checks():
+    d = _desc()
+    rc, need = _ws(d)
+    assert rc == 0
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE]
+    assert kv.lib.kvlr_decode_attn(d.ptr, *args, ctypes.c_float(0.1), FAKE, FAKE, need - 1, 0, None) == -5
+    assert kv.lib.kvlr_decode_attn(d.ptr, *args, ctypes.c_float(0.1), FAKE, None, need, 0, None) == -5
+    assert kv.lib.kvlr_decode_attn(d.ptr, *args, ctypes.c_float(float("nan")), FAKE, FAKE, need, 0, None) == -7
+    assert kv.lib.kvlr_decode_attn(d.ptr, *args, ctypes.c_float(float("inf")), FAKE, FAKE, need, 0, None) == -7
+    assert kv.lib.kvlr_decode_attn(d.ptr, *args, ctypes.c_float(0.1), FAKE, FAKE, need, 65, None) == -7
+
+
+def test_python_wrapper_raises_on_bad_desc():
+    with pytest.raises(kv.KvlrError) as e:
+        kv.cache_elems(_desc(n_q_heads=3))
+    assert e.value.code == -2
+
+
+def test_oracle_is_not_imported_by_the_product_path():
+    import sys
+    src = open(os.path.join(ROOT, "rank_compressed_kv_kvlr_amd", "__init__.py")).read()
+    assert "oracle" not in re.sub(r'""".*?"""', "", src, flags=re.S)
+    for f in os.listdir(os.path.join(ROOT, "rank_compressed_kv_kvlr_amd", "csrc")):
+        assert "oracle" not in open(os.path.join(ROOT, "rank_compressed_kv_kvlr_amd", "csrc", f)).read()
+    imports = re.compile(r"^\s*(?:import|from)\s+(\S+)", re.M)
+    for f in os.listdir(os.path.join(ROOT, "oracle")):
+        if f.endswith(".py"):
+            mods = imports.findall(open(os.path.join(ROOT, "oracle", f)).read())
+            assert not [m for m in mods if m.startswith(("rank_compressed_kv_kvlr_amd", "synth"))], (f, mods)
