@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark over a rank-compressed KV cache on one MI355X.
+
+Workload (default): one Llama-3-8B-shaped attention layer at decode, batch 8,
+32 query / 8 KV heads, head_dim 128, 32768 cached tokens per sequence,
+ranks r_k = r_v = 64 per KV head, bf16 latents (synthetic seeded inputs,
+4 key channels per head scaled x8). A step is one decode call: query
+projection, latent scores, online softmax, value mix, split merge and P_V^T
+back-projection for all 8 sequences, i.e. 8 new tokens.
+
+Inputs are resident in HBM before timing. Steps alternate between two
+independent cache replicas (1 GiB of latents) so that no step finds the
+previous step's bytes in the 256 MB last-level cache.
+
+Prints one JSON line with the throughput, the split kernel's roofline
+(algorithmic bytes per launch over its HIP-event duration, against the
+8 TB/s HBM peak) and the float64 oracle timed on a bounded sample on the
+host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_split_traffic.json")
+DECODE_SRC = os.path.join(ROOT, "rank_compressed_kv_kvlr_amd", "csrc", "decode.hip")
+METRIC = "compressed-KV decode attn: tokens/sec + achieved HBM GB/s (% of peak), 1 GPU"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--split-tokens", type=int, default=0, help="tokens per split (0: library choice)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle CPU time")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-compression measurement")
+    ap.add_argument("--traffic-reference", action="store_true",
+                    help="also run a plain 1 GiB device copy (a known-size reference for HBM traffic counters)")
+    return ap.parse_args()
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic():
+    """HBM bytes per launch from rocprofv3 counters, valid only for the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("decode_src_sha256_16") != source_hash(DECODE_SRC):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, seconds):
+    """The float64 oracle's latent-order decode on a bounded sample of the workload."""
+    import numpy as np
+    import oracle
+    from synth import host
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [(i.get("internal_api"), i.get("num_threads")) for i in threadpool_info()]
+    except Exception:  # pragma: no cover
+        blas = []
+    threads = max([n for _, n in blas if n] or [1])
+    b, h = 0, 0
+    T, G = cfg.T, cfg.G
+    PK, PV = host.bases(cfg, 0)
+    P32K, P32V = [p.astype(np.float32).astype(np.float64) for p in PK], [p.astype(np.float32).astype(np.float64) for p in PV]
+    stats = host.kv_stats(cfg, 0)
+    K = host.decode_to_f64(host.kv_rows(cfg, 0, "k", b, 0, T, heads=[h], stats=stats), cfg.in_dtype)[:, 0]
+    V = host.decode_to_f64(host.kv_rows(cfg, 0, "v", b, 0, T, heads=[h], stats=stats), cfg.in_dtype)[:, 0]
+    lat_k = oracle.bf16_round(oracle.compress(K, P32K[h]))
+    lat_v = oracle.bf16_round(oracle.compress(V, P32V[h]))
+    q = host.queries(cfg, 0, 0)[b, h * G:(h + 1) * G].astype(np.float64)
+    scale = 1 / np.sqrt(cfg.d)
+    oracle.decode_head_latent(q, lat_k, lat_v, P32K[h], P32V[h], scale)   # warm-up
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.decode_head_latent(q, lat_k, lat_v, P32K[h], P32V[h], scale)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    per_head = el / reps
+    # definition order (reconstruct K~, V~ then attend), once, for context
+    t1 = time.perf_counter()
+    oracle.decode_head_reconstructed(q, K, V, P32K[h], P32V[h], scale)
+    per_head_def = time.perf_counter() - t1
+    per_token = per_head * cfg.Hkv           # one token = one batch row over all KV heads
+    return {
+        "value": 1.0 / per_token, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+        "sample": (f"oracle latent-order decode (float64 numpy) of batch row 0, KV head 0 "
+                   f"({G} query heads) over {T} bf16-rounded latents, {reps} repetitions in {el:.1f} s; "
+                   f"scaled x{cfg.Hkv} KV heads to one token"),
+        "definition_order_tokens_per_s": 1.0 / (per_head_def * cfg.Hkv),
+        "blas": blas,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import rank_compressed_kv_kvlr_amd as kv
+    from synth import CONFIGS, host
+    from synth.device import KVGenerator
+
+    cfg = CONFIGS[1]
+    B, T, Hkv, d = cfg.B, cfg.T, cfg.Hkv, cfg.d
+    rk, rv = host.ranks(cfg)
+    PK, PV = host.bases(cfg)
+    desc = kv.Desc(B, cfg.Hq, Hkv, d, cfg.capacity, rk, rv, kv.BF16, kv.BF16)
+    pk, pv = kv.pack_bases(PK), kv.pack_bases(PV)
+    gen = KVGenerator(cfg, 0)
+    print(f"[bench] building 2 cache replicas of {cfg.name}", file=sys.stderr, flush=True)
+
+    replicas = []
+    prefill = None
+    for rep in range(2):
+        lat_k, lat_v = kv.alloc_cache(desc)
+        K = gen.make("k", B, T)
+        V = gen.make("v", B, T)
+        kv.prefill_compress(desc, K, V, 0, pk, pv, lat_k, lat_v)
+        if rep == 0 and not args.no_prefill:
+            # prefill compression of all 32768 tokens (both K and V), timed with HIP events
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            times = []
+            for _ in range(5):
+                ev[0].record()
+                kv.prefill_compress(desc, K, V, 0, pk, pv, lat_k, lat_v)
+                ev[1].record()
+                torch.cuda.synchronize()
+                times.append(ev[0].elapsed_time(ev[1]) * 1e-3)
+            t = float(np.median(times))
+            nbytes = B * T * Hkv * (2 * d * 2 + (int(rk[0]) + int(rv[0])) * 2)
+            flops = 2.0 * B * T * Hkv * d * (int(rk[0]) + int(rv[0]))
+            prefill = {"tokens": B * T, "us": t * 1e6, "GBps": nbytes / t / 1e9,
+                       "hbm_frac": nbytes / t / 1e9 / HBM_PEAK_GBPS,
+                       "mfma_util": flops / t / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                       "note": "MFMA utilisation counts useful flops; the kernel issues 2x (basis high/low parts)"}
+        del K, V
+        replicas.append((lat_k, lat_v))
+    torch.cuda.synchronize()
+
+    q = torch.from_numpy(host.queries(cfg, 0, 0)).cuda()
+    lens = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    split = args.split_tokens
+    ws = kv.alloc_workspace(desc, split)
+    out = torch.empty((B, cfg.Hq, d), dtype=torch.float32, device="cuda")
+    n_splits, split_len = kv.decode_plan(desc, split)
+
+    def step(k, evs=None):
+        # one kvlr_decode_attn call = one kernel launch (split workgroups merge in the last arrival)
+        lk, lv = replicas[k % 2]
+        if evs is not None:
+            evs[0].record()
+        kv.decode_attn(desc, q, pk, pv, lk, lv, lens, out=out, workspace=ws, split_tokens=split)
+        if evs is not None:
+            evs[1].record()
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(k, evs[k])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    if args.traffic_reference:
+        from synth.device import copy as device_copy
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+        dst = torch.empty_like(src)
+        src.fill_(1.0)
+        for _ in range(3):
+            device_copy(src, dst)
+        torch.cuda.synchronize()
+        del src, dst
+
+    split_us = np.array([e[0].elapsed_time(e[1]) * 1e3 for e in evs])
+    alg_bytes = B * T * int((rk + rv).sum()) * 2     # latent bytes read per launch
+    split_mean_s = float(split_us.mean()) * 1e-6
+    achieved = alg_bytes / split_mean_s / 1e9
+    ms_per_step = elapsed / args.steps * 1e3
+    tokens_per_s = B * args.steps / elapsed
+    traffic = load_traffic()
+
+    result = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": B, "cached_tokens": T, "q_heads": cfg.Hq, "kv_heads": Hkv,
+                   "head_dim": d, "r_k": int(rk[0]), "r_v": int(rv[0]), "latents": "bf16",
+                   "splits": n_splits, "split_tokens": split_len},
+        "step_hbm_GBps": alg_bytes / (elapsed / args.steps) / 1e9,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "kernel": "decode_split_bf16 (kvlr_decode_attn, merge fused)", "bytes_per_launch": alg_bytes,
+                     "launch_us_mean": float(split_us.mean()), "launch_us_p10": float(np.percentile(split_us, 10)),
+                     "launch_us_p90": float(np.percentile(split_us, 90))},
+    }
+    if prefill is not None:
+        result["prefill"] = prefill
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -108,7 +108,8 @@ KVLR_API int kvlr_cache_elems(const kvlr_desc* desc, size_t* k_elems, size_t* v_
 
 /* Bytes of decode workspace that kvlr_decode_attn needs for this
  * descriptor and split length (split_tokens as in kvlr_decode_attn; 0 picks
- * the library's choice, the same one kvlr_decode_attn makes for 0). */
+ * the library's choice, the same one kvlr_decode_attn makes for 0): one fp32
+ * record [B][Hq][n_splits][round_up(max_h r_v[h] + 2, 4)] per split. */
 KVLR_API int kvlr_decode_workspace_bytes(const kvlr_desc* desc, int32_t split_tokens, size_t* bytes);
 
 /* Splits that kvlr_decode_attn uses per (batch row, KV head) for
@@ -161,8 +162,8 @@ KVLR_API int kvlr_append(const kvlr_desc* desc, const void* k_new, const void* v
  *             ordered on one stream
  *   split_tokens 0 for the library's choice, or a multiple of 64: tokens
  *             per split of the sequence (every split yields a partial
- *             softmax state; a second kernel merges them and back-projects
- *             with P_V^T)
+ *             softmax state; a second kernel merges the states and
+ *             back-projects with P_V^T)
  * Scores and the softmax are computed in fp32; bf16 latents are read as
  * stored and multiplied in fp32 (the key side on MFMA with the query split
  * into a high and a low bf16 part). */
@@ -170,6 +171,28 @@ KVLR_API int kvlr_decode_attn(const kvlr_desc* desc, const float* q, const float
                               const void* lat_k, const void* lat_v, const int32_t* seq_lens, float scale,
                               float* out, void* workspace, size_t workspace_bytes, int32_t split_tokens,
                               void* stream);
+
+/* The two stages of kvlr_decode_attn, for callers that schedule them
+ * separately (e.g. to time or overlap them). kvlr_decode_attn(...) is
+ * exactly kvlr_decode_partials(...) followed by kvlr_decode_combine(...) on
+ * the same stream with the same workspace and split_tokens.
+ *
+ * kvlr_decode_partials: query projection q~ = q P_K, latent scores, online
+ * softmax and the p-weighted sum of value latents for every split of every
+ * (batch row, query head). Writes one record (running max in log2 units,
+ * softmax denominator, unnormalised latent sum of r_v(h) channels) per
+ * split into `workspace`; arguments as in kvlr_decode_attn. */
+KVLR_API int kvlr_decode_partials(const kvlr_desc* desc, const float* q, const float* P_K, const void* lat_k,
+                                  const void* lat_v, const int32_t* seq_lens, float scale, void* workspace,
+                                  size_t workspace_bytes, int32_t split_tokens, void* stream);
+
+/* kvlr_decode_combine: log-sum-exp merge of the split records written by
+ * kvlr_decode_partials with the same desc and split_tokens, normalisation,
+ * and back-projection o = o_lat P_V[h]^T (the value reconstruction of
+ * "Mecanismo Central" item 5, applied once per query head). Writes
+ * out [B][Hq][d] fp32; rows with an empty cache are zero. */
+KVLR_API int kvlr_decode_combine(const kvlr_desc* desc, const float* P_V, const void* workspace,
+                                 size_t workspace_bytes, int32_t split_tokens, float* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -29,7 +29,7 @@ import numpy as np
 __all__ = [
     "KvlrError", "Desc", "F32", "BF16", "lib", "version", "status_string",
     "cache_elems", "decode_workspace_bytes", "decode_plan",
-    "prefill_compress", "append", "decode_attn",
+    "prefill_compress", "append", "decode_attn", "decode_partials", "decode_combine",
     "alloc_cache", "alloc_workspace", "pack_bases", "head_view",
 ]
 
@@ -39,6 +39,12 @@ LIB_PATH = os.path.join(_HERE, "libkvlr.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m rank_compressed_kv_kvlr_amd.build`")
+
+# torch ships its own HIP runtime (soname libamdhip64.so.7). Loading it before
+# libkvlr.so lets the library bind to that same runtime; loading libkvlr.so
+# first would map the system runtime as well, and two HIP runtimes in one
+# process do not share devices, streams or allocations.
+import torch  # noqa: E402,F401
 
 
 class _CDesc(ctypes.Structure):
@@ -63,8 +69,10 @@ lib.kvlr_prefill_compress.argtypes = [_D, _P, _P, ctypes.c_int32, ctypes.c_int32
 lib.kvlr_append.argtypes = [_D, _P, _P, _P, _P, _P, _P, _P, _P]
 lib.kvlr_decode_attn.argtypes = [_D, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, ctypes.c_size_t,
                                  ctypes.c_int32, _P]
+lib.kvlr_decode_partials.argtypes = [_D, _P, _P, _P, _P, _P, ctypes.c_float, _P, ctypes.c_size_t, ctypes.c_int32, _P]
+lib.kvlr_decode_combine.argtypes = [_D, _P, _P, ctypes.c_size_t, ctypes.c_int32, _P, _P]
 for _f in ("kvlr_cache_elems", "kvlr_decode_workspace_bytes", "kvlr_decode_plan", "kvlr_prefill_compress",
-           "kvlr_append", "kvlr_decode_attn"):
+           "kvlr_append", "kvlr_decode_attn", "kvlr_decode_partials", "kvlr_decode_combine"):
     getattr(lib, _f).restype = ctypes.c_int
 
 
@@ -175,7 +183,7 @@ def alloc_cache(desc: Desc, device="cuda"):
 def alloc_workspace(desc: Desc, split_tokens: int = 0, device="cuda"):
     torch = _torch()
     n = decode_workspace_bytes(desc, split_tokens)
-    return torch.empty(max(n, 4) // 4, dtype=torch.float32, device=device)
+    return torch.empty((n + 3) // 4, dtype=torch.float32, device=device)
 
 
 def pack_bases(bases: Sequence, device="cuda"):
@@ -253,4 +261,32 @@ def decode_attn(desc: Desc, q, P_K, P_V, lat_k, lat_v, seq_lens, scale: Optional
             _need(out, "out", torch.float32, nq), _need(workspace, "workspace", workspace.dtype),
             ctypes.c_size_t(ws_bytes), split_tokens)
     _check(lib.kvlr_decode_attn(desc.ptr, *args, _stream()), "kvlr_decode_attn")
+    return out
+
+
+def decode_partials(desc: Desc, q, P_K, lat_k, lat_v, seq_lens, workspace, scale: Optional[float] = None,
+                    split_tokens: int = 0):
+    """First stage of decode_attn: per-split softmax records into `workspace`."""
+    torch = _torch()
+    if scale is None:
+        scale = 1.0 / math.sqrt(desc.head_dim)
+    nk, nv = cache_elems(desc)
+    lad = _dtype_of(desc.latent_dtype)
+    args = (_need(q, "q", torch.float32, desc.batch * desc.n_q_heads * desc.head_dim),
+            _need(P_K, "P_K", torch.float32, _basis_numel(desc, "k")),
+            _need(lat_k, "lat_k", lad, nk), _need(lat_v, "lat_v", lad, nv),
+            _need(seq_lens, "seq_lens", torch.int32, desc.batch), ctypes.c_float(scale),
+            _need(workspace, "workspace", workspace.dtype),
+            ctypes.c_size_t(workspace.numel() * workspace.element_size()), split_tokens)
+    _check(lib.kvlr_decode_partials(desc.ptr, *args, _stream()), "kvlr_decode_partials")
+
+
+def decode_combine(desc: Desc, P_V, workspace, out, split_tokens: int = 0):
+    """Second stage of decode_attn: merge split records and back-project by P_V^T into out [B][Hq][d]."""
+    torch = _torch()
+    args = (_need(P_V, "P_V", torch.float32, _basis_numel(desc, "v")),
+            _need(workspace, "workspace", workspace.dtype),
+            ctypes.c_size_t(workspace.numel() * workspace.element_size()), split_tokens,
+            _need(out, "out", torch.float32, desc.batch * desc.n_q_heads * desc.head_dim))
+    _check(lib.kvlr_decode_combine(desc.ptr, *args, _stream()), "kvlr_decode_combine")
     return out

@@ -13,7 +13,15 @@ using kvlr::HeadTable;
 
 constexpr int kVersion = 10000;   // 1.0.0
 constexpr int kSplitGranule = kvlr::kTile;
-constexpr long long kTargetWorkgroups = 2048;
+constexpr int kComputeUnits = 256;   // MI355X
+
+// Resident split workgroups per CU for each kernel variant (4 waves each;
+// limited by the variant's register count on gfx950). The default split
+// length gives one such round of workgroups over the whole device.
+int resident_wgs_per_cu(int latent_dtype, int rank_bound) {
+  if (latent_dtype == KVLR_BF16) return rank_bound <= 32 ? 3 : rank_bound <= 64 ? 2 : 1;
+  return rank_bound <= 64 ? 5 : 4;
+}
 
 bool valid_dtype(int t) { return t == KVLR_F32 || t == KVLR_BF16; }
 
@@ -52,6 +60,8 @@ int check_desc(const kvlr_desc* d, HeadTable* ht, int* Rk, int* Rv, int* rank_bo
 }
 
 int plan_split(const kvlr_desc* d, int32_t split_tokens, int* n_splits, int* split_len) {
+  int rank_bound = 0;
+  check_desc(d, nullptr, nullptr, nullptr, &rank_bound);   // callers validated the descriptor already
   const int G = d->n_q_heads / d->n_kv_heads;
   const int groups = (G + kvlr::kHeadsPerWg - 1) / kvlr::kHeadsPerWg;
   int len;
@@ -63,7 +73,8 @@ int plan_split(const kvlr_desc* d, int32_t split_tokens, int* n_splits, int* spl
     long long want = env ? atoll(env) : 0;
     if (want <= 0 || want % kSplitGranule) {
       const long long units = (long long)d->batch * d->n_kv_heads * groups;
-      want = (units * d->capacity + kTargetWorkgroups - 1) / kTargetWorkgroups;
+      const long long slots = (long long)kComputeUnits * resident_wgs_per_cu(d->latent_dtype, rank_bound);
+      want = (units * d->capacity + slots - 1) / slots;
       const long long g4 = (long long)kSplitGranule * kvlr::kWaves;
       want = (want + g4 - 1) / g4 * g4;   // whole tiles for every wave
       if (want < g4) want = g4;
@@ -190,59 +201,105 @@ KVLR_API int kvlr_append(const kvlr_desc* desc, const void* k_new, const void* v
   return hip_status(kvlr::launch_append(p, static_cast<hipStream_t>(stream)));
 }
 
+}  // extern "C"
+
+namespace {
+
+// Shared checks of the decode stages; fills the kernel parameter blocks.
+int prepare_decode(const kvlr_desc* desc, const float* q, const float* P_K, const void* lat_k, const void* lat_v,
+                   const int32_t* seq_lens, float scale, const float* P_V, float* out, bool need_partials,
+                   bool need_combine, void* workspace, size_t workspace_bytes, int32_t split_tokens,
+                   kvlr::DecodeParams* p, kvlr::MergeParams* m, int* rank_bound) {
+  int rc = check_desc(desc, &p->ht, &p->Rk, &p->Rv, rank_bound);
+  p->qt_in = nullptr;
+  p->qt_stride = 0;
+  if (rc) return rc;
+  if (need_partials && (!q || !P_K || !lat_k || !lat_v || !seq_lens)) return KVLR_ERR_NULL;
+  if (need_combine && (!P_V || !out)) return KVLR_ERR_NULL;
+  if (need_partials && !isfinite(scale)) return KVLR_ERR_ARG;
+  int ns = 0, len = 0;
+  rc = plan_split(desc, split_tokens, &ns, &len);
+  if (rc) return rc;
+  const int stride = ws_stride_of(p->ht, desc->n_kv_heads);
+  const size_t need = (size_t)desc->batch * desc->n_q_heads * ns * stride * sizeof(float);
+  if (!workspace || workspace_bytes < need) return KVLR_ERR_WORKSPACE;
+
+  const int G = desc->n_q_heads / desc->n_kv_heads;
+  p->q = q;
+  p->pk = P_K;
+  p->lat_k = lat_k;
+  p->lat_v = lat_v;
+  p->seq_lens = seq_lens;
+  p->ws = static_cast<float*>(workspace);
+  p->B = desc->batch;
+  p->Hq = desc->n_q_heads;
+  p->Hkv = desc->n_kv_heads;
+  p->G = G;
+  p->d = desc->head_dim;
+  p->cap = desc->capacity;
+  p->split_len = len;
+  p->n_splits = ns;
+  p->ws_stride = stride;
+  p->n_head_groups = (G + kvlr::kHeadsPerWg - 1) / kvlr::kHeadsPerWg;
+  p->scale_log2 = scale * 1.4426950408889634f;
+
+  m->ws = p->ws;
+  m->pv = P_V;
+  m->out = out;
+  m->B = p->B;
+  m->Hq = p->Hq;
+  m->Hkv = p->Hkv;
+  m->G = G;
+  m->d = p->d;
+  m->n_splits = ns;
+  m->ws_stride = stride;
+  m->n_head_groups = p->n_head_groups;
+  m->ht = p->ht;
+  return KVLR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+KVLR_API int kvlr_decode_partials(const kvlr_desc* desc, const float* q, const float* P_K, const void* lat_k,
+                                  const void* lat_v, const int32_t* seq_lens, float scale, void* workspace,
+                                  size_t workspace_bytes, int32_t split_tokens, void* stream) {
+  kvlr::DecodeParams p;
+  kvlr::MergeParams m;
+  int rank_bound = 0;
+  const int rc = prepare_decode(desc, q, P_K, lat_k, lat_v, seq_lens, scale, nullptr, nullptr, true, false,
+                                workspace, workspace_bytes, split_tokens, &p, &m, &rank_bound);
+  if (rc) return rc;
+  return hip_status(kvlr::launch_decode(p, desc->latent_dtype == KVLR_BF16, rank_bound,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+KVLR_API int kvlr_decode_combine(const kvlr_desc* desc, const float* P_V, const void* workspace,
+                                 size_t workspace_bytes, int32_t split_tokens, float* out, void* stream) {
+  kvlr::DecodeParams p;
+  kvlr::MergeParams m;
+  int rank_bound = 0;
+  const int rc = prepare_decode(desc, nullptr, nullptr, nullptr, nullptr, nullptr, 1.f, P_V, out, false, true,
+                                const_cast<void*>(workspace), workspace_bytes, split_tokens, &p, &m, &rank_bound);
+  if (rc) return rc;
+  return hip_status(kvlr::launch_merge(m, rank_bound, static_cast<hipStream_t>(stream)));
+}
+
 KVLR_API int kvlr_decode_attn(const kvlr_desc* desc, const float* q, const float* P_K, const float* P_V,
                               const void* lat_k, const void* lat_v, const int32_t* seq_lens, float scale,
                               float* out, void* workspace, size_t workspace_bytes, int32_t split_tokens,
                               void* stream) {
   kvlr::DecodeParams p;
-  int rank_bound = 0;
-  int rc = check_desc(desc, &p.ht, &p.Rk, &p.Rv, &rank_bound);
-  if (rc) return rc;
-  if (!q || !P_K || !P_V || !lat_k || !lat_v || !seq_lens || !out) return KVLR_ERR_NULL;
-  if (!isfinite(scale)) return KVLR_ERR_ARG;
-  int ns = 0, len = 0;
-  rc = plan_split(desc, split_tokens, &ns, &len);
-  if (rc) return rc;
-  const int stride = ws_stride_of(p.ht, desc->n_kv_heads);
-  const size_t need = (size_t)desc->batch * desc->n_q_heads * ns * stride * sizeof(float);
-  if (!workspace || workspace_bytes < need) return KVLR_ERR_WORKSPACE;
-
-  const int G = desc->n_q_heads / desc->n_kv_heads;
-  p.q = q;
-  p.pk = P_K;
-  p.lat_k = lat_k;
-  p.lat_v = lat_v;
-  p.seq_lens = seq_lens;
-  p.ws = static_cast<float*>(workspace);
-  p.B = desc->batch;
-  p.Hq = desc->n_q_heads;
-  p.Hkv = desc->n_kv_heads;
-  p.G = G;
-  p.d = desc->head_dim;
-  p.cap = desc->capacity;
-  p.split_len = len;
-  p.n_splits = ns;
-  p.ws_stride = stride;
-  p.n_head_groups = (G + kvlr::kHeadsPerWg - 1) / kvlr::kHeadsPerWg;
-  p.scale_log2 = scale * 1.4426950408889634f;
-
   kvlr::MergeParams m;
-  m.ws = p.ws;
-  m.pv = P_V;
-  m.out = out;
-  m.B = p.B;
-  m.Hq = p.Hq;
-  m.Hkv = p.Hkv;
-  m.G = G;
-  m.d = p.d;
-  m.n_splits = ns;
-  m.ws_stride = stride;
-  m.ht = p.ht;
-
+  int rank_bound = 0;
+  int rc = prepare_decode(desc, q, P_K, lat_k, lat_v, seq_lens, scale, P_V, out, true, true, workspace,
+                          workspace_bytes, split_tokens, &p, &m, &rank_bound);
+  if (rc) return rc;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   rc = hip_status(kvlr::launch_decode(p, desc->latent_dtype == KVLR_BF16, rank_bound, s));
   if (rc) return rc;
-  return hip_status(kvlr::launch_merge(m, s));
+  return hip_status(kvlr::launch_merge(m, rank_bound, s));
 }
 
 }  // extern "C"

@@ -46,25 +46,89 @@ constexpr int value_iters_bound(int rb) {
 // ---------------------------------------------------------------------------
 // shared prologue: q~ = (q P_K) * scale * log2(e) for the workgroup's heads
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void project_query(const DecodeParams& p, int b, int h, int hq0, int gpw,
-                                              int rk, float* q_lds, float* qt_lds, int qt_stride) {
-  const int tid = threadIdx.x;
+// The four waves split the d rows of P_K[h]; each lane issues all of its
+// 16-byte basis loads at once (one memory round trip), forms partial dot
+// products for the 4 heads, and partials are summed across lanes with
+// shuffles and across waves through LDS. With a caller-given q~ (bases
+// folded into the query projection) the loads are of q~ itself.
+//   q_lds [4][d], red [4 waves][4 heads][RB], qt_lds [4][RB]
+template <int RB>
+__device__ __forceinline__ void project_query(const DecodeParams& p, int b, int h, int hq0, int gpw, int rk,
+                                              float* q_lds, float* red, float* qt_lds) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int d = p.d;
-  for (int idx = tid; idx < gpw * d; idx += blockDim.x) {
+  if (p.qt_in) {   // folded mode: q~ [B][Hq][qt_stride] given in latent space
+    for (int idx = tid; idx < kHeadsPerWg * RB; idx += blockDim.x) {
+      const int g = idx / RB, j = idx - g * RB;
+      qt_lds[idx] = (g < gpw && j < rk) ? p.qt_in[((size_t)b * p.Hq + hq0 + g) * p.qt_stride + j] * p.scale_log2 : 0.f;
+    }
+    __syncthreads();
+    return;
+  }
+  for (int idx = tid; idx < kHeadsPerWg * d; idx += blockDim.x) {
     const int g = idx / d, i = idx - g * d;
-    q_lds[g * d + i] = p.q[((size_t)b * p.Hq + hq0 + g) * d + i];
+    q_lds[idx] = (g < gpw) ? p.q[((size_t)b * p.Hq + hq0 + g) * d + i] : 0.f;
   }
   __syncthreads();
+  constexpr int NH = (RB + 63) / 64;      // 64-column halves of P
+  constexpr int RPL = 16;                 // rows per lane bound: d / 16 <= 16
   const float* P = p.pk + (size_t)d * p.ht.rk_pre[h];
-  for (int idx = tid; idx < kHeadsPerWg * qt_stride; idx += blockDim.x) {
-    const int g = idx / qt_stride, j = idx - g * qt_stride;
-    float acc = 0.f;
-    if (g < gpw && j < rk) {
-      const float* qg = q_lds + g * d;
-      for (int i = 0; i < d; ++i) acc = fmaf(qg[i], P[(size_t)i * rk + j], acc);
-      acc *= p.scale_log2;
+  const int isub = lane >> 4, m = lane & 15;
+  const int rows_per_wave = d >> 2, rpl = d >> 4;
+#pragma unroll
+  for (int hf = 0; hf < NH; ++hf) {
+    const int col = 64 * hf + 4 * m;
+    const bool cvalid = col < rk;
+    float4 pr[RPL];
+#pragma unroll
+    for (int e = 0; e < RPL; ++e) {
+      const int i = wave * rows_per_wave + isub + 4 * e;
+      pr[e] = (e < rpl && cvalid) ? *reinterpret_cast<const float4*>(P + (size_t)i * rk + col)
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    qt_lds[idx] = acc;   // zero rows for heads beyond gpw and channels beyond rk
+    float part[4][4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) part[g][jj] = 0.f;
+#pragma unroll
+    for (int e = 0; e < RPL; ++e) {
+      if (e < rpl) {
+        const int i = wave * rows_per_wave + isub + 4 * e;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float qv = q_lds[g * d + i];
+          part[g][0] = fmaf(qv, pr[e].x, part[g][0]);
+          part[g][1] = fmaf(qv, pr[e].y, part[g][1]);
+          part[g][2] = fmaf(qv, pr[e].z, part[g][2]);
+          part[g][3] = fmaf(qv, pr[e].w, part[g][3]);
+        }
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        float v = part[g][jj];
+        v += __shfl_xor(v, 16, 64);
+        v += __shfl_xor(v, 32, 64);
+        part[g][jj] = v;
+      }
+    if (isub == 0 && col < RB) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<float4*>(red + (wave * 4 + g) * RB + col) =
+            make_float4(part[g][0], part[g][1], part[g][2], part[g][3]);
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < kHeadsPerWg * RB; idx += blockDim.x) {
+    const int g = idx / RB, j = idx - g * RB;
+    float v = 0.f;
+    if (g < gpw && j < rk)
+      v = (red[(0 * 4 + g) * RB + j] + red[(1 * 4 + g) * RB + j] + red[(2 * 4 + g) * RB + j] +
+           red[(3 * 4 + g) * RB + j]) * p.scale_log2;
+    qt_lds[idx] = v;   // zero rows for heads beyond gpw and channels beyond rk
   }
   __syncthreads();
 }
@@ -140,7 +204,8 @@ __global__ __launch_bounds__(256) void decode_split_bf16(DecodeParams p) {
   // ---- prologue: q~ into LDS, then MFMA A operands (hi/lo) into registers
   float* q_lds = smem;                          // [4][d]  (d <= 256)
   float* qt_lds = smem + kHeadsPerWg * 256;     // [4][QTS]
-  project_query(p, b, h, hq0, gpw, rk, q_lds, qt_lds, QTS);
+  float* qred = qt_lds + kHeadsPerWg * QTS;     // [4 waves][4][QTS]
+  project_query<RB>(p, b, h, hq0, gpw, rk, q_lds, qred, qt_lds);
 
   const int np = rk >> 5;           // full 32-channel pairs
   const int tail = (rk >> 4) & 1;   // one trailing 16-channel block
@@ -190,9 +255,9 @@ __global__ __launch_bounds__(256) void decode_split_bf16(DecodeParams p) {
     for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
   }
 
-  uint4 kreg[4][NP];
-  uint2 ktail[4];
-  uint4 vreg[NIT];
+  u32x4_t kreg[4][NP];
+  u32x2_t ktail[4];
+  u32x4_t vreg[NIT];
 
   auto load_k = [&](int t0) {
 #pragma unroll
@@ -201,8 +266,8 @@ __global__ __launch_bounds__(256) void decode_split_bf16(DecodeParams p) {
       const uint16_t* row = Kb + (size_t)t * rk;
 #pragma unroll
       for (int pp = 0; pp < NP; ++pp)
-        if (pp < np) kreg[blk][pp] = *reinterpret_cast<const uint4*>(row + 32 * pp + 8 * q4);
-      if (tail) ktail[blk] = *reinterpret_cast<const uint2*>(row + 32 * np + 4 * q4);
+        if (pp < np) kreg[blk][pp] = load_stream16(row + 32 * pp + 8 * q4);
+      if (tail) ktail[blk] = load_stream8(row + 32 * np + 4 * q4);
     }
   };
   auto load_v = [&](int t0) {
@@ -211,7 +276,7 @@ __global__ __launch_bounds__(256) void decode_split_bf16(DecodeParams p) {
       if (it < n_it) {
         const int r = it * rpi + ro;
         const int t = min(t0 + min(r, 63), t_end - 1);
-        vreg[it] = *reinterpret_cast<const uint4*>(Vb + (size_t)t * rv + 8 * cch);
+        vreg[it] = load_stream16(Vb + (size_t)t * rv + 8 * cch);
       }
     }
   };
@@ -297,7 +362,7 @@ __global__ __launch_bounds__(256) void decode_split_bf16(DecodeParams p) {
         const int r = it * rpi + ro;
         if (v_active && r < 64) {
           const float4 pw = *reinterpret_cast<const float4*>(p_lds + r * 4);
-          const uint4 w = vreg[it];
+          const u32x4_t w = vreg[it];
           const float v[8] = {bf16lo_to_f32(w.x), bf16hi_to_f32(w.x), bf16lo_to_f32(w.y), bf16hi_to_f32(w.y),
                               bf16lo_to_f32(w.z), bf16hi_to_f32(w.z), bf16lo_to_f32(w.w), bf16hi_to_f32(w.w)};
 #pragma unroll
@@ -377,7 +442,7 @@ __global__ __launch_bounds__(256) void decode_split_f32(DecodeParams p) {
   float* qt_lds = q_lds + kHeadsPerWg * 256;          // [4][QTS]
   float* wm = qt_lds + kHeadsPerWg * QTS;             // [wave][head]
   float* wl = wm + 16;
-  project_query(p, b, h, hq0, gpw, rk, q_lds, qt_lds, QTS);
+  project_query<RB>(p, b, h, hq0, gpw, rk, q_lds, red, qt_lds);
 
   const float* Kb = static_cast<const float*>(p.lat_k) + (size_t)p.cap * ((size_t)b * p.Rk + p.ht.rk_pre[h]);
   const float* Vb = static_cast<const float*>(p.lat_v) + (size_t)p.cap * ((size_t)b * p.Rv + p.ht.rv_pre[h]);
@@ -474,61 +539,128 @@ __global__ __launch_bounds__(256) void decode_split_f32(DecodeParams p) {
 // ---------------------------------------------------------------------------
 // merge of split records and back-projection by P_V^T
 // ---------------------------------------------------------------------------
+// One workgroup per (KV head, group of <= 4 query heads, batch row): the
+// group shares its P_V[h] rows. The group's split records and the rows of
+// P_V[h] are staged in LDS with all loads issued at once, so the kernel
+// costs about one memory round trip. Records are combined with log-sum-exp
+// weights exp2(m_s - M); the normalised latent output is back-projected,
+// o[dd] = sum_j o_lat[j] P_V[dd][j], one output channel dd per thread.
 constexpr int kMergeThreads = 256;
-constexpr int kMergeChunk = 1024;
+constexpr int kMergeRecLds = 8192;    // floats of staged records (32 KiB)
+constexpr int kMergePLds = 16384;     // floats of staged basis rows (64 KiB)
 
+template <int RB>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge(MergeParams p) {
-  __shared__ float f_lds[kMergeChunk];
-  __shared__ float olat[kMaxRank];
-  __shared__ float red[kMergeThreads / 64];
-  const int i = blockIdx.x, b = blockIdx.y;
-  const int h = i / p.G;
+  __shared__ __attribute__((aligned(16))) float rec_lds[kMergeRecLds];
+  __shared__ __attribute__((aligned(16))) float p_lds[kMergePLds];
+  __shared__ __attribute__((aligned(16))) float olat[RB][kHeadsPerWg];   // head-minor
+  __shared__ float m_red[kHeadsPerWg][4];
+  const int h = blockIdx.x / p.n_head_groups;
+  const int hg = blockIdx.x - h * p.n_head_groups;
+  const int b = blockIdx.y;
+  const int hq0 = h * p.G + hg * kHeadsPerWg;
+  const int gpw = min(kHeadsPerWg, p.G - hg * kHeadsPerWg);
   const int rv = p.ht.rv[h];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const float* recs = p.ws + ((size_t)b * p.Hq + i) * p.n_splits * p.ws_stride;
+  const int ns = p.n_splits, stride = p.ws_stride, d = p.d;
+  const size_t head_stride = (size_t)ns * stride;
+  const float* recs = p.ws + ((size_t)b * p.Hq + hq0) * head_stride;
+  const int chunk = kMergeRecLds / (kHeadsPerWg * stride);   // splits staged per pass (>= 15)
+  const float* P = p.pv + (size_t)d * p.ht.rv_pre[h];
+  const int pst = rv + 4;                                    // padded LDS row stride of P_V
+  const int p_rows = min(d, kMergePLds / pst);                // rows staged per pass
 
-  // global max of the split maxima
-  float M = kNegInf;
-  for (int s = tid; s < p.n_splits; s += kMergeThreads) M = fmaxf(M, recs[(size_t)s * p.ws_stride]);
-  M = wave_allreduce<true>(M);
-  if (lane == 0) red[wave] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-
-  float* outp = p.out + ((size_t)b * p.Hq + i) * p.d;
-  if (M == kNegInf) {   // empty sequence
-    for (int dd = tid; dd < p.d; dd += kMergeThreads) outp[dd] = 0.f;
-    return;
-  }
-  float L = 0.f, o = 0.f;   // thread j < rv accumulates channel j
-  for (int s0 = 0; s0 < p.n_splits; s0 += kMergeChunk) {
-    const int ns = min(kMergeChunk, p.n_splits - s0);
-    for (int s = tid; s < ns; s += kMergeThreads) {
-      const float* r = recs + (size_t)(s0 + s) * p.ws_stride;
-      f_lds[s] = fast_exp2(r[0] - M);   // empty split: exp2(-inf) = 0
+  auto stage_records = [&](int s0, int nc) {
+    const int per_head4 = nc * stride / 4;   // stride is a multiple of 4
+    for (int i = tid; i < gpw * per_head4; i += kMergeThreads) {
+      const int g = i / per_head4, k4 = i - g * per_head4;
+      *reinterpret_cast<float4*>(rec_lds + (size_t)g * chunk * stride + 4 * k4) =
+          *reinterpret_cast<const float4*>(recs + g * head_stride + (size_t)s0 * stride + 4 * k4);
     }
-    __syncthreads();
-    if (tid < rv) {
-      for (int s = 0; s < ns; ++s) {
-        const float f = f_lds[s];
-        if (f != 0.f) {
-          const float* r = recs + (size_t)(s0 + s) * p.ws_stride;
-          o = fmaf(f, r[2 + tid], o);
-          L = fmaf(f, r[1], L);
-        }
+  };
+  auto stage_basis = [&](int r0, int nr) {
+    const int per_row4 = rv / 4;
+    for (int i = tid; i < nr * per_row4; i += kMergeThreads) {
+      const int r = i / per_row4, c4 = i - r * per_row4;
+      *reinterpret_cast<float4*>(p_lds + r * pst + 4 * c4) =
+          *reinterpret_cast<const float4*>(P + (size_t)(r0 + r) * rv + 4 * c4);
+    }
+  };
+
+  // 1. stage records and the first rows of P_V; maximum of the split maxima per head
+  const bool one_pass = ns <= chunk;
+  if (one_pass) stage_records(0, ns);
+  stage_basis(0, p_rows);
+  __syncthreads();
+#pragma unroll
+  for (int g = 0; g < kHeadsPerWg; ++g) {
+    float mx = kNegInf;
+    if (g < gpw)
+      for (int s = tid; s < ns; s += kMergeThreads)
+        mx = fmaxf(mx, one_pass ? rec_lds[((size_t)g * chunk + s) * stride] : recs[g * head_stride + (size_t)s * stride]);
+    mx = wave_allreduce<true>(mx);
+    if (lane == 0) m_red[g][wave] = mx;
+  }
+  __syncthreads();
+
+  // 2. weighted sum of the split latents: wave g owns head g, lane j channels j, j + 64
+  const int g_own = wave;
+  const bool own = g_own < gpw;
+  const float M = fmaxf(fmaxf(m_red[g_own][0], m_red[g_own][1]), fmaxf(m_red[g_own][2], m_red[g_own][3]));
+  float o0 = 0.f, o1 = 0.f, L = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += chunk) {
+    const int nc = min(chunk, ns - s0);
+    if (!one_pass) {
+      __syncthreads();
+      stage_records(s0, nc);
+      __syncthreads();
+    }
+    if (own && M != kNegInf) {
+      const float* r = rec_lds + (size_t)g_own * chunk * stride;
+#pragma unroll 4
+      for (int s = 0; s < nc; ++s, r += stride) {
+        const float f = fast_exp2(r[0] - M);   // empty split: exp2(-inf) = 0
+        L = fmaf(f, r[1], L);
+        if (lane < rv) o0 = fmaf(f, r[2 + lane], o0);
+        if (lane + 64 < rv) o1 = fmaf(f, r[2 + 64 + lane], o1);
       }
     }
-    __syncthreads();
   }
-  if (tid < rv) olat[tid] = o / L;
+  {
+    const float inv = (own && L > 0.f) ? 1.f / L : 0.f;   // empty sequence or idle head: zero
+    if (lane < RB) olat[lane][g_own] = (lane < rv) ? o0 * inv : 0.f;
+    if (lane + 64 < RB) olat[lane + 64][g_own] = (lane + 64 < rv) ? o1 * inv : 0.f;
+  }
   __syncthreads();
-  const float* P = p.pv + (size_t)p.d * p.ht.rv_pre[h];
-  for (int dd = tid; dd < p.d; dd += kMergeThreads) {
-    const float* prow = P + (size_t)dd * rv;
-    float acc = 0.f;
-    for (int j = 0; j < rv; ++j) acc = fmaf(olat[j], prow[j], acc);
-    outp[dd] = acc;
+
+  // 3. back-projection, P_V rows from LDS (restaged when d * (rv + 4) exceeds the buffer)
+  for (int r0 = 0; r0 < d; r0 += p_rows) {
+    const int nr = min(p_rows, d - r0);
+    if (r0 > 0) {
+      __syncthreads();
+      stage_basis(r0, nr);
+      __syncthreads();
+    }
+    for (int r = tid; r < nr; r += kMergeThreads) {
+      float acc[kHeadsPerWg] = {0.f, 0.f, 0.f, 0.f};
+      const float* prow = p_lds + r * pst;
+#pragma unroll 2
+      for (int j = 0; j < rv; j += 4) {
+        const float4 pj = *reinterpret_cast<const float4*>(prow + j);
+        const float pk[4] = {pj.x, pj.y, pj.z, pj.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float4 ol = *reinterpret_cast<const float4*>(&olat[j + k][0]);
+          acc[0] = fmaf(ol.x, pk[k], acc[0]);
+          acc[1] = fmaf(ol.y, pk[k], acc[1]);
+          acc[2] = fmaf(ol.z, pk[k], acc[2]);
+          acc[3] = fmaf(ol.w, pk[k], acc[3]);
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < kHeadsPerWg; ++g)
+        if (g < gpw) p.out[((size_t)b * p.Hq + hq0 + g) * d + r0 + r] = acc[g];
+    }
   }
 }
 
@@ -555,8 +687,14 @@ hipError_t launch_decode(const DecodeParams& p, int latent_bf16, int rank_bound,
   return hipGetLastError();
 }
 
-hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(decode_merge, dim3(p.Hq, p.B), dim3(kMergeThreads), 0, stream, p);
+hipError_t launch_merge(const MergeParams& p, int rank_bound, hipStream_t stream) {
+  const dim3 grid(p.Hkv * p.n_head_groups, p.B);
+  switch (rank_bound) {
+    case 32: hipLaunchKernelGGL(decode_merge<32>, grid, dim3(kMergeThreads), 0, stream, p); break;
+    case 64: hipLaunchKernelGGL(decode_merge<64>, grid, dim3(kMergeThreads), 0, stream, p); break;
+    case 96: hipLaunchKernelGGL(decode_merge<96>, grid, dim3(kMergeThreads), 0, stream, p); break;
+    default: hipLaunchKernelGGL(decode_merge<128>, grid, dim3(kMergeThreads), 0, stream, p); break;
+  }
   return hipGetLastError();
 }
 

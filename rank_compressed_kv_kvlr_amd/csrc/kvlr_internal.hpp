@@ -25,6 +25,8 @@ struct HeadTable {
 
 struct DecodeParams {
   const float* q;        // [B][Hq][d]
+  const float* qt_in;    // optional q~ [B][Hq][qt_stride] (bases folded into the query projection)
+  int qt_stride;
   const float* pk;       // packed [h][d][rk(h)]
   const void* lat_k;     // latent caches
   const void* lat_v;
@@ -42,7 +44,7 @@ struct MergeParams {
   const float* pv;       // packed [h][d][rv(h)]
   float* out;            // [B][Hq][d]
   int B, Hq, Hkv, G, d;
-  int n_splits, ws_stride;
+  int n_splits, ws_stride, n_head_groups;
   HeadTable ht;
 };
 
@@ -75,7 +77,7 @@ struct AppendParams {
 
 // Launchers (return hipGetLastError() of their launches).
 hipError_t launch_decode(const DecodeParams& p, int latent_bf16, int rank_bound, hipStream_t s);
-hipError_t launch_merge(const MergeParams& p, hipStream_t s);
+hipError_t launch_merge(const MergeParams& p, int rank_bound, hipStream_t s);
 hipError_t launch_compress(const CompressParams& p, hipStream_t s);
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
 
@@ -85,6 +87,16 @@ hipError_t launch_append(const AppendParams& p, hipStream_t s);
 typedef short bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// Streaming (non-temporal) loads for data read exactly once per call.
+__device__ __forceinline__ u32x4_t load_stream16(const void* ptr) {
+  return __builtin_nontemporal_load(static_cast<const u32x4_t*>(ptr));
+}
+__device__ __forceinline__ u32x2_t load_stream8(const void* ptr) {
+  return __builtin_nontemporal_load(static_cast<const u32x2_t*>(ptr));
+}
 
 __device__ __forceinline__ float bf16lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }

@@ -73,9 +73,26 @@ __global__ void touch_kernel(uint4* __restrict__ buf, uint64_t n, uint32_t salt)
     buf[i] = make_uint4((uint32_t)i, salt, (uint32_t)(i >> 32), ~salt);
 }
 
+__global__ void copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, uint64_t n) {
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (uint64_t)gridDim.x * blockDim.x)
+    dst[i] = src[i];
+}
+
 }  // namespace
 
 extern "C" {
+
+// Plain copy of `bytes` (multiple of 16): reads and writes exactly that many
+// bytes, a reference for scaling hardware traffic counters.
+int synth_copy(const void* src, void* dst, uint64_t bytes, void* stream) {
+  if (!src || !dst || bytes % 16) return -1;
+  const uint64_t n = bytes / 16;
+  uint64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                     static_cast<const uint4*>(src), static_cast<uint4*>(dst), n);
+  return (int)hipGetLastError();
+}
 
 // Writes out[B][n_tok][Hkv][d] (float32 if out_bf16 == 0, bf16 bits otherwise)
 // for tokens t0 .. t0+n_tok-1. mu, sigma, mult: device float64 [Hkv][d].

@@ -19,6 +19,7 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
+        import torch  # noqa: F401  (bind to torch's HIP runtime, see rank_compressed_kv_kvlr_amd)
         if not os.path.exists(_LIB_PATH):
             raise ImportError(f"{_LIB_PATH} is missing; run __graft_entry__.build() first")
         _lib = ctypes.CDLL(_LIB_PATH)
@@ -29,6 +30,8 @@ def lib():
                                        ctypes.c_void_p]
         _lib.synth_touch.restype = ctypes.c_int
         _lib.synth_touch.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_void_p]
+        _lib.synth_copy.restype = ctypes.c_int
+        _lib.synth_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]
     return _lib
 
 
@@ -77,3 +80,14 @@ def touch(buf, salt: int = 0):
                            ctypes.c_uint32(salt & 0xFFFFFFFF), _stream_ptr(torch))
     if rc != 0:
         raise RuntimeError(f"synth_touch failed with {rc}")
+
+
+def copy(src, dst):
+    """Plain device copy of src into dst (same byte size): a known-size traffic reference."""
+    import torch
+    nbytes = src.numel() * src.element_size()
+    assert nbytes == dst.numel() * dst.element_size() and nbytes % 16 == 0
+    rc = lib().synth_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                          ctypes.c_uint64(nbytes), _stream_ptr(torch))
+    if rc != 0:
+        raise RuntimeError(f"synth_copy failed with {rc}")

@@ -135,3 +135,13 @@ def test_oracle_is_not_imported_by_the_product_path():
         if f.endswith(".py"):
             mods = imports.findall(open(os.path.join(ROOT, "oracle", f)).read())
             assert not [m for m in mods if m.startswith(("rank_compressed_kv_kvlr_amd", "synth"))], (f, mods)
+
+
+def test_single_hip_runtime_whatever_the_import_order():
+    """Importing the binding before torch must not map a second HIP runtime."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r); import rank_compressed_kv_kvlr_amd, torch; "
+            "print(sorted({l.split()[-1] for l in open('/proc/self/maps') if 'amdhip64' in l}))" % ROOT)
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300).stdout
+    assert out.count("amdhip64") == 1, out

@@ -297,6 +297,25 @@ def test_outputs_fully_written_and_deterministic(gpu):
     assert torch.equal(first, out)
 
 
+@pytest.mark.parametrize("cid,split", [(1, 0), (1, 128), (0, 256), (2, 0)])
+def test_decode_attn_equals_two_stages(gpu, cid, split):
+    """kvlr_decode_attn == kvlr_decode_partials followed by kvlr_decode_combine, bitwise."""
+    import torch
+    kv = _kv()
+    extra = {0: dict(T=1000), 1: dict(B=2, Hq=16, Hkv=2, T=700), 2: dict(B=3, T_range=(10, 900))}[cid]
+    cfg = CONFIGS[cid].scaled(**extra)
+    case = build_case(cfg)
+    lens_t = torch.from_numpy(host.lengths(cfg)).cuda()
+    q = torch.from_numpy(host.queries(cfg, 0, 0)).cuda()
+    fused = kv.decode_attn(case.desc, q, case.pk, case.pv, case.lat_k, case.lat_v, lens_t, split_tokens=split)
+    ws = kv.alloc_workspace(case.desc, split)
+    kv.decode_partials(case.desc, q, case.pk, case.lat_k, case.lat_v, lens_t, ws, split_tokens=split)
+    out = torch.empty_like(fused)
+    kv.decode_combine(case.desc, case.pv, ws, out, split_tokens=split)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, out)
+
+
 def test_latent_guard_bands(gpu):
     """Compression and append write only their rows: canaries around the caches survive."""
     import torch
