@@ -108,9 +108,14 @@ KVLR_API int kvlr_cache_elems(const kvlr_desc* desc, size_t* k_elems, size_t* v_
 
 /* Bytes of decode workspace that kvlr_decode_attn needs for this
  * descriptor and split length (split_tokens as in kvlr_decode_attn; 0 picks
- * the library's choice, the same one kvlr_decode_attn makes for 0): one fp32
- * record [B][Hq][n_splits][round_up(max_h r_v[h] + 2, 4)] per split. */
+ * the library's choice, the same one kvlr_decode_attn makes for 0).
+ * Layout: int32 arrival counters (kvlr_decode_counter_bytes bytes), then one
+ * fp32 record [B][Hq][n_splits][round_up(max_h r_v[h] + 2, 4)] per split. */
 KVLR_API int kvlr_decode_workspace_bytes(const kvlr_desc* desc, int32_t split_tokens, size_t* bytes);
+
+/* Size of the counter region at the start of a decode workspace:
+ * 4 * B * Hkv * ceil(G / 4) bytes rounded up to a multiple of 256. */
+KVLR_API int kvlr_decode_counter_bytes(const kvlr_desc* desc, size_t* bytes);
 
 /* Splits that kvlr_decode_attn uses per (batch row, KV head) for
  * split_tokens (0 = library choice), and the tokens per split. */
@@ -157,13 +162,16 @@ KVLR_API int kvlr_append(const kvlr_desc* desc, const void* k_new, const void* v
  *   scale     finite score scale (1/sqrt(d) for standard attention)
  *   out       device fp32 [B][Hq][d], fully overwritten
  *   workspace device scratch of at least kvlr_decode_workspace_bytes(desc,
- *             split_tokens) bytes; contents need no initialisation and are
- *             garbage afterwards; calls sharing one workspace must be
- *             ordered on one stream
+ *             split_tokens) bytes. Its counter region (the first
+ *             kvlr_decode_counter_bytes bytes) must be all zero before the
+ *             first kvlr_decode_attn call that uses it; every completed call
+ *             leaves it zero again. The records need no initialisation.
+ *             Calls sharing one workspace must be ordered on one stream.
  *   split_tokens 0 for the library's choice, or a multiple of 64: tokens
  *             per split of the sequence (every split yields a partial
- *             softmax state; a second kernel merges the states and
- *             back-projects with P_V^T)
+ *             softmax state; the workgroup that finishes last for a group of
+ *             query heads merges the states and back-projects with P_V^T,
+ *             all in one kernel launch)
  * Scores and the softmax are computed in fp32; bf16 latents are read as
  * stored and multiplied in fp32 (the key side on MFMA with the query split
  * into a high and a low bf16 part). */
@@ -181,7 +189,8 @@ KVLR_API int kvlr_decode_attn(const kvlr_desc* desc, const float* q, const float
  * softmax and the p-weighted sum of value latents for every split of every
  * (batch row, query head). Writes one record (running max in log2 units,
  * softmax denominator, unnormalised latent sum of r_v(h) channels) per
- * split into `workspace`; arguments as in kvlr_decode_attn. */
+ * split into the record region of `workspace`; arguments as in
+ * kvlr_decode_attn. Neither stage reads or writes the counter region. */
 KVLR_API int kvlr_decode_partials(const kvlr_desc* desc, const float* q, const float* P_K, const void* lat_k,
                                   const void* lat_v, const int32_t* seq_lens, float scale, void* workspace,
                                   size_t workspace_bytes, int32_t split_tokens, void* stream);

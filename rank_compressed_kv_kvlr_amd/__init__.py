@@ -28,7 +28,7 @@ import numpy as np
 
 __all__ = [
     "KvlrError", "Desc", "F32", "BF16", "lib", "version", "status_string",
-    "cache_elems", "decode_workspace_bytes", "decode_plan",
+    "cache_elems", "decode_workspace_bytes", "decode_plan", "decode_counter_bytes",
     "prefill_compress", "append", "decode_attn", "decode_partials", "decode_combine",
     "alloc_cache", "alloc_workspace", "pack_bases", "head_view",
 ]
@@ -65,13 +65,14 @@ lib.kvlr_status_string.argtypes = [ctypes.c_int]
 lib.kvlr_cache_elems.argtypes = [_D, _SZ, _SZ]
 lib.kvlr_decode_workspace_bytes.argtypes = [_D, ctypes.c_int32, _SZ]
 lib.kvlr_decode_plan.argtypes = [_D, ctypes.c_int32, _I32P, _I32P]
+lib.kvlr_decode_counter_bytes.argtypes = [_D, _SZ]
 lib.kvlr_prefill_compress.argtypes = [_D, _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P]
 lib.kvlr_append.argtypes = [_D, _P, _P, _P, _P, _P, _P, _P, _P]
 lib.kvlr_decode_attn.argtypes = [_D, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, ctypes.c_size_t,
                                  ctypes.c_int32, _P]
 lib.kvlr_decode_partials.argtypes = [_D, _P, _P, _P, _P, _P, ctypes.c_float, _P, ctypes.c_size_t, ctypes.c_int32, _P]
 lib.kvlr_decode_combine.argtypes = [_D, _P, _P, ctypes.c_size_t, ctypes.c_int32, _P, _P]
-for _f in ("kvlr_cache_elems", "kvlr_decode_workspace_bytes", "kvlr_decode_plan", "kvlr_prefill_compress",
+for _f in ("kvlr_cache_elems", "kvlr_decode_workspace_bytes", "kvlr_decode_plan", "kvlr_decode_counter_bytes", "kvlr_prefill_compress",
            "kvlr_append", "kvlr_decode_attn", "kvlr_decode_partials", "kvlr_decode_combine"):
     getattr(lib, _f).restype = ctypes.c_int
 
@@ -180,10 +181,17 @@ def alloc_cache(desc: Desc, device="cuda"):
     return torch.empty(nk, dtype=dt, device=device), torch.empty(nv, dtype=dt, device=device)
 
 
+def decode_counter_bytes(desc: Desc) -> int:
+    n = ctypes.c_size_t()
+    _check(lib.kvlr_decode_counter_bytes(desc.ptr, ctypes.byref(n)), "kvlr_decode_counter_bytes")
+    return n.value
+
+
 def alloc_workspace(desc: Desc, split_tokens: int = 0, device="cuda"):
+    """Decode workspace with its counter region zeroed (as kvlr_decode_attn requires)."""
     torch = _torch()
     n = decode_workspace_bytes(desc, split_tokens)
-    return torch.empty((n + 3) // 4, dtype=torch.float32, device=device)
+    return torch.zeros((n + 3) // 4, dtype=torch.float32, device=device)
 
 
 def pack_bases(bases: Sequence, device="cuda"):

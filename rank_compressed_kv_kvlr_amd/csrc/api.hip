@@ -20,7 +20,7 @@ constexpr int kComputeUnits = 256;   // MI355X
 // length gives one such round of workgroups over the whole device.
 int resident_wgs_per_cu(int latent_dtype, int rank_bound) {
   if (latent_dtype == KVLR_BF16) return rank_bound <= 32 ? 3 : rank_bound <= 64 ? 2 : 1;
-  return rank_bound <= 64 ? 5 : 4;
+  return 3;   // fp32 variants: limited by the 48 KiB of LDS the merge tail needs
 }
 
 bool valid_dtype(int t) { return t == KVLR_F32 || t == KVLR_BF16; }
@@ -96,6 +96,15 @@ int ws_stride_of(const HeadTable& ht, int Hkv) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? KVLR_OK : KVLR_ERR_HIP; }
 
+// Workspace layout: arrival counters [B][Hkv][head groups] int32, padded to
+// 256 bytes, then the split records [B][Hq][n_splits][stride] fp32.
+size_t counter_bytes_of(const kvlr_desc* d) {
+  const int G = d->n_q_heads / d->n_kv_heads;
+  const size_t groups = (size_t)(G + kvlr::kHeadsPerWg - 1) / kvlr::kHeadsPerWg;
+  const size_t n = (size_t)d->batch * d->n_kv_heads * groups * sizeof(int32_t);
+  return (n + 255) / 256 * 256;
+}
+
 }  // namespace
 
 extern "C" {
@@ -147,7 +156,16 @@ KVLR_API int kvlr_decode_workspace_bytes(const kvlr_desc* desc, int32_t split_to
   int ns = 0, len = 0;
   rc = plan_split(desc, split_tokens, &ns, &len);
   if (rc) return rc;
-  *bytes = (size_t)desc->batch * desc->n_q_heads * ns * ws_stride_of(ht, desc->n_kv_heads) * sizeof(float);
+  *bytes = counter_bytes_of(desc) +
+           (size_t)desc->batch * desc->n_q_heads * ns * ws_stride_of(ht, desc->n_kv_heads) * sizeof(float);
+  return KVLR_OK;
+}
+
+KVLR_API int kvlr_decode_counter_bytes(const kvlr_desc* desc, size_t* bytes) {
+  const int rc = check_desc(desc, nullptr, nullptr, nullptr, nullptr);
+  if (rc) return rc;
+  if (!bytes) return KVLR_ERR_NULL;
+  *bytes = counter_bytes_of(desc);
   return KVLR_OK;
 }
 
@@ -221,7 +239,8 @@ int prepare_decode(const kvlr_desc* desc, const float* q, const float* P_K, cons
   rc = plan_split(desc, split_tokens, &ns, &len);
   if (rc) return rc;
   const int stride = ws_stride_of(p->ht, desc->n_kv_heads);
-  const size_t need = (size_t)desc->batch * desc->n_q_heads * ns * stride * sizeof(float);
+  const size_t cbytes = counter_bytes_of(desc);
+  const size_t need = cbytes + (size_t)desc->batch * desc->n_q_heads * ns * stride * sizeof(float);
   if (!workspace || workspace_bytes < need) return KVLR_ERR_WORKSPACE;
 
   const int G = desc->n_q_heads / desc->n_kv_heads;
@@ -230,7 +249,11 @@ int prepare_decode(const kvlr_desc* desc, const float* q, const float* P_K, cons
   p->lat_k = lat_k;
   p->lat_v = lat_v;
   p->seq_lens = seq_lens;
-  p->ws = static_cast<float*>(workspace);
+  p->counters = static_cast<int*>(workspace);
+  p->ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + cbytes);
+  p->pv = P_V;
+  p->out = out;
+  p->fuse = 0;
   p->B = desc->batch;
   p->Hq = desc->n_q_heads;
   p->Hkv = desc->n_kv_heads;
@@ -293,13 +316,12 @@ KVLR_API int kvlr_decode_attn(const kvlr_desc* desc, const float* q, const float
   kvlr::DecodeParams p;
   kvlr::MergeParams m;
   int rank_bound = 0;
-  int rc = prepare_decode(desc, q, P_K, lat_k, lat_v, seq_lens, scale, P_V, out, true, true, workspace,
-                          workspace_bytes, split_tokens, &p, &m, &rank_bound);
+  const int rc = prepare_decode(desc, q, P_K, lat_k, lat_v, seq_lens, scale, P_V, out, true, true, workspace,
+                                workspace_bytes, split_tokens, &p, &m, &rank_bound);
   if (rc) return rc;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  rc = hip_status(kvlr::launch_decode(p, desc->latent_dtype == KVLR_BF16, rank_bound, s));
-  if (rc) return rc;
-  return hip_status(kvlr::launch_merge(m, rank_bound, s));
+  p.fuse = 1;   // one launch: the last split workgroup of each group merges and back-projects
+  return hip_status(kvlr::launch_decode(p, desc->latent_dtype == KVLR_BF16, rank_bound,
+                                        static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -133,11 +133,22 @@ __device__ __forceinline__ void project_query(const DecodeParams& p, int b, int 
   __syncthreads();
 }
 
+// Split records are written and read with agent-scope relaxed atomic
+// accesses: on gfx950 these are plain stores/loads with the agent-coherence
+// bit (sc1), so a record written by one workgroup is read back coherently by
+// another workgroup on any XCD without a whole-L2 writeback.
+__device__ __forceinline__ void store_rec(float* addr, float v) {
+  __hip_atomic_store(addr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_rec(const float* addr) {
+  return __hip_atomic_load(addr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ void write_empty_records(const DecodeParams& p, int b, int hq0, int gpw, int s, int rv) {
   for (int idx = threadIdx.x; idx < gpw * (rv + 2); idx += blockDim.x) {
     const int g = idx / (rv + 2), j = idx - g * (rv + 2);
     float* rec = p.ws + (((size_t)b * p.Hq + hq0 + g) * p.n_splits + s) * p.ws_stride;
-    rec[j] = (j == 0) ? kNegInf : 0.f;
+    store_rec(rec + j, (j == 0) ? kNegInf : 0.f);
   }
 }
 
@@ -163,12 +174,120 @@ __device__ __forceinline__ void merge_waves_and_store(const DecodeParams& p, int
       }
     }
     float* rec = p.ws + (((size_t)b * p.Hq + hq0 + g) * p.n_splits + s) * p.ws_stride;
-    rec[2 + j] = o;
+    store_rec(rec + 2 + j, o);
     if (j == 0) {
-      rec[0] = M;
-      rec[1] = L;
+      store_rec(rec, M);
+      store_rec(rec + 1, L);
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// merge in the last split workgroup of a group (single-launch decode)
+// ---------------------------------------------------------------------------
+// Every split workgroup of a (batch row, KV head, head group) counts its
+// arrival after its records are complete (s_waitcnt 0 + barrier: the sc1
+// stores have reached the coherence point); the workgroup that arrives last
+// merges the records and applies P_V^T, then resets the counter, so every
+// completed call leaves the counters at zero.
+//   wave g merges head g: one pass over the records with a running maximum,
+//   then o[dd] = sum_j o_lat[j] P_V[dd][j] for dd = lane + 64 k, with o_lat[j]
+//   broadcast from lane j by readlane and the P_V row prefetched into
+//   registers before the records are read.
+constexpr int kTailLds = 12288;   // floats of LDS a split kernel provides for the merge tail
+
+template <int RB>
+__device__ __forceinline__ void finish_split(const DecodeParams& p, int b, int h, int hg, int hq0, int gpw,
+                                             int rv, float* scratch) {
+  if (!p.fuse) return;
+  int* flag = reinterpret_cast<int*>(scratch + kTailLds - 1);
+  int* counter = p.counters + ((size_t)b * p.Hkv + h) * p.n_head_groups + hg;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *flag = (__hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == p.n_splits - 1);
+  __syncthreads();
+  if (*flag == 0) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, g = tid >> 6;
+  const int d = p.d;
+  float* olat = scratch;                        // [RB][4] head-minor
+  float* p_lds = scratch + 4 * RB;              // P_V rows, padded stride
+  const int pst = rv + 4;
+  const int p_rows = min(d, (kTailLds - 4 * RB - 16) / pst);
+  const float* P = p.pv + (size_t)d * p.ht.rv_pre[h];
+  auto stage_basis = [&](int r0, int nr) {
+    const int per_row4 = rv / 4;
+    for (int i = tid; i < nr * per_row4; i += blockDim.x) {
+      const int r = i / per_row4, c4 = i - r * per_row4;
+      *reinterpret_cast<float4*>(p_lds + r * pst + 4 * c4) =
+          *reinterpret_cast<const float4*>(P + (size_t)(r0 + r) * rv + 4 * c4);
+    }
+  };
+  stage_basis(0, p_rows);   // in flight together with the record loads below
+
+  // wave g folds the records of head g in one pass with a running maximum
+  float M = kNegInf, L = 0.f, o0 = 0.f, o1 = 0.f;
+  if (g < gpw) {
+    const float* r0 = p.ws + ((size_t)b * p.Hq + hq0 + g) * p.n_splits * p.ws_stride;
+    for (int s0 = 0; s0 < p.n_splits; s0 += 8) {
+      float ms[8], ls[8], v0[8], v1[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const bool ok = s0 + u < p.n_splits;
+        const float* r = r0 + (size_t)(s0 + u) * p.ws_stride;
+        ms[u] = ok ? load_rec(r) : kNegInf;
+        ls[u] = ok ? load_rec(r + 1) : 0.f;
+        v0[u] = (ok && lane < rv) ? load_rec(r + 2 + lane) : 0.f;
+        v1[u] = (ok && lane + 64 < rv) ? load_rec(r + 66 + lane) : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (ms[u] == kNegInf) continue;   // empty split or beyond n_splits
+        const float Mn = fmaxf(M, ms[u]);
+        const float a = fast_exp2(M - Mn), f = fast_exp2(ms[u] - Mn);
+        L = fmaf(L, a, f * ls[u]);
+        o0 = fmaf(o0, a, f * v0[u]);
+        o1 = fmaf(o1, a, f * v1[u]);
+        M = Mn;
+      }
+    }
+  }
+  const float inv = (g < gpw && L > 0.f) ? 1.f / L : 0.f;   // empty sequence or idle head: zero
+  if (lane < RB) olat[lane * 4 + g] = o0 * inv;
+  if (lane + 64 < RB) olat[(lane + 64) * 4 + g] = o1 * inv;
+  __syncthreads();
+
+  // back-projection of the 4 heads, P_V rows from LDS (restaged when they do not fit)
+  for (int r0 = 0; r0 < d; r0 += p_rows) {
+    const int nr = min(p_rows, d - r0);
+    if (r0 > 0) {
+      __syncthreads();
+      stage_basis(r0, nr);
+      __syncthreads();
+    }
+    for (int r = tid; r < nr; r += blockDim.x) {
+      float acc[kHeadsPerWg] = {0.f, 0.f, 0.f, 0.f};
+      const float* prow = p_lds + r * pst;
+#pragma unroll 2
+      for (int j = 0; j < rv; j += 4) {
+        const float4 pj = *reinterpret_cast<const float4*>(prow + j);
+        const float pk[4] = {pj.x, pj.y, pj.z, pj.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float4 ol = *reinterpret_cast<const float4*>(olat + (j + e) * 4);
+          acc[0] = fmaf(ol.x, pk[e], acc[0]);
+          acc[1] = fmaf(ol.y, pk[e], acc[1]);
+          acc[2] = fmaf(ol.z, pk[e], acc[2]);
+          acc[3] = fmaf(ol.w, pk[e], acc[3]);
+        }
+      }
+#pragma unroll
+      for (int gg = 0; gg < kHeadsPerWg; ++gg)
+        if (gg < gpw) p.out[((size_t)b * p.Hq + hq0 + gg) * d + r0 + r] = acc[gg];
+    }
+  }
+  if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -181,7 +300,7 @@ __global__ __launch_bounds__(256) void decode_split_bf16(DecodeParams p) {
   constexpr int NP = RB / 32;                 // full 32-channel key pairs
   constexpr int NIT = value_iters_bound(RB);  // bound on value iterations (see n_it below)
   constexpr int QTS = RB;                     // q~ LDS row stride
-  __shared__ __attribute__((aligned(16))) float smem[kWaves * 64 * 4 * 8 + 64];
+  __shared__ __attribute__((aligned(16))) float smem[kWaves * 64 * 4 * 8 + 64 > kTailLds ? kWaves * 64 * 4 * 8 + 64 : kTailLds];
 
   const int s = blockIdx.x;
   const int h = blockIdx.y / p.n_head_groups;
@@ -195,6 +314,7 @@ __global__ __launch_bounds__(256) void decode_split_bf16(DecodeParams p) {
   const int t_end = min(T, t_begin + p.split_len);
   if (t_begin >= t_end) {
     write_empty_records(p, b, hq0, gpw, s, rv);
+    finish_split<RB>(p, b, h, hg, hq0, gpw, rv, smem);
     return;
   }
 
@@ -408,6 +528,7 @@ __global__ __launch_bounds__(256) void decode_split_bf16(DecodeParams p) {
     for (int r = 0; r < rpi; ++r) sum += red[((w * 64 + r * C + c) * 4 + g) * 8 + e];
     return sum;
   });
+  finish_split<RB>(p, b, h, hg, hq0, gpw, rv, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -419,7 +540,8 @@ __global__ __launch_bounds__(256) void decode_split_f32(DecodeParams p) {
   constexpr int QTS = RB;
   constexpr int VJ = (RB + 63) / 64;          // value channels per lane
   constexpr int RED = kWaves * 4 * (RB > 64 ? RB : 64);   // also holds the per-wave [64][4] p tiles
-  __shared__ __attribute__((aligned(16))) float smem[RED + kHeadsPerWg * 256 + kHeadsPerWg * RB + 64];
+  constexpr int SM = RED + kHeadsPerWg * 256 + kHeadsPerWg * RB + 64;
+  __shared__ __attribute__((aligned(16))) float smem[SM > kTailLds ? SM : kTailLds];
 
   const int s = blockIdx.x;
   const int h = blockIdx.y / p.n_head_groups;
@@ -433,6 +555,7 @@ __global__ __launch_bounds__(256) void decode_split_f32(DecodeParams p) {
   const int t_end = min(T, t_begin + p.split_len);
   if (t_begin >= t_end) {
     write_empty_records(p, b, hq0, gpw, s, rv);
+    finish_split<RB>(p, b, h, hg, hq0, gpw, rv, smem);
     return;
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -534,6 +657,7 @@ __global__ __launch_bounds__(256) void decode_split_f32(DecodeParams p) {
   __syncthreads();
   merge_waves_and_store(p, b, hq0, gpw, s, rv, wm, wl,
                         [&](int w, int g, int j) { return red[(w * 4 + g) * RB + j]; });
+  finish_split<RB>(p, b, h, hg, hq0, gpw, rv, smem);
 }
 
 // ---------------------------------------------------------------------------

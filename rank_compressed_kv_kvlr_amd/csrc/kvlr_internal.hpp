@@ -32,6 +32,10 @@ struct DecodeParams {
   const void* lat_v;
   const int* seq_lens;   // [B]
   float* ws;             // partial records [B][Hq][n_splits][ws_stride]
+  int* counters;         // arrival counters [B][Hkv][n_head_groups] (single-launch merge)
+  const float* pv;       // single-launch merge: packed [h][d][rv(h)]
+  float* out;            // single-launch merge: [B][Hq][d]
+  int fuse;              // 1: the last split workgroup of a group merges and back-projects
   int B, Hq, Hkv, G, d, cap;
   int split_len, n_splits, ws_stride, n_head_groups;
   int Rk, Rv;            // sum of ranks over heads

@@ -81,7 +81,10 @@ def test_workspace_and_plan():
     ns, length = kv.decode_plan(d, 1024)
     assert (ns, length) == (32, 1024)
     rc, n = _ws(d, 1024)
-    assert rc == 0 and n == 2 * 8 * 32 * 36 * 4      # stride = round_up(32 + 2, 4)
+    assert rc == 0 and n == 256 + 2 * 8 * 32 * 36 * 4   # counters (padded to 256 B) + records, stride round_up(32 + 2, 4)
+    assert kv.decode_counter_bytes(d) == 256
+    big = _desc(batch=64, n_kv_heads=8, n_q_heads=96)   # G = 12: 3 head groups
+    assert kv.decode_counter_bytes(big) == (4 * 64 * 8 * 3 + 255) // 256 * 256
     assert kv.lib.kvlr_decode_workspace_bytes(d.ptr, 100, ctypes.byref(ctypes.c_size_t())) == -7
     assert kv.lib.kvlr_decode_workspace_bytes(d.ptr, -64, ctypes.byref(ctypes.c_size_t())) == -7
     ns, length = kv.decode_plan(d, 0)

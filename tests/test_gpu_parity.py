@@ -285,7 +285,8 @@ def test_outputs_fully_written_and_deterministic(gpu):
     big[-guard:] = 7.0
     out = big[guard:guard + nout]
     ws = kv.alloc_workspace(case.desc)
-    ws.fill_(float("nan"))
+    nc = kv.decode_counter_bytes(case.desc) // 4
+    ws[nc:].fill_(float("nan"))   # records poisoned; counters start at zero as the ABI requires
     kv.decode_attn(case.desc, q, case.pk, case.pv, case.lat_k, case.lat_v, lens_t, out=out, workspace=ws)
     torch.cuda.synchronize()
     first = out.clone()
@@ -295,11 +296,15 @@ def test_outputs_fully_written_and_deterministic(gpu):
         kv.decode_attn(case.desc, q, case.pk, case.pv, case.lat_k, case.lat_v, lens_t, out=out, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(first, out)
+    assert (ws[:nc].view(torch.int32) == 0).all(), "every call must leave the arrival counters at zero"
 
 
 @pytest.mark.parametrize("cid,split", [(1, 0), (1, 128), (0, 256), (2, 0)])
 def test_decode_attn_equals_two_stages(gpu, cid, split):
-    """kvlr_decode_attn == kvlr_decode_partials followed by kvlr_decode_combine, bitwise."""
+    """kvlr_decode_attn (one launch, merge in the last workgroup) matches partials + combine.
+
+    Same split records; the merges sum them in different orders, so fp32 rounding may differ.
+    """
     import torch
     kv = _kv()
     extra = {0: dict(T=1000), 1: dict(B=2, Hq=16, Hkv=2, T=700), 2: dict(B=3, T_range=(10, 900))}[cid]
@@ -313,7 +318,8 @@ def test_decode_attn_equals_two_stages(gpu, cid, split):
     out = torch.empty_like(fused)
     kv.decode_combine(case.desc, case.pv, ws, out, split_tokens=split)
     torch.cuda.synchronize()
-    assert torch.equal(fused, out)
+    a, b = fused.cpu().numpy().astype(np.float64), out.cpu().numpy().astype(np.float64)
+    assert rel_inf_rows(a, b).max() <= 1e-6
 
 
 def test_latent_guard_bands(gpu):
