@@ -182,13 +182,18 @@ def main():
     for k in range(args.warmup):
         step(k)
     torch.cuda.synchronize()
+    # headline: exactly K steps, nothing between the launches
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(k)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    # roofline: the same K steps again, each launch bracketed by HIP events on the launch stream
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for k in range(args.steps):
         step(k, evs[k])
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
 
     if args.traffic_reference:
         from synth.device import copy as device_copy

@@ -321,39 +321,8 @@ __global__ __launch_bounds__(256) void decode_split_bf16(DecodeParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n16 = lane & 15, q4 = lane >> 4;
 
-  // ---- prologue: q~ into LDS, then MFMA A operands (hi/lo) into registers
-  float* q_lds = smem;                          // [4][d]  (d <= 256)
-  float* qt_lds = smem + kHeadsPerWg * 256;     // [4][QTS]
-  float* qred = qt_lds + kHeadsPerWg * QTS;     // [4 waves][4][QTS]
-  project_query<RB>(p, b, h, hq0, gpw, rk, q_lds, qred, qt_lds);
-
   const int np = rk >> 5;           // full 32-channel pairs
   const int tail = (rk >> 4) & 1;   // one trailing 16-channel block
-  bf16x8_t a_hi[NP], a_lo[NP];
-  bf16x4_t t_hi, t_lo;
-#pragma unroll
-  for (int pp = 0; pp < NP; ++pp) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float x = (n16 < kHeadsPerWg) ? qt_lds[n16 * QTS + 32 * pp + 8 * q4 + e] : 0.f;
-      if (32 * pp + 8 * q4 + e >= rk) x = 0.f;
-      const uint16_t hi = f32_to_bf16_bits(x);
-      const uint16_t lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
-      a_hi[pp][e] = (short)hi;
-      a_lo[pp][e] = (short)lo;
-    }
-  }
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int j = 32 * np + 4 * q4 + e;
-    float x = (n16 < kHeadsPerWg && tail && j < rk) ? qt_lds[n16 * QTS + j] : 0.f;
-    const uint16_t hi = f32_to_bf16_bits(x);
-    const uint16_t lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
-    t_hi[e] = (short)hi;
-    t_lo[e] = (short)lo;
-  }
-  __syncthreads();   // LDS is reused below
-
   // ---- value-side lane mapping: C chunks of 8 channels per row
   const int C = rv >> 3;
   const int rpi = 64 / C;                 // rows per load instruction
@@ -401,11 +370,45 @@ __global__ __launch_bounds__(256) void decode_split_bf16(DecodeParams p) {
     }
   };
 
+  // the first tile's loads do not depend on q~: issue them before the prologue
   int t0 = t_begin + wave * kTile;
   if (t0 < t_end) {
     load_k(t0);
     load_v(t0);
   }
+
+  // ---- prologue: q~ into LDS, then MFMA A operands (hi/lo) into registers
+  float* q_lds = smem;                          // [4][d]  (d <= 256)
+  float* qt_lds = smem + kHeadsPerWg * 256;     // [4][QTS]
+  float* qred = qt_lds + kHeadsPerWg * QTS;     // [4 waves][4][QTS]
+  project_query<RB>(p, b, h, hq0, gpw, rk, q_lds, qred, qt_lds);
+
+  bf16x8_t a_hi[NP], a_lo[NP];
+  bf16x4_t t_hi, t_lo;
+#pragma unroll
+  for (int pp = 0; pp < NP; ++pp) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = (n16 < kHeadsPerWg) ? qt_lds[n16 * QTS + 32 * pp + 8 * q4 + e] : 0.f;
+      if (32 * pp + 8 * q4 + e >= rk) x = 0.f;
+      const uint16_t hi = f32_to_bf16_bits(x);
+      const uint16_t lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
+      a_hi[pp][e] = (short)hi;
+      a_lo[pp][e] = (short)lo;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int j = 32 * np + 4 * q4 + e;
+    float x = (n16 < kHeadsPerWg && tail && j < rk) ? qt_lds[n16 * QTS + j] : 0.f;
+    const uint16_t hi = f32_to_bf16_bits(x);
+    const uint16_t lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
+    t_hi[e] = (short)hi;
+    t_lo[e] = (short)lo;
+  }
+  __syncthreads();   // LDS is reused below
+
+
   for (; t0 < t_end; t0 += kWaves * kTile) {
     const int t_next = t0 + kWaves * kTile;
     // ---- scores on MFMA
