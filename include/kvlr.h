@@ -69,7 +69,7 @@ typedef enum kvlr_dtype {
  *   n_q_heads   Hq  >= 1, a multiple of n_kv_heads, with G = Hq / Hkv <= 16
  *   n_kv_heads  Hkv in [1, 64]; query head i reads KV head i / G
  *   head_dim    d   in [32, 256], a multiple of 32
- *   capacity    T_cap >= 1: rows allocated per (batch row, KV head)
+ *   capacity    T_cap in [1, 2^30]: usable rows per (batch row, KV head)
  *   r_k, r_v    host arrays [Hkv]: ranks of each KV head (uniform per-layer
  *               ranks repeat one value); 1 <= r <= min(d, 128), a multiple of 16
  *               for bf16 latents and of 4 for fp32 latents
@@ -77,10 +77,17 @@ typedef enum kvlr_dtype {
  *   latent_dtype dtype of the latent cache
  *
  * Latent cache layout (lat_k; lat_v likewise with r_v): with
- * R = sum_h r_k[h] and R_pre(h) = sum_{h' < h} r_k[h'], element (b, h, t, j)
- * sits at index  T_cap * (b * R + R_pre(h)) + t * r_k[h] + j.
- * With uniform ranks this is a contiguous [B][Hkv][T_cap][r] array; each
- * (b, h) is one contiguous block of T_cap rows of r_k[h] elements.
+ * R = sum_h r_k[h], R_pre(h) = sum_{h' < h} r_k[h'] and
+ * C16 = T_cap rounded up to a multiple of 16, the block of (b, h) starts at
+ * element C16 * (b * R + R_pre(h)) and holds C16 rows of r_k[h] elements.
+ * Inside a block:
+ *  - value latents, fp32 key latents: row-major, (t, j) at t * r + j;
+ *  - bf16 key latents: MFMA operand order, so that the decode kernel's
+ *    64-lane loads read 1 KiB contiguously. With n = t % 16 and
+ *    np = r / 32, 16-row group t / 16 starts at (t / 16) * 16 * r and holds,
+ *    for j < 32 np: (j / 32) * 512 + ((j % 32) / 8) * 128 + n * 8 + j % 8;
+ *    for the 16-channel tail jj = j - 32 np: np * 512 + (jj / 4) * 64 + n * 4 + jj % 4.
+ * Blocks are contiguous, so a split of a sequence streams one byte range.
  *
  * Basis layout: P_K is fp32, heads packed back to back, head h a row-major
  * [d][r_k[h]] block starting at element d * R_pre(h); P_V likewise. */
@@ -103,7 +110,8 @@ KVLR_API int kvlr_version(void);
 KVLR_API const char* kvlr_status_string(int status);
 
 /* Validates `desc` and returns, through k_elems / v_elems, the number of
- * latent elements of lat_k and lat_v: B * T_cap * sum_h r(h). */
+ * latent elements of lat_k and lat_v: B * C16 * sum_h r(h), C16 = T_cap
+ * rounded up to a multiple of 16. */
 KVLR_API int kvlr_cache_elems(const kvlr_desc* desc, size_t* k_elems, size_t* v_elems);
 
 /* Bytes of decode workspace that kvlr_decode_attn needs for this

@@ -30,7 +30,7 @@ __all__ = [
     "KvlrError", "Desc", "F32", "BF16", "lib", "version", "status_string",
     "cache_elems", "decode_workspace_bytes", "decode_plan", "decode_counter_bytes",
     "prefill_compress", "append", "decode_attn", "decode_partials", "decode_combine",
-    "alloc_cache", "alloc_workspace", "pack_bases", "head_view",
+    "alloc_cache", "alloc_workspace", "pack_bases", "block_view", "latent_rows", "cap_rows", "k_tiled_index",
 ]
 
 F32, BF16 = 0, 1
@@ -201,13 +201,43 @@ def pack_bases(bases: Sequence, device="cuda"):
     return torch.from_numpy(flat).to(device)
 
 
-def head_view(lat, desc: Desc, which: str, b: int, h: int):
-    """View [capacity][r] of the latent rows of (batch row b, KV head h)."""
+def cap_rows(desc: Desc) -> int:
+    """Rows allocated per (batch row, KV head) block: capacity rounded up to 16."""
+    return (desc.capacity + 15) // 16 * 16
+
+
+def block_view(lat, desc: Desc, which: str, b: int, h: int):
+    """The raw storage block of (batch row b, KV head h): cap_rows * r elements, 1-D."""
     r = int((desc.r_k if which == "k" else desc.r_v)[h])
     off = desc.rank_offsets(which)
     R = int(off[-1])
-    start = desc.capacity * (b * R + int(off[h]))
-    return lat[start:start + desc.capacity * r].view(desc.capacity, r)
+    rows = cap_rows(desc)
+    start = rows * (b * R + int(off[h]))
+    return lat[start:start + rows * r]
+
+
+def k_tiled_index(T: int, r: int):
+    """Element offsets [T][r] of bf16 key latents inside a block (MFMA operand order, see kvlr.h)."""
+    t = np.arange(T)[:, None]
+    j = np.arange(r)[None, :]
+    np_ = r // 32
+    base = (t >> 4) * 16 * r
+    n = t & 15
+    pair = base + (j >> 5) * 512 + ((j >> 3) & 3) * 128 + n * 8 + (j & 7)
+    jj = j - 32 * np_
+    tail = base + np_ * 512 + (jj >> 2) * 64 + n * 4 + (jj & 3)
+    return np.where(j < 32 * np_, pair, tail)
+
+
+def latent_rows(lat, desc: Desc, which: str, b: int, h: int):
+    """Logical latent rows [capacity][r] of (b, h) (a gather for bf16 keys, a view otherwise)."""
+    torch = _torch()
+    r = int((desc.r_k if which == "k" else desc.r_v)[h])
+    blk = block_view(lat, desc, which, b, h)
+    if which == "k" and desc.latent_dtype == BF16:
+        idx = torch.from_numpy(k_tiled_index(desc.capacity, r).ravel()).to(blk.device)
+        return blk[idx].view(desc.capacity, r)
+    return blk[:desc.capacity * r].view(desc.capacity, r)
 
 
 def _basis_numel(desc: Desc, which: str) -> int:

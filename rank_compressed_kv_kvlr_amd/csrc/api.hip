@@ -19,7 +19,7 @@ constexpr int kComputeUnits = 256;   // MI355X
 // limited by the variant's register count on gfx950). The default split
 // length gives one such round of workgroups over the whole device.
 int resident_wgs_per_cu(int latent_dtype, int rank_bound) {
-  if (latent_dtype == KVLR_BF16) return rank_bound <= 32 ? 3 : rank_bound <= 64 ? 2 : 1;
+  if (latent_dtype == KVLR_BF16) return rank_bound <= 32 ? 3 : rank_bound <= 64 ? 2 : 1;   // measured best
   return 3;   // fp32 variants: limited by the 48 KiB of LDS the merge tail needs
 }
 
@@ -31,7 +31,7 @@ int check_desc(const kvlr_desc* d, HeadTable* ht, int* Rk, int* Rv, int* rank_bo
   if (!valid_dtype(d->in_dtype) || !valid_dtype(d->latent_dtype)) return KVLR_ERR_DTYPE;
   if (d->batch < 1 || d->n_kv_heads < 1 || d->n_kv_heads > kvlr::kMaxKvHeads || d->n_q_heads < 1 ||
       d->n_q_heads % d->n_kv_heads != 0 || d->n_q_heads / d->n_kv_heads > 16 || d->capacity < 1 ||
-      d->head_dim < 32 || d->head_dim > 256 || d->head_dim % 32 != 0)
+      d->head_dim < 32 || d->head_dim > 256 || d->head_dim % 32 != 0 || d->capacity > (1 << 30))
     return KVLR_ERR_SHAPE;
   const int granule = d->latent_dtype == KVLR_BF16 ? 16 : 4;
   const int rmax = d->head_dim < kvlr::kMaxRank ? d->head_dim : kvlr::kMaxRank;
@@ -96,6 +96,15 @@ int ws_stride_of(const HeadTable& ht, int Hkv) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? KVLR_OK : KVLR_ERR_HIP; }
 
+// Tokens per wave iteration of the bf16 split kernel (32 or 64; 32 measured
+// faster: fewer registers, 3 waves per SIMD at rank 64); KVLR_TILE overrides
+// for tuning.
+int decode_tile() {
+  const char* env = getenv("KVLR_TILE");
+  if (env && atoi(env) == 64) return 64;
+  return 32;
+}
+
 // Workspace layout: arrival counters [B][Hkv][head groups] int32, padded to
 // 256 bytes, then the split records [B][Hq][n_splits][stride] fp32.
 size_t counter_bytes_of(const kvlr_desc* d) {
@@ -130,8 +139,9 @@ KVLR_API int kvlr_cache_elems(const kvlr_desc* desc, size_t* k_elems, size_t* v_
   const int rc = check_desc(desc, nullptr, &Rk, &Rv, nullptr);
   if (rc) return rc;
   if (!k_elems || !v_elems) return KVLR_ERR_NULL;
-  *k_elems = (size_t)desc->batch * desc->capacity * Rk;
-  *v_elems = (size_t)desc->batch * desc->capacity * Rv;
+  const size_t rows = (size_t)kvlr::cap_rows_of(desc->capacity);
+  *k_elems = (size_t)desc->batch * rows * Rk;
+  *v_elems = (size_t)desc->batch * rows * Rv;
   return KVLR_OK;
 }
 
@@ -294,7 +304,7 @@ KVLR_API int kvlr_decode_partials(const kvlr_desc* desc, const float* q, const f
   const int rc = prepare_decode(desc, q, P_K, lat_k, lat_v, seq_lens, scale, nullptr, nullptr, true, false,
                                 workspace, workspace_bytes, split_tokens, &p, &m, &rank_bound);
   if (rc) return rc;
-  return hip_status(kvlr::launch_decode(p, desc->latent_dtype == KVLR_BF16, rank_bound,
+  return hip_status(kvlr::launch_decode(p, desc->latent_dtype == KVLR_BF16, rank_bound, decode_tile(),
                                         static_cast<hipStream_t>(stream)));
 }
 
@@ -320,7 +330,7 @@ KVLR_API int kvlr_decode_attn(const kvlr_desc* desc, const float* q, const float
                                 workspace_bytes, split_tokens, &p, &m, &rank_bound);
   if (rc) return rc;
   p.fuse = 1;   // one launch: the last split workgroup of each group merges and back-projects
-  return hip_status(kvlr::launch_decode(p, desc->latent_dtype == KVLR_BF16, rank_bound,
+  return hip_status(kvlr::launch_decode(p, desc->latent_dtype == KVLR_BF16, rank_bound, decode_tile(),
                                         static_cast<hipStream_t>(stream)));
 }
 

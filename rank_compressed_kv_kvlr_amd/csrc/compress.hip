@@ -76,7 +76,8 @@ __global__ __launch_bounds__(256) void compress_bf16_mfma(CompressParams p) {
 
   const size_t row_stride = (size_t)p.Hkv * d;   // elements between consecutive tokens
   const uint16_t* Xb = X + (size_t)b * p.n_tok * row_stride + (size_t)h * d;
-  const size_t lat_base = (size_t)p.cap * ((size_t)b * R + r_pre);
+  const size_t lat_base = (size_t)cap_rows_of(p.cap) * ((size_t)b * R + r_pre);
+  const bool k_tiled = kOutBf16 && kind == 0;   // bf16 key latents: MFMA operand order
   const int tok_wg0 = blockIdx.x * kTokensPerWg;
 
   for (int it = 0; it < kWaveIters; ++it) {
@@ -114,7 +115,8 @@ __global__ __launch_bounds__(256) void compress_bf16_mfma(CompressParams p) {
       for (int nt = 0; nt < 4; ++nt) {
         const int t = tw0 + 16 * nt + n16;
         if (t < p.n_tok) {
-          const size_t off = lat_base + (size_t)(p.start + t) * r + 16 * mt + 4 * q4;
+          const int j0 = 16 * mt + 4 * q4;   // 4 consecutive channels stay contiguous in both layouts
+          const size_t off = lat_base + (k_tiled ? k_tiled_offset(p.start + t, j0, r) : (size_t)(p.start + t) * r + j0);
           if (kOutBf16) {
             const uint32_t w0 = (uint32_t)f32_to_bf16_bits(acc[nt][0]) | ((uint32_t)f32_to_bf16_bits(acc[nt][1]) << 16);
             const uint32_t w1 = (uint32_t)f32_to_bf16_bits(acc[nt][2]) | ((uint32_t)f32_to_bf16_bits(acc[nt][3]) << 16);
@@ -155,13 +157,15 @@ __global__ __launch_bounds__(256) void compress_valu(CompressParams p) {
     xs[idx] = p.in_bf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(X)[src]) : static_cast<const float*>(X)[src];
   }
   __syncthreads();
-  const size_t lat_base = (size_t)p.cap * ((size_t)b * R + r_pre);
+  const size_t lat_base = (size_t)cap_rows_of(p.cap) * ((size_t)b * R + r_pre);
+  const bool k_tiled = p.out_bf16 && kind == 0;
   for (int idx = threadIdx.x; idx < nt * r; idx += blockDim.x) {
     const int t = idx / r, j = idx - t * r;
     const float* x = xs + t * d;
     float acc = 0.f;
     for (int i = 0; i < d; ++i) acc = fmaf(x[i], P[(size_t)i * r + j], acc);
-    const size_t off = lat_base + (size_t)(p.start + t0 + t) * r + j;
+    const int row = p.start + t0 + t;
+    const size_t off = lat_base + (k_tiled ? k_tiled_offset(row, j, r) : (size_t)row * r + j);
     if (p.out_bf16)
       static_cast<uint16_t*>(kind ? p.lat_v : p.lat_k)[off] = f32_to_bf16_bits(acc);
     else
@@ -186,14 +190,16 @@ __global__ __launch_bounds__(128) void append_kernel(AppendParams p) {
     xs[i] = p.in_bf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(X)[src0 + i])
                       : static_cast<const float*>(X)[src0 + i];
   __syncthreads();
-  const size_t off0 = (size_t)p.cap * ((size_t)b * R + r_pre) + (size_t)pos * r;
+  const size_t base = (size_t)cap_rows_of(p.cap) * ((size_t)b * R + r_pre);
+  const bool k_tiled = p.out_bf16 && kind == 0;
   for (int j = threadIdx.x; j < r; j += blockDim.x) {
     float acc = 0.f;
     for (int i = 0; i < d; ++i) acc = fmaf(xs[i], P[(size_t)i * r + j], acc);
+    const size_t off = base + (k_tiled ? k_tiled_offset(pos, j, r) : (size_t)pos * r + j);
     if (p.out_bf16)
-      static_cast<uint16_t*>(kind ? p.lat_v : p.lat_k)[off0 + j] = f32_to_bf16_bits(acc);
+      static_cast<uint16_t*>(kind ? p.lat_v : p.lat_k)[off] = f32_to_bf16_bits(acc);
     else
-      static_cast<float*>(kind ? p.lat_v : p.lat_k)[off0 + j] = acc;
+      static_cast<float*>(kind ? p.lat_v : p.lat_k)[off] = acc;
   }
 }
 

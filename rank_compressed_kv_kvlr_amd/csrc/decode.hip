@@ -30,14 +30,14 @@ namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
-// Largest number of 64-lane value loads per 64-token tile over ranks r <= rb
+// Largest number of 64-lane value loads per tile of `tile` tokens over ranks r <= rb
 // (multiples of 16): a row has r/8 chunks of 8 channels, a load instruction
 // covers floor(64 / (r/8)) rows.
-constexpr int value_iters_bound(int rb) {
+constexpr int value_iters_bound(int rb, int tile) {
   int worst = 0;
   for (int r = 16; r <= rb; r += 16) {
     const int rpi = 64 / (r / 8);
-    const int it = (64 + rpi - 1) / rpi;
+    const int it = (tile + rpi - 1) / rpi;
     worst = it > worst ? it : worst;
   }
   return worst;
@@ -65,27 +65,31 @@ __device__ __forceinline__ void project_query(const DecodeParams& p, int b, int 
     __syncthreads();
     return;
   }
-  for (int idx = tid; idx < kHeadsPerWg * d; idx += blockDim.x) {
-    const int g = idx / d, i = idx - g * d;
-    q_lds[idx] = (g < gpw) ? p.q[((size_t)b * p.Hq + hq0 + g) * d + i] : 0.f;
-  }
-  __syncthreads();
   constexpr int NH = (RB + 63) / 64;      // 64-column halves of P
   constexpr int RPL = 16;                 // rows per lane bound: d / 16 <= 16
   const float* P = p.pk + (size_t)d * p.ht.rk_pre[h];
   const int isub = lane >> 4, m = lane & 15;
   const int rows_per_wave = d >> 2, rpl = d >> 4;
-#pragma unroll
-  for (int hf = 0; hf < NH; ++hf) {
+  float4 pr[RPL];
+  auto load_half = [&](int hf) {
     const int col = 64 * hf + 4 * m;
-    const bool cvalid = col < rk;
-    float4 pr[RPL];
 #pragma unroll
     for (int e = 0; e < RPL; ++e) {
       const int i = wave * rows_per_wave + isub + 4 * e;
-      pr[e] = (e < rpl && cvalid) ? *reinterpret_cast<const float4*>(P + (size_t)i * rk + col)
-                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+      pr[e] = (e < rpl && col < rk) ? *reinterpret_cast<const float4*>(P + (size_t)i * rk + col)
+                                    : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+  };
+  load_half(0);   // basis loads in flight together with the query rows
+  for (int idx = tid; idx < kHeadsPerWg * d; idx += blockDim.x) {
+    const int g = idx / d, i = idx - g * d;
+    q_lds[idx] = (g < gpw) ? p.q[((size_t)b * p.Hq + hq0 + g) * d + i] : 0.f;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int hf = 0; hf < NH; ++hf) {
+    const int col = 64 * hf + 4 * m;
+    if (hf > 0) load_half(hf);
     float part[4][4];
 #pragma unroll
     for (int g = 0; g < 4; ++g)
@@ -196,9 +200,30 @@ __device__ __forceinline__ void merge_waves_and_store(const DecodeParams& p, int
 //   registers before the records are read.
 constexpr int kTailLds = 12288;   // floats of LDS a split kernel provides for the merge tail
 
+// Float4s of P_V[h] each thread prefetches into registers when its split work
+// ends (RB * 128 floats: all of P_V[h] for head_dim 128), so the workgroup
+// that turns out to merge has the basis on chip already.
+template <int RB>
+struct BasisPrefetch {
+  static constexpr int kN = RB / 8;
+  float4 v[kN];
+};
+
+template <int RB>
+__device__ __forceinline__ void prefetch_basis(const DecodeParams& p, int h, int rv, BasisPrefetch<RB>& pf) {
+  if (!p.fuse) return;
+  const float* P = p.pv + (size_t)p.d * p.ht.rv_pre[h];
+  const int n4 = p.d * rv / 4;
+#pragma unroll
+  for (int k = 0; k < BasisPrefetch<RB>::kN; ++k) {
+    const int i = threadIdx.x + k * blockDim.x;
+    pf.v[k] = (i < n4) ? *reinterpret_cast<const float4*>(P + 4 * (size_t)i) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
 template <int RB>
 __device__ __forceinline__ void finish_split(const DecodeParams& p, int b, int h, int hg, int hq0, int gpw,
-                                             int rv, float* scratch) {
+                                             int rv, float* scratch, const BasisPrefetch<RB>& pf) {
   if (!p.fuse) return;
   int* flag = reinterpret_cast<int*>(scratch + kTailLds - 1);
   int* counter = p.counters + ((size_t)b * p.Hkv + h) * p.n_head_groups + hg;
@@ -216,15 +241,23 @@ __device__ __forceinline__ void finish_split(const DecodeParams& p, int b, int h
   const int pst = rv + 4;
   const int p_rows = min(d, (kTailLds - 4 * RB - 16) / pst);
   const float* P = p.pv + (size_t)d * p.ht.rv_pre[h];
-  auto stage_basis = [&](int r0, int nr) {
-    const int per_row4 = rv / 4;
+  const int per_row4 = rv / 4;
+  // rows [r0, r0 + nr) into LDS; float4 index i of P_V[h] below `have` is already in registers
+  auto stage_basis = [&](int r0, int nr, int have) {
     for (int i = tid; i < nr * per_row4; i += blockDim.x) {
       const int r = i / per_row4, c4 = i - r * per_row4;
-      *reinterpret_cast<float4*>(p_lds + r * pst + 4 * c4) =
-          *reinterpret_cast<const float4*>(P + (size_t)(r0 + r) * rv + 4 * c4);
+      if (r0 * per_row4 + i >= have)
+        *reinterpret_cast<float4*>(p_lds + r * pst + 4 * c4) =
+            *reinterpret_cast<const float4*>(P + (size_t)(r0 + r) * rv + 4 * c4);
     }
   };
-  stage_basis(0, p_rows);   // in flight together with the record loads below
+  const int have = BasisPrefetch<RB>::kN * (int)blockDim.x;
+#pragma unroll
+  for (int k = 0; k < BasisPrefetch<RB>::kN; ++k) {
+    const int i = tid + k * (int)blockDim.x, r = i / per_row4, c4 = i - r * per_row4;
+    if (r < p_rows) *reinterpret_cast<float4*>(p_lds + r * pst + 4 * c4) = pf.v[k];
+  }
+  stage_basis(0, p_rows, have);   // the rest (large head_dim), in flight with the record loads below
 
   // wave g folds the records of head g in one pass with a running maximum
   float M = kNegInf, L = 0.f, o0 = 0.f, o1 = 0.f;
@@ -263,7 +296,7 @@ __device__ __forceinline__ void finish_split(const DecodeParams& p, int b, int h
     const int nr = min(p_rows, d - r0);
     if (r0 > 0) {
       __syncthreads();
-      stage_basis(r0, nr);
+      stage_basis(r0, nr, 0);
       __syncthreads();
     }
     for (int r = tid; r < nr; r += blockDim.x) {
@@ -295,10 +328,12 @@ __device__ __forceinline__ void finish_split(const DecodeParams& p, int b, int h
 // ---------------------------------------------------------------------------
 // RB: rank bound (32, 64, 96 or 128) sizing the register tiles; the actual
 // per-head ranks are runtime values <= RB (multiples of 16).
-template <int RB>
+// TT: tokens per wave iteration (32 or 64), i.e. TT/16 MFMA column blocks.
+template <int RB, int TT>
 __global__ __launch_bounds__(256) void decode_split_bf16(DecodeParams p) {
+  constexpr int NB = TT / 16;
   constexpr int NP = RB / 32;                 // full 32-channel key pairs
-  constexpr int NIT = value_iters_bound(RB);  // bound on value iterations (see n_it below)
+  constexpr int NIT = value_iters_bound(RB, TT);  // bound on value iterations (see n_it below)
   constexpr int QTS = RB;                     // q~ LDS row stride
   __shared__ __attribute__((aligned(16))) float smem[kWaves * 64 * 4 * 8 + 64 > kTailLds ? kWaves * 64 * 4 * 8 + 64 : kTailLds];
 
@@ -314,7 +349,9 @@ __global__ __launch_bounds__(256) void decode_split_bf16(DecodeParams p) {
   const int t_end = min(T, t_begin + p.split_len);
   if (t_begin >= t_end) {
     write_empty_records(p, b, hq0, gpw, s, rv);
-    finish_split<RB>(p, b, h, hg, hq0, gpw, rv, smem);
+    BasisPrefetch<RB> pf;
+    prefetch_basis<RB>(p, h, rv, pf);
+    finish_split<RB>(p, b, h, hg, hq0, gpw, rv, smem, pf);
     return;
   }
 
@@ -328,12 +365,13 @@ __global__ __launch_bounds__(256) void decode_split_bf16(DecodeParams p) {
   const int rpi = 64 / C;                 // rows per load instruction
   const int ro = lane / C, cch = lane - ro * C;
   const bool v_active = ro < rpi;
-  const int n_it = (64 + rpi - 1) / rpi;  // <= NIT
+  const int n_it = (TT + rpi - 1) / rpi;  // <= NIT
 
-  const uint16_t* Kb = static_cast<const uint16_t*>(p.lat_k) + (size_t)p.cap * ((size_t)b * p.Rk + p.ht.rk_pre[h]);
-  const uint16_t* Vb = static_cast<const uint16_t*>(p.lat_v) + (size_t)p.cap * ((size_t)b * p.Rv + p.ht.rv_pre[h]);
+  const size_t rows = cap_rows_of(p.cap);
+  const uint16_t* Kb = static_cast<const uint16_t*>(p.lat_k) + rows * ((size_t)b * p.Rk + p.ht.rk_pre[h]);
+  const uint16_t* Vb = static_cast<const uint16_t*>(p.lat_v) + rows * ((size_t)b * p.Rv + p.ht.rv_pre[h]);
 
-  float* p_lds = smem + wave * (64 * 4);  // [64 tokens][4 heads] per wave
+  float* p_lds = smem + wave * (TT * 4);  // [TT tokens][4 heads] per wave
 
   float m[4], l[4], acc[4][8];
 #pragma unroll
@@ -344,19 +382,24 @@ __global__ __launch_bounds__(256) void decode_split_bf16(DecodeParams p) {
     for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
   }
 
-  u32x4_t kreg[4][NP];
-  u32x2_t ktail[4];
+  u32x4_t kreg[NB][NP];
+  u32x2_t ktail[NB];
   u32x4_t vreg[NIT];
 
+  // key latents are stored in MFMA operand order (k_tiled_offset): lane l reads
+  // 16 contiguous bytes at 16 l within each 1 KiB pair block of a 16-row block.
+  // Blocks entirely past the valid rows re-read the last valid block; their
+  // scores are masked.
+  const int last_blk = (t_end - 1) >> 4;
   auto load_k = [&](int t0) {
 #pragma unroll
-    for (int blk = 0; blk < 4; ++blk) {
-      const int t = min(t0 + 16 * blk + n16, t_end - 1);
-      const uint16_t* row = Kb + (size_t)t * rk;
+    for (int blk = 0; blk < NB; ++blk) {
+      const int kb16 = min((t0 >> 4) + blk, last_blk);
+      const uint16_t* kblk = Kb + (size_t)kb16 * 16 * rk;
 #pragma unroll
       for (int pp = 0; pp < NP; ++pp)
-        if (pp < np) kreg[blk][pp] = load_stream16(row + 32 * pp + 8 * q4);
-      if (tail) ktail[blk] = load_stream8(row + 32 * np + 4 * q4);
+        if (pp < np) kreg[blk][pp] = load_stream16(kblk + pp * 512 + lane * 8);
+      if (tail) ktail[blk] = load_stream8(kblk + np * 512 + lane * 4);
     }
   };
   auto load_v = [&](int t0) {
@@ -364,14 +407,14 @@ __global__ __launch_bounds__(256) void decode_split_bf16(DecodeParams p) {
     for (int it = 0; it < NIT; ++it) {
       if (it < n_it) {
         const int r = it * rpi + ro;
-        const int t = min(t0 + min(r, 63), t_end - 1);
+        const int t = min(t0 + min(r, TT - 1), t_end - 1);
         vreg[it] = load_stream16(Vb + (size_t)t * rv + 8 * cch);
       }
     }
   };
 
   // the first tile's loads do not depend on q~: issue them before the prologue
-  int t0 = t_begin + wave * kTile;
+  int t0 = t_begin + wave * TT;
   if (t0 < t_end) {
     load_k(t0);
     load_v(t0);
@@ -409,12 +452,12 @@ __global__ __launch_bounds__(256) void decode_split_bf16(DecodeParams p) {
   __syncthreads();   // LDS is reused below
 
 
-  for (; t0 < t_end; t0 += kWaves * kTile) {
-    const int t_next = t0 + kWaves * kTile;
+  for (; t0 < t_end; t0 += kWaves * TT) {
+    const int t_next = t0 + kWaves * TT;
     // ---- scores on MFMA
-    f32x4_t sc[4];
+    f32x4_t sc[NB];
 #pragma unroll
-    for (int blk = 0; blk < 4; ++blk) {
+    for (int blk = 0; blk < NB; ++blk) {
       f32x4_t d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int pp = 0; pp < NP; ++pp) {
@@ -439,7 +482,7 @@ __global__ __launch_bounds__(256) void decode_split_bf16(DecodeParams p) {
     for (int i = 0; i < 4; ++i) {
       float mx = kNegInf;
 #pragma unroll
-      for (int blk = 0; blk < 4; ++blk) {
+      for (int blk = 0; blk < NB; ++blk) {
         const bool valid = (t0 + 16 * blk + n16) < t_end;
         sc[blk][i] = valid ? sc[blk][i] : kNegInf;
         mx = fmaxf(mx, sc[blk][i]);
@@ -450,7 +493,7 @@ __global__ __launch_bounds__(256) void decode_split_bf16(DecodeParams p) {
       alpha[i] = fast_exp2(m[i] - m_use);
       float ls = 0.f;
 #pragma unroll
-      for (int blk = 0; blk < 4; ++blk) {
+      for (int blk = 0; blk < NB; ++blk) {
         const float pr = fast_exp2(sc[blk][i] - m_use);
         sc[blk][i] = pr;
         ls += pr;
@@ -460,7 +503,7 @@ __global__ __launch_bounds__(256) void decode_split_bf16(DecodeParams p) {
     }
     if (q4 == 0) {
 #pragma unroll
-      for (int blk = 0; blk < 4; ++blk)
+      for (int blk = 0; blk < NB; ++blk)
         *reinterpret_cast<float4*>(p_lds + (16 * blk + n16) * 4) =
             make_float4(sc[blk][0], sc[blk][1], sc[blk][2], sc[blk][3]);
     }
@@ -483,7 +526,7 @@ __global__ __launch_bounds__(256) void decode_split_bf16(DecodeParams p) {
     for (int it = 0; it < NIT; ++it) {
       if (it < n_it) {
         const int r = it * rpi + ro;
-        if (v_active && r < 64) {
+        if (v_active && r < TT) {
           const float4 pw = *reinterpret_cast<const float4*>(p_lds + r * 4);
           const u32x4_t w = vreg[it];
           const float v[8] = {bf16lo_to_f32(w.x), bf16hi_to_f32(w.x), bf16lo_to_f32(w.y), bf16hi_to_f32(w.y),
@@ -504,6 +547,8 @@ __global__ __launch_bounds__(256) void decode_split_bf16(DecodeParams p) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 
+  BasisPrefetch<RB> pf;
+  prefetch_basis<RB>(p, h, rv, pf);
   // ---- workgroup merge of the 4 waves
 #pragma unroll
   for (int i = 0; i < 4; ++i) l[i] = row16_allreduce<false>(l[i]);
@@ -531,7 +576,7 @@ __global__ __launch_bounds__(256) void decode_split_bf16(DecodeParams p) {
     for (int r = 0; r < rpi; ++r) sum += red[((w * 64 + r * C + c) * 4 + g) * 8 + e];
     return sum;
   });
-  finish_split<RB>(p, b, h, hg, hq0, gpw, rv, smem);
+  finish_split<RB>(p, b, h, hg, hq0, gpw, rv, smem, pf);
 }
 
 // ---------------------------------------------------------------------------
@@ -558,7 +603,9 @@ __global__ __launch_bounds__(256) void decode_split_f32(DecodeParams p) {
   const int t_end = min(T, t_begin + p.split_len);
   if (t_begin >= t_end) {
     write_empty_records(p, b, hq0, gpw, s, rv);
-    finish_split<RB>(p, b, h, hg, hq0, gpw, rv, smem);
+    BasisPrefetch<RB> pf;
+    prefetch_basis<RB>(p, h, rv, pf);
+    finish_split<RB>(p, b, h, hg, hq0, gpw, rv, smem, pf);
     return;
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -570,8 +617,9 @@ __global__ __launch_bounds__(256) void decode_split_f32(DecodeParams p) {
   float* wl = wm + 16;
   project_query<RB>(p, b, h, hq0, gpw, rk, q_lds, red, qt_lds);
 
-  const float* Kb = static_cast<const float*>(p.lat_k) + (size_t)p.cap * ((size_t)b * p.Rk + p.ht.rk_pre[h]);
-  const float* Vb = static_cast<const float*>(p.lat_v) + (size_t)p.cap * ((size_t)b * p.Rv + p.ht.rv_pre[h]);
+  const size_t rows = cap_rows_of(p.cap);
+  const float* Kb = static_cast<const float*>(p.lat_k) + rows * ((size_t)b * p.Rk + p.ht.rk_pre[h]);
+  const float* Vb = static_cast<const float*>(p.lat_v) + rows * ((size_t)b * p.Rv + p.ht.rv_pre[h]);
   // per-wave probability tile lives in the (not yet used) reduction area
   float* p_lds = red + wave * 64 * 4;
 
@@ -640,6 +688,8 @@ __global__ __launch_bounds__(256) void decode_split_f32(DecodeParams p) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
+  BasisPrefetch<RB> pf;
+  prefetch_basis<RB>(p, h, rv, pf);
 #pragma unroll
   for (int i = 0; i < 4; ++i) l[i] = wave_allreduce<false>(l[i]);
   __syncthreads();
@@ -660,7 +710,7 @@ __global__ __launch_bounds__(256) void decode_split_f32(DecodeParams p) {
   __syncthreads();
   merge_waves_and_store(p, b, hq0, gpw, s, rv, wm, wl,
                         [&](int w, int g, int j) { return red[(w * 4 + g) * RB + j]; });
-  finish_split<RB>(p, b, h, hg, hq0, gpw, rv, smem);
+  finish_split<RB>(p, b, h, hg, hq0, gpw, rv, smem, pf);
 }
 
 // ---------------------------------------------------------------------------
@@ -793,15 +843,24 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge(MergeParams p) {
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeParams& p, int latent_bf16, int rank_bound, hipStream_t stream) {
+hipError_t launch_decode(const DecodeParams& p, int latent_bf16, int rank_bound, int tile, hipStream_t stream) {
   const dim3 grid(p.n_splits, p.Hkv * p.n_head_groups, p.B);
   const dim3 block(kWaves * 64);
   if (latent_bf16) {
-    switch (rank_bound) {
-      case 32: hipLaunchKernelGGL(decode_split_bf16<32>, grid, block, 0, stream, p); break;
-      case 64: hipLaunchKernelGGL(decode_split_bf16<64>, grid, block, 0, stream, p); break;
-      case 96: hipLaunchKernelGGL(decode_split_bf16<96>, grid, block, 0, stream, p); break;
-      default: hipLaunchKernelGGL(decode_split_bf16<128>, grid, block, 0, stream, p); break;
+    if (tile == 32) {
+      switch (rank_bound) {
+        case 32: hipLaunchKernelGGL((decode_split_bf16<32, 32>), grid, block, 0, stream, p); break;
+        case 64: hipLaunchKernelGGL((decode_split_bf16<64, 32>), grid, block, 0, stream, p); break;
+        case 96: hipLaunchKernelGGL((decode_split_bf16<96, 32>), grid, block, 0, stream, p); break;
+        default: hipLaunchKernelGGL((decode_split_bf16<128, 32>), grid, block, 0, stream, p); break;
+      }
+    } else {
+      switch (rank_bound) {
+        case 32: hipLaunchKernelGGL((decode_split_bf16<32, 64>), grid, block, 0, stream, p); break;
+        case 64: hipLaunchKernelGGL((decode_split_bf16<64, 64>), grid, block, 0, stream, p); break;
+        case 96: hipLaunchKernelGGL((decode_split_bf16<96, 64>), grid, block, 0, stream, p); break;
+        default: hipLaunchKernelGGL((decode_split_bf16<128, 64>), grid, block, 0, stream, p); break;
+      }
     }
   } else {
     switch (rank_bound) {

@@ -79,8 +79,26 @@ struct AppendParams {
   HeadTable ht;
 };
 
+// Rows allocated per (batch row, KV head) block: the capacity rounded up to
+// whole 16-row MFMA blocks.
+__host__ __device__ inline int cap_rows_of(int cap) { return (cap + 15) & ~15; }
+
+// Offset (elements) of bf16 key latent (t, j) inside its (batch row, KV head)
+// block, rank rk (a multiple of 16). Each 16-row block holds the rows in the
+// order the score MFMA reads its B operand: for every 32-channel pair
+// [lane group q][token n][8 channels], then a 16-channel tail as
+// [q][n][4 channels]; a 64-lane load then reads 1 KiB (512 B for the tail)
+// contiguously.
+__host__ __device__ inline size_t k_tiled_offset(int t, int j, int rk) {
+  const size_t base = (size_t)(t >> 4) * 16 * rk;
+  const int n = t & 15, np = rk >> 5;
+  if (j < 32 * np) return base + (size_t)(j >> 5) * 512 + ((j >> 3) & 3) * 128 + n * 8 + (j & 7);
+  const int jj = j - 32 * np;
+  return base + (size_t)np * 512 + (jj >> 2) * 64 + n * 4 + (jj & 3);
+}
+
 // Launchers (return hipGetLastError() of their launches).
-hipError_t launch_decode(const DecodeParams& p, int latent_bf16, int rank_bound, hipStream_t s);
+hipError_t launch_decode(const DecodeParams& p, int latent_bf16, int rank_bound, int tile, hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, int rank_bound, hipStream_t s);
 hipError_t launch_compress(const CompressParams& p, hipStream_t s);
 hipError_t launch_append(const AppendParams& p, hipStream_t s);

@@ -72,8 +72,23 @@ def test_fp32_latents_allow_rank_multiple_of_four():
 def test_cache_elems_and_layout():
     d = _desc(r_k=[16, 48], r_v=[32, 80], capacity=100)
     nk, nv = kv.cache_elems(d)
-    assert nk == 2 * 100 * 64 and nv == 2 * 100 * 112
+    assert nk == 2 * 112 * 64 and nv == 2 * 112 * 112     # capacity rounded up to 16 rows
     assert list(d.rank_offsets("v")) == [0, 32, 112]
+
+
+@pytest.mark.parametrize("r", [16, 32, 48, 64, 80, 96, 112, 128])
+def test_key_tile_order_is_a_permutation_of_each_block(r):
+    """The MFMA-order key layout maps every (t, j) of a 16-row block to a distinct slot of that block."""
+    idx = kv.k_tiled_index(64, r)
+    for blk in range(4):
+        sub = idx[16 * blk:16 * blk + 16]
+        assert sub.min() == 16 * r * blk and sub.max() == 16 * r * (blk + 1) - 1
+        assert len(np.unique(sub)) == 16 * r
+    # lane l = 16 q + n of pair p reads 16 contiguous bytes: token n, channels 32 p + 8 q .. + 7
+    for p in range(r // 32):
+        for lane in range(64):
+            q, n = lane // 16, lane % 16
+            assert list(idx[n, 32 * p + 8 * q:32 * p + 8 * q + 8]) == list(range(512 * p + 8 * lane, 512 * p + 8 * lane + 8))
 
 
 def test_workspace_and_plan():

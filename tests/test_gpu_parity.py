@@ -87,7 +87,7 @@ def test_prefill_compress_matches_oracle(gpu, cid, extra):
             n = case.n_rows
             for which, P, r in (("k", case.P32K[h], rk[h]), ("v", case.P32V[h], rv[h])):
                 X = case.host_rows(which, b, h, n)
-                lat = kv.head_view(case.lat_k if which == "k" else case.lat_v, case.desc, which, b, h)[:n]
+                lat = kv.latent_rows(case.lat_k if which == "k" else case.lat_v, case.desc, which, b, h)[:n]
                 got = lat.float().cpu().numpy().astype(np.float64)
                 assert_latents_close(got, X, P, cfg.latent_dtype)
 
@@ -184,8 +184,8 @@ def test_gqa_equals_mha_with_repeated_heads(gpu):
     lk, lv = kv.alloc_cache(desc)
     for b in range(cfg.B):
         for i in range(8):
-            kv.head_view(lk, desc, "k", b, i).copy_(kv.head_view(case.lat_k, case.desc, "k", b, i // 4))
-            kv.head_view(lv, desc, "v", b, i).copy_(kv.head_view(case.lat_v, case.desc, "v", b, i // 4))
+            kv.block_view(lk, desc, "k", b, i).copy_(kv.block_view(case.lat_k, case.desc, "k", b, i // 4))
+            kv.block_view(lv, desc, "v", b, i).copy_(kv.block_view(case.lat_v, case.desc, "v", b, i // 4))
     pk = kv.pack_bases([case.PK[i // 4] for i in range(8)])
     pv = kv.pack_bases([case.PV[i // 4] for i in range(8)])
     o = kv.decode_attn(desc, torch.from_numpy(q).cuda(), pk, pv, lk, lv, torch.from_numpy(lens).cuda())
@@ -219,8 +219,8 @@ def test_per_head_ranks_equal_single_head_calls(gpu):
         desc = kv.Desc(cfg.B, G, 1, cfg.d, cfg.capacity, rk[h], rv[h], kv.BF16, kv.BF16)
         lk, lv = kv.alloc_cache(desc)
         for b in range(cfg.B):
-            kv.head_view(lk, desc, "k", b, 0).copy_(kv.head_view(case.lat_k, case.desc, "k", b, h))
-            kv.head_view(lv, desc, "v", b, 0).copy_(kv.head_view(case.lat_v, case.desc, "v", b, h))
+            kv.block_view(lk, desc, "k", b, 0).copy_(kv.block_view(case.lat_k, case.desc, "k", b, h))
+            kv.block_view(lv, desc, "v", b, 0).copy_(kv.block_view(case.lat_v, case.desc, "v", b, h))
         qh = np.ascontiguousarray(q[:, h * G:(h + 1) * G])
         o = kv.decode_attn(desc, torch.from_numpy(qh).cuda(), kv.pack_bases([case.PK[h]]),
                            kv.pack_bases([case.PV[h]]), lk, lv, torch.from_numpy(lens).cuda())
@@ -257,8 +257,8 @@ def test_append_matches_oracle_and_prefill(gpu, cid):
         f = full.lat_k if which == "k" else full.lat_v
         for b in range(cfg.B):
             for h in range(cfg.Hkv):
-                got = kv.head_view(a, case.desc, which, b, h)[:T + 3].float().cpu().numpy().astype(np.float64)
-                ref = kv.head_view(f, full.desc, which, b, h)[:T + 3].float().cpu().numpy().astype(np.float64)
+                got = kv.latent_rows(a, case.desc, which, b, h)[:T + 3].float().cpu().numpy().astype(np.float64)
+                ref = kv.latent_rows(f, full.desc, which, b, h)[:T + 3].float().cpu().numpy().astype(np.float64)
                 P = (case.P32K if which == "k" else case.P32V)[h]
                 X = case.host_rows(which, b, h, 3, t0=T)
                 assert_latents_close(got[T:], X, P, cfg.latent_dtype, exact_frac=0.9)
@@ -349,7 +349,7 @@ def test_latent_guard_bands(gpu):
     # untouched rows keep the canary too: rows 0..39 (except row 5 of batch 1), 100, 101 of batch 1
     for b in range(cfg.B):
         for h in range(cfg.Hkv):
-            rows = kv.head_view(lk, desc, "k", b, h)
+            rows = kv.latent_rows(lk, desc, "k", b, h)
             written = set(range(40, 100)) | {int(pos[b])}
             for t in (0, 39, 100, 101):
                 expect_canary = t not in written
