@@ -195,6 +195,22 @@ def main():
         step(k, evs[k])
     torch.cuda.synchronize()
 
+    # folded form (q_lat = q P_K in, o_lat out, P_V^T left to the caller's output projection)
+    q_lat = torch.zeros((B, cfg.Hq, int(rk.max())), dtype=torch.float32, device="cuda")
+    rk_pre = np.concatenate([[0], np.cumsum(rk)])
+    for i in range(cfg.Hq):
+        h = i // cfg.G
+        q_lat[:, i, :int(rk[h])] = q[:, i] @ pk[d * int(rk_pre[h]): d * int(rk_pre[h + 1])].view(d, int(rk[h]))
+    o_lat = torch.empty((B, cfg.Hq, int(rv.max())), dtype=torch.float32, device="cuda")
+    fevs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        lk, lv = replicas[k % 2]
+        fevs[k][0].record()
+        kv.decode_attn_latent(desc, q_lat, lk, lv, lens, o_lat=o_lat, workspace=ws, split_tokens=split)
+        fevs[k][1].record()
+    torch.cuda.synchronize()
+    folded_us = float(np.mean([e[0].elapsed_time(e[1]) * 1e3 for e in fevs]))
+
     if args.traffic_reference:
         from synth.device import copy as device_copy
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
@@ -232,10 +248,12 @@ def main():
         "step_hbm_GBps": alg_bytes / (elapsed / args.steps) / 1e9,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "kernel": "decode_split_bf16 (kvlr_decode_attn, merge fused)", "bytes_per_launch": alg_bytes,
+                     "kernel": "decode_split_bf16<64, 32> (kvlr_decode_attn, merge fused)", "bytes_per_launch": alg_bytes,
                      "launch_us_mean": float(split_us.mean()), "launch_us_p10": float(np.percentile(split_us, 10)),
                      "launch_us_p90": float(np.percentile(split_us, 90))},
     }
+    result["folded"] = {"entry": "kvlr_decode_attn_latent", "launch_us_mean": folded_us,
+                        "GBps": alg_bytes / (folded_us * 1e-6) / 1e9}
     if prefill is not None:
         result["prefill"] = prefill
     if not args.no_cpu_baseline:

@@ -188,6 +188,24 @@ KVLR_API int kvlr_decode_attn(const kvlr_desc* desc, const float* q, const float
                               float* out, void* workspace, size_t workspace_bytes, int32_t split_tokens,
                               void* stream);
 
+/* Folded decode: the bases are folded into the attention projections
+ * (StiefAttention technical summary, "Mecanismo Central" item 5: the
+ * projection bases can be incorporated into the attention linear weights;
+ * STAR-KV "Metodologia" section 2: reconstruction absorbed into the output
+ * projection). The caller supplies the query already in key latent space and
+ * receives the normalised latent output, to be multiplied by its output
+ * projection with P_V folded in:
+ *   o_lat[b, i, :] = softmax_t(K_lat[b, h, t] . q_lat[b, i] * scale) V_lat[b, h, t]
+ *   q_lat     device fp32 [B][Hq][rk_max], rk_max = max_h r_k[h]; row i reads
+ *             its first r_k[i / G] entries
+ *   o_lat     device fp32 [B][Hq][rv_max], rv_max = max_h r_v[h]; entries
+ *             j >= r_v[i / G] are written as zero; empty caches give zero rows
+ * Other arguments as in kvlr_decode_attn (one launch; same workspace rules). */
+KVLR_API int kvlr_decode_attn_latent(const kvlr_desc* desc, const float* q_lat, const void* lat_k,
+                                     const void* lat_v, const int32_t* seq_lens, float scale, float* o_lat,
+                                     void* workspace, size_t workspace_bytes, int32_t split_tokens,
+                                     void* stream);
+
 /* The two stages of kvlr_decode_attn, for callers that schedule them
  * separately (e.g. to time or overlap them). kvlr_decode_attn(...) is
  * exactly kvlr_decode_partials(...) followed by kvlr_decode_combine(...) on

@@ -17,12 +17,16 @@ What it computes (all in float64, plain numpy, no blocking or fusion):
   (STAR-KV technical summary, "Metodologia" section 1, "Inferenza": hard
   thresholds truncate the projections per decoder block and attention head);
 * the same quantity in latent order, q~ = q P_K, scores K_lat q~, and
-  (p V_lat) P_V^T, which is equal by associativity.
+  (p V_lat) P_V^T, which is equal by associativity;
+* the folded form, where the bases sit in the caller's query and output
+  projections: q~ in, o_lat = p V_lat out (StiefAttention, "Mecanismo
+  Central" item 5; STAR-KV, "Metodologia" section 2).
 
 Pins (tests/test_oracle_pins.py): orthonormality of the bases, the textbook
 softmax attention at full rank, invariance under P -> P O, definition mode
 equals latent mode, a 50-digit mpmath brute force on tiny shapes, closed
-forms (T=1, q=0, T=2, values inside span(P_V)), hand-derived golden
+forms (T=1, q=0, T=2, values inside span(P_V)), the folded output against
+the brute force through o_lat = o P_V, hand-derived golden
 examples under tests/golden/, and a planted-mistake battery showing that a
 dropped term, a wrong scale, a swapped basis, a wrong head mapping or an
 off-by-one length each fails at least one pin. No function here is
@@ -37,6 +41,8 @@ from .kvlr_oracle import (  # noqa: F401
     attend_latent,
     decode,
     decode_latents,
+    attend_folded,
+    decode_folded,
     decode_head_reconstructed,
     decode_head_latent,
     kv_head_of,

@@ -138,3 +138,40 @@ def decode_latents(q, lat_k, lat_v, P_K, P_V, lens, scale) -> np.ndarray:
             out[b, i] = attend_latent(q[b, i], np.asarray(lat_k[b][h])[:T], np.asarray(lat_v[b][h])[:T],
                                       P_K[h], P_V[h], scale)
     return out
+
+
+def attend_folded(q_lat, K_lat, V_lat, scale) -> np.ndarray:
+    """Folded form for one query over one KV head: the bases live in the caller's
+    projections (StiefAttention technical summary, "Mecanismo Central" item 5,
+    bases incorporated into the attention linear weights; STAR-KV technical
+    summary, "Metodologia" section 2, reconstruction absorbed into the output
+    projection). In: q_lat = q P_K [r_k]. Out: o_lat = softmax(K_lat q_lat * scale) V_lat
+    [r_v], so that o = o_lat P_V^T. Zero row when T = 0.
+    """
+    K_lat = np.asarray(K_lat, np.float64)
+    V_lat = np.asarray(V_lat, np.float64)
+    if K_lat.shape[0] == 0:
+        return np.zeros(V_lat.shape[1])
+    p = softmax((K_lat @ np.asarray(q_lat, np.float64)) * scale)
+    return p @ V_lat
+
+
+def decode_folded(q_lat, lat_k, lat_v, lens, scale, Hkv: int) -> np.ndarray:
+    """Folded form over a batch.
+
+    q_lat [B][Hq][>= r_k(h)] (query head i reads its first r_k entries, h = i // G);
+    lat_k[b][h], lat_v[b][h]: [>= lens[b]][r]. Returns o_lat [B][Hq][max r_v],
+    entries past a head's r_v zero.
+    """
+    q_lat = np.asarray(q_lat, np.float64)
+    B, Hq = q_lat.shape[:2]
+    rv_max = max(np.asarray(lat_v[0][h]).shape[1] for h in range(Hkv))
+    out = np.zeros((B, Hq, rv_max))
+    for b in range(B):
+        T = int(lens[b])
+        for i in range(Hq):
+            h = kv_head_of(i, Hq, Hkv)
+            Kl, Vl = np.asarray(lat_k[b][h]), np.asarray(lat_v[b][h])
+            rk, rv = Kl.shape[1], Vl.shape[1]
+            out[b, i, :rv] = attend_folded(q_lat[b, i, :rk], Kl[:T], Vl[:T], scale)
+    return out

@@ -15,7 +15,9 @@ Entry points mirror the C ABI:
 * ``append(desc, k_new, v_new, pos, P_K, P_V, lat_k, lat_v)`` stores one
   token per batch row at row pos[b];
 * ``decode_attn(desc, q, P_K, P_V, lat_k, lat_v, seq_lens, scale, out, workspace)``
-  computes softmax((K_lat P_K^T) q * scale) (V_lat P_V^T) in latent order.
+  computes softmax((K_lat P_K^T) q * scale) (V_lat P_V^T) in latent order;
+* ``decode_attn_latent(desc, q_lat, lat_k, lat_v, seq_lens, scale, o_lat)``
+  is the folded form: q_lat = q P_K in, o_lat out (P_V^T left to the caller).
 """
 from __future__ import annotations
 
@@ -29,7 +31,7 @@ import numpy as np
 __all__ = [
     "KvlrError", "Desc", "F32", "BF16", "lib", "version", "status_string",
     "cache_elems", "decode_workspace_bytes", "decode_plan", "decode_counter_bytes",
-    "prefill_compress", "append", "decode_attn", "decode_partials", "decode_combine",
+    "prefill_compress", "append", "decode_attn", "decode_partials", "decode_combine", "decode_attn_latent",
     "alloc_cache", "alloc_workspace", "pack_bases", "block_view", "latent_rows", "cap_rows", "k_tiled_index",
 ]
 
@@ -72,8 +74,11 @@ lib.kvlr_decode_attn.argtypes = [_D, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P,
                                  ctypes.c_int32, _P]
 lib.kvlr_decode_partials.argtypes = [_D, _P, _P, _P, _P, _P, ctypes.c_float, _P, ctypes.c_size_t, ctypes.c_int32, _P]
 lib.kvlr_decode_combine.argtypes = [_D, _P, _P, ctypes.c_size_t, ctypes.c_int32, _P, _P]
+lib.kvlr_decode_attn_latent.argtypes = [_D, _P, _P, _P, _P, ctypes.c_float, _P, _P, ctypes.c_size_t,
+                                        ctypes.c_int32, _P]
 for _f in ("kvlr_cache_elems", "kvlr_decode_workspace_bytes", "kvlr_decode_plan", "kvlr_decode_counter_bytes", "kvlr_prefill_compress",
-           "kvlr_append", "kvlr_decode_attn", "kvlr_decode_partials", "kvlr_decode_combine"):
+           "kvlr_append", "kvlr_decode_attn", "kvlr_decode_partials", "kvlr_decode_combine",
+           "kvlr_decode_attn_latent"):
     getattr(lib, _f).restype = ctypes.c_int
 
 
@@ -328,3 +333,26 @@ def decode_combine(desc: Desc, P_V, workspace, out, split_tokens: int = 0):
             _need(out, "out", torch.float32, desc.batch * desc.n_q_heads * desc.head_dim))
     _check(lib.kvlr_decode_combine(desc.ptr, *args, _stream()), "kvlr_decode_combine")
     return out
+
+
+def decode_attn_latent(desc: Desc, q_lat, lat_k, lat_v, seq_lens, scale: Optional[float] = None, o_lat=None,
+                       workspace=None, split_tokens: int = 0):
+    """Folded decode: q_lat [B][Hq][max r_k] (query in key latent space) -> o_lat [B][Hq][max r_v]."""
+    torch = _torch()
+    if scale is None:
+        scale = 1.0 / math.sqrt(desc.head_dim)
+    rk_max, rv_max = int(desc.r_k.max()), int(desc.r_v.max())
+    if o_lat is None:
+        o_lat = torch.empty((desc.batch, desc.n_q_heads, rv_max), dtype=torch.float32, device=q_lat.device)
+    if workspace is None:
+        workspace = alloc_workspace(desc, split_tokens, q_lat.device)
+    nk, nv = cache_elems(desc)
+    lad = _dtype_of(desc.latent_dtype)
+    args = (_need(q_lat, "q_lat", torch.float32, desc.batch * desc.n_q_heads * rk_max),
+            _need(lat_k, "lat_k", lad, nk), _need(lat_v, "lat_v", lad, nv),
+            _need(seq_lens, "seq_lens", torch.int32, desc.batch), ctypes.c_float(scale),
+            _need(o_lat, "o_lat", torch.float32, desc.batch * desc.n_q_heads * rv_max),
+            _need(workspace, "workspace", workspace.dtype),
+            ctypes.c_size_t(workspace.numel() * workspace.element_size()), split_tokens)
+    _check(lib.kvlr_decode_attn_latent(desc.ptr, *args, _stream()), "kvlr_decode_attn_latent")
+    return o_lat

@@ -259,6 +259,8 @@ int prepare_decode(const kvlr_desc* desc, const float* q, const float* P_K, cons
   p->lat_k = lat_k;
   p->lat_v = lat_v;
   p->seq_lens = seq_lens;
+  p->out_latent = 0;
+  p->out_stride = desc->head_dim;
   p->counters = static_cast<int*>(workspace);
   p->ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + cbytes);
   p->pv = P_V;
@@ -330,6 +332,34 @@ KVLR_API int kvlr_decode_attn(const kvlr_desc* desc, const float* q, const float
                                 workspace_bytes, split_tokens, &p, &m, &rank_bound);
   if (rc) return rc;
   p.fuse = 1;   // one launch: the last split workgroup of each group merges and back-projects
+  return hip_status(kvlr::launch_decode(p, desc->latent_dtype == KVLR_BF16, rank_bound, decode_tile(),
+                                        static_cast<hipStream_t>(stream)));
+}
+
+KVLR_API int kvlr_decode_attn_latent(const kvlr_desc* desc, const float* q_lat, const void* lat_k,
+                                     const void* lat_v, const int32_t* seq_lens, float scale, float* o_lat,
+                                     void* workspace, size_t workspace_bytes, int32_t split_tokens,
+                                     void* stream) {
+  kvlr::DecodeParams p;
+  kvlr::MergeParams m;
+  int rank_bound = 0;
+  // q_lat stands in for q and P_K (checked non-NULL through the same slots); no P_V is read
+  const int rc = prepare_decode(desc, q_lat, q_lat, lat_k, lat_v, seq_lens, scale, q_lat, o_lat, true, true,
+                                workspace, workspace_bytes, split_tokens, &p, &m, &rank_bound);
+  if (rc) return rc;
+  int rk_max = 0, rv_max = 0;
+  for (int h = 0; h < desc->n_kv_heads; ++h) {
+    rk_max = desc->r_k[h] > rk_max ? desc->r_k[h] : rk_max;
+    rv_max = desc->r_v[h] > rv_max ? desc->r_v[h] : rv_max;
+  }
+  p.q = nullptr;
+  p.pk = nullptr;
+  p.pv = nullptr;
+  p.qt_in = q_lat;
+  p.qt_stride = rk_max;
+  p.out_latent = 1;
+  p.out_stride = rv_max;
+  p.fuse = 1;
   return hip_status(kvlr::launch_decode(p, desc->latent_dtype == KVLR_BF16, rank_bound, decode_tile(),
                                         static_cast<hipStream_t>(stream)));
 }

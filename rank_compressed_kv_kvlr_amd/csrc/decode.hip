@@ -211,7 +211,7 @@ struct BasisPrefetch {
 
 template <int RB>
 __device__ __forceinline__ void prefetch_basis(const DecodeParams& p, int h, int rv, BasisPrefetch<RB>& pf) {
-  if (!p.fuse) return;
+  if (!p.fuse || p.out_latent) return;
   const float* P = p.pv + (size_t)p.d * p.ht.rv_pre[h];
   const int n4 = p.d * rv / 4;
 #pragma unroll
@@ -251,13 +251,15 @@ __device__ __forceinline__ void finish_split(const DecodeParams& p, int b, int h
             *reinterpret_cast<const float4*>(P + (size_t)(r0 + r) * rv + 4 * c4);
     }
   };
-  const int have = BasisPrefetch<RB>::kN * (int)blockDim.x;
+  if (!p.out_latent) {   // folded mode reads no P_V
+    const int have = BasisPrefetch<RB>::kN * (int)blockDim.x;
 #pragma unroll
-  for (int k = 0; k < BasisPrefetch<RB>::kN; ++k) {
-    const int i = tid + k * (int)blockDim.x, r = i / per_row4, c4 = i - r * per_row4;
-    if (r < p_rows) *reinterpret_cast<float4*>(p_lds + r * pst + 4 * c4) = pf.v[k];
+    for (int k = 0; k < BasisPrefetch<RB>::kN; ++k) {
+      const int i = tid + k * (int)blockDim.x, r = i / per_row4, c4 = i - r * per_row4;
+      if (r < p_rows) *reinterpret_cast<float4*>(p_lds + r * pst + 4 * c4) = pf.v[k];
+    }
+    stage_basis(0, p_rows, have);   // the rest (large head_dim), in flight with the record loads below
   }
-  stage_basis(0, p_rows, have);   // the rest (large head_dim), in flight with the record loads below
 
   // wave g folds the records of head g in one pass with a running maximum
   float M = kNegInf, L = 0.f, o0 = 0.f, o1 = 0.f;
@@ -287,6 +289,17 @@ __device__ __forceinline__ void finish_split(const DecodeParams& p, int b, int h
     }
   }
   const float inv = (g < gpw && L > 0.f) ? 1.f / L : 0.f;   // empty sequence or idle head: zero
+  if (p.out_latent) {
+    // folded mode: the caller applies P_V^T (absorbed into its output projection)
+    if (g < gpw) {
+      float* o = p.out + ((size_t)b * p.Hq + hq0 + g) * p.out_stride;
+      if (lane < p.out_stride) o[lane] = o0 * inv;
+      if (lane + 64 < p.out_stride) o[lane + 64] = o1 * inv;
+    }
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
   if (lane < RB) olat[lane * 4 + g] = o0 * inv;
   if (lane + 64 < RB) olat[(lane + 64) * 4 + g] = o1 * inv;
   __syncthreads();

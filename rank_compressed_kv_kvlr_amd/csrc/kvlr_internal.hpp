@@ -36,6 +36,8 @@ struct DecodeParams {
   const float* pv;       // single-launch merge: packed [h][d][rv(h)]
   float* out;            // single-launch merge: [B][Hq][d]
   int fuse;              // 1: the last split workgroup of a group merges and back-projects
+  int out_latent;        // 1: write the normalised latent output o_lat [B][Hq][out_stride] (no P_V^T)
+  int out_stride;
   int B, Hq, Hkv, G, d, cap;
   int split_len, n_splits, ws_stride, n_head_groups;
   int Rk, Rv;            // sum of ranks over heads

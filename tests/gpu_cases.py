@@ -76,6 +76,27 @@ class Case:
                                          self.P32K[h], self.P32V[h], 1 / np.sqrt(self.cfg.d))
 
 
+    def folded_queries(self, q: np.ndarray) -> np.ndarray:
+        """q_lat [B][Hq][max r_k] float32 = q P_K per query head (the caller's folded query
+        projection, formed on the host from the seeded queries); zero past a head's r_k."""
+        cfg = self.cfg
+        rk = [p.shape[1] for p in self.PK]
+        out = np.zeros((q.shape[0], cfg.Hq, max(rk)), np.float32)
+        for i in range(cfg.Hq):
+            h = i // cfg.G
+            out[:, i, :rk[h]] = (q[:, i].astype(np.float64) @ self.P32K[h]).astype(np.float32)
+        return out
+
+    def reference_folded(self, q_lat: np.ndarray, b: int, h: int, T: int) -> np.ndarray:
+        """Oracle folded output [G][r_v(h)] for KV head h of batch row b over rows t < T."""
+        G = self.cfg.G
+        rk = self.PK[h].shape[1]
+        lk = oracle.compress(self.host_rows("k", b, h, T), self.P32K[h])
+        lv = oracle.compress(self.host_rows("v", b, h, T), self.P32V[h])
+        return np.stack([oracle.attend_folded(q_lat[b, i, :rk].astype(np.float64), lk, lv, 1 / np.sqrt(self.cfg.d))
+                         for i in range(h * G, (h + 1) * G)])
+
+
 def dtype_code(kv, name):
     return kv.BF16 if name == "bf16" else kv.F32
 

@@ -163,6 +163,37 @@ def pin_closed_forms(impl) -> float:
     return worst
 
 
+def pin_folded(impl, quick=False) -> float:
+    """Folded form: o = o_lat P_V^T and P_V^T P_V = I give o_lat = o P_V, with o from the
+    50-digit brute force; plus T = 1 (o_lat = the one value latent) and q_lat = 0 (the mean)."""
+    worst = 0.0
+    for seed, B, T, Hkv, G, d, r_k, r_v, lens in brute_cases(quick):
+        rng = np.random.default_rng(seed)
+        Hq = Hkv * G
+        P_K = [_orth(rng, d, r_k) for _ in range(Hkv)]
+        P_V = [_orth(rng, d, r_v) for _ in range(Hkv)]
+        K = rng.standard_normal((B, T, Hkv, d))
+        V = rng.standard_normal((B, T, Hkv, d))
+        q = rng.standard_normal((B, Hq, d))
+        scale = 1 / np.sqrt(d)
+        q_lat = np.stack([np.stack([q[b, i] @ P_K[i // G] for i in range(Hq)]) for b in range(B)])
+        lat_k = [[K[b, :, h] @ P_K[h] for h in range(Hkv)] for b in range(B)]
+        lat_v = [[V[b, :, h] @ P_V[h] for h in range(Hkv)] for b in range(B)]
+        got = impl.decode_folded(q_lat, lat_k, lat_v, lens, scale, Hkv)
+        ref = brute.decode_brute(q.tolist(), K.tolist(), V.tolist(),
+                                 [p.tolist() for p in P_K], [p.tolist() for p in P_V], lens, scale)
+        ref = np.array([[[float(x) for x in row] for row in bb] for bb in ref])
+        ref_lat = np.stack([np.stack([ref[b, i] @ P_V[i // G] for i in range(Hq)]) for b in range(B)])
+        den = max(np.abs(ref_lat).max(), 1e-300)
+        worst = max(worst, float(np.abs(got - ref_lat).max() / den))
+    rng = np.random.default_rng(16)
+    Kl, Vl, ql = rng.standard_normal((1, 5)), rng.standard_normal((1, 3)), rng.standard_normal(5) * 4
+    worst = max(worst, _rel(impl.attend_folded(ql, Kl, Vl, 0.3), Vl[0]))
+    Kl, Vl = rng.standard_normal((17, 5)), rng.standard_normal((17, 3))
+    worst = max(worst, _rel(impl.attend_folded(np.zeros(5), Kl, Vl, 0.3), Vl.mean(axis=0)))
+    return worst
+
+
 def pin_golden(impl) -> float:
     """Hand-derived examples in tests/golden/hand_examples.json."""
     with open(GOLDEN) as f:
@@ -184,6 +215,7 @@ PINS = {
     "large_scores": (pin_large_scores, 1e-12),
     "closed_forms": (pin_closed_forms, 1e-12),
     "golden": (pin_golden, 1e-14),
+    "folded": (pin_folded, 1e-13),
 }
 
 

@@ -113,6 +113,12 @@ def test_null_pointers_rejected():
                                    1 << 30, 0, None) == -1
     assert kv.lib.kvlr_append(d.ptr, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None) == -1
     assert kv.lib.kvlr_prefill_compress(d.ptr, None, FAKE, 0, 10, FAKE, FAKE, FAKE, FAKE, None) == -1
+    for k in range(5):
+        a = [FAKE] * 5
+        a[k] = None
+        q, lk, lv, lens, o = a
+        assert kv.lib.kvlr_decode_attn_latent(d.ptr, q, lk, lv, lens, ctypes.c_float(0.1), o, FAKE, 1 << 30, 0,
+                                              None) == -1
 
 
 def test_prefill_bounds_and_noop():
@@ -134,6 +140,10 @@ def test_decode_workspace_and_scale_checks():
     assert kv.lib.kvlr_decode_attn(d.ptr, *args, ctypes.c_float(float("nan")), FAKE, FAKE, need, 0, None) == -7
     assert kv.lib.kvlr_decode_attn(d.ptr, *args, ctypes.c_float(float("inf")), FAKE, FAKE, need, 0, None) == -7
     assert kv.lib.kvlr_decode_attn(d.ptr, *args, ctypes.c_float(0.1), FAKE, FAKE, need, 65, None) == -7
+    lat = [FAKE] * 4
+    assert kv.lib.kvlr_decode_attn_latent(d.ptr, *lat, ctypes.c_float(0.1), FAKE, FAKE, need - 1, 0, None) == -5
+    assert kv.lib.kvlr_decode_attn_latent(d.ptr, *lat, ctypes.c_float(float("nan")), FAKE, FAKE, need, 0,
+                                          None) == -7
 
 
 def test_python_wrapper_raises_on_bad_desc():

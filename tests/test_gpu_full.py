@@ -66,6 +66,21 @@ def test_full_llama3_layer_32k(gpu):
     lens = host.lengths(cfg)
     got = _decode(case, q, lens)
     _check(case, got, q, lens, _sample(cfg, 3, 0))
+    # folded form on the same cache: q_lat = q P_K in, o_lat out
+    import torch
+    kv = _kv()
+    q_lat = case.folded_queries(q)
+    o_lat = kv.decode_attn_latent(case.desc, torch.from_numpy(q_lat).cuda(), case.lat_k, case.lat_v,
+                                  torch.from_numpy(np.asarray(lens, np.int32)).cuda())
+    torch.cuda.synchronize()
+    o_lat = o_lat.cpu().numpy().astype(np.float64)
+    metric, bound = tolerance(cfg)
+    worst = 0.0
+    for b, h in _sample(cfg, 2, 1):
+        ref = case.reference_folded(q_lat, b, h, int(lens[b]))
+        worst = max(worst, float(metric(o_lat[b, h * cfg.G:(h + 1) * cfg.G], ref).max()))
+    say(f"[full] folded worst={worst:.3e} bound={bound}")
+    assert worst <= bound, worst
 
 
 def test_full_per_head_ranks_ragged(gpu):

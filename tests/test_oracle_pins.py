@@ -70,7 +70,8 @@ def test_decode_latents_matches_decode():
 # --------------------------------------------------------------------------
 def _impl(**override):
     ns = types.SimpleNamespace(attend_reconstructed=ko.attend_reconstructed, attend_latent=ko.attend_latent,
-                               decode=ko.decode, compress=ko.compress)
+                               decode=ko.decode, compress=ko.compress, attend_folded=ko.attend_folded,
+                               decode_folded=ko.decode_folded)
     for k, v in override.items():
         setattr(ns, k, v)
     return ns
@@ -148,6 +149,36 @@ def _m_max_weight_normaliser(q, K, V, P_K, P_V, scale):
     return (w / w.max()) @ Vt
 
 
+def _m_folded_unscaled(q_lat, K_lat, V_lat, scale):
+    return ko.attend_folded(q_lat, K_lat, V_lat, 1.0)
+
+
+def _folded_with(attend, head_of=ko.kv_head_of):
+    def decode_folded(q_lat, lat_k, lat_v, lens, scale, Hkv):
+        q_lat = np.asarray(q_lat, np.float64)
+        B, Hq = q_lat.shape[:2]
+        rv_max = max(np.asarray(lat_v[0][h]).shape[1] for h in range(Hkv))
+        out = np.zeros((B, Hq, rv_max))
+        for b in range(B):
+            T = int(lens[b])
+            for i in range(Hq):
+                h = head_of(i, Hq, Hkv)
+                Kl, Vl = np.asarray(lat_k[b][h]), np.asarray(lat_v[b][h])
+                out[b, i, :Vl.shape[1]] = attend(q_lat[b, i, :Kl.shape[1]], Kl[:T], Vl[:T], scale)
+        return out
+    return decode_folded
+
+
+def _m_folded_key_latents_as_values(q_lat, K_lat, V_lat, scale):
+    K_lat, V_lat = np.asarray(K_lat), np.asarray(V_lat)
+    if K_lat.shape[0] == 0:
+        return np.zeros(V_lat.shape[1])
+    r = min(K_lat.shape[1], V_lat.shape[1])
+    out = np.zeros(V_lat.shape[1])
+    out[:r] = ko.softmax(K_lat @ q_lat * scale) @ K_lat[:, :r]
+    return out
+
+
 MUTANTS = {
     "dropped_reconstruction": _impl(attend_reconstructed=_m_no_reconstruction,
                                     decode=_decode_with(_m_no_reconstruction)),
@@ -162,6 +193,11 @@ MUTANTS = {
     "head_mapping_modulo": _impl(decode=_decode_with(ko.attend_reconstructed,
                                                      head_of=lambda i, Hq, Hkv: i % Hkv)),
     "length_off_by_one": _impl(decode=_decode_with(ko.attend_reconstructed, len_shift=1)),
+    "folded_unscaled": _impl(attend_folded=_m_folded_unscaled, decode_folded=_folded_with(_m_folded_unscaled)),
+    "folded_head_mapping_modulo": _impl(decode_folded=_folded_with(ko.attend_folded,
+                                                                   head_of=lambda i, Hq, Hkv: i % Hkv)),
+    "folded_key_latents_as_values": _impl(attend_folded=_m_folded_key_latents_as_values,
+                                          decode_folded=_folded_with(_m_folded_key_latents_as_values)),
 }
 
 
@@ -170,7 +206,7 @@ def test_planted_mistake_is_caught(mutant):
     impl = MUTANTS[mutant]
     failed = []
     for name in pins.PINS:
-        kw = {"quick": True} if name == "brute_force" else {}
+        kw = {"quick": True} if name in ("brute_force", "folded") else {}
         try:
             ok = pins.check(name, impl, **kw)
         except Exception:  # a crash is a caught mistake too
