@@ -194,31 +194,37 @@ __device__ __forceinline__ void merge_waves_and_store(const DecodeParams& p, int
 // stores have reached the coherence point); the workgroup that arrives last
 // merges the records and applies P_V^T, then resets the counter, so every
 // completed call leaves the counters at zero.
-//   wave g merges head g: one pass over the records with a running maximum,
-//   then o[dd] = sum_j o_lat[j] P_V[dd][j] for dd = lane + 64 k, with o_lat[j]
-//   broadcast from lane j by readlane and the P_V row prefetched into
-//   registers before the records are read.
+//   wave g merges head g: one pass over the records with a running maximum;
+//   then o[dd] = sum_j o_lat[j] P_V[dd][j]. For head_dim <= 128 the basis is
+//   already in registers (prefetched when the split work ended): each thread
+//   forms partial sums over its 4-column slices for its 8 rows and 4 heads,
+//   and the 16 lanes of a DPP row add them up. Larger head dims stage P_V
+//   rows through LDS.
 constexpr int kTailLds = 12288;   // floats of LDS a split kernel provides for the merge tail
 
-// Float4s of P_V[h] each thread prefetches into registers when its split work
-// ends (RB * 128 floats: all of P_V[h] for head_dim 128), so the workgroup
-// that turns out to merge has the basis on chip already.
+// P_V[h] in registers for head_dim <= 128 (256 threads): thread t holds rows
+// t/16 + 16 k (k < 8) and the 4-column slices t%16 and, when r_v > 64,
+// t%16 + 16. The workgroup that turns out to merge has the basis on chip.
 template <int RB>
 struct BasisPrefetch {
-  static constexpr int kN = RB / 8;
-  float4 v[kN];
+  static constexpr int kS = RB > 64 ? 2 : 1;   // column slices per thread
+  float4 v[8][kS];
 };
 
 template <int RB>
 __device__ __forceinline__ void prefetch_basis(const DecodeParams& p, int h, int rv, BasisPrefetch<RB>& pf) {
-  if (!p.fuse || p.out_latent) return;
+  if (!p.fuse || p.out_latent || p.d > 128) return;
   const float* P = p.pv + (size_t)p.d * p.ht.rv_pre[h];
-  const int n4 = p.d * rv / 4;
+  const int m = threadIdx.x & 15, rg = threadIdx.x >> 4;
+  const int per_row4 = rv >> 2;
 #pragma unroll
-  for (int k = 0; k < BasisPrefetch<RB>::kN; ++k) {
-    const int i = threadIdx.x + k * blockDim.x;
-    pf.v[k] = (i < n4) ? *reinterpret_cast<const float4*>(P + 4 * (size_t)i) : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
+  for (int k = 0; k < 8; ++k)
+#pragma unroll
+    for (int sl = 0; sl < BasisPrefetch<RB>::kS; ++sl) {
+      const int r = rg + 16 * k, c4 = m + 16 * sl;
+      pf.v[k][sl] = (r < p.d && c4 < per_row4) ? *reinterpret_cast<const float4*>(P + (size_t)r * rv + 4 * c4)
+                                                : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
 }
 
 template <int RB>
@@ -236,30 +242,21 @@ __device__ __forceinline__ void finish_split(const DecodeParams& p, int b, int h
 
   const int tid = threadIdx.x, lane = tid & 63, g = tid >> 6;
   const int d = p.d;
+  const bool reg_basis = d <= 128;              // P_V already in registers (see BasisPrefetch)
   float* olat = scratch;                        // [RB][4] head-minor
-  float* p_lds = scratch + 4 * RB;              // P_V rows, padded stride
+  float* p_lds = scratch + 4 * RB;              // P_V rows, padded stride (head_dim > 128)
   const int pst = rv + 4;
   const int p_rows = min(d, (kTailLds - 4 * RB - 16) / pst);
   const float* P = p.pv + (size_t)d * p.ht.rv_pre[h];
   const int per_row4 = rv / 4;
-  // rows [r0, r0 + nr) into LDS; float4 index i of P_V[h] below `have` is already in registers
-  auto stage_basis = [&](int r0, int nr, int have) {
+  auto stage_basis = [&](int r0, int nr) {      // rows [r0, r0 + nr) into LDS
     for (int i = tid; i < nr * per_row4; i += blockDim.x) {
       const int r = i / per_row4, c4 = i - r * per_row4;
-      if (r0 * per_row4 + i >= have)
-        *reinterpret_cast<float4*>(p_lds + r * pst + 4 * c4) =
-            *reinterpret_cast<const float4*>(P + (size_t)(r0 + r) * rv + 4 * c4);
+      *reinterpret_cast<float4*>(p_lds + r * pst + 4 * c4) =
+          *reinterpret_cast<const float4*>(P + (size_t)(r0 + r) * rv + 4 * c4);
     }
   };
-  if (!p.out_latent) {   // folded mode reads no P_V
-    const int have = BasisPrefetch<RB>::kN * (int)blockDim.x;
-#pragma unroll
-    for (int k = 0; k < BasisPrefetch<RB>::kN; ++k) {
-      const int i = tid + k * (int)blockDim.x, r = i / per_row4, c4 = i - r * per_row4;
-      if (r < p_rows) *reinterpret_cast<float4*>(p_lds + r * pst + 4 * c4) = pf.v[k];
-    }
-    stage_basis(0, p_rows, have);   // the rest (large head_dim), in flight with the record loads below
-  }
+  if (!p.out_latent && !reg_basis) stage_basis(0, p_rows);   // in flight with the record loads below
 
   // wave g folds the records of head g in one pass with a running maximum
   float M = kNegInf, L = 0.f, o0 = 0.f, o1 = 0.f;
@@ -304,12 +301,55 @@ __device__ __forceinline__ void finish_split(const DecodeParams& p, int b, int h
   if (lane + 64 < RB) olat[(lane + 64) * 4 + g] = o1 * inv;
   __syncthreads();
 
+  if (reg_basis) {
+    // back-projection from registers: partial sums over this thread's column slices,
+    // then a sum over the 16 lanes of the DPP row (which share the rows)
+    const int m = tid & 15, rg = tid >> 4;
+    float part[8][4];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) part[k][gg] = 0.f;
+#pragma unroll
+    for (int sl = 0; sl < BasisPrefetch<RB>::kS; ++sl) {
+      const int c4 = m + 16 * sl;
+      if (c4 < per_row4) {
+        float4 o[4];   // o_lat of channels 4 c4 .. 4 c4 + 3, four heads each
+#pragma unroll
+        for (int c = 0; c < 4; ++c) o[c] = *reinterpret_cast<const float4*>(olat + (4 * c4 + c) * 4);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float4 pv = pf.v[k][sl];
+          part[k][0] += pv.x * o[0].x + pv.y * o[1].x + pv.z * o[2].x + pv.w * o[3].x;
+          part[k][1] += pv.x * o[0].y + pv.y * o[1].y + pv.z * o[2].y + pv.w * o[3].y;
+          part[k][2] += pv.x * o[0].z + pv.y * o[1].z + pv.z * o[2].z + pv.w * o[3].z;
+          part[k][3] += pv.x * o[0].w + pv.y * o[1].w + pv.z * o[2].w + pv.w * o[3].w;
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) part[k][gg] = row16_allreduce<false>(part[k][gg]);
+    // lane m of the row stores outputs (k, head) with (4 k + head) % 16 == m
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        const int r = rg + 16 * k;
+        if (((4 * k + gg) & 15) == m && gg < gpw && r < d)
+          p.out[((size_t)b * p.Hq + hq0 + gg) * d + r] = part[k][gg];
+      }
+    if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+
   // back-projection of the 4 heads, P_V rows from LDS (restaged when they do not fit)
   for (int r0 = 0; r0 < d; r0 += p_rows) {
     const int nr = min(p_rows, d - r0);
     if (r0 > 0) {
       __syncthreads();
-      stage_basis(r0, nr, 0);
+      stage_basis(r0, nr);
       __syncthreads();
     }
     for (int r = tid; r < nr; r += blockDim.x) {
@@ -348,7 +388,8 @@ __global__ __launch_bounds__(256) void decode_split_bf16(DecodeParams p) {
   constexpr int NP = RB / 32;                 // full 32-channel key pairs
   constexpr int NIT = value_iters_bound(RB, TT);  // bound on value iterations (see n_it below)
   constexpr int QTS = RB;                     // q~ LDS row stride
-  __shared__ __attribute__((aligned(16))) float smem[kWaves * 64 * 4 * 8 + 64 > kTailLds ? kWaves * 64 * 4 * 8 + 64 : kTailLds];
+  constexpr int kRS = 36;   // per-lane stride of the wave reduction: 4 heads x 8 channels + 4 (bank spread)
+  __shared__ __attribute__((aligned(16))) float smem[kWaves * 64 * kRS + 64 > kTailLds ? kWaves * 64 * kRS + 64 : kTailLds];
 
   const int s = blockIdx.x;
   const int h = blockIdx.y / p.n_head_groups;
@@ -566,14 +607,14 @@ __global__ __launch_bounds__(256) void decode_split_bf16(DecodeParams p) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) l[i] = row16_allreduce<false>(l[i]);
   __syncthreads();
-  float* red = smem;                          // [wave][lane][head][8]
-  float* wm = smem + kWaves * 64 * 32;        // [wave][head]
+  float* red = smem;                          // [wave][lane][kRS]: (head, channel) at head * 8 + channel
+  float* wm = smem + kWaves * 64 * kRS;       // [wave][head]
   float* wl = wm + 16;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int e = 0; e < 8; e += 4)
-      *reinterpret_cast<float4*>(red + ((wave * 64 + lane) * 4 + i) * 8 + e) =
+      *reinterpret_cast<float4*>(red + (wave * 64 + lane) * kRS + i * 8 + e) =
           make_float4(acc[i][e], acc[i][e + 1], acc[i][e + 2], acc[i][e + 3]);
   if (lane == 0) {
 #pragma unroll
@@ -585,8 +626,11 @@ __global__ __launch_bounds__(256) void decode_split_bf16(DecodeParams p) {
   __syncthreads();
   merge_waves_and_store(p, b, hq0, gpw, s, rv, wm, wl, [&](int w, int g, int j) {
     const int c = j >> 3, e = j & 7;
+    const float* base = red + (w * 64 + c) * kRS + g * 8 + e;
+    const int step = C * kRS;
     float sum = 0.f;
-    for (int r = 0; r < rpi; ++r) sum += red[((w * 64 + r * C + c) * 4 + g) * 8 + e];
+#pragma unroll 8
+    for (int r = 0; r < rpi; ++r) sum += base[r * step];   // rows r C + c of wave w
     return sum;
   });
   finish_split<RB>(p, b, h, hg, hq0, gpw, rv, smem, pf);
