@@ -126,7 +126,8 @@ KVLR_API int kvlr_decode_workspace_bytes(const kvlr_desc* desc, int32_t split_to
 KVLR_API int kvlr_decode_counter_bytes(const kvlr_desc* desc, size_t* bytes);
 
 /* Splits that kvlr_decode_attn uses per (batch row, KV head) for
- * split_tokens (0 = library choice), and the tokens per split. */
+ * split_tokens (0 = library choice: one round of workgroups over the
+ * device), and the tokens per split. */
 KVLR_API int kvlr_decode_plan(const kvlr_desc* desc, int32_t split_tokens, int32_t* n_splits,
                               int32_t* tokens_per_split);
 
@@ -175,8 +176,9 @@ KVLR_API int kvlr_append(const kvlr_desc* desc, const void* k_new, const void* v
  *             first kvlr_decode_attn call that uses it; every completed call
  *             leaves it zero again. The records need no initialisation.
  *             Calls sharing one workspace must be ordered on one stream.
- *   split_tokens 0 for the library's choice, or a multiple of 64: tokens
- *             per split of the sequence (every split yields a partial
+ *   split_tokens 0 for the library's choice (see kvlr_decode_plan), or a
+ *             multiple of 64: tokens per split of the sequence (every split
+ *             yields a partial
  *             softmax state; the workgroup that finishes last for a group of
  *             query heads merges the states and back-projects with P_V^T,
  *             all in one kernel launch)

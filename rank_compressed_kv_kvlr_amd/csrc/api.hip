@@ -19,7 +19,7 @@ constexpr int kComputeUnits = 256;   // MI355X
 // limited by the variant's register count on gfx950). The default split
 // length gives one such round of workgroups over the whole device.
 int resident_wgs_per_cu(int latent_dtype, int rank_bound) {
-  if (latent_dtype == KVLR_BF16) return rank_bound <= 32 ? 3 : rank_bound <= 64 ? 2 : 1;   // measured best
+  if (latent_dtype == KVLR_BF16) return rank_bound <= 32 ? 3 : 2;   // measured best
   return 3;   // fp32 variants: limited by the 48 KiB of LDS the merge tail needs
 }
 
@@ -59,7 +59,13 @@ int check_desc(const kvlr_desc* d, HeadTable* ht, int* Rk, int* Rv, int* rank_bo
   return KVLR_OK;
 }
 
-int plan_split(const kvlr_desc* d, int32_t split_tokens, int* n_splits, int* split_len) {
+// Split plan of the decode kernels: one split length for every KV head.
+// With split_tokens > 0 that length; with 0 the library sizes the splits so
+// that one round of workgroups fills the device. (Rank-weighted per-head
+// lengths were measured slower on ragged batches: the extra, shorter splits of
+// the heavy heads spill into a second round.) split_len (optional) receives the
+// per-head lengths the kernels read.
+int plan_split(const kvlr_desc* d, int32_t split_tokens, int* n_splits, int* len_out, int* split_len = nullptr) {
   int rank_bound = 0;
   check_desc(d, nullptr, nullptr, nullptr, &rank_bound);   // callers validated the descriptor already
   const int G = d->n_q_heads / d->n_kv_heads;
@@ -84,7 +90,9 @@ int plan_split(const kvlr_desc* d, int32_t split_tokens, int* n_splits, int* spl
   const long long ns = ((long long)d->capacity + len - 1) / len;
   if (ns > 65535) return KVLR_ERR_ARG;   // grid.x limit of the split kernel
   *n_splits = (int)ns;
-  *split_len = len;
+  *len_out = len;
+  if (split_len)
+    for (int h = 0; h < d->n_kv_heads; ++h) split_len[h] = len;
   return KVLR_OK;
 }
 
@@ -246,7 +254,7 @@ int prepare_decode(const kvlr_desc* desc, const float* q, const float* P_K, cons
   if (need_combine && (!P_V || !out)) return KVLR_ERR_NULL;
   if (need_partials && !isfinite(scale)) return KVLR_ERR_ARG;
   int ns = 0, len = 0;
-  rc = plan_split(desc, split_tokens, &ns, &len);
+  rc = plan_split(desc, split_tokens, &ns, &len, p->ht.split_len);
   if (rc) return rc;
   const int stride = ws_stride_of(p->ht, desc->n_kv_heads);
   const size_t cbytes = counter_bytes_of(desc);

@@ -399,8 +399,8 @@ __global__ __launch_bounds__(256) void decode_split_bf16(DecodeParams p) {
   const int gpw = min(kHeadsPerWg, p.G - hg * kHeadsPerWg);
   const int rk = p.ht.rk[h], rv = p.ht.rv[h];
   const int T = min(max(p.seq_lens[b], 0), p.cap);
-  const int t_begin = s * p.split_len;
-  const int t_end = min(T, t_begin + p.split_len);
+  const int t_begin = min(s * p.ht.split_len[h], T);   // clamped: no overflow for far splits
+  const int t_end = min(T, t_begin + p.ht.split_len[h]);
   if (t_begin >= t_end) {
     write_empty_records(p, b, hq0, gpw, s, rv);
     BasisPrefetch<RB> pf;
@@ -656,8 +656,8 @@ __global__ __launch_bounds__(256) void decode_split_f32(DecodeParams p) {
   const int gpw = min(kHeadsPerWg, p.G - hg * kHeadsPerWg);
   const int rk = p.ht.rk[h], rv = p.ht.rv[h];
   const int T = min(max(p.seq_lens[b], 0), p.cap);
-  const int t_begin = s * p.split_len;
-  const int t_end = min(T, t_begin + p.split_len);
+  const int t_begin = min(s * p.ht.split_len[h], T);   // clamped: no overflow for far splits
+  const int t_end = min(T, t_begin + p.ht.split_len[h]);
   if (t_begin >= t_end) {
     write_empty_records(p, b, hq0, gpw, s, rv);
     BasisPrefetch<RB> pf;

@@ -21,6 +21,7 @@ struct HeadTable {
   int rv[kMaxKvHeads];
   int rk_pre[kMaxKvHeads];
   int rv_pre[kMaxKvHeads];
+  int split_len[kMaxKvHeads];   // decode: tokens per split of KV head h (splits past the sequence are empty)
 };
 
 struct DecodeParams {
