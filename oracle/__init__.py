@@ -22,6 +22,11 @@ What it computes (all in float64, plain numpy, no blocking or fusion):
   projections: q~ in, o_lat = p V_lat out (StiefAttention, "Mecanismo
   Central" item 5; STAR-KV, "Metodologia" section 2).
 
+* mixed-precision latent storage (``oracle/quant.py``): block-wise Hadamard
+  folded into the bases, 4-bit outlier and 3-bit inlier blocks per token,
+  and decode over the dequantised latents (STAR-KV technical summary,
+  "Metodologia" section 3), pinned in tests/test_quant_oracle.py.
+
 Pins (tests/test_oracle_pins.py): orthonormality of the bases, the textbook
 softmax attention at full rank, invariance under P -> P O, definition mode
 equals latent mode, a 50-digit mpmath brute force on tiny shapes, closed
@@ -47,3 +52,4 @@ from .kvlr_oracle import (  # noqa: F401
     decode_head_latent,
     kv_head_of,
 )
+from . import quant  # noqa: F401
