@@ -51,7 +51,7 @@ typedef enum kvlr_status {
   KVLR_ERR_NULL = -1,      /* a required pointer is NULL */
   KVLR_ERR_SHAPE = -2,     /* inconsistent shape: Hq % Hkv, head_dim, start + n_tok > capacity ... */
   KVLR_ERR_RANK = -3,      /* rank outside [1, min(head_dim, 128)] or not a multiple of the
-                              storage granule (16 for bf16 latents, 4 for fp32 latents) */
+                              storage granule (16 for bf16 and 4/3-bit latents, 4 for fp32 latents) */
   KVLR_ERR_DTYPE = -4,     /* unsupported dtype code */
   KVLR_ERR_WORKSPACE = -5, /* workspace NULL or smaller than kvlr_decode_workspace_bytes() */
   KVLR_ERR_HIP = -6,       /* a kernel launch failed (hipGetLastError) */
@@ -61,7 +61,9 @@ typedef enum kvlr_status {
 /* Element types. */
 typedef enum kvlr_dtype {
   KVLR_F32 = 0,  /* IEEE binary32 */
-  KVLR_BF16 = 1  /* bfloat16, stored as the upper 16 bits of binary32; fp32 -> bf16 rounds to nearest even */
+  KVLR_BF16 = 1, /* bfloat16, stored as the upper 16 bits of binary32; fp32 -> bf16 rounds to nearest even */
+  KVLR_Q43 = 2   /* latent caches only: mixed-precision rows, 4-bit outlier block and 3-bit inlier
+                    block per token (layout below) */
 } kvlr_dtype;
 
 /* Shape of one layer's cache.
@@ -89,6 +91,28 @@ typedef enum kvlr_dtype {
  *    for the 16-channel tail jj = j - 32 np: np * 512 + (jj / 4) * 64 + n * 4 + jj % 4.
  * Blocks are contiguous, so a split of a sequence streams one byte range.
  *
+ * Mixed-precision latents (latent_dtype KVLR_Q43; STAR-KV technical summary,
+ * "Metodologia" section 3): the leading n_o(r) = 16 * max(1, (r + 40) / 80)
+ * latent channels form the outlier block (20% of the channels, in whole
+ * 16-channel Hadamard blocks), the rest the inlier block. Each block of each
+ * token is quantised on its own: asymmetric round-to-nearest between its
+ * minimum and maximum, 15 steps (4 bits) for the outlier block, 7 steps
+ * (3 bits) for the inlier block, with the step and the minimum kept as IEEE
+ * half floats; the stored value is step * code + minimum. In fp32 the code is
+ *   step = half((max - min) / (2^bits - 1)), base = half(min),
+ *   code = clamp(rint((x - base) * (1 / step)), 0, 2^bits - 1)   (0 if step == 0).
+ * The caches are byte arrays; a row of rank r takes
+ *   rb(r) = round_up(8 + n_o / 2 + ceil(3 (r - n_o) / 8), 4) bytes:
+ *   [0:2] outlier step, [2:4] outlier minimum, [4:6] inlier step,
+ *   [6:8] inlier minimum (half floats), then the outlier codes two per byte
+ *   (channel 2k in the low nibble of byte k), then the inlier codes as one
+ *   little-endian bit stream (channel c at bits 3c .. 3c+2), zero padding.
+ * With RB = sum_h rb(r_k[h]) and RB_pre(h) its prefix sum, the block of
+ * (b, h) starts at byte C16 * (b * RB + RB_pre(h)) and row t at t * rb(r).
+ * The bases used with such a cache must have the block-wise Hadamard folded
+ * in (kvlr_hadamard_bases); compression, append and decode all take those
+ * folded bases.
+ *
  * Basis layout: P_K is fp32, heads packed back to back, head h a row-major
  * [d][r_k[h]] block starting at element d * R_pre(h); P_V likewise. */
 typedef struct kvlr_desc {
@@ -111,7 +135,8 @@ KVLR_API const char* kvlr_status_string(int status);
 
 /* Validates `desc` and returns, through k_elems / v_elems, the number of
  * latent elements of lat_k and lat_v: B * C16 * sum_h r(h), C16 = T_cap
- * rounded up to a multiple of 16. */
+ * rounded up to a multiple of 16 (bytes, B * C16 * sum_h rb(r(h)), for
+ * KVLR_Q43 latents). */
 KVLR_API int kvlr_cache_elems(const kvlr_desc* desc, size_t* k_elems, size_t* v_elems);
 
 /* Bytes of decode workspace that kvlr_decode_attn needs for this
@@ -131,6 +156,20 @@ KVLR_API int kvlr_decode_counter_bytes(const kvlr_desc* desc, size_t* bytes);
 KVLR_API int kvlr_decode_plan(const kvlr_desc* desc, int32_t split_tokens, int32_t* n_splits,
                               int32_t* tokens_per_split);
 
+/* Fold the block-wise Hadamard rotation into bases (STAR-KV technical
+ * summary, "Metodologia" section 3: every block of latent channels gets its own
+ * Hadamard transform, and the factors are fused into the projection matrices,
+ * so the rotation costs nothing when the cache is written or read):
+ *   out[h] = P[h] R,  R = diag(H16 / 4, ..., H16 / 4) of order r(h),
+ * H16 the Sylvester Hadamard matrix (entries +-1). R is orthogonal, so the
+ * folded bases stay orthonormal and span the same space. Required before
+ * using a KVLR_Q43 cache.
+ *   P_K, P_V     device fp32 packed bases (layout above)
+ *   out_K, out_V device fp32 packed bases of the same size; each may alias its
+ *                input (the transform works in place) */
+KVLR_API int kvlr_hadamard_bases(const kvlr_desc* desc, const float* P_K, const float* P_V, float* out_K,
+                                 float* out_V, void* stream);
+
 /* Prefill compression: store the latents of n_tok consecutive tokens.
  * (StiefAttention technical summary, "Mecanismo Central" item 5: keys are
  * stored as K P_K; values likewise as V P_V.)
@@ -143,7 +182,9 @@ KVLR_API int kvlr_decode_plan(const kvlr_desc* desc, int32_t split_tokens, int32
  *             rows start .. start+n_tok-1 of every (b, h) are overwritten,
  *             nothing else is written.
  * Products accumulate in fp32 (bf16 inputs: MFMA with the basis split into a
- * high and a low bf16 part); results are rounded to the latent dtype. */
+ * high and a low bf16 part); results are rounded to the latent dtype
+ * (KVLR_Q43: quantised as described above, from the fp32 latents; the
+ * bases must be the Hadamard-folded ones). */
 KVLR_API int kvlr_prefill_compress(const kvlr_desc* desc, const void* K, const void* V, int32_t start,
                                    int32_t n_tok, const float* P_K, const float* P_V, void* lat_k,
                                    void* lat_v, void* stream);

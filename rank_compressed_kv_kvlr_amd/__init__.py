@@ -29,13 +29,14 @@ from typing import Optional, Sequence
 import numpy as np
 
 __all__ = [
-    "KvlrError", "Desc", "F32", "BF16", "lib", "version", "status_string",
+    "KvlrError", "Desc", "F32", "BF16", "Q43", "lib", "version", "status_string",
     "cache_elems", "decode_workspace_bytes", "decode_plan", "decode_counter_bytes",
     "prefill_compress", "append", "decode_attn", "decode_partials", "decode_combine", "decode_attn_latent",
+    "hadamard_bases", "q43_outlier", "q43_row_bytes",
     "alloc_cache", "alloc_workspace", "pack_bases", "block_view", "latent_rows", "cap_rows", "k_tiled_index",
 ]
 
-F32, BF16 = 0, 1
+F32, BF16, Q43 = 0, 1, 2
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvlr.so")
 
@@ -76,9 +77,10 @@ lib.kvlr_decode_partials.argtypes = [_D, _P, _P, _P, _P, _P, ctypes.c_float, _P,
 lib.kvlr_decode_combine.argtypes = [_D, _P, _P, ctypes.c_size_t, ctypes.c_int32, _P, _P]
 lib.kvlr_decode_attn_latent.argtypes = [_D, _P, _P, _P, _P, ctypes.c_float, _P, _P, ctypes.c_size_t,
                                         ctypes.c_int32, _P]
+lib.kvlr_hadamard_bases.argtypes = [_D, _P, _P, _P, _P, _P]
 for _f in ("kvlr_cache_elems", "kvlr_decode_workspace_bytes", "kvlr_decode_plan", "kvlr_decode_counter_bytes", "kvlr_prefill_compress",
            "kvlr_append", "kvlr_decode_attn", "kvlr_decode_partials", "kvlr_decode_combine",
-           "kvlr_decode_attn_latent"):
+           "kvlr_decode_attn_latent", "kvlr_hadamard_bases"):
     getattr(lib, _f).restype = ctypes.c_int
 
 
@@ -156,7 +158,23 @@ def _torch():
 
 def _dtype_of(code: int):
     torch = _torch()
-    return torch.bfloat16 if code == BF16 else torch.float32
+    return {BF16: torch.bfloat16, F32: torch.float32, Q43: torch.uint8}[code]
+
+
+def q43_outlier(r: int) -> int:
+    """Channels of the 4-bit outlier block of a 4/3-bit row of rank r (layout in kvlr.h)."""
+    return 16 * max(1, (r + 40) // 80)
+
+
+def q43_row_bytes(r: int) -> int:
+    """Bytes of one stored 4/3-bit row of rank r (layout in kvlr.h)."""
+    no = q43_outlier(r)
+    n = 8 + no // 2 + (3 * (r - no) + 7) // 8
+    return (n + 3) // 4 * 4
+
+
+def _row_storage(desc, r: int) -> int:
+    return q43_row_bytes(r) if desc.latent_dtype == Q43 else r
 
 
 def _stream():
@@ -212,13 +230,13 @@ def cap_rows(desc: Desc) -> int:
 
 
 def block_view(lat, desc: Desc, which: str, b: int, h: int):
-    """The raw storage block of (batch row b, KV head h): cap_rows * r elements, 1-D."""
-    r = int((desc.r_k if which == "k" else desc.r_v)[h])
-    off = desc.rank_offsets(which)
-    R = int(off[-1])
+    """The raw storage block of (batch row b, KV head h), 1-D: cap_rows * r elements
+    (cap_rows * q43_row_bytes(r) bytes for 4/3-bit rows)."""
+    ranks = desc.r_k if which == "k" else desc.r_v
+    sizes = [_row_storage(desc, int(x)) for x in ranks]
     rows = cap_rows(desc)
-    start = rows * (b * R + int(off[h]))
-    return lat[start:start + rows * r]
+    start = rows * (b * sum(sizes) + sum(sizes[:h]))
+    return lat[start:start + rows * sizes[h]]
 
 
 def k_tiled_index(T: int, r: int):
@@ -235,14 +253,16 @@ def k_tiled_index(T: int, r: int):
 
 
 def latent_rows(lat, desc: Desc, which: str, b: int, h: int):
-    """Logical latent rows [capacity][r] of (b, h) (a gather for bf16 keys, a view otherwise)."""
+    """Logical latent rows [capacity][r] of (b, h) (a gather for bf16 keys, a view otherwise;
+    [capacity][q43_row_bytes(r)] stored bytes for 4/3-bit rows)."""
     torch = _torch()
     r = int((desc.r_k if which == "k" else desc.r_v)[h])
     blk = block_view(lat, desc, which, b, h)
     if which == "k" and desc.latent_dtype == BF16:
         idx = torch.from_numpy(k_tiled_index(desc.capacity, r).ravel()).to(blk.device)
         return blk[idx].view(desc.capacity, r)
-    return blk[:desc.capacity * r].view(desc.capacity, r)
+    w = _row_storage(desc, r)
+    return blk[:desc.capacity * w].view(desc.capacity, w)
 
 
 def _basis_numel(desc: Desc, which: str) -> int:
@@ -356,3 +376,15 @@ def decode_attn_latent(desc: Desc, q_lat, lat_k, lat_v, seq_lens, scale: Optiona
             ctypes.c_size_t(workspace.numel() * workspace.element_size()), split_tokens)
     _check(lib.kvlr_decode_attn_latent(desc.ptr, *args, _stream()), "kvlr_decode_attn_latent")
     return o_lat
+
+
+def hadamard_bases(desc: Desc, P_K, P_V, out_K=None, out_V=None):
+    """Fold the block-wise Hadamard rotation into packed bases (in place when no outputs are given)."""
+    torch = _torch()
+    nk, nv = _basis_numel(desc, "k"), _basis_numel(desc, "v")
+    out_K = P_K if out_K is None else out_K
+    out_V = P_V if out_V is None else out_V
+    args = (_need(P_K, "P_K", torch.float32, nk), _need(P_V, "P_V", torch.float32, nv),
+            _need(out_K, "out_K", torch.float32, nk), _need(out_V, "out_V", torch.float32, nv))
+    _check(lib.kvlr_hadamard_bases(desc.ptr, *args, _stream()), "kvlr_hadamard_bases")
+    return out_K, out_V

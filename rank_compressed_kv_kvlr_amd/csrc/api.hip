@@ -20,22 +20,29 @@ constexpr int kComputeUnits = 256;   // MI355X
 // length gives one such round of workgroups over the whole device.
 int resident_wgs_per_cu(int latent_dtype, int rank_bound) {
   if (latent_dtype == KVLR_BF16) return rank_bound <= 32 ? 3 : 2;   // measured best
+  if (latent_dtype == KVLR_Q43) return 2;
   return 3;   // fp32 variants: limited by the 48 KiB of LDS the merge tail needs
 }
 
 bool valid_dtype(int t) { return t == KVLR_F32 || t == KVLR_BF16; }
+bool valid_latent_dtype(int t) { return valid_dtype(t) || t == KVLR_Q43; }
 
-// Validates the descriptor and fills the per-head tables.
-int check_desc(const kvlr_desc* d, HeadTable* ht, int* Rk, int* Rv, int* rank_bound) {
+// Storage of one latent row of rank r: elements, or bytes for 4/3-bit rows.
+int row_storage(int latent_dtype, int r) { return latent_dtype == KVLR_Q43 ? kvlr::q43_row_bytes(r) : r; }
+
+// Validates the descriptor and fills the per-head tables (ranks, rank and
+// storage prefix sums); Sk / Sv receive the per-row storage summed over heads.
+int check_desc(const kvlr_desc* d, HeadTable* ht, int* Rk, int* Rv, int* rank_bound, int* Sk = nullptr,
+               int* Sv = nullptr) {
   if (!d || !d->r_k || !d->r_v) return KVLR_ERR_NULL;
-  if (!valid_dtype(d->in_dtype) || !valid_dtype(d->latent_dtype)) return KVLR_ERR_DTYPE;
+  if (!valid_dtype(d->in_dtype) || !valid_latent_dtype(d->latent_dtype)) return KVLR_ERR_DTYPE;
   if (d->batch < 1 || d->n_kv_heads < 1 || d->n_kv_heads > kvlr::kMaxKvHeads || d->n_q_heads < 1 ||
       d->n_q_heads % d->n_kv_heads != 0 || d->n_q_heads / d->n_kv_heads > 16 || d->capacity < 1 ||
       d->head_dim < 32 || d->head_dim > 256 || d->head_dim % 32 != 0 || d->capacity > (1 << 30))
     return KVLR_ERR_SHAPE;
-  const int granule = d->latent_dtype == KVLR_BF16 ? 16 : 4;
+  const int granule = d->latent_dtype == KVLR_F32 ? 4 : 16;
   const int rmax = d->head_dim < kvlr::kMaxRank ? d->head_dim : kvlr::kMaxRank;
-  int sk = 0, sv = 0, bound = 0;
+  int sk = 0, sv = 0, bound = 0, stk = 0, stv = 0;
   for (int h = 0; h < d->n_kv_heads; ++h) {
     const int rk = d->r_k[h], rv = d->r_v[h];
     if (rk < 1 || rv < 1 || rk > rmax || rv > rmax || rk % granule || rv % granule) return KVLR_ERR_RANK;
@@ -44,17 +51,23 @@ int check_desc(const kvlr_desc* d, HeadTable* ht, int* Rk, int* Rv, int* rank_bo
       ht->rv[h] = rv;
       ht->rk_pre[h] = sk;
       ht->rv_pre[h] = sv;
+      ht->sk_pre[h] = stk;
+      ht->sv_pre[h] = stv;
     }
     sk += rk;
     sv += rv;
+    stk += row_storage(d->latent_dtype, rk);
+    stv += row_storage(d->latent_dtype, rv);
     bound = rk > bound ? rk : bound;
     bound = rv > bound ? rv : bound;
   }
   // every per-(b, h) block offset T_cap * (b * R + R_pre) must fit comfortably in size_t;
   // kernels index rows with 32-bit token counts
-  if ((long long)d->capacity * d->batch * (sk > sv ? sk : sv) > (1LL << 46)) return KVLR_ERR_SHAPE;
+  if ((long long)d->capacity * d->batch * (stk > stv ? stk : stv) > (1LL << 46)) return KVLR_ERR_SHAPE;
   if (Rk) *Rk = sk;
   if (Rv) *Rv = sv;
+  if (Sk) *Sk = stk;
+  if (Sv) *Sv = stv;
   if (rank_bound) *rank_bound = bound <= 32 ? 32 : bound <= 64 ? 64 : bound <= 96 ? 96 : 128;
   return KVLR_OK;
 }
@@ -143,13 +156,13 @@ KVLR_API const char* kvlr_status_string(int status) {
 }
 
 KVLR_API int kvlr_cache_elems(const kvlr_desc* desc, size_t* k_elems, size_t* v_elems) {
-  int Rk = 0, Rv = 0;
-  const int rc = check_desc(desc, nullptr, &Rk, &Rv, nullptr);
+  int Sk = 0, Sv = 0;
+  const int rc = check_desc(desc, nullptr, nullptr, nullptr, nullptr, &Sk, &Sv);
   if (rc) return rc;
   if (!k_elems || !v_elems) return KVLR_ERR_NULL;
   const size_t rows = (size_t)kvlr::cap_rows_of(desc->capacity);
-  *k_elems = (size_t)desc->batch * rows * Rk;
-  *v_elems = (size_t)desc->batch * rows * Rv;
+  *k_elems = (size_t)desc->batch * rows * Sk;
+  *v_elems = (size_t)desc->batch * rows * Sv;
   return KVLR_OK;
 }
 
@@ -191,7 +204,7 @@ KVLR_API int kvlr_prefill_compress(const kvlr_desc* desc, const void* K, const v
                                    int32_t n_tok, const float* P_K, const float* P_V, void* lat_k,
                                    void* lat_v, void* stream) {
   kvlr::CompressParams p;
-  int rc = check_desc(desc, &p.ht, &p.Rk, &p.Rv, nullptr);
+  int rc = check_desc(desc, &p.ht, &p.Rk, &p.Rv, nullptr, &p.Sk, &p.Sv);
   if (rc) return rc;
   if (start < 0 || n_tok < 0) return KVLR_ERR_ARG;
   if ((long long)start + n_tok > desc->capacity) return KVLR_ERR_SHAPE;
@@ -212,13 +225,14 @@ KVLR_API int kvlr_prefill_compress(const kvlr_desc* desc, const void* K, const v
   p.n_tok = n_tok;
   p.in_bf16 = desc->in_dtype == KVLR_BF16;
   p.out_bf16 = desc->latent_dtype == KVLR_BF16;
+  p.out_q43 = desc->latent_dtype == KVLR_Q43;
   return hip_status(kvlr::launch_compress(p, static_cast<hipStream_t>(stream)));
 }
 
 KVLR_API int kvlr_append(const kvlr_desc* desc, const void* k_new, const void* v_new, const int32_t* pos,
                          const float* P_K, const float* P_V, void* lat_k, void* lat_v, void* stream) {
   kvlr::AppendParams p;
-  const int rc = check_desc(desc, &p.ht, &p.Rk, &p.Rv, nullptr);
+  const int rc = check_desc(desc, &p.ht, &p.Rk, &p.Rv, nullptr, &p.Sk, &p.Sv);
   if (rc) return rc;
   if (!k_new || !v_new || !pos || !P_K || !P_V || !lat_k || !lat_v) return KVLR_ERR_NULL;
   p.k_new = k_new;
@@ -234,7 +248,23 @@ KVLR_API int kvlr_append(const kvlr_desc* desc, const void* k_new, const void* v
   p.cap = desc->capacity;
   p.in_bf16 = desc->in_dtype == KVLR_BF16;
   p.out_bf16 = desc->latent_dtype == KVLR_BF16;
+  p.out_q43 = desc->latent_dtype == KVLR_Q43;
   return hip_status(kvlr::launch_append(p, static_cast<hipStream_t>(stream)));
+}
+
+KVLR_API int kvlr_hadamard_bases(const kvlr_desc* desc, const float* P_K, const float* P_V, float* out_K,
+                                 float* out_V, void* stream) {
+  int Rk = 0, Rv = 0;
+  const int rc = check_desc(desc, nullptr, &Rk, &Rv, nullptr);
+  if (rc) return rc;
+  if (!P_K || !P_V || !out_K || !out_V) return KVLR_ERR_NULL;
+  // every head's block is row-major [d][r(h)] with r(h) a multiple of 16, so the
+  // transform acts on consecutive runs of 16 floats of the packed arrays
+  if (Rk % 16 || Rv % 16) return KVLR_ERR_RANK;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = kvlr::launch_hadamard(P_K, out_K, (size_t)desc->head_dim * Rk / 16, s);
+  if (e == hipSuccess) e = kvlr::launch_hadamard(P_V, out_V, (size_t)desc->head_dim * Rv / 16, s);
+  return hip_status(e);
 }
 
 }  // extern "C"
@@ -246,13 +276,14 @@ int prepare_decode(const kvlr_desc* desc, const float* q, const float* P_K, cons
                    const int32_t* seq_lens, float scale, const float* P_V, float* out, bool need_partials,
                    bool need_combine, void* workspace, size_t workspace_bytes, int32_t split_tokens,
                    kvlr::DecodeParams* p, kvlr::MergeParams* m, int* rank_bound) {
-  int rc = check_desc(desc, &p->ht, &p->Rk, &p->Rv, rank_bound);
+  int rc = check_desc(desc, &p->ht, &p->Rk, &p->Rv, rank_bound, &p->Sk, &p->Sv);
   p->qt_in = nullptr;
   p->qt_stride = 0;
   if (rc) return rc;
   if (need_partials && (!q || !P_K || !lat_k || !lat_v || !seq_lens)) return KVLR_ERR_NULL;
   if (need_combine && (!P_V || !out)) return KVLR_ERR_NULL;
   if (need_partials && !isfinite(scale)) return KVLR_ERR_ARG;
+  if (desc->latent_dtype == KVLR_Q43) return KVLR_ERR_DTYPE;   // decode kernel for 4/3-bit rows: not yet built
   int ns = 0, len = 0;
   rc = plan_split(desc, split_tokens, &ns, &len, p->ht.split_len);
   if (rc) return rc;
@@ -314,7 +345,7 @@ KVLR_API int kvlr_decode_partials(const kvlr_desc* desc, const float* q, const f
   const int rc = prepare_decode(desc, q, P_K, lat_k, lat_v, seq_lens, scale, nullptr, nullptr, true, false,
                                 workspace, workspace_bytes, split_tokens, &p, &m, &rank_bound);
   if (rc) return rc;
-  return hip_status(kvlr::launch_decode(p, desc->latent_dtype == KVLR_BF16, rank_bound, decode_tile(),
+  return hip_status(kvlr::launch_decode(p, desc->latent_dtype, rank_bound, decode_tile(),
                                         static_cast<hipStream_t>(stream)));
 }
 
@@ -340,7 +371,7 @@ KVLR_API int kvlr_decode_attn(const kvlr_desc* desc, const float* q, const float
                                 workspace_bytes, split_tokens, &p, &m, &rank_bound);
   if (rc) return rc;
   p.fuse = 1;   // one launch: the last split workgroup of each group merges and back-projects
-  return hip_status(kvlr::launch_decode(p, desc->latent_dtype == KVLR_BF16, rank_bound, decode_tile(),
+  return hip_status(kvlr::launch_decode(p, desc->latent_dtype, rank_bound, decode_tile(),
                                         static_cast<hipStream_t>(stream)));
 }
 
@@ -368,7 +399,7 @@ KVLR_API int kvlr_decode_attn_latent(const kvlr_desc* desc, const float* q_lat, 
   p.out_latent = 1;
   p.out_stride = rv_max;
   p.fuse = 1;
-  return hip_status(kvlr::launch_decode(p, desc->latent_dtype == KVLR_BF16, rank_bound, decode_tile(),
+  return hip_status(kvlr::launch_decode(p, desc->latent_dtype, rank_bound, decode_tile(),
                                         static_cast<hipStream_t>(stream)));
 }
 

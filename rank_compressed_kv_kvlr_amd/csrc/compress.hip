@@ -17,10 +17,112 @@
 //
 // fp32 inputs (and any other combination) use a plain VALU kernel; append
 // uses one workgroup per (batch row, KV head, K or V).
+//
+// Mixed 4/3-bit latents (STAR-KV technical summary, "Metodologia" section 3)
+// are quantised from the fp32 latents of a row by one thread per row; the
+// block-wise Hadamard rotation is already folded into the bases it receives
+// (hadamard_fold below, run once per set of bases).
 #include "kvlr_internal.hpp"
 
 namespace kvlr {
 namespace {
+
+// ---- 4/3-bit rows --------------------------------------------------------
+__device__ __forceinline__ uint32_t half_bits(_Float16 h) { return (uint32_t)__builtin_bit_cast(uint16_t, h); }
+
+// Step, base and 1/step of one block of x[c0, c1) (fp32, in the order of the
+// layout comment in kvlr.h); meta = step | base << 16 as half floats. A zero
+// step gives inv = 0 and therefore code 0 everywhere.
+__device__ __forceinline__ void q43_block_params(const float* x, int c0, int c1, float levels, float& base,
+                                                 float& inv, uint32_t& meta) {
+  float lo = x[c0], hi = x[c0];
+  for (int c = c0 + 1; c < c1; ++c) {
+    lo = fminf(lo, x[c]);
+    hi = fmaxf(hi, x[c]);
+  }
+  const _Float16 s16 = (_Float16)((hi - lo) / levels);
+  const _Float16 b16 = (_Float16)lo;
+  const float step = (float)s16;
+  base = (float)b16;
+  inv = step != 0.f ? 1.f / step : 0.f;
+  meta = half_bits(s16) | (half_bits(b16) << 16);
+}
+
+__device__ __forceinline__ uint32_t q43_code(float x, float base, float inv, float levels) {
+  const float t = rintf((x - base) * inv);
+  return (uint32_t)fminf(fmaxf(t, 0.f), levels);
+}
+
+// Quantise one row of r fp32 latents x[] (LDS) and store its rb(r) bytes at dst
+// (4-byte aligned). NO = outlier channels (16 or 32); the word indices of the
+// unrolled loops are compile-time constants, so the row is built in registers.
+template <int NO>
+__device__ void q43_store_row(const float* x, int r, uint32_t* dst) {
+  constexpr int kWords = 15;               // q43_row_bytes(128) / 4
+  constexpr int kInBase = (8 + NO / 2) / 4;  // first word of the inlier bit stream
+  uint32_t w[kWords];
+#pragma unroll
+  for (int k = 0; k < kWords; ++k) w[k] = 0;
+  float base, inv;
+  q43_block_params(x, 0, NO, 15.f, base, inv, w[0]);
+#pragma unroll
+  for (int c = 0; c < NO; ++c) w[2 + c / 8] |= q43_code(x[c], base, inv, 15.f) << (4 * (c % 8));
+  if (r > NO) {
+    q43_block_params(x, NO, r, 7.f, base, inv, w[1]);
+#pragma unroll
+    for (int c = 0; c < kMaxRank - NO; ++c) {
+      if (NO + c < r) {
+        const uint32_t v = q43_code(x[NO + c], base, inv, 7.f);
+        const int pos = 3 * c;
+        w[kInBase + pos / 32] |= v << (pos % 32);
+        if (pos % 32 > 29) w[kInBase + pos / 32 + 1] |= v >> (32 - pos % 32);
+      }
+    }
+  }
+  const int words = q43_row_bytes(r) / 4;
+#pragma unroll
+  for (int k = 0; k < kWords; ++k)
+    if (k < words) dst[k] = w[k];
+}
+
+__device__ __forceinline__ void q43_store_row_any(const float* x, int r, uint32_t* dst) {
+  if (q43_outlier(r) == 16)
+    q43_store_row<16>(x, r, dst);
+  else
+    q43_store_row<32>(x, r, dst);
+}
+
+// Block-wise Hadamard fold: every run of 16 floats becomes x H16 / 4 (a fast
+// Walsh-Hadamard transform in registers; in place is safe).
+__global__ __launch_bounds__(256) void hadamard_fold(const float* __restrict__ in, float* __restrict__ out,
+                                                     size_t n_groups) {
+  const size_t g = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= n_groups) return;
+  float v[16];
+  const float4* src = reinterpret_cast<const float4*>(in + 16 * g);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float4 f = src[k];
+    v[4 * k] = f.x;
+    v[4 * k + 1] = f.y;
+    v[4 * k + 2] = f.z;
+    v[4 * k + 3] = f.w;
+  }
+#pragma unroll
+  for (int len = 1; len < 16; len <<= 1)
+#pragma unroll
+    for (int i = 0; i < 16; i += 2 * len)
+#pragma unroll
+      for (int j = 0; j < len; ++j) {
+        const float a = v[i + j], c = v[i + j + len];
+        v[i + j] = a + c;
+        v[i + j + len] = a - c;
+      }
+  float4* dst = reinterpret_cast<float4*>(out + 16 * g);
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    dst[k] = make_float4(0.25f * v[4 * k], 0.25f * v[4 * k + 1], 0.25f * v[4 * k + 2], 0.25f * v[4 * k + 3]);
+}
 
 constexpr int kCompressWaves = 4;
 constexpr int kTokensPerWave = 64;        // 4 MFMA column tiles of 16 tokens
@@ -138,7 +240,7 @@ __global__ __launch_bounds__(256) void compress_bf16_mfma(CompressParams p) {
 constexpr int kValuTile = 64;
 
 __global__ __launch_bounds__(256) void compress_valu(CompressParams p) {
-  extern __shared__ __attribute__((aligned(16))) float xs[];   // [64][d]
+  extern __shared__ __attribute__((aligned(16))) float xs[];   // [64][d], then (4/3-bit rows) latents [64][r]
   const int kind = blockIdx.y & 1;
   const int h = blockIdx.y >> 1;
   const int b = blockIdx.z;
@@ -157,6 +259,24 @@ __global__ __launch_bounds__(256) void compress_valu(CompressParams p) {
     xs[idx] = p.in_bf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(X)[src]) : static_cast<const float*>(X)[src];
   }
   __syncthreads();
+  if (p.out_q43) {   // latents of the tile into LDS, then one thread per row quantises and stores
+    float* lat = xs + kValuTile * d;
+    for (int idx = threadIdx.x; idx < nt * r; idx += blockDim.x) {
+      const int t = idx / r, j = idx - t * r;
+      const float* x = xs + t * d;
+      float acc = 0.f;
+      for (int i = 0; i < d; ++i) acc = fmaf(x[i], P[(size_t)i * r + j], acc);
+      lat[t * r + j] = acc;
+    }
+    __syncthreads();
+    const int S = kind ? p.Sv : p.Sk;
+    const int s_pre = kind ? p.ht.sv_pre[h] : p.ht.sk_pre[h];
+    const int rb = q43_row_bytes(r);
+    uint8_t* blk = static_cast<uint8_t*>(kind ? p.lat_v : p.lat_k) + (size_t)cap_rows_of(p.cap) * ((size_t)b * S + s_pre);
+    for (int t = threadIdx.x; t < nt; t += blockDim.x)
+      q43_store_row_any(lat + t * r, r, reinterpret_cast<uint32_t*>(blk + (size_t)(p.start + t0 + t) * rb));
+    return;
+  }
   const size_t lat_base = (size_t)cap_rows_of(p.cap) * ((size_t)b * R + r_pre);
   const bool k_tiled = p.out_bf16 && kind == 0;
   for (int idx = threadIdx.x; idx < nt * r; idx += blockDim.x) {
@@ -176,6 +296,7 @@ __global__ __launch_bounds__(256) void compress_valu(CompressParams p) {
 // Append: one workgroup per (batch row, KV head, K or V).
 __global__ __launch_bounds__(128) void append_kernel(AppendParams p) {
   __shared__ float xs[256];
+  __shared__ float lat[kMaxRank];   // 4/3-bit rows: the fp32 latents before quantisation
   const int b = blockIdx.x, h = blockIdx.y, kind = blockIdx.z;
   const int d = p.d;
   const int pos = p.pos[b];
@@ -190,6 +311,21 @@ __global__ __launch_bounds__(128) void append_kernel(AppendParams p) {
     xs[i] = p.in_bf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(X)[src0 + i])
                       : static_cast<const float*>(X)[src0 + i];
   __syncthreads();
+  if (p.out_q43) {
+    for (int j = threadIdx.x; j < r; j += blockDim.x) {
+      float acc = 0.f;
+      for (int i = 0; i < d; ++i) acc = fmaf(xs[i], P[(size_t)i * r + j], acc);
+      lat[j] = acc;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int S = kind ? p.Sv : p.Sk;
+      const int s_pre = kind ? p.ht.sv_pre[h] : p.ht.sk_pre[h];
+      uint8_t* blk = static_cast<uint8_t*>(kind ? p.lat_v : p.lat_k) + (size_t)cap_rows_of(p.cap) * ((size_t)b * S + s_pre);
+      q43_store_row_any(lat, r, reinterpret_cast<uint32_t*>(blk + (size_t)pos * q43_row_bytes(r)));
+    }
+    return;
+  }
   const size_t base = (size_t)cap_rows_of(p.cap) * ((size_t)b * R + r_pre);
   const bool k_tiled = p.out_bf16 && kind == 0;
   for (int j = threadIdx.x; j < r; j += blockDim.x) {
@@ -209,7 +345,7 @@ hipError_t launch_compress(const CompressParams& p, hipStream_t stream) {
   if (p.n_tok <= 0) return hipSuccess;
   int max_r = 0;
   for (int h = 0; h < p.Hkv; ++h) max_r = max(max_r, max(p.ht.rk[h], p.ht.rv[h]));
-  if (p.in_bf16) {
+  if (p.in_bf16 && !p.out_q43) {
     const size_t lds = (size_t)4 * max_r * p.d;   // hi + lo operand tiles
     const dim3 grid((p.n_tok + kTokensPerWg - 1) / kTokensPerWg, 2 * p.Hkv, p.B);
 #define KVLR_COMPRESS_CASE(NKB)                                                              \
@@ -231,10 +367,16 @@ hipError_t launch_compress(const CompressParams& p, hipStream_t stream) {
     }
 #undef KVLR_COMPRESS_CASE
   } else {
-    const size_t lds = (size_t)kValuTile * p.d * sizeof(float);
+    const size_t lds = (size_t)kValuTile * (p.d + (p.out_q43 ? max_r : 0)) * sizeof(float);
     const dim3 grid((p.n_tok + kValuTile - 1) / kValuTile, 2 * p.Hkv, p.B);
     hipLaunchKernelGGL(compress_valu, grid, dim3(256), lds, stream, p);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_hadamard(const float* in, float* out, size_t n_groups, hipStream_t stream) {
+  if (n_groups == 0) return hipSuccess;
+  hipLaunchKernelGGL(hadamard_fold, dim3((unsigned)((n_groups + 255) / 256)), dim3(256), 0, stream, in, out, n_groups);
   return hipGetLastError();
 }
 

@@ -900,7 +900,8 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge(MergeParams p) {
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeParams& p, int latent_bf16, int rank_bound, int tile, hipStream_t stream) {
+hipError_t launch_decode(const DecodeParams& p, int latent_dtype, int rank_bound, int tile, hipStream_t stream) {
+  const bool latent_bf16 = latent_dtype == KVLR_BF16;
   const dim3 grid(p.n_splits, p.Hkv * p.n_head_groups, p.B);
   const dim3 block(kWaves * 64);
   if (latent_bf16) {

@@ -22,6 +22,8 @@ struct HeadTable {
   int rk_pre[kMaxKvHeads];
   int rv_pre[kMaxKvHeads];
   int split_len[kMaxKvHeads];   // decode: tokens per split of KV head h (splits past the sequence are empty)
+  int sk_pre[kMaxKvHeads];      // prefix sums of per-row storage (elements; bytes for 4/3-bit rows)
+  int sv_pre[kMaxKvHeads];
 };
 
 struct DecodeParams {
@@ -42,6 +44,7 @@ struct DecodeParams {
   int B, Hq, Hkv, G, d, cap;
   int split_len, n_splits, ws_stride, n_head_groups;
   int Rk, Rv;            // sum of ranks over heads
+  int Sk, Sv;            // per-row storage summed over heads (elements; bytes for 4/3-bit rows)
   float scale_log2;      // scale * log2(e): scores live in the base-2 domain
   HeadTable ht;
 };
@@ -64,7 +67,8 @@ struct CompressParams {
   void* lat_v;
   int B, Hkv, d, cap, start, n_tok;
   int Rk, Rv;
-  int in_bf16, out_bf16;
+  int Sk, Sv;
+  int in_bf16, out_bf16, out_q43;
   HeadTable ht;
 };
 
@@ -78,7 +82,8 @@ struct AppendParams {
   void* lat_v;
   int B, Hkv, d, cap;
   int Rk, Rv;
-  int in_bf16, out_bf16;
+  int Sk, Sv;
+  int in_bf16, out_bf16, out_q43;
   HeadTable ht;
 };
 
@@ -100,8 +105,22 @@ __host__ __device__ inline size_t k_tiled_offset(int t, int j, int rk) {
   return base + (size_t)np * 512 + (jj >> 2) * 64 + n * 4 + (jj & 3);
 }
 
+// Mixed 4/3-bit latent rows (STAR-KV technical summary, "Metodologia" section 3):
+// channels in the 4-bit outlier block (20% of r in whole 16-channel blocks) and
+// bytes per stored row.
+__host__ __device__ inline int q43_outlier(int r) {
+  const int n = (r + 40) / 80;
+  return 16 * (n > 1 ? n : 1);
+}
+__host__ __device__ inline int q43_row_bytes(int r) {
+  const int no = q43_outlier(r);
+  const int n = 8 + no / 2 + (3 * (r - no) + 7) / 8;
+  return (n + 3) / 4 * 4;
+}
+
 // Launchers (return hipGetLastError() of their launches).
-hipError_t launch_decode(const DecodeParams& p, int latent_bf16, int rank_bound, int tile, hipStream_t s);
+hipError_t launch_decode(const DecodeParams& p, int latent_dtype, int rank_bound, int tile, hipStream_t s);
+hipError_t launch_hadamard(const float* in, float* out, size_t n_groups, hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, int rank_bound, hipStream_t s);
 hipError_t launch_compress(const CompressParams& p, hipStream_t s);
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
