@@ -45,6 +45,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle CPU time")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-compression measurement")
+    ap.add_argument("--no-q43", action="store_true", help="skip the 4/3-bit latent measurement")
     ap.add_argument("--traffic-reference", action="store_true",
                     help="also run a plain 1 GiB device copy (a known-size reference for HBM traffic counters)")
     return ap.parse_args()
@@ -65,6 +66,50 @@ def load_traffic():
     if t.get("decode_src_sha256_16") != source_hash(DECODE_SRC):
         return None
     return t.get("bytes_per_launch")
+
+
+def measure_q43(kv, torch, np, cfg, gen, q, lens, steps, warmup):
+    """The same workload with mixed 4/3-bit latents (4-bit outlier, 3-bit inlier block per
+    token, block-wise Hadamard folded into the bases): kvlr_decode_attn launches timed with
+    HIP events, two cache replicas alternating."""
+    from synth import host
+    B, T, Hkv, d = cfg.B, cfg.T, cfg.Hkv, cfg.d
+    rk, rv = host.ranks(cfg)
+    PK, PV = host.bases(cfg)
+    desc = kv.Desc(B, cfg.Hq, Hkv, d, cfg.capacity, rk, rv, kv.BF16, kv.Q43)
+    pk, pv = kv.pack_bases(PK), kv.pack_bases(PV)
+    kv.hadamard_bases(desc, pk, pv)
+    print("[bench] building 2 replicas with 4/3-bit latents", file=sys.stderr, flush=True)
+    reps = []
+    for _ in range(2):
+        lk, lv = kv.alloc_cache(desc)
+        for t0 in range(0, T, 8192):
+            n = min(8192, T - t0)
+            kv.prefill_compress(desc, gen.make("k", B, n, t0=t0), gen.make("v", B, n, t0=t0), t0, pk, pv, lk, lv)
+        reps.append((lk, lv))
+    ws = kv.alloc_workspace(desc)
+    out = torch.empty((B, cfg.Hq, d), dtype=torch.float32, device="cuda")
+    for k in range(warmup):
+        lk, lv = reps[k % 2]
+        kv.decode_attn(desc, q, pk, pv, lk, lv, lens, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    t_start = time.perf_counter()
+    for k in range(steps):
+        lk, lv = reps[k % 2]
+        evs[k][0].record()
+        kv.decode_attn(desc, q, pk, pv, lk, lv, lens, out=out, workspace=ws)
+        evs[k][1].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    us = float(np.mean([e[0].elapsed_time(e[1]) * 1e3 for e in evs]))
+    row_k = sum(kv.q43_row_bytes(int(r)) for r in rk)
+    row_v = sum(kv.q43_row_bytes(int(r)) for r in rv)
+    nbytes = B * T * (row_k + row_v)
+    return {"entry": "kvlr_decode_attn on KVLR_Q43 caches", "kernel": "decode_split_q43<64>",
+            "bytes_per_launch": nbytes, "launch_us_mean": us, "GBps": nbytes / (us * 1e-6) / 1e9,
+            "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, "tokens_per_s": B * steps / elapsed,
+            "bytes_vs_bf16": nbytes / (B * T * int((rk + rv).sum()) * 2)}
 
 
 def cpu_baseline(cfg, seconds):
@@ -211,6 +256,10 @@ def main():
     torch.cuda.synchronize()
     folded_us = float(np.mean([e[0].elapsed_time(e[1]) * 1e3 for e in fevs]))
 
+    q43 = None
+    if not args.no_q43:
+        q43 = measure_q43(kv, torch, np, cfg, gen, q, lens, args.steps, args.warmup)
+
     if args.traffic_reference:
         from synth.device import copy as device_copy
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
@@ -254,6 +303,8 @@ def main():
     }
     result["folded"] = {"entry": "kvlr_decode_attn_latent", "launch_us_mean": folded_us,
                         "GBps": alg_bytes / (folded_us * 1e-6) / 1e9}
+    if q43 is not None:
+        result["q43"] = q43
     if prefill is not None:
         result["prefill"] = prefill
     if not args.no_cpu_baseline:

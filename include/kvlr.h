@@ -111,7 +111,8 @@ typedef enum kvlr_dtype {
  * (b, h) starts at byte C16 * (b * RB + RB_pre(h)) and row t at t * rb(r).
  * The bases used with such a cache must have the block-wise Hadamard folded
  * in (kvlr_hadamard_bases); compression, append and decode all take those
- * folded bases.
+ * folded bases. The cache base addresses must be 16-byte aligned (checked:
+ * KVLR_ERR_ARG otherwise).
  *
  * Basis layout: P_K is fp32, heads packed back to back, head h a row-major
  * [d][r_k[h]] block starting at element d * R_pre(h); P_V likewise. */

@@ -3,6 +3,7 @@
 // never synchronises. Every check runs before the first HIP call.
 #include <math.h>
 #include <stdlib.h>
+#include <stdint.h>
 #include <string.h>
 
 #include "kvlr_internal.hpp"
@@ -25,6 +26,11 @@ int resident_wgs_per_cu(int latent_dtype, int rank_bound) {
 }
 
 bool valid_dtype(int t) { return t == KVLR_F32 || t == KVLR_BF16; }
+
+// 4/3-bit caches are streamed with 16-byte loads: their base addresses must be 16-byte aligned.
+bool q43_aligned(int latent_dtype, const void* a, const void* b) {
+  return latent_dtype != KVLR_Q43 || (((uintptr_t)a | (uintptr_t)b) & 15) == 0;
+}
 bool valid_latent_dtype(int t) { return valid_dtype(t) || t == KVLR_Q43; }
 
 // Storage of one latent row of rank r: elements, or bytes for 4/3-bit rows.
@@ -210,6 +216,7 @@ KVLR_API int kvlr_prefill_compress(const kvlr_desc* desc, const void* K, const v
   if ((long long)start + n_tok > desc->capacity) return KVLR_ERR_SHAPE;
   if (n_tok == 0) return KVLR_OK;
   if (!K || !V || !P_K || !P_V || !lat_k || !lat_v) return KVLR_ERR_NULL;
+  if (!q43_aligned(desc->latent_dtype, lat_k, lat_v)) return KVLR_ERR_ARG;
   if ((long long)desc->batch * n_tok * desc->n_kv_heads * desc->head_dim > (1LL << 40)) return KVLR_ERR_SHAPE;
   p.x_k = K;
   p.x_v = V;
@@ -235,6 +242,7 @@ KVLR_API int kvlr_append(const kvlr_desc* desc, const void* k_new, const void* v
   const int rc = check_desc(desc, &p.ht, &p.Rk, &p.Rv, nullptr, &p.Sk, &p.Sv);
   if (rc) return rc;
   if (!k_new || !v_new || !pos || !P_K || !P_V || !lat_k || !lat_v) return KVLR_ERR_NULL;
+  if (!q43_aligned(desc->latent_dtype, lat_k, lat_v)) return KVLR_ERR_ARG;
   p.k_new = k_new;
   p.v_new = v_new;
   p.pos = pos;
@@ -283,7 +291,7 @@ int prepare_decode(const kvlr_desc* desc, const float* q, const float* P_K, cons
   if (need_partials && (!q || !P_K || !lat_k || !lat_v || !seq_lens)) return KVLR_ERR_NULL;
   if (need_combine && (!P_V || !out)) return KVLR_ERR_NULL;
   if (need_partials && !isfinite(scale)) return KVLR_ERR_ARG;
-  if (desc->latent_dtype == KVLR_Q43) return KVLR_ERR_DTYPE;   // decode kernel for 4/3-bit rows: not yet built
+  if (need_partials && !q43_aligned(desc->latent_dtype, lat_k, lat_v)) return KVLR_ERR_ARG;
   int ns = 0, len = 0;
   rc = plan_split(desc, split_tokens, &ns, &len, p->ht.split_len);
   if (rc) return rc;

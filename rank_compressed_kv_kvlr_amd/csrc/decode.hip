@@ -637,6 +637,383 @@ __global__ __launch_bounds__(256) void decode_split_bf16(DecodeParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// 4/3-bit latents (STAR-KV technical summary, "Metodologia" section 3): keys on
+// MFMA, values on VALU, both read as stored codes
+// ---------------------------------------------------------------------------
+// A wave streams ST consecutive rows of keys and of values per iteration with
+// 16-byte loads (the rows of a (batch row, KV head) block are contiguous and a
+// tile starts 16-byte aligned), parks them in its own LDS region while the
+// next ST rows are in flight, and reads the codes it needs from LDS. Compressed
+// rows are short, so a tile of ST = 128 rows keeps as many bytes in flight per
+// wave as the bf16 kernel's 32-row tile.
+// Scores: a code c enters the MFMA as the bf16 number 128 + c (bits 0x4300 | c,
+// exact), so per token and block of channels
+//   sum_j q~_j (step c_j + base) = step (acc - 128 Q) + base Q,
+// with acc = sum_j q~_j (128 + c_j) from the MFMA and Q = sum_j q~_j over the
+// block, q~ as the MFMA sees it (high plus low bf16 part). Outlier slices hold
+// 16 channels (16x16x16), inlier slices 32 (16x16x32) plus a 16-channel tail.
+// Values: a lane owns 8 channels of a row, all inside one block, and
+// accumulates sum_t p_t step_t c_t per channel and sum_t p_t base_t once per
+// head; the two are added when the split ends.
+template <int RB>
+__global__ __launch_bounds__(256) void decode_split_q43(DecodeParams p) {
+  constexpr int TT = 32;                     // tokens per score/softmax/value step
+  constexpr int NB = TT / 16;
+  constexpr int ST = RB <= 64 ? 128 : 64;    // rows per wave iteration
+  constexpr int NSUB = ST / TT;
+  constexpr int RBM = q43_row_bytes(RB);     // bytes of the longest row
+  constexpr int CH = (ST * RBM + 1023) / 1024;   // 16-byte chunks per lane per tile (keys or values)
+  constexpr int MSO = RB == 128 ? 2 : 1;     // outlier 16-channel slices (bound)
+  constexpr int MSI = RB > 32 ? (RB - 16) / 32 : 1;   // full 32-channel inlier slices (bound; >= 1)
+  constexpr int NIT = value_iters_bound(RB, TT);
+  constexpr int QTS = RB;
+  constexpr int kRS = 36;                    // per-lane stride of the wave reduction
+  constexpr int kStageF = kWaves * ST * 2 * RBM / 4;   // floats of LDS for the staged rows
+  static_assert(kStageF + kWaves * TT * 4 <= kTailLds, "staged rows and p tiles must fit the LDS block");
+  __shared__ __attribute__((aligned(16))) float smem[kWaves * 64 * kRS + 64 > kTailLds ? kWaves * 64 * kRS + 64 : kTailLds];
+  __shared__ float qsum[2][kHeadsPerWg];     // Q of the outlier and inlier key blocks per head
+
+  const int s = blockIdx.x;
+  const int h = blockIdx.y / p.n_head_groups;
+  const int hg = blockIdx.y - h * p.n_head_groups;
+  const int b = blockIdx.z;
+  const int hq0 = h * p.G + hg * kHeadsPerWg;
+  const int gpw = min(kHeadsPerWg, p.G - hg * kHeadsPerWg);
+  const int rk = p.ht.rk[h], rv = p.ht.rv[h];
+  const int T = min(max(p.seq_lens[b], 0), p.cap);
+  const int t_begin = min(s * p.ht.split_len[h], T);
+  const int t_end = min(T, t_begin + p.ht.split_len[h]);
+  if (t_begin >= t_end) {
+    write_empty_records(p, b, hq0, gpw, s, rv);
+    BasisPrefetch<RB> pf;
+    prefetch_basis<RB>(p, h, rv, pf);
+    finish_split<RB>(p, b, h, hg, hq0, gpw, rv, smem, pf);
+    return;
+  }
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n16 = lane & 15, q4 = lane >> 4;
+
+  // ---- key row geometry and this lane's byte offsets inside a row
+  const int nok = q43_outlier(rk), nik = rk - nok;
+  const int nso = nok >> 4, nsi = nik >> 5, ktail = (nik >> 4) & 1;
+  const int rbk = q43_row_bytes(rk);
+  const int kib = 8 + nok / 2;                          // inlier bit stream
+  const int ko_off = 8 + 4 * (q4 >> 1), ko_sh = 16 * (q4 & 1);
+  const int ki_off = kib + 4 * ((24 * q4) >> 5), ki_sh = (24 * q4) & 31;
+  const bool ki_two = ki_sh > 8;
+  const int kt_off = kib + 4 * (3 * nsi + ((12 * q4) >> 5)), kt_sh = (12 * q4) & 31;
+  const bool kt_two = kt_sh > 20;
+  // ---- value row geometry: C chunks of 8 channels per row
+  const int nov = q43_outlier(rv);
+  const int rbv = q43_row_bytes(rv);
+  const int C = rv >> 3;
+  const int rpi = 64 / C;
+  const int ro = lane / C, cch = lane - ro * C;
+  const bool v_active = ro < rpi;
+  const int n_it = (TT + rpi - 1) / rpi;
+  const bool v_out = cch < (nov >> 3);                 // chunk in the 4-bit outlier block
+  const int v_meta = v_out ? 0 : 4;
+  const int v_bits = v_out ? 4 : 3;
+  const int v_bit0 = v_out ? 0 : 24 * (cch - (nov >> 3));
+  const int v_off = v_out ? 8 + 4 * cch : 8 + nov / 2 + 4 * (v_bit0 >> 5);
+  const int v_sh = v_out ? 0 : v_bit0 & 31;
+  const bool v_two = v_sh > 8;
+
+  const size_t rows = cap_rows_of(p.cap);
+  const uint8_t* Kb = static_cast<const uint8_t*>(p.lat_k) + rows * ((size_t)b * p.Sk + p.ht.sk_pre[h]);
+  const uint8_t* Vb = static_cast<const uint8_t*>(p.lat_v) + rows * ((size_t)b * p.Sv + p.ht.sv_pre[h]);
+
+  // this wave's LDS: staged key rows, staged value rows, then (after all staging) its p tile
+  uint8_t* kst = reinterpret_cast<uint8_t*>(smem) + (size_t)wave * ST * 2 * RBM;
+  uint8_t* vst = kst + ST * RBM;
+  float* p_lds = smem + kStageF + wave * (TT * 4);     // [TT tokens][4 heads]
+
+  float m[4], l[4], acc[4][8], accb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m[i] = kNegInf;
+    l[i] = 0.f;
+    accb[i] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
+  }
+
+  // ---- tile streaming: rows [t0, t0 + ST) of keys and values as 16-byte chunks.
+  // Chunks past the last valid row's bytes are not read (they never cross the end
+  // of the block: it is a multiple of 16 bytes, as is every tile start).
+  u32x4_t kraw[CH], vraw[CH];
+  int nk_ch = 0, nv_ch = 0;
+  auto load_raw = [&](int t0) {
+    const int n = min(ST, t_end - t0);
+    nk_ch = (n * rbk + 15) >> 4;
+    nv_ch = (n * rbv + 15) >> 4;
+    const uint8_t* ks = Kb + (size_t)t0 * rbk;
+    const uint8_t* vs = Vb + (size_t)t0 * rbv;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int ch = c * 64 + lane;
+      if (ch < nk_ch) kraw[c] = load_stream16(ks + 16 * ch);
+      if (ch < nv_ch) vraw[c] = load_stream16(vs + 16 * ch);
+    }
+  };
+  auto stage_raw = [&]() {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int ch = c * 64 + lane;
+      if (ch < nk_ch) *reinterpret_cast<u32x4_t*>(kst + 16 * ch) = kraw[c];
+      if (ch < nv_ch) *reinterpret_cast<u32x4_t*>(vst + 16 * ch) = vraw[c];
+    }
+  };
+  auto lds32 = [](const uint8_t* ptr) { return *reinterpret_cast<const uint32_t*>(ptr); };
+
+  // the first tile's loads do not depend on q~: issue them before the prologue
+  int t0 = t_begin + wave * ST;
+  if (t0 < t_end) load_raw(t0);
+
+  // ---- prologue: q~ into LDS, block sums Q, MFMA A operands (hi/lo) into registers
+  float* q_lds = smem;                          // [4][d]  (d <= 256)
+  float* qt_lds = smem + kHeadsPerWg * 256;     // [4][QTS]
+  float* qred = qt_lds + kHeadsPerWg * QTS;     // [4 waves][4][QTS]
+  project_query<RB>(p, b, h, hq0, gpw, rk, q_lds, qred, qt_lds);
+  if (tid < 2 * kHeadsPerWg) {
+    const int g = tid & 3, region = tid >> 2;
+    const int j1 = region ? rk : nok;
+    float Q = 0.f;
+    for (int j = region ? nok : 0; j < j1; ++j) {
+      const float x = qt_lds[g * QTS + j];
+      const uint16_t hi = f32_to_bf16_bits(x);
+      const uint16_t lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
+      Q += bf16_bits_to_f32(hi) + bf16_bits_to_f32(lo);
+    }
+    qsum[region][g] = Q;
+  }
+  auto qt_at = [&](int j, bool valid) { return (n16 < kHeadsPerWg && valid) ? qt_lds[n16 * QTS + j] : 0.f; };
+  auto bf_hi = [](float x) { return (short)f32_to_bf16_bits(x); };
+  auto bf_lo = [](float x) { return (short)f32_to_bf16_bits(x - bf16_bits_to_f32(f32_to_bf16_bits(x))); };
+  bf16x4_t ao_hi[MSO], ao_lo[MSO], at_hi, at_lo;
+  bf16x8_t ai_hi[MSI], ai_lo[MSI];
+#pragma unroll
+  for (int sl = 0; sl < MSO; ++sl)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float x = qt_at(16 * sl + 4 * q4 + e, sl < nso);
+      ao_hi[sl][e] = bf_hi(x);
+      ao_lo[sl][e] = bf_lo(x);
+    }
+#pragma unroll
+  for (int sl = 0; sl < MSI; ++sl)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = qt_at(nok + 32 * sl + 8 * q4 + e, sl < nsi);
+      ai_hi[sl][e] = bf_hi(x);
+      ai_lo[sl][e] = bf_lo(x);
+    }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float x = qt_at(nok + 32 * nsi + 4 * q4 + e, ktail != 0);
+    at_hi[e] = bf_hi(x);
+    at_lo[e] = bf_lo(x);
+  }
+  __syncthreads();   // LDS is reused below
+  float Qo[4], Qi[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    Qo[i] = qsum[0][i];
+    Qi[i] = qsum[1][i];
+  }
+  if (t0 < t_end) stage_raw();
+
+  for (; t0 < t_end; t0 += kWaves * ST) {
+    const int t_next = t0 + kWaves * ST;
+    const int n_valid = min(ST, t_end - t0);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (t_next < t_end) load_raw(t_next);   // in flight while this tile is processed from LDS
+
+    for (int sub = 0; sub < NSUB; ++sub) {
+      const int ts = 32 * sub;                 // first row of the step inside the tile
+      if (ts >= n_valid) break;
+      // ---- scores on MFMA from the codes (128 + c as bf16)
+      f32x4_t sc[NB];
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk) {
+        const uint8_t* row = kst + min(ts + 16 * blk + n16, n_valid - 1) * rbk;
+        f32x4_t ao = {0.f, 0.f, 0.f, 0.f}, ai = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int sl = 0; sl < MSO; ++sl) {
+          if (sl < nso) {
+            const uint32_t x = lds32(row + ko_off + 8 * sl) >> ko_sh;   // 4 nibbles: channels 4 q4 ..
+            const uint32_t lo = x & 0x0F0Fu, hi = (x >> 4) & 0x0F0Fu;
+            u32x2_t w;
+            w.x = __builtin_amdgcn_perm(hi, lo, 0x0C040C00u) | 0x43004300u;
+            w.y = __builtin_amdgcn_perm(hi, lo, 0x0C050C01u) | 0x43004300u;
+            const bf16x4_t kb = __builtin_bit_cast(bf16x4_t, w);
+            ao = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ao_hi[sl], kb, ao, 0, 0, 0);
+            ao = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ao_lo[sl], kb, ao, 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int sl = 0; sl < MSI; ++sl) {
+          if (sl < nsi) {
+            const uint32_t w0 = lds32(row + ki_off + 12 * sl);
+            const uint32_t w1 = ki_two ? lds32(row + ki_off + 12 * sl + 4) : 0u;
+            const uint32_t bits = __builtin_amdgcn_alignbit(w1, w0, ki_sh);
+            u32x4_t w;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              w[k] = __builtin_amdgcn_ubfe(bits, 6 * k, 3) | (__builtin_amdgcn_ubfe(bits, 6 * k + 3, 3) << 16) |
+                     0x43004300u;
+            const bf16x8_t kb = __builtin_bit_cast(bf16x8_t, w);
+            ai = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ai_hi[sl], kb, ai, 0, 0, 0);
+            ai = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ai_lo[sl], kb, ai, 0, 0, 0);
+          }
+        }
+        if (ktail) {
+          const uint32_t w0 = lds32(row + kt_off);
+          const uint32_t w1 = kt_two ? lds32(row + kt_off + 4) : 0u;
+          const uint32_t bits = __builtin_amdgcn_alignbit(w1, w0, kt_sh);
+          u32x2_t w;
+          w.x = __builtin_amdgcn_ubfe(bits, 0, 3) | (__builtin_amdgcn_ubfe(bits, 3, 3) << 16) | 0x43004300u;
+          w.y = __builtin_amdgcn_ubfe(bits, 6, 3) | (__builtin_amdgcn_ubfe(bits, 9, 3) << 16) | 0x43004300u;
+          const bf16x4_t kb = __builtin_bit_cast(bf16x4_t, w);
+          ai = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(at_hi, kb, ai, 0, 0, 0);
+          ai = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(at_lo, kb, ai, 0, 0, 0);
+        }
+        // block parameters of this lane's token (lanes 0..15 hold heads 0..3)
+        const uint32_t m0 = lds32(row), m1 = lds32(row + 4);
+        const float so = half_bits_to_f32(m0 & 0xFFFFu), bo = half_bits_to_f32(m0 >> 16);
+        const float si = half_bits_to_f32(m1 & 0xFFFFu), bi = half_bits_to_f32(m1 >> 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sc[blk][i] = so * (ao[i] - 128.f * Qo[i]) + bo * Qo[i] + si * (ai[i] - 128.f * Qi[i]) + bi * Qi[i];
+      }
+
+      // ---- online softmax (as in the bf16 kernel)
+      const int tb = t0 + ts;
+      float alpha[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float mx = kNegInf;
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) {
+          const bool valid = (tb + 16 * blk + n16) < t_end;
+          sc[blk][i] = valid ? sc[blk][i] : kNegInf;
+          mx = fmaxf(mx, sc[blk][i]);
+        }
+        mx = row16_allreduce<true>(mx);
+        const float m_new = fmaxf(m[i], mx);
+        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+        alpha[i] = fast_exp2(m[i] - m_use);
+        float ls = 0.f;
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) {
+          const float pr = fast_exp2(sc[blk][i] - m_use);
+          sc[blk][i] = pr;
+          ls += pr;
+        }
+        l[i] = fmaf(l[i], alpha[i], ls);
+        m[i] = m_new;
+      }
+      if (q4 == 0) {
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk)
+          *reinterpret_cast<float4*>(p_lds + (16 * blk + n16) * 4) =
+              make_float4(sc[blk][0], sc[blk][1], sc[blk][2], sc[blk][3]);
+      }
+      float a_s[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a_s[i] = readlane_f(alpha[i], 0);
+      if (a_s[0] != 1.f || a_s[1] != 1.f || a_s[2] != 1.f || a_s[3] != 1.f) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          accb[i] *= a_s[i];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[i][e] *= a_s[i];
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+      // ---- value mix on VALU from the codes
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        if (it < n_it) {
+          const int r = it * rpi + ro;
+          if (v_active && r < TT) {
+            const uint8_t* row = vst + min(ts + r, n_valid - 1) * rbv;
+            const float4 pw = *reinterpret_cast<const float4*>(p_lds + r * 4);
+            const uint32_t mt = lds32(row + v_meta);
+            const float step = half_bits_to_f32(mt & 0xFFFFu), base = half_bits_to_f32(mt >> 16);
+            const uint32_t c0 = lds32(row + v_off);
+            const uint32_t c1 = v_two ? lds32(row + v_off + 4) : 0u;
+            const uint32_t bits = __builtin_amdgcn_alignbit(c1, c0, v_sh);
+            accb[0] = fmaf(pw.x, base, accb[0]);
+            accb[1] = fmaf(pw.y, base, accb[1]);
+            accb[2] = fmaf(pw.z, base, accb[2]);
+            accb[3] = fmaf(pw.w, base, accb[3]);
+            const float w0 = pw.x * step, w1 = pw.y * step, w2 = pw.z * step, w3 = pw.w * step;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float c = (float)__builtin_amdgcn_ubfe(bits, e * v_bits, v_bits);
+              acc[0][e] = fmaf(w0, c, acc[0][e]);
+              acc[1][e] = fmaf(w1, c, acc[1][e]);
+              acc[2][e] = fmaf(w2, c, acc[2][e]);
+              acc[3][e] = fmaf(w3, c, acc[3][e]);
+            }
+          }
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    if (t_next < t_end) stage_raw();   // this tile's LDS reads are done (in order within the wave)
+  }
+  // the block minimum enters every channel of this lane's chunk once per unit of weight
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[i][e] += accb[i];
+
+  BasisPrefetch<RB> pf;
+  prefetch_basis<RB>(p, h, rv, pf);
+  // ---- workgroup merge of the 4 waves
+#pragma unroll
+  for (int i = 0; i < 4; ++i) l[i] = row16_allreduce<false>(l[i]);
+  __syncthreads();
+  float* red = smem;                          // [wave][lane][kRS]
+  float* wm = smem + kWaves * 64 * kRS;       // [wave][head]
+  float* wl = wm + 16;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; e += 4)
+      *reinterpret_cast<float4*>(red + (wave * 64 + lane) * kRS + i * 8 + e) =
+          make_float4(acc[i][e], acc[i][e + 1], acc[i][e + 2], acc[i][e + 3]);
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      wm[wave * 4 + i] = m[i];
+      wl[wave * 4 + i] = l[i];
+    }
+  }
+  __syncthreads();
+  merge_waves_and_store(p, b, hq0, gpw, s, rv, wm, wl, [&](int w, int g, int j) {
+    const int c = j >> 3, e = j & 7;
+    const float* base = red + (w * 64 + c) * kRS + g * 8 + e;
+    const int step = C * kRS;
+    float sum = 0.f;
+#pragma unroll 8
+    for (int r = 0; r < rpi; ++r) sum += base[r * step];
+    return sum;
+  });
+  finish_split<RB>(p, b, h, hg, hq0, gpw, rv, smem, pf);
+}
+
+// ---------------------------------------------------------------------------
 // fp32 latents: VALU throughout (token per lane for scores, channel per lane
 // for the value mix)
 // ---------------------------------------------------------------------------
@@ -904,6 +1281,15 @@ hipError_t launch_decode(const DecodeParams& p, int latent_dtype, int rank_bound
   const bool latent_bf16 = latent_dtype == KVLR_BF16;
   const dim3 grid(p.n_splits, p.Hkv * p.n_head_groups, p.B);
   const dim3 block(kWaves * 64);
+  if (latent_dtype == KVLR_Q43) {
+    switch (rank_bound) {
+      case 32: hipLaunchKernelGGL(decode_split_q43<32>, grid, block, 0, stream, p); break;
+      case 64: hipLaunchKernelGGL(decode_split_q43<64>, grid, block, 0, stream, p); break;
+      case 96: hipLaunchKernelGGL(decode_split_q43<96>, grid, block, 0, stream, p); break;
+      default: hipLaunchKernelGGL(decode_split_q43<128>, grid, block, 0, stream, p); break;
+    }
+    return hipGetLastError();
+  }
   if (latent_bf16) {
     if (tile == 32) {
       switch (rank_bound) {

@@ -108,11 +108,11 @@ __host__ __device__ inline size_t k_tiled_offset(int t, int j, int rk) {
 // Mixed 4/3-bit latent rows (STAR-KV technical summary, "Metodologia" section 3):
 // channels in the 4-bit outlier block (20% of r in whole 16-channel blocks) and
 // bytes per stored row.
-__host__ __device__ inline int q43_outlier(int r) {
+__host__ __device__ constexpr int q43_outlier(int r) {
   const int n = (r + 40) / 80;
   return 16 * (n > 1 ? n : 1);
 }
-__host__ __device__ inline int q43_row_bytes(int r) {
+__host__ __device__ constexpr int q43_row_bytes(int r) {
   const int no = q43_outlier(r);
   const int n = 8 + no / 2 + (3 * (r - no) + 7) / 8;
   return (n + 3) / 4 * 4;
@@ -151,6 +151,9 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, h);
 }
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+__device__ __forceinline__ float half_bits_to_f32(uint32_t b) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
 
 // All-reduce over the 16 lanes of a DPP row (max or sum) with row rotations
 // and quad permutations; every lane of the row ends with the result.

@@ -118,3 +118,171 @@ def test_quantised_compression_matches_oracle(gpu):
     frac = n_same / n_codes
     say(f"[q43] identical codes {frac:.6f}")
     assert frac >= 0.999, frac
+
+
+# ---------------------------------------------------------------------------
+# decode over 4/3-bit caches
+# ---------------------------------------------------------------------------
+def _q43_case(cfg, n_rows=None, ranks=None, chunk=None):
+    """Device caches of cfg's rows stored as 4/3-bit latents with Hadamard-folded bases."""
+    import torch
+    kv = _kv()
+    rk, rv = host.ranks(cfg) if ranks is None else ranks
+    PK, PV = host.bases(cfg)
+    if ranks is not None:
+        PK = [P[:, :int(r)] for P, r in zip(PK, rk)] if PK[0].shape[1] >= max(rk) else PK
+    n_rows = cfg.capacity if n_rows is None else n_rows
+    desc = kv.Desc(cfg.B, cfg.Hq, cfg.Hkv, cfg.d, cfg.capacity, rk, rv, kv.BF16, kv.Q43)
+    pk, pv = kv.pack_bases(PK), kv.pack_bases(PV)
+    kv.hadamard_bases(desc, pk, pv)
+    lk, lv = kv.alloc_cache(desc)
+    gen = KVGenerator(cfg, 0)
+    chunk = chunk or n_rows
+    for t0 in range(0, n_rows, chunk):
+        n = min(chunk, n_rows - t0)
+        kv.prefill_compress(desc, gen.make("k", cfg.B, n, t0=t0), gen.make("v", cfg.B, n, t0=t0), t0, pk, pv, lk, lv)
+    torch.cuda.synchronize()
+    say(f"[q43 case] {cfg.name} B={cfg.B} T={n_rows} rk={list(rk)} rv={list(rv)}")
+    return dict(cfg=cfg, desc=desc, pk=pk, pv=pv, lk=lk, lv=lv, PK=PK, PV=PV, stats=host.kv_stats(cfg, 0))
+
+
+def _q43_reference(case, q, b, h, T):
+    cfg = case["cfg"]
+    G = cfg.G
+    K = host.decode_to_f64(host.kv_rows(cfg, 0, "k", b, 0, T, heads=[h], stats=case["stats"]), cfg.in_dtype)[:, 0]
+    V = host.decode_to_f64(host.kv_rows(cfg, 0, "v", b, 0, T, heads=[h], stats=case["stats"]), cfg.in_dtype)[:, 0]
+    return qo.decode_head_quantized(q[b, h * G:(h + 1) * G].astype(np.float64), K, V, bases32([case["PK"][h]])[0],
+                                    bases32([case["PV"][h]])[0], 1 / np.sqrt(cfg.d))
+
+
+def _q43_decode(case, q, lens, split=0):
+    import torch
+    kv = _kv()
+    out = kv.decode_attn(case["desc"], torch.from_numpy(q).cuda(), case["pk"], case["pv"], case["lk"], case["lv"],
+                         torch.as_tensor(np.asarray(lens, np.int32)).cuda(), split_tokens=split)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+def _q43_check(case, got, q, lens, units=None, bound=2e-2, long_bound=2e-3, long_T=256):
+    """Rows against the oracle's decode over its own quantised latents.
+
+    The two sides quantise fp32 latents that differ in the last bit (MFMA with a
+    split basis vs a float64 product rounded once), so a code lying on a rounding
+    boundary can come out one step apart (about 6 in a million codes). For a short
+    sequence one such code moves the output by up to a step, so the bound is the
+    bf16-latent bound 2e-2; with long_T rows or more the weights spread over many
+    tokens and the outputs must agree to long_bound."""
+    from tests.gpu_cases import rel_l2_rows
+    cfg = case["cfg"]
+    G = cfg.G
+    worst = worst_long = 0.0
+    units = [(b, h) for b in range(cfg.B) for h in range(cfg.Hkv)] if units is None else units
+    for b, h in units:
+        T = int(lens[b])
+        g = got[b, h * G:(h + 1) * G]
+        if T == 0:
+            assert np.all(g == 0)
+            continue
+        err = float(rel_l2_rows(g, _q43_reference(case, q, b, h, T)).max())
+        worst = max(worst, err)
+        if T >= long_T:
+            worst_long = max(worst_long, err)
+    say(f"[q43 check] worst rel L2 {worst:.3e} (rows >= {long_T}: {worst_long:.3e})")
+    assert worst <= bound, worst
+    assert worst_long <= long_bound, worst_long
+    return worst
+
+
+@pytest.mark.parametrize("cid,extra", [
+    (1, dict(B=2, T=1000)),
+    (2, dict(B=3, T_range=(1, 700))),
+    (1, dict(B=2, Hq=10, Hkv=2, T=333, r_k=128, r_v=16)),
+    (1, dict(B=2, Hq=8, Hkv=2, T=300, r_k=16, r_v=128)),
+    (1, dict(B=2, Hq=6, Hkv=2, T=257, r_k=112, r_v=48)),
+])
+def test_q43_decode_matches_oracle(gpu, cid, extra):
+    cfg = CONFIGS[cid].scaled(**extra)
+    case = _q43_case(cfg)
+    lens = host.lengths(cfg)
+    q = host.queries(cfg, 0, 0)
+    _q43_check(case, _q43_decode(case, q, lens), q, lens)
+
+
+@pytest.mark.parametrize("lens,split", [([0, 5], 64), ([1, 300], 64), ([257, 256], 0), ([300, 129], 128)])
+def test_q43_decode_edge_lengths(gpu, lens, split):
+    cfg = CONFIGS[1].scaled(B=2, Hq=8, Hkv=2, T=300)
+    case = _q43_case(cfg)
+    q = host.queries(cfg, 0, 0)
+    lens = np.array(lens, np.int32)
+    got = _q43_decode(case, q, lens, split)
+    assert np.isfinite(got).all()
+    _q43_check(case, got, q, lens)
+
+
+def test_q43_decode_exact_storage(gpu):
+    """Integer rows and +-1/16 bases: the GPU stores exactly the oracle's codes, so decode
+    differs from the oracle only by the kernel's fp32 arithmetic."""
+    import torch
+    kv = _kv()
+    from oracle import kvlr_oracle as ko
+    rng = np.random.default_rng(43)
+    B, Hq, Hkv, d, T = 2, 8, 2, 128, 200
+    rk, rv = [64, 128], [80, 48]
+    PKf = [rng.choice([-1 / 16, 1 / 16], size=(d, r)) for r in rk]
+    PVf = [rng.choice([-1 / 16, 1 / 16], size=(d, r)) for r in rv]
+    K = rng.integers(-8, 9, size=(B, T, Hkv, d)).astype(np.float32)
+    V = rng.integers(-8, 9, size=(B, T, Hkv, d)).astype(np.float32)
+    q = rng.standard_normal((B, Hq, d)).astype(np.float32)
+    desc = kv.Desc(B, Hq, Hkv, d, T, rk, rv, kv.F32, kv.Q43)
+    pk, pv = kv.pack_bases(PKf), kv.pack_bases(PVf)
+    lk, lv = kv.alloc_cache(desc)
+    kv.prefill_compress(desc, torch.from_numpy(K).cuda(), torch.from_numpy(V).cuda(), 0, pk, pv, lk, lv)
+    lens = np.array([T, 137], np.int32)
+    out = kv.decode_attn(desc, torch.from_numpy(q).cuda(), pk, pv, lk, lv, torch.from_numpy(lens).cuda())
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    G = Hq // Hkv
+    worst = 0.0
+    for b in range(B):
+        for h in range(Hkv):
+            n = int(lens[b])
+            Kl = qo.dequantize_rows(*qo.quantize_rows((K[b, :n, h].astype(np.float64) @ PKf[h]).astype(np.float32)))
+            Vl = qo.dequantize_rows(*qo.quantize_rows((V[b, :n, h].astype(np.float64) @ PVf[h]).astype(np.float32)))
+            ref = ko.decode_head_latent(q[b, h * G:(h + 1) * G].astype(np.float64), Kl, Vl, PKf[h], PVf[h],
+                                        1 / np.sqrt(d))
+            err = np.abs(got[b, h * G:(h + 1) * G] - ref).max() / np.abs(ref).max()
+            worst = max(worst, float(err))
+    say(f"[q43 exact storage] worst {worst:.3e}")
+    assert worst <= 1e-4, worst
+
+
+def test_q43_folded_and_two_stage(gpu):
+    """The folded entry point and partials + combine run the same kernel on 4/3-bit caches."""
+    import torch
+    kv = _kv()
+    cfg = CONFIGS[1].scaled(B=2, Hq=16, Hkv=2, T=700)
+    case = _q43_case(cfg)
+    lens = host.lengths(cfg)
+    q = host.queries(cfg, 0, 0)
+    lt = torch.from_numpy(lens).cuda()
+    qd = torch.from_numpy(q).cuda()
+    full = kv.decode_attn(case["desc"], qd, case["pk"], case["pv"], case["lk"], case["lv"], lt)
+    ws = kv.alloc_workspace(case["desc"])
+    kv.decode_partials(case["desc"], qd, case["pk"], case["lk"], case["lv"], lt, ws)
+    two = torch.empty_like(full)
+    kv.decode_combine(case["desc"], case["pv"], ws, two)
+    # folded: q_lat = q P'_K (folded bases, fp32 on the device), o = o_lat P'_V^T
+    rk = int(case["desc"].r_k[0])
+    d = cfg.d
+    PKf = case["pk"].view(cfg.Hkv, d, rk)
+    q_lat = torch.stack([qd[:, i] @ PKf[i // cfg.G] for i in range(cfg.Hq)], 1).contiguous()
+    o_lat = kv.decode_attn_latent(case["desc"], q_lat, case["lk"], case["lv"], lt)
+    torch.cuda.synchronize()
+    rv = int(case["desc"].r_v[0])
+    PVf = case["pv"].view(cfg.Hkv, d, rv)
+    back = torch.stack([o_lat[:, i, :rv] @ PVf[i // cfg.G].T for i in range(cfg.Hq)], 1)
+    f, t2, bk = (x.cpu().numpy().astype(np.float64) for x in (full, two, back))
+    assert np.abs(f - t2).max() <= 1e-6 * np.abs(f).max()
+    assert np.abs(f - bk).max() <= 2e-4 * np.abs(f).max()
+    _q43_check(case, f, q, lens)
