@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle CPU time")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-compression measurement")
     ap.add_argument("--no-q43", action="store_true", help="skip the 4/3-bit latent measurement")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the other workloads (ragged per-head ranks, 128K steps, 32 layers)")
     ap.add_argument("--traffic-reference", action="store_true",
                     help="also run a plain 1 GiB device copy (a known-size reference for HBM traffic counters)")
     return ap.parse_args()
@@ -66,6 +68,124 @@ def load_traffic():
     if t.get("decode_src_sha256_16") != source_hash(DECODE_SRC):
         return None
     return t.get("bytes_per_launch")
+
+
+def _build(kv, torch, cfg, layer=0, n_rows=None, chunk=8192):
+    """Device caches of one layer of a workload (seeded synthetic rows, prefill-compressed)."""
+    from synth import host
+    from synth.device import KVGenerator
+    rk, rv = host.ranks(cfg, layer)
+    PK, PV = host.bases(cfg, layer)
+    desc = kv.Desc(cfg.B, cfg.Hq, cfg.Hkv, cfg.d, cfg.capacity, rk, rv, kv.BF16, kv.BF16)
+    pk, pv = kv.pack_bases(PK), kv.pack_bases(PV)
+    lk, lv = kv.alloc_cache(desc)
+    gen = KVGenerator(cfg, layer)
+    n_rows = cfg.capacity if n_rows is None else n_rows
+    for t0 in range(0, n_rows, chunk):
+        n = min(chunk, n_rows - t0)
+        kv.prefill_compress(desc, gen.make("k", cfg.B, n, t0=t0), gen.make("v", cfg.B, n, t0=t0), t0, pk, pv, lk, lv)
+    return dict(desc=desc, pk=pk, pv=pv, lk=lk, lv=lv, rk=rk, rv=rv, gen=gen)
+
+
+def _timed(torch, fn, reps):
+    fn()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        fn()
+        torch.cuda.synchronize()
+        times.append(time.perf_counter() - t0)
+    return min(times)
+
+
+def _graph_of(torch, fn):
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
+def measure_workloads(kv, torch, np):
+    """The other workloads, each with its own algorithmic bytes: one decode over ragged
+    sequences with per-head ranks; 64 x (append + decode) over 128K rows; a 32-layer decode
+    step. The last two also as one captured HIP graph replayed (launch gaps removed)."""
+    from synth import CONFIGS, host
+    out = {}
+    print("[bench] workload per_head_ranks_ragged", file=sys.stderr, flush=True)
+    cfg = CONFIGS[2]
+    c = _build(kv, torch, cfg, chunk=4096)
+    lens_np = host.lengths(cfg)
+    lens = torch.from_numpy(lens_np).cuda()
+    q = torch.from_numpy(host.queries(cfg)).cuda()
+    ws = kv.alloc_workspace(c["desc"])
+    o = torch.empty((cfg.B, cfg.Hq, cfg.d), device="cuda")
+    nbytes = int(lens_np.astype(np.int64).sum()) * int((c["rk"] + c["rv"]).sum()) * 2
+    call = lambda: kv.decode_attn(c["desc"], q, c["pk"], c["pv"], c["lk"], c["lv"], lens, out=o, workspace=ws)  # noqa: E731
+    t = _timed(torch, lambda: [call() for _ in range(20)], 3) / 20
+    out[cfg.name] = {"us_per_call": t * 1e6, "bytes": nbytes, "GBps": nbytes / t / 1e9,
+                     "hbm_frac": nbytes / t / 1e9 / HBM_PEAK_GBPS, "tokens_per_s": cfg.B / t}
+    del c, ws
+    torch.cuda.empty_cache()
+
+    print("[bench] workload long_context_128k", file=sys.stderr, flush=True)
+    cfg = CONFIGS[3]
+    T, S = cfg.T, cfg.decode_steps
+    c = _build(kv, torch, cfg, n_rows=T, chunk=16384)
+    ks = [c["gen"].make("k", cfg.B, 1, t0=T + s)[:, 0].contiguous() for s in range(S)]
+    vs = [c["gen"].make("v", cfg.B, 1, t0=T + s)[:, 0].contiguous() for s in range(S)]
+    qs = [torch.from_numpy(host.queries(cfg, 0, s)).cuda() for s in range(S)]
+    pos = [torch.full((cfg.B,), T + s, dtype=torch.int32, device="cuda") for s in range(S)]
+    lns = [torch.full((cfg.B,), T + s + 1, dtype=torch.int32, device="cuda") for s in range(S)]
+    ws = kv.alloc_workspace(c["desc"])
+    o = torch.empty((cfg.B, cfg.Hq, cfg.d), device="cuda")
+
+    def loop():
+        for s in range(S):
+            kv.append(c["desc"], ks[s], vs[s], pos[s], c["pk"], c["pv"], c["lk"], c["lv"])
+            kv.decode_attn(c["desc"], qs[s], c["pk"], c["pv"], c["lk"], c["lv"], lns[s], out=o, workspace=ws)
+    t_e = _timed(torch, loop, 3)
+    g = _graph_of(torch, loop)
+    t_g = _timed(torch, g.replay, 3)
+    rk, rv = int(c["rk"][0]), int(c["rv"][0])
+    nbytes = sum(T + s + 1 for s in range(S)) * cfg.B * cfg.Hkv * (rk + rv) * 2
+    out[cfg.name] = {"steps": S, "eager_us_per_step": t_e / S * 1e6, "graph_us_per_step": t_g / S * 1e6,
+                     "bytes": nbytes, "graph_GBps": nbytes / t_g / 1e9, "graph_hbm_frac": nbytes / t_g / 1e9 / HBM_PEAK_GBPS,
+                     "graph_tokens_per_s": cfg.B * S / t_g}
+    del c, ws, g
+    torch.cuda.empty_cache()
+
+    print("[bench] workload llama3_8b_32_layers", file=sys.stderr, flush=True)
+    cfg = CONFIGS[4]
+    layers = []
+    for layer in range(cfg.n_layers):
+        c = _build(kv, torch, cfg, layer=layer)
+        c["q"] = torch.from_numpy(host.queries(cfg, layer)).cuda()
+        c["ws"] = kv.alloc_workspace(c["desc"])
+        c["o"] = torch.empty((cfg.B, cfg.Hq, cfg.d), device="cuda")
+        del c["gen"]
+        layers.append(c)
+    lens = torch.from_numpy(host.lengths(cfg)).cuda()
+
+    def step():
+        for c in layers:
+            kv.decode_attn(c["desc"], c["q"], c["pk"], c["pv"], c["lk"], c["lv"], lens, out=c["o"], workspace=c["ws"])
+    t_e = _timed(torch, step, 5)
+    g = _graph_of(torch, step)
+    t_g = _timed(torch, g.replay, 5)
+    nbytes = sum(cfg.B * cfg.T * int((c["rk"] + c["rv"]).sum()) * 2 for c in layers)
+    out[cfg.name] = {"layers": cfg.n_layers, "eager_ms_per_step": t_e * 1e3, "graph_ms_per_step": t_g * 1e3,
+                     "bytes": nbytes, "graph_GBps": nbytes / t_g / 1e9, "graph_hbm_frac": nbytes / t_g / 1e9 / HBM_PEAK_GBPS,
+                     "graph_tokens_per_s": cfg.B / t_g}
+    del layers, g
+    torch.cuda.empty_cache()
+    return out
 
 
 def measure_q43(kv, torch, np, cfg, gen, q, lens, steps, warmup):
@@ -256,6 +376,9 @@ def main():
     torch.cuda.synchronize()
     folded_us = float(np.mean([e[0].elapsed_time(e[1]) * 1e3 for e in fevs]))
 
+    workloads = None
+    if not args.no_workloads:
+        workloads = measure_workloads(kv, torch, np)
     q43 = None
     if not args.no_q43:
         q43 = measure_q43(kv, torch, np, cfg, gen, q, lens, args.steps, args.warmup)
@@ -305,6 +428,8 @@ def main():
                         "GBps": alg_bytes / (folded_us * 1e-6) / 1e9}
     if q43 is not None:
         result["q43"] = q43
+    if workloads is not None:
+        result["workloads"] = workloads
     if prefill is not None:
         result["prefill"] = prefill
     if not args.no_cpu_baseline:
