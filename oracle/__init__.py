@@ -27,6 +27,11 @@ What it computes (all in float64, plain numpy, no blocking or fusion):
   and decode over the dequantised latents (STAR-KV technical summary,
   "Metodologia" section 3), pinned in tests/test_quant_oracle.py.
 
+* joint values with per-head keys (``oracle/joint.py``): the values of all
+  heads of a token share one latent V_all P_J, and head h reconstructs with
+  its own rows of P_J (STAR-KV technical summary, "Metodologia" section 2),
+  pinned in tests/test_joint_oracle.py.
+
 Pins (tests/test_oracle_pins.py): orthonormality of the bases, the textbook
 softmax attention at full rank, invariance under P -> P O, definition mode
 equals latent mode, a 50-digit mpmath brute force on tiny shapes, closed
@@ -52,4 +57,4 @@ from .kvlr_oracle import (  # noqa: F401
     decode_head_latent,
     kv_head_of,
 )
-from . import quant  # noqa: F401
+from . import joint, quant  # noqa: F401

@@ -56,3 +56,38 @@ def decode_brute(q, K, V, P_K, P_V, lens, scale):
             row.append(attend_brute(q[b][i], Kb, Vb, P_K[h], P_V[h], scale))
         out.append(row)
     return out
+
+
+def decode_joint_brute(q, K, V, P_K, P_J, lens, scale):
+    """Joint values (STAR-KV technical summary, "Metodologia" section 2): the values of
+    all heads of a token concatenated, V_lat = V_all P_J, head h reconstructed with rows
+    h d .. (h+1) d - 1 of P_J. Keys per head as in decode_brute. Nested lists in, mpmath out."""
+    B, Hq = len(q), len(q[0])
+    Hkv = len(P_K)
+    G = Hq // Hkv
+    d = len(P_K[0])
+    r = len(P_J[0])
+    out = []
+    for b in range(B):
+        T = int(lens[b])
+        vlat = [[mpmath.fsum(_mp(V[b][t][hh][c]) * _mp(P_J[hh * d + c][j]) for hh in range(Hkv) for c in range(d))
+                 for j in range(r)] for t in range(T)]
+        row = []
+        for i in range(Hq):
+            h = i // G
+            if T == 0:
+                row.append([mpmath.mpf(0)] * d)
+                continue
+            rk = len(P_K[h][0])
+            Kt = []
+            for t in range(T):
+                kl = [mpmath.fsum(_mp(K[b][t][h][c]) * _mp(P_K[h][c][j]) for c in range(d)) for j in range(rk)]
+                Kt.append([mpmath.fsum(kl[j] * _mp(P_K[h][c][j]) for j in range(rk)) for c in range(d)])
+            Vt = [[mpmath.fsum(vlat[t][j] * _mp(P_J[h * d + c][j]) for j in range(r)) for c in range(d)]
+                  for t in range(T)]
+            s = [mpmath.fsum(Kt[t][c] * _mp(q[b][i][c]) for c in range(d)) * _mp(scale) for t in range(T)]
+            w = [mpmath.exp(x) for x in s]
+            Z = mpmath.fsum(w)
+            row.append([mpmath.fsum(w[t] * Vt[t][c] for t in range(T)) / Z for c in range(d)])
+        out.append(row)
+    return out
