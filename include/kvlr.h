@@ -66,6 +66,17 @@ typedef enum kvlr_dtype {
                     block per token (layout below) */
 } kvlr_dtype;
 
+/* How values are decomposed (STAR-KV technical summary, "Metodologia" section 2:
+ * joint decomposition factorises the concatenated heads, per-head decomposition
+ * each head on its own; STAR-KV keeps keys per head and decomposes values
+ * jointly). Keys are always per head. */
+typedef enum kvlr_value_mode {
+  KVLR_VALUES_PER_HEAD = 0, /* V_lat[h] = V_h P_V[h] */
+  KVLR_VALUES_JOINT = 1     /* one latent per token shared by every head:
+                               V_lat = [V_0 ... V_{Hkv-1}] P_J, P_J of shape [Hkv d][r];
+                               head h reconstructs with rows h d .. (h+1) d - 1 of P_J */
+} kvlr_value_mode;
+
 /* Shape of one layer's cache.
  *   batch       B   >= 1
  *   n_q_heads   Hq  >= 1, a multiple of n_kv_heads, with G = Hq / Hkv <= 16
@@ -77,6 +88,11 @@ typedef enum kvlr_dtype {
  *               for bf16 latents and of 4 for fp32 latents
  *   in_dtype    dtype of the full-width K/V rows given to compression and append
  *   latent_dtype dtype of the latent cache
+ *   value_mode  KVLR_VALUES_PER_HEAD or KVLR_VALUES_JOINT. Joint values: every
+ *               r_v[h] holds the joint rank r (1 <= r <= min(Hkv d, 128), same
+ *               granule), the value bases argument is P_J row-major [Hkv d][r]
+ *               (which is the per-head packing of its d-row slices), and the
+ *               value cache holds one block per batch row (below)
  *
  * Latent cache layout (lat_k; lat_v likewise with r_v): with
  * R = sum_h r_k[h], R_pre(h) = sum_{h' < h} r_k[h'] and
@@ -90,6 +106,8 @@ typedef enum kvlr_dtype {
  *    for j < 32 np: (j / 32) * 512 + ((j % 32) / 8) * 128 + n * 8 + j % 8;
  *    for the 16-channel tail jj = j - 32 np: np * 512 + (jj / 4) * 64 + n * 4 + jj % 4.
  * Blocks are contiguous, so a split of a sequence streams one byte range.
+ * Joint values: the value cache holds one block of C16 rows of r elements per
+ * batch row, at element C16 * b * r, read by every head of that batch row.
  *
  * Mixed-precision latents (latent_dtype KVLR_Q43; STAR-KV technical summary,
  * "Metodologia" section 3): the leading n_o(r) = 16 * max(1, (r + 40) / 80)
@@ -126,6 +144,7 @@ typedef struct kvlr_desc {
   const int32_t* r_v;
   int32_t in_dtype;
   int32_t latent_dtype;
+  int32_t value_mode;
 } kvlr_desc;
 
 /* Library version as 10000 * major + 100 * minor + patch. */

@@ -29,7 +29,7 @@ from typing import Optional, Sequence
 import numpy as np
 
 __all__ = [
-    "KvlrError", "Desc", "F32", "BF16", "Q43", "lib", "version", "status_string",
+    "KvlrError", "Desc", "F32", "BF16", "Q43", "VALUES_PER_HEAD", "VALUES_JOINT", "lib", "version", "status_string",
     "cache_elems", "decode_workspace_bytes", "decode_plan", "decode_counter_bytes",
     "prefill_compress", "append", "decode_attn", "decode_partials", "decode_combine", "decode_attn_latent",
     "hadamard_bases", "q43_outlier", "q43_row_bytes",
@@ -37,6 +37,7 @@ __all__ = [
 ]
 
 F32, BF16, Q43 = 0, 1, 2
+VALUES_PER_HEAD, VALUES_JOINT = 0, 1
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvlr.so")
 
@@ -54,7 +55,7 @@ class _CDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("capacity", ctypes.c_int32),
                 ("r_k", ctypes.POINTER(ctypes.c_int32)), ("r_v", ctypes.POINTER(ctypes.c_int32)),
-                ("in_dtype", ctypes.c_int32), ("latent_dtype", ctypes.c_int32)]
+                ("in_dtype", ctypes.c_int32), ("latent_dtype", ctypes.c_int32), ("value_mode", ctypes.c_int32)]
 
 
 lib = ctypes.CDLL(LIB_PATH)
@@ -107,15 +108,15 @@ class Desc:
     """One layer's cache shape (mirrors ``kvlr_desc``); keeps the rank arrays alive."""
 
     def __init__(self, batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, capacity: int,
-                 r_k, r_v, in_dtype: int = BF16, latent_dtype: int = BF16):
+                 r_k, r_v, in_dtype: int = BF16, latent_dtype: int = BF16, value_mode: int = VALUES_PER_HEAD):
         rk = np.broadcast_to(np.asarray(r_k, dtype=np.int32), (n_kv_heads,)).copy()
         rv = np.broadcast_to(np.asarray(r_v, dtype=np.int32), (n_kv_heads,)).copy()
         self.r_k, self.r_v = rk, rv
         self.batch, self.n_q_heads, self.n_kv_heads = batch, n_q_heads, n_kv_heads
         self.head_dim, self.capacity = head_dim, capacity
-        self.in_dtype, self.latent_dtype = in_dtype, latent_dtype
+        self.in_dtype, self.latent_dtype, self.value_mode = in_dtype, latent_dtype, value_mode
         self._c = _CDesc(batch, n_q_heads, n_kv_heads, head_dim, capacity,
-                         rk.ctypes.data_as(_I32P), rv.ctypes.data_as(_I32P), in_dtype, latent_dtype)
+                         rk.ctypes.data_as(_I32P), rv.ctypes.data_as(_I32P), in_dtype, latent_dtype, value_mode)
 
     @property
     def ptr(self):
@@ -235,6 +236,8 @@ def block_view(lat, desc: Desc, which: str, b: int, h: int):
     ranks = desc.r_k if which == "k" else desc.r_v
     sizes = [_row_storage(desc, int(x)) for x in ranks]
     rows = cap_rows(desc)
+    if which == "v" and desc.value_mode == VALUES_JOINT:   # one block per batch row, shared by the heads
+        return lat[rows * b * sizes[0]:rows * (b + 1) * sizes[0]]
     start = rows * (b * sum(sizes) + sum(sizes[:h]))
     return lat[start:start + rows * sizes[h]]
 

@@ -46,24 +46,29 @@ int check_desc(const kvlr_desc* d, HeadTable* ht, int* Rk, int* Rv, int* rank_bo
       d->n_q_heads % d->n_kv_heads != 0 || d->n_q_heads / d->n_kv_heads > 16 || d->capacity < 1 ||
       d->head_dim < 32 || d->head_dim > 256 || d->head_dim % 32 != 0 || d->capacity > (1 << 30))
     return KVLR_ERR_SHAPE;
+  if (d->value_mode != KVLR_VALUES_PER_HEAD && d->value_mode != KVLR_VALUES_JOINT) return KVLR_ERR_ARG;
+  const bool joint = d->value_mode == KVLR_VALUES_JOINT;
   const int granule = d->latent_dtype == KVLR_F32 ? 4 : 16;
   const int rmax = d->head_dim < kvlr::kMaxRank ? d->head_dim : kvlr::kMaxRank;
+  const long long jmax_ll = (long long)d->n_kv_heads * d->head_dim;
+  const int rvmax = joint ? (int)(jmax_ll < kvlr::kMaxRank ? jmax_ll : kvlr::kMaxRank) : rmax;
   int sk = 0, sv = 0, bound = 0, stk = 0, stv = 0;
   for (int h = 0; h < d->n_kv_heads; ++h) {
     const int rk = d->r_k[h], rv = d->r_v[h];
-    if (rk < 1 || rv < 1 || rk > rmax || rv > rmax || rk % granule || rv % granule) return KVLR_ERR_RANK;
+    if (rk < 1 || rv < 1 || rk > rmax || rv > rvmax || rk % granule || rv % granule) return KVLR_ERR_RANK;
+    if (joint && rv != d->r_v[0]) return KVLR_ERR_RANK;   // one joint rank
     if (ht) {
       ht->rk[h] = rk;
       ht->rv[h] = rv;
       ht->rk_pre[h] = sk;
       ht->rv_pre[h] = sv;
       ht->sk_pre[h] = stk;
-      ht->sv_pre[h] = stv;
+      ht->sv_pre[h] = joint ? 0 : stv;   // joint values: every head reads the batch row's block
     }
     sk += rk;
     sv += rv;
     stk += row_storage(d->latent_dtype, rk);
-    stv += row_storage(d->latent_dtype, rv);
+    if (!joint || h == 0) stv += row_storage(d->latent_dtype, rv);
     bound = rk > bound ? rk : bound;
     bound = rv > bound ? rv : bound;
   }
@@ -233,6 +238,8 @@ KVLR_API int kvlr_prefill_compress(const kvlr_desc* desc, const void* K, const v
   p.in_bf16 = desc->in_dtype == KVLR_BF16;
   p.out_bf16 = desc->latent_dtype == KVLR_BF16;
   p.out_q43 = desc->latent_dtype == KVLR_Q43;
+  p.joint_v = desc->value_mode == KVLR_VALUES_JOINT;
+  p.only_kind = -1;
   return hip_status(kvlr::launch_compress(p, static_cast<hipStream_t>(stream)));
 }
 
@@ -257,6 +264,7 @@ KVLR_API int kvlr_append(const kvlr_desc* desc, const void* k_new, const void* v
   p.in_bf16 = desc->in_dtype == KVLR_BF16;
   p.out_bf16 = desc->latent_dtype == KVLR_BF16;
   p.out_q43 = desc->latent_dtype == KVLR_Q43;
+  p.joint_v = desc->value_mode == KVLR_VALUES_JOINT;
   return hip_status(kvlr::launch_append(p, static_cast<hipStream_t>(stream)));
 }
 

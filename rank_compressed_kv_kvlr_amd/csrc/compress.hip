@@ -136,13 +136,12 @@ constexpr int kStageBytes = 4 * kMaxRank * 256;   // r <= 128, d <= 256
 template <bool kOutBf16, int NKB>
 __global__ __launch_bounds__(256) void compress_bf16_mfma(CompressParams p) {
   extern __shared__ __attribute__((aligned(16))) uint4 stage[];   // [mt][kb][lane] hi, then lo
-  const int kind = blockIdx.y & 1;             // 0 keys, 1 values
-  const int h = blockIdx.y >> 1;
+  const int kind = p.only_kind >= 0 ? p.only_kind : (int)(blockIdx.y & 1);   // 0 keys, 1 values
+  const int h = p.only_kind >= 0 ? (int)blockIdx.y : (int)(blockIdx.y >> 1);
   const int b = blockIdx.z;
   const int d = p.d;
   const int r = kind ? p.ht.rv[h] : p.ht.rk[h];
   const int r_pre = kind ? p.ht.rv_pre[h] : p.ht.rk_pre[h];
-  const int R = kind ? p.Rv : p.Rk;
   const float* P = (kind ? p.pv : p.pk) + (size_t)d * r_pre;
   const uint16_t* X = static_cast<const uint16_t*>(kind ? p.x_v : p.x_k);
   const int n_mt = r >> 4, dq = d >> 2;
@@ -178,7 +177,8 @@ __global__ __launch_bounds__(256) void compress_bf16_mfma(CompressParams p) {
 
   const size_t row_stride = (size_t)p.Hkv * d;   // elements between consecutive tokens
   const uint16_t* Xb = X + (size_t)b * p.n_tok * row_stride + (size_t)h * d;
-  const size_t lat_base = (size_t)cap_rows_of(p.cap) * ((size_t)b * R + r_pre);
+  const size_t lat_base = (size_t)cap_rows_of(p.cap) * ((size_t)b * (kind ? p.Sv : p.Sk) +
+                                                      (kind ? p.ht.sv_pre[h] : p.ht.sk_pre[h]));
   const bool k_tiled = kOutBf16 && kind == 0;   // bf16 key latents: MFMA operand order
   const int tok_wg0 = blockIdx.x * kTokensPerWg;
 
@@ -234,120 +234,149 @@ __global__ __launch_bounds__(256) void compress_bf16_mfma(CompressParams p) {
   }
 }
 
-// Plain VALU compression for fp32 inputs (any latent dtype): one workgroup
-// per (64-token tile, KV head x {K, V}, batch row); the tile is staged in LDS
-// as fp32 and each thread forms latent channels as fp32 dot products.
+// Plain VALU compression (fp32 inputs, 4/3-bit latents, joint values): one
+// workgroup per (64-token tile, KV head x {K, V}, batch row); the tile is staged
+// in LDS as fp32 and each thread forms latent channels as fp32 dot products,
+// kept in registers (at most 64 * 128 / 256 = 32 per thread). Joint values
+// (STAR-KV technical summary, "Metodologia" section 2) sum the contributions of
+// every KV head's rows, V_all P_J = sum_h V_h P_J[h d .. (h+1) d), staging one
+// head's tile at a time.
 constexpr int kValuTile = 64;
+constexpr int kValuOuts = kValuTile * kMaxRank / 256;
 
 __global__ __launch_bounds__(256) void compress_valu(CompressParams p) {
   extern __shared__ __attribute__((aligned(16))) float xs[];   // [64][d], then (4/3-bit rows) latents [64][r]
-  const int kind = blockIdx.y & 1;
-  const int h = blockIdx.y >> 1;
+  const int kind = p.only_kind >= 0 ? p.only_kind : (int)(blockIdx.y & 1);
+  const int h = p.only_kind >= 0 ? (int)blockIdx.y : (int)(blockIdx.y >> 1);
+  const bool joint = kind == 1 && p.joint_v;
   const int b = blockIdx.z;
   const int d = p.d;
   const int r = kind ? p.ht.rv[h] : p.ht.rk[h];
-  const int r_pre = kind ? p.ht.rv_pre[h] : p.ht.rk_pre[h];
-  const int R = kind ? p.Rv : p.Rk;
-  const float* P = (kind ? p.pv : p.pk) + (size_t)d * r_pre;
   const void* X = kind ? p.x_v : p.x_k;
   const int t0 = blockIdx.x * kValuTile;
   const int nt = min(kValuTile, p.n_tok - t0);
   const size_t row_stride = (size_t)p.Hkv * d;
-  for (int idx = threadIdx.x; idx < nt * d; idx += blockDim.x) {
-    const int t = idx / d, i = idx - t * d;
-    const size_t src = ((size_t)b * p.n_tok + t0 + t) * row_stride + (size_t)h * d + i;
-    xs[idx] = p.in_bf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(X)[src]) : static_cast<const float*>(X)[src];
-  }
-  __syncthreads();
-  if (p.out_q43) {   // latents of the tile into LDS, then one thread per row quantises and stores
-    float* lat = xs + kValuTile * d;
-    for (int idx = threadIdx.x; idx < nt * r; idx += blockDim.x) {
-      const int t = idx / r, j = idx - t * r;
-      const float* x = xs + t * d;
-      float acc = 0.f;
-      for (int i = 0; i < d; ++i) acc = fmaf(x[i], P[(size_t)i * r + j], acc);
-      lat[t * r + j] = acc;
+  float acc[kValuOuts];
+#pragma unroll
+  for (int k = 0; k < kValuOuts; ++k) acc[k] = 0.f;
+  const int heads = joint ? p.Hkv : 1;
+  for (int hs = 0; hs < heads; ++hs) {
+    const int hh = joint ? hs : h;          // KV head whose input rows are staged
+    if (hs > 0) __syncthreads();             // the previous head's tile is no longer read
+    for (int idx = threadIdx.x; idx < nt * d; idx += blockDim.x) {
+      const int t = idx / d, i = idx - t * d;
+      const size_t src = ((size_t)b * p.n_tok + t0 + t) * row_stride + (size_t)hh * d + i;
+      xs[idx] = p.in_bf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(X)[src]) : static_cast<const float*>(X)[src];
     }
     __syncthreads();
-    const int S = kind ? p.Sv : p.Sk;
-    const int s_pre = kind ? p.ht.sv_pre[h] : p.ht.sk_pre[h];
+    const float* P = (kind ? p.pv : p.pk) + (size_t)d * (kind ? p.ht.rv_pre[hh] : p.ht.rk_pre[hh]);
+#pragma unroll
+    for (int k = 0; k < kValuOuts; ++k) {
+      const int idx = threadIdx.x + k * blockDim.x;
+      if (idx < nt * r) {
+        const int t = idx / r, j = idx - t * r;
+        const float* x = xs + t * d;
+        float a = acc[k];
+        for (int i = 0; i < d; ++i) a = fmaf(x[i], P[(size_t)i * r + j], a);
+        acc[k] = a;
+      }
+    }
+  }
+  const int S = kind ? p.Sv : p.Sk;
+  const int s_pre = kind ? p.ht.sv_pre[h] : p.ht.sk_pre[h];
+  if (p.out_q43) {   // latents of the tile into LDS, then one thread per row quantises and stores
+    float* lat = xs + kValuTile * d;
+#pragma unroll
+    for (int k = 0; k < kValuOuts; ++k) {
+      const int idx = threadIdx.x + k * blockDim.x;
+      if (idx < nt * r) lat[idx] = acc[k];
+    }
+    __syncthreads();
     const int rb = q43_row_bytes(r);
     uint8_t* blk = static_cast<uint8_t*>(kind ? p.lat_v : p.lat_k) + (size_t)cap_rows_of(p.cap) * ((size_t)b * S + s_pre);
     for (int t = threadIdx.x; t < nt; t += blockDim.x)
       q43_store_row_any(lat + t * r, r, reinterpret_cast<uint32_t*>(blk + (size_t)(p.start + t0 + t) * rb));
     return;
   }
-  const size_t lat_base = (size_t)cap_rows_of(p.cap) * ((size_t)b * R + r_pre);
+  const size_t lat_base = (size_t)cap_rows_of(p.cap) * ((size_t)b * S + s_pre);
   const bool k_tiled = p.out_bf16 && kind == 0;
-  for (int idx = threadIdx.x; idx < nt * r; idx += blockDim.x) {
-    const int t = idx / r, j = idx - t * r;
-    const float* x = xs + t * d;
-    float acc = 0.f;
-    for (int i = 0; i < d; ++i) acc = fmaf(x[i], P[(size_t)i * r + j], acc);
-    const int row = p.start + t0 + t;
-    const size_t off = lat_base + (k_tiled ? k_tiled_offset(row, j, r) : (size_t)row * r + j);
-    if (p.out_bf16)
-      static_cast<uint16_t*>(kind ? p.lat_v : p.lat_k)[off] = f32_to_bf16_bits(acc);
-    else
-      static_cast<float*>(kind ? p.lat_v : p.lat_k)[off] = acc;
+#pragma unroll
+  for (int k = 0; k < kValuOuts; ++k) {
+    const int idx = threadIdx.x + k * blockDim.x;
+    if (idx < nt * r) {
+      const int t = idx / r, j = idx - t * r;
+      const int row = p.start + t0 + t;
+      const size_t off = lat_base + (k_tiled ? k_tiled_offset(row, j, r) : (size_t)row * r + j);
+      if (p.out_bf16)
+        static_cast<uint16_t*>(kind ? p.lat_v : p.lat_k)[off] = f32_to_bf16_bits(acc[k]);
+      else
+        static_cast<float*>(kind ? p.lat_v : p.lat_k)[off] = acc[k];
+    }
   }
 }
 
-// Append: one workgroup per (batch row, KV head, K or V).
+// Append: one workgroup per (batch row, KV head, K or V); thread j forms latent
+// channel j (r <= 128 = blockDim). Joint values: the h == 0 workgroup sums the
+// contributions of every head's new row; the others have nothing to write.
 __global__ __launch_bounds__(128) void append_kernel(AppendParams p) {
   __shared__ float xs[256];
   __shared__ float lat[kMaxRank];   // 4/3-bit rows: the fp32 latents before quantisation
   const int b = blockIdx.x, h = blockIdx.y, kind = blockIdx.z;
+  const bool joint = kind == 1 && p.joint_v;
+  if (joint && h != 0) return;
   const int d = p.d;
   const int pos = p.pos[b];
   if (pos < 0 || pos >= p.cap) return;   // rows outside the cache are not written
   const int r = kind ? p.ht.rv[h] : p.ht.rk[h];
-  const int r_pre = kind ? p.ht.rv_pre[h] : p.ht.rk_pre[h];
-  const int R = kind ? p.Rv : p.Rk;
-  const float* P = (kind ? p.pv : p.pk) + (size_t)d * r_pre;
   const void* X = kind ? p.v_new : p.k_new;
-  const size_t src0 = ((size_t)b * p.Hkv + h) * d;
-  for (int i = threadIdx.x; i < d; i += blockDim.x)
-    xs[i] = p.in_bf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(X)[src0 + i])
-                      : static_cast<const float*>(X)[src0 + i];
-  __syncthreads();
-  if (p.out_q43) {
-    for (int j = threadIdx.x; j < r; j += blockDim.x) {
-      float acc = 0.f;
+  const int j = threadIdx.x;
+  float acc = 0.f;
+  const int heads = joint ? p.Hkv : 1;
+  for (int hs = 0; hs < heads; ++hs) {
+    const int hh = joint ? hs : h;
+    if (hs > 0) __syncthreads();
+    const size_t src0 = ((size_t)b * p.Hkv + hh) * d;
+    for (int i = threadIdx.x; i < d; i += blockDim.x)
+      xs[i] = p.in_bf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(X)[src0 + i])
+                        : static_cast<const float*>(X)[src0 + i];
+    __syncthreads();
+    const float* P = (kind ? p.pv : p.pk) + (size_t)d * (kind ? p.ht.rv_pre[hh] : p.ht.rk_pre[hh]);
+    if (j < r)
       for (int i = 0; i < d; ++i) acc = fmaf(xs[i], P[(size_t)i * r + j], acc);
-      lat[j] = acc;
-    }
+  }
+  const int S = kind ? p.Sv : p.Sk;
+  const int s_pre = kind ? p.ht.sv_pre[h] : p.ht.sk_pre[h];
+  if (p.out_q43) {
+    if (j < r) lat[j] = acc;
     __syncthreads();
     if (threadIdx.x == 0) {
-      const int S = kind ? p.Sv : p.Sk;
-      const int s_pre = kind ? p.ht.sv_pre[h] : p.ht.sk_pre[h];
       uint8_t* blk = static_cast<uint8_t*>(kind ? p.lat_v : p.lat_k) + (size_t)cap_rows_of(p.cap) * ((size_t)b * S + s_pre);
       q43_store_row_any(lat, r, reinterpret_cast<uint32_t*>(blk + (size_t)pos * q43_row_bytes(r)));
     }
     return;
   }
-  const size_t base = (size_t)cap_rows_of(p.cap) * ((size_t)b * R + r_pre);
+  if (j >= r) return;
+  const size_t base = (size_t)cap_rows_of(p.cap) * ((size_t)b * S + s_pre);
   const bool k_tiled = p.out_bf16 && kind == 0;
-  for (int j = threadIdx.x; j < r; j += blockDim.x) {
-    float acc = 0.f;
-    for (int i = 0; i < d; ++i) acc = fmaf(xs[i], P[(size_t)i * r + j], acc);
-    const size_t off = base + (k_tiled ? k_tiled_offset(pos, j, r) : (size_t)pos * r + j);
-    if (p.out_bf16)
-      static_cast<uint16_t*>(kind ? p.lat_v : p.lat_k)[off] = f32_to_bf16_bits(acc);
-    else
-      static_cast<float*>(kind ? p.lat_v : p.lat_k)[off] = acc;
-  }
+  const size_t off = base + (k_tiled ? k_tiled_offset(pos, j, r) : (size_t)pos * r + j);
+  if (p.out_bf16)
+    static_cast<uint16_t*>(kind ? p.lat_v : p.lat_k)[off] = f32_to_bf16_bits(acc);
+  else
+    static_cast<float*>(kind ? p.lat_v : p.lat_k)[off] = acc;
 }
 
 }  // namespace
 
-hipError_t launch_compress(const CompressParams& p, hipStream_t stream) {
-  if (p.n_tok <= 0) return hipSuccess;
+hipError_t launch_compress(const CompressParams& p_in, hipStream_t stream) {
+  if (p_in.n_tok <= 0) return hipSuccess;
   int max_r = 0;
-  for (int h = 0; h < p.Hkv; ++h) max_r = max(max_r, max(p.ht.rk[h], p.ht.rv[h]));
+  for (int h = 0; h < p_in.Hkv; ++h) max_r = max(max_r, max(p_in.ht.rk[h], p_in.ht.rv[h]));
+  CompressParams p = p_in;
+  p.only_kind = p.joint_v ? 0 : -1;   // joint values get a launch of their own below
+  const int ykinds = p.joint_v ? 1 : 2;
   if (p.in_bf16 && !p.out_q43) {
     const size_t lds = (size_t)4 * max_r * p.d;   // hi + lo operand tiles
-    const dim3 grid((p.n_tok + kTokensPerWg - 1) / kTokensPerWg, 2 * p.Hkv, p.B);
+    const dim3 grid((p.n_tok + kTokensPerWg - 1) / kTokensPerWg, ykinds * p.Hkv, p.B);
 #define KVLR_COMPRESS_CASE(NKB)                                                              \
   case NKB:                                                                                  \
     if (p.out_bf16)                                                                          \
@@ -368,8 +397,15 @@ hipError_t launch_compress(const CompressParams& p, hipStream_t stream) {
 #undef KVLR_COMPRESS_CASE
   } else {
     const size_t lds = (size_t)kValuTile * (p.d + (p.out_q43 ? max_r : 0)) * sizeof(float);
-    const dim3 grid((p.n_tok + kValuTile - 1) / kValuTile, 2 * p.Hkv, p.B);
+    const dim3 grid((p.n_tok + kValuTile - 1) / kValuTile, ykinds * p.Hkv, p.B);
     hipLaunchKernelGGL(compress_valu, grid, dim3(256), lds, stream, p);
+  }
+  if (p.joint_v) {   // joint values: one workgroup per (tile, batch row) sums over every head
+    CompressParams pv = p_in;
+    pv.only_kind = 1;
+    const size_t lds = (size_t)kValuTile * (p.d + (p.out_q43 ? max_r : 0)) * sizeof(float);
+    const dim3 grid((p.n_tok + kValuTile - 1) / kValuTile, 1, p.B);
+    hipLaunchKernelGGL(compress_valu, grid, dim3(256), lds, stream, pv);
   }
   return hipGetLastError();
 }

@@ -422,8 +422,8 @@ __global__ __launch_bounds__(256) void decode_split_bf16(DecodeParams p) {
   const int n_it = (TT + rpi - 1) / rpi;  // <= NIT
 
   const size_t rows = cap_rows_of(p.cap);
-  const uint16_t* Kb = static_cast<const uint16_t*>(p.lat_k) + rows * ((size_t)b * p.Rk + p.ht.rk_pre[h]);
-  const uint16_t* Vb = static_cast<const uint16_t*>(p.lat_v) + rows * ((size_t)b * p.Rv + p.ht.rv_pre[h]);
+  const uint16_t* Kb = static_cast<const uint16_t*>(p.lat_k) + rows * ((size_t)b * p.Sk + p.ht.sk_pre[h]);
+  const uint16_t* Vb = static_cast<const uint16_t*>(p.lat_v) + rows * ((size_t)b * p.Sv + p.ht.sv_pre[h]);
 
   float* p_lds = smem + wave * (TT * 4);  // [TT tokens][4 heads] per wave
 
@@ -1052,8 +1052,8 @@ __global__ __launch_bounds__(256) void decode_split_f32(DecodeParams p) {
   project_query<RB>(p, b, h, hq0, gpw, rk, q_lds, red, qt_lds);
 
   const size_t rows = cap_rows_of(p.cap);
-  const float* Kb = static_cast<const float*>(p.lat_k) + rows * ((size_t)b * p.Rk + p.ht.rk_pre[h]);
-  const float* Vb = static_cast<const float*>(p.lat_v) + rows * ((size_t)b * p.Rv + p.ht.rv_pre[h]);
+  const float* Kb = static_cast<const float*>(p.lat_k) + rows * ((size_t)b * p.Sk + p.ht.sk_pre[h]);
+  const float* Vb = static_cast<const float*>(p.lat_v) + rows * ((size_t)b * p.Sv + p.ht.sv_pre[h]);
   // per-wave probability tile lives in the (not yet used) reduction area
   float* p_lds = red + wave * 64 * 4;
 

@@ -69,6 +69,8 @@ struct CompressParams {
   int Rk, Rv;
   int Sk, Sv;
   int in_bf16, out_bf16, out_q43;
+  int only_kind;         // -1: keys and values (grid.y = 2 Hkv); 0 or 1: that kind only (grid.y = Hkv)
+  int joint_v;           // values: one latent per token from all heads (grid.y = 1 for the value launch)
   HeadTable ht;
 };
 
@@ -84,6 +86,7 @@ struct AppendParams {
   int Rk, Rv;
   int Sk, Sv;
   int in_bf16, out_bf16, out_q43;
+  int joint_v;           // values: one latent per token from all heads, written by the h == 0 workgroup
   HeadTable ht;
 };
 

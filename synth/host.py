@@ -36,6 +36,7 @@ from .configs import Config
 # kinds of seeded streams
 KIND_PK, KIND_PV, KIND_KSTAT, KIND_VSTAT, KIND_K, KIND_V, KIND_Q = 0, 1, 2, 3, 4, 5, 6
 KIND_OUTLIER, KIND_RANKS, KIND_LENGTHS = 7, 8, 9
+KIND_PJ = 10
 
 GAMMA = 0x9E3779B97F4A7C15
 MIX1 = 0xBF58476D1CE4E5B9
@@ -158,6 +159,13 @@ def lengths(cfg: Config) -> np.ndarray:
     lo, hi = cfg.T_range
     g = rng(cfg, 0, 0, 0, KIND_LENGTHS)
     return g.integers(lo, hi, endpoint=True, size=cfg.B).astype(np.int32)
+
+
+def joint_value_basis(cfg: Config, r: int, layer: int = 0):
+    """Orthonormal joint value basis [Hkv d][r]: Q factor of QR of a seeded Gaussian."""
+    A = rng(cfg, layer, 0, 0, KIND_PJ).standard_normal((cfg.Hkv * cfg.d, int(r)))
+    Q, _ = np.linalg.qr(A)
+    return Q
 
 
 def bases(cfg: Config, layer: int = 0):

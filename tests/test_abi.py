@@ -173,3 +173,21 @@ def test_single_hip_runtime_whatever_the_import_order():
             "print(sorted({l.split()[-1] for l in open('/proc/self/maps') if 'amdhip64' in l}))" % ROOT)
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300).stdout
     assert out.count("amdhip64") == 1, out
+
+
+def test_joint_value_mode_validation():
+    # joint values: one rank for every head, up to min(Hkv d, 128); storage is one block per batch row
+    d = kv.Desc(2, 8, 4, 32, 100, 32, [96, 96, 96, 96], kv.BF16, kv.BF16, kv.VALUES_JOINT)
+    nk, nv = kv.cache_elems(d)
+    assert nk == 2 * 112 * 4 * 32 and nv == 2 * 112 * 96
+    bad = kv.Desc(2, 8, 4, 32, 100, 32, [96, 96, 64, 96], kv.BF16, kv.BF16, kv.VALUES_JOINT)
+    with pytest.raises(kv.KvlrError) as e:
+        kv.cache_elems(bad)
+    assert e.value.code == -3
+    per_head = kv.Desc(2, 8, 4, 32, 100, 32, [96] * 4, kv.BF16, kv.BF16)   # 96 > head_dim per head
+    with pytest.raises(kv.KvlrError):
+        kv.cache_elems(per_head)
+    odd = kv.Desc(2, 8, 4, 32, 100, 32, 32, kv.BF16, kv.BF16, 7)
+    with pytest.raises(kv.KvlrError) as e:
+        kv.cache_elems(odd)
+    assert e.value.code == -7

@@ -1,0 +1,171 @@
+"""GPU parity of joint value decomposition (per-head keys, one value latent per token
+shared by every head) against oracle/joint.py."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from oracle import joint as jo
+from oracle import kvlr_oracle as ko
+from oracle import quant as qo
+from synth import CONFIGS, host
+from synth.device import KVGenerator
+from tests.gpu_cases import bases32, rel_inf_rows, rel_l2_rows, say, tolerance
+
+pytestmark = pytest.mark.gpu
+
+
+def _kv():
+    import rank_compressed_kv_kvlr_amd as kv
+    return kv
+
+
+def _joint_case(cfg, rj, latent="bf16", n_rows=None, chunk=None):
+    import torch
+    kv = _kv()
+    rk, _ = host.ranks(cfg)
+    PK, _ = host.bases(cfg)
+    PJ = host.joint_value_basis(cfg, rj)
+    lat = {"bf16": kv.BF16, "f32": kv.F32, "q43": kv.Q43}[latent]
+    ind = kv.BF16 if cfg.in_dtype == "bf16" else kv.F32
+    desc = kv.Desc(cfg.B, cfg.Hq, cfg.Hkv, cfg.d, cfg.capacity, rk, [rj] * cfg.Hkv, ind, lat, kv.VALUES_JOINT)
+    pk = kv.pack_bases(PK)
+    pj = kv.pack_bases([PJ])             # row-major [Hkv d][r]: the per-head packing of its slices
+    if latent == "q43":
+        kv.hadamard_bases(desc, pk, pj)
+        PK = [qo.fuse_bases(P) for P in bases32(PK)]
+        PJ = qo.fuse_bases(bases32([PJ])[0])
+    else:
+        PK, PJ = bases32(PK), bases32([PJ])[0]
+    lk, lv = kv.alloc_cache(desc)
+    gen = KVGenerator(cfg, 0)
+    n_rows = cfg.capacity if n_rows is None else n_rows
+    chunk = chunk or n_rows
+    for t0 in range(0, n_rows, chunk):
+        n = min(chunk, n_rows - t0)
+        kv.prefill_compress(desc, gen.make("k", cfg.B, n, t0=t0), gen.make("v", cfg.B, n, t0=t0), t0, pk, pj, lk, lv)
+    torch.cuda.synchronize()
+    say(f"[joint case] {cfg.name} B={cfg.B} rows={n_rows} rk={list(rk)} r_joint={rj} latents={latent}")
+    return dict(cfg=cfg, desc=desc, pk=pk, pj=pj, lk=lk, lv=lv, PK=PK, PJ=PJ, latent=latent,
+                stats=host.kv_stats(cfg, 0), gen=gen)
+
+
+def _rows(case, kind, b, T):
+    """Host rows [T][Hkv][d] of batch row b, as the device holds its inputs."""
+    cfg = case["cfg"]
+    enc = host.kv_rows(cfg, 0, kind, b, 0, T, heads=list(range(cfg.Hkv)), stats=case["stats"])
+    return host.decode_to_f64(enc, cfg.in_dtype)
+
+
+def _reference(case, q, b, T):
+    """Oracle output [Hq][d] of batch row b over rows t < T."""
+    cfg = case["cfg"]
+    if T == 0:
+        return np.zeros((cfg.Hq, cfg.d))
+    K, V = _rows(case, "k", b, T), _rows(case, "v", b, T)
+    scale = 1 / np.sqrt(cfg.d)
+    if case["latent"] != "q43":
+        return jo.decode_joint(q[b:b + 1], K[None], V[None], case["PK"], case["PJ"], [T], scale)[0]
+    # 4/3-bit rows: the oracle quantises its own latents (bases already folded)
+    G = cfg.G
+    V_lat = qo.dequantize_rows(*qo.quantize_rows(jo.joint_latents(V.reshape(T, -1), case["PJ"]).astype(np.float32)))
+    out = np.zeros((cfg.Hq, cfg.d))
+    for h in range(cfg.Hkv):
+        K_lat = qo.dequantize_rows(*qo.quantize_rows((K[:, h] @ case["PK"][h]).astype(np.float32)))
+        out[h * G:(h + 1) * G] = jo.decode_joint_latent_head(q[b, h * G:(h + 1) * G], K_lat, V_lat, case["PK"][h],
+                                                             jo.joint_slice(case["PJ"], h, cfg.d), scale)
+    return out
+
+
+def _decode(case, q, lens, split=0):
+    import torch
+    kv = _kv()
+    out = kv.decode_attn(case["desc"], torch.from_numpy(q).cuda(), case["pk"], case["pj"], case["lk"], case["lv"],
+                         torch.as_tensor(np.asarray(lens, np.int32)).cuda(), split_tokens=split)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+def _check(case, got, q, lens, bound=None):
+    cfg = case["cfg"]
+    metric, tol = tolerance(cfg) if case["latent"] != "q43" else (rel_l2_rows, 2e-2)
+    bound = tol if bound is None else bound
+    worst = 0.0
+    for b in range(cfg.B):
+        ref = _reference(case, q, b, int(lens[b]))
+        if int(lens[b]) == 0:
+            assert np.all(got[b] == 0)
+            continue
+        worst = max(worst, float(metric(got[b], ref).max()))
+    say(f"[joint check] worst {worst:.3e} (bound {bound})")
+    assert worst <= bound, worst
+
+
+def test_joint_latents_match_oracle(gpu):
+    """Joint value latents from prefill compression and append: sum over heads of V_h P_J[h]."""
+    import torch
+    kv = _kv()
+    cfg = CONFIGS[1].scaled(B=2, Hq=8, Hkv=4, T=200)
+    case = _joint_case(cfg, 96, n_rows=199)
+    k_new = case["gen"].make("k", cfg.B, 1, t0=199)[:, 0].contiguous()
+    v_new = case["gen"].make("v", cfg.B, 1, t0=199)[:, 0].contiguous()
+    pos = torch.full((cfg.B,), 199, dtype=torch.int32, device="cuda")
+    kv.append(case["desc"], k_new, v_new, pos, case["pk"], case["pj"], case["lk"], case["lv"])
+    torch.cuda.synchronize()
+    for b in range(cfg.B):
+        V = _rows(case, "v", b, 200)
+        want = jo.joint_latents(V.reshape(200, -1), case["PJ"])
+        got = kv.latent_rows(case["lv"], case["desc"], "v", b, 0)[:200].float().cpu().numpy().astype(np.float64)
+        mag = np.abs(V.reshape(200, -1)) @ np.abs(case["PJ"])
+        ulp = np.ldexp(1.0, np.frexp(np.abs(want))[1] - 8)
+        assert np.all(np.abs(got - want) <= ulp + mag * 2.0 ** -14), b
+
+
+@pytest.mark.parametrize("cid,extra,rj", [
+    (1, dict(B=2, T=1000), 128),
+    (1, dict(B=3, Hq=12, Hkv=3, T=777), 48),
+    (2, dict(B=3, T_range=(1, 600)), 64),
+])
+def test_joint_decode_matches_oracle(gpu, cid, extra, rj):
+    cfg = CONFIGS[cid].scaled(**extra)
+    case = _joint_case(cfg, rj)
+    lens = host.lengths(cfg)
+    q = host.queries(cfg, 0, 0)
+    _check(case, _decode(case, q, lens), q, lens)
+
+
+def test_joint_decode_f32(gpu):
+    cfg = CONFIGS[0].scaled(B=2, Hq=4, Hkv=2, T=300)
+    case = _joint_case(cfg, 40, latent="f32")
+    lens = np.array([300, 133], np.int32)
+    q = host.queries(cfg, 0, 0)
+    _check(case, _decode(case, q, lens, split=64), q, lens)
+
+
+def test_joint_decode_q43(gpu):
+    cfg = CONFIGS[1].scaled(B=2, T=700)
+    case = _joint_case(cfg, 128, latent="q43")
+    lens = host.lengths(cfg)
+    q = host.queries(cfg, 0, 0)
+    _check(case, _decode(case, q, lens), q, lens, bound=2e-3)
+
+
+def test_joint_folded_latent_output(gpu):
+    """Weight absorption: o_lat = p V_lat per query head; o = o_lat P_J[h]^T."""
+    import torch
+    kv = _kv()
+    cfg = CONFIGS[1].scaled(B=2, Hq=16, Hkv=4, T=500)
+    case = _joint_case(cfg, 64)
+    lens = host.lengths(cfg)
+    q = host.queries(cfg, 0, 0)
+    full = _decode(case, q, lens)
+    rk = int(case["desc"].r_k[0])
+    q_lat = np.zeros((cfg.B, cfg.Hq, rk), np.float32)
+    for i in range(cfg.Hq):
+        q_lat[:, i] = (q[:, i].astype(np.float64) @ case["PK"][i // cfg.G]).astype(np.float32)
+    o_lat = kv.decode_attn_latent(case["desc"], torch.from_numpy(q_lat).cuda(), case["lk"], case["lv"],
+                                  torch.as_tensor(lens).cuda())
+    torch.cuda.synchronize()
+    o_lat = o_lat.cpu().numpy().astype(np.float64)
+    back = np.stack([o_lat[:, i] @ jo.joint_slice(case["PJ"], i // cfg.G, cfg.d).T for i in range(cfg.Hq)], 1)
+    assert float(rel_inf_rows(back, full).max()) <= 2e-4
