@@ -46,6 +46,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle CPU time")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-compression measurement")
     ap.add_argument("--no-q43", action="store_true", help="skip the 4/3-bit latent measurement")
+    ap.add_argument("--no-joint", action="store_true", help="skip the joint-value measurement")
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the other workloads (ragged per-head ranks, 128K steps, 32 layers)")
     ap.add_argument("--traffic-reference", action="store_true",
@@ -186,6 +187,46 @@ def measure_workloads(kv, torch, np):
     del layers, g
     torch.cuda.empty_cache()
     return out
+
+
+def measure_joint(kv, torch, np, cfg, gen, q, lens, steps, warmup, r_joint=128):
+    """The same workload with STAR-KV's hybrid decomposition: keys per head (r_k = 64),
+    values of all 8 heads in one joint latent of rank 128 per token (0.625x the bytes)."""
+    from synth import host
+    B, T, Hkv, d = cfg.B, cfg.T, cfg.Hkv, cfg.d
+    rk, _ = host.ranks(cfg)
+    PK, _ = host.bases(cfg)
+    desc = kv.Desc(B, cfg.Hq, Hkv, d, cfg.capacity, rk, [r_joint] * Hkv, kv.BF16, kv.BF16, kv.VALUES_JOINT)
+    pk, pj = kv.pack_bases(PK), kv.pack_bases([host.joint_value_basis(cfg, r_joint)])
+    print("[bench] building 2 replicas with joint values", file=sys.stderr, flush=True)
+    reps = []
+    for _ in range(2):
+        lk, lv = kv.alloc_cache(desc)
+        for t0 in range(0, T, 8192):
+            n = min(8192, T - t0)
+            kv.prefill_compress(desc, gen.make("k", B, n, t0=t0), gen.make("v", B, n, t0=t0), t0, pk, pj, lk, lv)
+        reps.append((lk, lv))
+    ws = kv.alloc_workspace(desc)
+    out = torch.empty((B, cfg.Hq, d), dtype=torch.float32, device="cuda")
+    for k in range(warmup):
+        lk, lv = reps[k % 2]
+        kv.decode_attn(desc, q, pk, pj, lk, lv, lens, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    t_start = time.perf_counter()
+    for k in range(steps):
+        lk, lv = reps[k % 2]
+        evs[k][0].record()
+        kv.decode_attn(desc, q, pk, pj, lk, lv, lens, out=out, workspace=ws)
+        evs[k][1].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    us = float(np.mean([e[0].elapsed_time(e[1]) * 1e3 for e in evs]))
+    nbytes = B * T * (int(rk.sum()) + r_joint) * 2
+    return {"entry": "kvlr_decode_attn, value_mode KVLR_VALUES_JOINT", "r_k": int(rk[0]), "r_joint": r_joint,
+            "bytes_per_launch": nbytes, "launch_us_mean": us, "GBps": nbytes / (us * 1e-6) / 1e9,
+            "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, "tokens_per_s": B * steps / elapsed,
+            "note": "the value latent is read once per KV head (from L2 / the last-level cache after the first)"}
 
 
 def measure_q43(kv, torch, np, cfg, gen, q, lens, steps, warmup):
@@ -379,6 +420,9 @@ def main():
     workloads = None
     if not args.no_workloads:
         workloads = measure_workloads(kv, torch, np)
+    joint = None
+    if not args.no_joint:
+        joint = measure_joint(kv, torch, np, cfg, gen, q, lens, args.steps, args.warmup)
     q43 = None
     if not args.no_q43:
         q43 = measure_q43(kv, torch, np, cfg, gen, q, lens, args.steps, args.warmup)
@@ -428,6 +472,8 @@ def main():
                         "GBps": alg_bytes / (folded_us * 1e-6) / 1e9}
     if q43 is not None:
         result["q43"] = q43
+    if joint is not None:
+        result["joint_values"] = joint
     if workloads is not None:
         result["workloads"] = workloads
     if prefill is not None:
