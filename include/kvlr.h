@@ -80,6 +80,7 @@ typedef enum kvlr_value_mode {
 /* Shape of one layer's cache.
  *   batch       B   >= 1
  *   n_q_heads   Hq  >= 1, a multiple of n_kv_heads, with G = Hq / Hkv <= 16
+ *               (joint values with bf16 latents: Hq <= 32 and Hkv <= 8)
  *   n_kv_heads  Hkv in [1, 64]; query head i reads KV head i / G
  *   head_dim    d   in [32, 256], a multiple of 32
  *   capacity    T_cap in [1, 2^30]: usable rows per (batch row, KV head)
@@ -108,6 +109,14 @@ typedef enum kvlr_value_mode {
  * Blocks are contiguous, so a split of a sequence streams one byte range.
  * Joint values: the value cache holds one block of C16 rows of r elements per
  * batch row, at element C16 * b * r, read by every head of that batch row.
+ * In bf16 its rows are in the operand order of the decode kernel's value
+ * product (tokens as the reduction dimension): with q = (t % 16) / 4,
+ * e = t % 4 and np = r / 32, 16-row group t / 16 starts at (t / 16) * 16 * r
+ * and holds, for j < 32 np:
+ *   (j / 32) * 512 + q * 128 + (j % 16) * 8 + ((j % 32) / 16) * 4 + e;
+ * for the 16-channel tail jj = j - 32 np: np * 512 + q * 64 + jj * 4 + e.
+ * (A 64-lane load then reads 1 KiB contiguously: lane 16 q + n gets tokens
+ * 4 q .. 4 q + 3 of channels n and n + 16 of a pair.)
  *
  * Mixed-precision latents (latent_dtype KVLR_Q43; STAR-KV technical summary,
  * "Metodologia" section 3): the leading n_o(r) = 16 * max(1, (r + 40) / 80)
@@ -163,7 +172,9 @@ KVLR_API int kvlr_cache_elems(const kvlr_desc* desc, size_t* k_elems, size_t* v_
  * descriptor and split length (split_tokens as in kvlr_decode_attn; 0 picks
  * the library's choice, the same one kvlr_decode_attn makes for 0).
  * Layout: int32 arrival counters (kvlr_decode_counter_bytes bytes), then one
- * fp32 record [B][Hq][n_splits][round_up(max_h r_v[h] + 2, 4)] per split. */
+ * fp32 record [B][Hq][n_splits][round_up(max_h r_v[h] + 2, 4)] per split,
+ * then (joint values with bf16 latents only) the projected queries, fp32
+ * [B][Hq][max_h r_k[h]]. */
 KVLR_API int kvlr_decode_workspace_bytes(const kvlr_desc* desc, int32_t split_tokens, size_t* bytes);
 
 /* Size of the counter region at the start of a decode workspace:
@@ -245,7 +256,13 @@ KVLR_API int kvlr_append(const kvlr_desc* desc, const void* k_new, const void* v
  *             all in one kernel launch)
  * Scores and the softmax are computed in fp32; bf16 latents are read as
  * stored and multiplied in fp32 (the key side on MFMA with the query split
- * into a high and a low bf16 part). */
+ * into a high and a low bf16 part).
+ * Joint values with bf16 latents take three launches instead: the query
+ * projection (q~ into the workspace), one workgroup per (split, batch row)
+ * that streams every head's keys and the shared value latent once (the value
+ * product on MFMA too, with the softmax weights split into a high and a low
+ * bf16 part), and a merge per (query head, batch row); the counter region is
+ * not used. */
 KVLR_API int kvlr_decode_attn(const kvlr_desc* desc, const float* q, const float* P_K, const float* P_V,
                               const void* lat_k, const void* lat_v, const int32_t* seq_lens, float scale,
                               float* out, void* workspace, size_t workspace_bytes, int32_t split_tokens,
@@ -263,7 +280,8 @@ KVLR_API int kvlr_decode_attn(const kvlr_desc* desc, const float* q, const float
  *             its first r_k[i / G] entries
  *   o_lat     device fp32 [B][Hq][rv_max], rv_max = max_h r_v[h]; entries
  *             j >= r_v[i / G] are written as zero; empty caches give zero rows
- * Other arguments as in kvlr_decode_attn (one launch; same workspace rules). */
+ * Other arguments as in kvlr_decode_attn (one launch, two for joint bf16
+ * values; same workspace rules). */
 KVLR_API int kvlr_decode_attn_latent(const kvlr_desc* desc, const float* q_lat, const void* lat_k,
                                      const void* lat_v, const int32_t* seq_lens, float scale, float* o_lat,
                                      void* workspace, size_t workspace_bytes, int32_t split_tokens,

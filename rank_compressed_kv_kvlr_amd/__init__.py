@@ -34,6 +34,7 @@ __all__ = [
     "prefill_compress", "append", "decode_attn", "decode_partials", "decode_combine", "decode_attn_latent",
     "hadamard_bases", "q43_outlier", "q43_row_bytes",
     "alloc_cache", "alloc_workspace", "pack_bases", "block_view", "latent_rows", "cap_rows", "k_tiled_index",
+    "v_joint_index",
 ]
 
 F32, BF16, Q43 = 0, 1, 2
@@ -255,14 +256,28 @@ def k_tiled_index(T: int, r: int):
     return np.where(j < 32 * np_, pair, tail)
 
 
+def v_joint_index(T: int, r: int):
+    """Element offsets [T][r] of bf16 joint value latents inside a batch row's block
+    (value-product operand order, see kvlr.h)."""
+    t = np.arange(T)[:, None]
+    j = np.arange(r)[None, :]
+    np_ = r // 32
+    base = (t >> 4) * 16 * r
+    q, e = (t & 15) >> 2, t & 3
+    pair = base + (j >> 5) * 512 + q * 128 + (j & 15) * 8 + ((j >> 4) & 1) * 4 + e
+    tail = base + np_ * 512 + q * 64 + (j - 32 * np_) * 4 + e
+    return np.where(j < 32 * np_, pair, tail)
+
+
 def latent_rows(lat, desc: Desc, which: str, b: int, h: int):
-    """Logical latent rows [capacity][r] of (b, h) (a gather for bf16 keys, a view otherwise;
-    [capacity][q43_row_bytes(r)] stored bytes for 4/3-bit rows)."""
+    """Logical latent rows [capacity][r] of (b, h) (a gather for bf16 keys and bf16 joint
+    values, a view otherwise; [capacity][q43_row_bytes(r)] stored bytes for 4/3-bit rows)."""
     torch = _torch()
     r = int((desc.r_k if which == "k" else desc.r_v)[h])
     blk = block_view(lat, desc, which, b, h)
-    if which == "k" and desc.latent_dtype == BF16:
-        idx = torch.from_numpy(k_tiled_index(desc.capacity, r).ravel()).to(blk.device)
+    if desc.latent_dtype == BF16 and (which == "k" or desc.value_mode == VALUES_JOINT):
+        index = k_tiled_index if which == "k" else v_joint_index
+        idx = torch.from_numpy(index(desc.capacity, r).ravel()).to(blk.device)
         return blk[idx].view(desc.capacity, r)
     w = _row_storage(desc, r)
     return blk[:desc.capacity * w].view(desc.capacity, w)

@@ -8,6 +8,7 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -18,9 +19,16 @@ SYNTH_LIB = os.path.join(ROOT, "synth", "libkvlr_synth.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 VALU forms are switched off for all device code.
-COMMON = ["--offload-arch=gfx950", "-O3", "-fPIC", "-shared", "-std=c++17",
+COMMON = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-SOURCES = ["api.hip", "decode.hip", "compress.hip"]
+# Sources of libkvlr.so with their extra flags. The joint-value decode keeps its
+# MFMA accumulators in ordinary VGPRs (its softmax rescales them between MFMAs).
+SOURCES = {
+    "api.hip": [],
+    "decode.hip": [],
+    "decode_joint.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "compress.hip": [],
+}
 
 
 def _run(cmd):
@@ -31,13 +39,33 @@ def _run(cmd):
     return err
 
 
+def _compile_all(objdir: str) -> tuple[list, str]:
+    """Compiles every source to an object (in parallel); returns the objects and the log."""
+    procs, objs = [], []
+    for src, extra in SOURCES.items():
+        obj = os.path.join(objdir, src.replace(".hip", ".o"))
+        cmd = [HIPCC, *COMMON, *extra, "-fvisibility=hidden", "-c", "-o", obj, os.path.join(CSRC, src)]
+        procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+        objs.append(obj)
+    log = ""
+    for cmd, pr in procs:
+        _, err = pr.communicate()
+        err = "\n".join(l for l in err.splitlines() if "not a recognized feature" not in l)
+        if pr.returncode != 0:
+            raise RuntimeError(f"build failed: {' '.join(cmd)}\n{err}")
+        log += err
+    return objs, log
+
+
 def build(verbose: bool = False) -> None:
     """Compile every HIP library of the repository (always recompiles)."""
-    tmp = LIB + ".tmp"
-    log = _run([HIPCC, *COMMON, "-fvisibility=hidden", "-o", tmp, *[os.path.join(CSRC, s) for s in SOURCES]])
+    with tempfile.TemporaryDirectory(prefix="kvlr_build_") as objdir:
+        objs, log = _compile_all(objdir)
+        tmp = LIB + ".tmp"
+        log += _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)
     tmp = SYNTH_LIB + ".tmp"
-    log += _run([HIPCC, *COMMON, "-ffp-contract=off", "-o", tmp, SYNTH_SRC])
+    log += _run([HIPCC, *COMMON, "-shared", "-ffp-contract=off", "-o", tmp, SYNTH_SRC])
     os.replace(tmp, SYNTH_LIB)
     if verbose and log.strip():
         print(log, file=sys.stderr)

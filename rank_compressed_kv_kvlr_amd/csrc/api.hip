@@ -25,7 +25,25 @@ int resident_wgs_per_cu(int latent_dtype, int rank_bound) {
   return 3;   // fp32 variants: limited by the 48 KiB of LDS the merge tail needs
 }
 
+// Split workgroups per CU of the joint-value kernel (one per (split, batch row)).
+constexpr int kJointResident = 2;
+
 bool valid_dtype(int t) { return t == KVLR_F32 || t == KVLR_BF16; }
+
+// Joint values in bf16 run the joint split kernel (its own value layout, a
+// separate query projection and merge); every other combination the per-head kernels.
+bool joint_bf16(const kvlr_desc* d) {
+  return d->value_mode == KVLR_VALUES_JOINT && d->latent_dtype == KVLR_BF16;
+}
+
+int rank_bound_of(int r) { return r <= 32 ? 32 : r <= 64 ? 64 : r <= 96 ? 96 : 128; }
+
+// Largest key rank and its kernel bound.
+int rk_max_of(const kvlr_desc* d) {
+  int m = 0;
+  for (int h = 0; h < d->n_kv_heads; ++h) m = d->r_k[h] > m ? d->r_k[h] : m;
+  return m;
+}
 
 // 4/3-bit caches are streamed with 16-byte loads: their base addresses must be 16-byte aligned.
 bool q43_aligned(int latent_dtype, const void* a, const void* b) {
@@ -48,6 +66,8 @@ int check_desc(const kvlr_desc* d, HeadTable* ht, int* Rk, int* Rv, int* rank_bo
     return KVLR_ERR_SHAPE;
   if (d->value_mode != KVLR_VALUES_PER_HEAD && d->value_mode != KVLR_VALUES_JOINT) return KVLR_ERR_ARG;
   const bool joint = d->value_mode == KVLR_VALUES_JOINT;
+  // the joint bf16 kernel holds at most two 16-query row tiles of four KV heads
+  if (joint && d->latent_dtype == KVLR_BF16 && (d->n_q_heads > 32 || d->n_kv_heads > 8)) return KVLR_ERR_SHAPE;
   const int granule = d->latent_dtype == KVLR_F32 ? 4 : 16;
   const int rmax = d->head_dim < kvlr::kMaxRank ? d->head_dim : kvlr::kMaxRank;
   const long long jmax_ll = (long long)d->n_kv_heads * d->head_dim;
@@ -79,7 +99,7 @@ int check_desc(const kvlr_desc* d, HeadTable* ht, int* Rk, int* Rv, int* rank_bo
   if (Rv) *Rv = sv;
   if (Sk) *Sk = stk;
   if (Sv) *Sv = stv;
-  if (rank_bound) *rank_bound = bound <= 32 ? 32 : bound <= 64 ? 64 : bound <= 96 ? 96 : 128;
+  if (rank_bound) *rank_bound = rank_bound_of(bound);
   return KVLR_OK;
 }
 
@@ -102,8 +122,10 @@ int plan_split(const kvlr_desc* d, int32_t split_tokens, int* n_splits, int* len
     const char* env = getenv("KVLR_SPLIT_TOKENS");   // tuning override
     long long want = env ? atoll(env) : 0;
     if (want <= 0 || want % kSplitGranule) {
-      const long long units = (long long)d->batch * d->n_kv_heads * groups;
-      const long long slots = (long long)kComputeUnits * resident_wgs_per_cu(d->latent_dtype, rank_bound);
+      const bool jd = joint_bf16(d);   // one workgroup per (split, batch row)
+      const long long units = jd ? (long long)d->batch : (long long)d->batch * d->n_kv_heads * groups;
+      const long long slots =
+          (long long)kComputeUnits * (jd ? kJointResident : resident_wgs_per_cu(d->latent_dtype, rank_bound));
       want = (units * d->capacity + slots - 1) / slots;
       const long long g4 = (long long)kSplitGranule * kvlr::kWaves;
       want = (want + g4 - 1) / g4 * g4;   // whole tiles for every wave
@@ -138,12 +160,17 @@ int decode_tile() {
 }
 
 // Workspace layout: arrival counters [B][Hkv][head groups] int32, padded to
-// 256 bytes, then the split records [B][Hq][n_splits][stride] fp32.
+// 256 bytes, then the split records [B][Hq][n_splits][stride] fp32, then (joint
+// bf16 values) the projected queries [B][Hq][max_h r_k[h]] fp32.
 size_t counter_bytes_of(const kvlr_desc* d) {
   const int G = d->n_q_heads / d->n_kv_heads;
   const size_t groups = (size_t)(G + kvlr::kHeadsPerWg - 1) / kvlr::kHeadsPerWg;
   const size_t n = (size_t)d->batch * d->n_kv_heads * groups * sizeof(int32_t);
   return (n + 255) / 256 * 256;
+}
+
+size_t qt_bytes_of(const kvlr_desc* d) {
+  return joint_bf16(d) ? (size_t)d->batch * d->n_q_heads * rk_max_of(d) * sizeof(float) : 0;
 }
 
 }  // namespace
@@ -199,7 +226,8 @@ KVLR_API int kvlr_decode_workspace_bytes(const kvlr_desc* desc, int32_t split_to
   rc = plan_split(desc, split_tokens, &ns, &len);
   if (rc) return rc;
   *bytes = counter_bytes_of(desc) +
-           (size_t)desc->batch * desc->n_q_heads * ns * ws_stride_of(ht, desc->n_kv_heads) * sizeof(float);
+           (size_t)desc->batch * desc->n_q_heads * ns * ws_stride_of(ht, desc->n_kv_heads) * sizeof(float) +
+           qt_bytes_of(desc);
   return KVLR_OK;
 }
 
@@ -305,7 +333,8 @@ int prepare_decode(const kvlr_desc* desc, const float* q, const float* P_K, cons
   if (rc) return rc;
   const int stride = ws_stride_of(p->ht, desc->n_kv_heads);
   const size_t cbytes = counter_bytes_of(desc);
-  const size_t need = cbytes + (size_t)desc->batch * desc->n_q_heads * ns * stride * sizeof(float);
+  const size_t rec_bytes = (size_t)desc->batch * desc->n_q_heads * ns * stride * sizeof(float);
+  const size_t need = cbytes + rec_bytes + qt_bytes_of(desc);
   if (!workspace || workspace_bytes < need) return KVLR_ERR_WORKSPACE;
 
   const int G = desc->n_q_heads / desc->n_kv_heads;
@@ -318,6 +347,7 @@ int prepare_decode(const kvlr_desc* desc, const float* q, const float* P_K, cons
   p->out_stride = desc->head_dim;
   p->counters = static_cast<int*>(workspace);
   p->ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + cbytes);
+  p->qt_out = joint_bf16(desc) ? reinterpret_cast<float*>(static_cast<char*>(workspace) + cbytes + rec_bytes) : nullptr;
   p->pv = P_V;
   p->out = out;
   p->fuse = 0;
@@ -336,6 +366,8 @@ int prepare_decode(const kvlr_desc* desc, const float* q, const float* P_K, cons
   m->ws = p->ws;
   m->pv = P_V;
   m->out = out;
+  m->out_latent = 0;
+  m->out_stride = desc->head_dim;
   m->B = p->B;
   m->Hq = p->Hq;
   m->Hkv = p->Hkv;
@@ -346,6 +378,28 @@ int prepare_decode(const kvlr_desc* desc, const float* q, const float* P_K, cons
   m->n_head_groups = p->n_head_groups;
   m->ht = p->ht;
   return KVLR_OK;
+}
+
+// 16-token blocks per wave step of the joint split kernel: one (measured faster
+// than two at rank 64/128, which doubles the loads in flight and the registers);
+// KVLR_JOINT_BLOCKS=2 selects two for tuning.
+int joint_blocks() {
+  const char* env = getenv("KVLR_JOINT_BLOCKS");
+  return env && atoi(env) == 2 ? 2 : 1;
+}
+
+// Joint bf16 values: q~ = q P_K into the workspace, then the split kernel over it.
+hipError_t joint_partials(const kvlr_desc* desc, kvlr::DecodeParams p, hipStream_t s) {
+  const int rk_max = rk_max_of(desc);
+  kvlr::DecodeParams pq = p;
+  pq.qt_in = nullptr;
+  pq.qt_stride = rk_max;
+  pq.scale_log2 = 1.f;   // the split kernel applies the scale as it loads q~
+  hipError_t e = kvlr::launch_project_queries(pq, rank_bound_of(rk_max), s);
+  if (e != hipSuccess) return e;
+  p.qt_in = p.qt_out;
+  p.qt_stride = rk_max;
+  return kvlr::launch_decode_joint(p, rank_bound_of(rk_max), joint_blocks(), s);
 }
 
 }  // namespace
@@ -361,6 +415,7 @@ KVLR_API int kvlr_decode_partials(const kvlr_desc* desc, const float* q, const f
   const int rc = prepare_decode(desc, q, P_K, lat_k, lat_v, seq_lens, scale, nullptr, nullptr, true, false,
                                 workspace, workspace_bytes, split_tokens, &p, &m, &rank_bound);
   if (rc) return rc;
+  if (joint_bf16(desc)) return hip_status(joint_partials(desc, p, static_cast<hipStream_t>(stream)));
   return hip_status(kvlr::launch_decode(p, desc->latent_dtype, rank_bound, decode_tile(),
                                         static_cast<hipStream_t>(stream)));
 }
@@ -373,6 +428,7 @@ KVLR_API int kvlr_decode_combine(const kvlr_desc* desc, const float* P_V, const 
   const int rc = prepare_decode(desc, nullptr, nullptr, nullptr, nullptr, nullptr, 1.f, P_V, out, false, true,
                                 const_cast<void*>(workspace), workspace_bytes, split_tokens, &p, &m, &rank_bound);
   if (rc) return rc;
+  if (joint_bf16(desc)) return hip_status(kvlr::launch_merge_heads(m, static_cast<hipStream_t>(stream)));
   return hip_status(kvlr::launch_merge(m, rank_bound, static_cast<hipStream_t>(stream)));
 }
 
@@ -386,6 +442,12 @@ KVLR_API int kvlr_decode_attn(const kvlr_desc* desc, const float* q, const float
   const int rc = prepare_decode(desc, q, P_K, lat_k, lat_v, seq_lens, scale, P_V, out, true, true, workspace,
                                 workspace_bytes, split_tokens, &p, &m, &rank_bound);
   if (rc) return rc;
+  if (joint_bf16(desc)) {   // projection, split and merge launches
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = joint_partials(desc, p, s);
+    if (e == hipSuccess) e = kvlr::launch_merge_heads(m, s);
+    return hip_status(e);
+  }
   p.fuse = 1;   // one launch: the last split workgroup of each group merges and back-projects
   return hip_status(kvlr::launch_decode(p, desc->latent_dtype, rank_bound, decode_tile(),
                                         static_cast<hipStream_t>(stream)));
@@ -412,6 +474,16 @@ KVLR_API int kvlr_decode_attn_latent(const kvlr_desc* desc, const float* q_lat, 
   p.pv = nullptr;
   p.qt_in = q_lat;
   p.qt_stride = rk_max;
+  if (joint_bf16(desc)) {   // split and merge launches
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    m.pv = nullptr;
+    m.out = o_lat;
+    m.out_latent = 1;
+    m.out_stride = rv_max;
+    hipError_t e = kvlr::launch_decode_joint(p, rank_bound_of(rk_max), joint_blocks(), s);
+    if (e == hipSuccess) e = kvlr::launch_merge_heads(m, s);
+    return hip_status(e);
+  }
   p.out_latent = 1;
   p.out_stride = rv_max;
   p.fuse = 1;

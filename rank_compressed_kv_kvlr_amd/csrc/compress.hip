@@ -300,13 +300,16 @@ __global__ __launch_bounds__(256) void compress_valu(CompressParams p) {
   }
   const size_t lat_base = (size_t)cap_rows_of(p.cap) * ((size_t)b * S + s_pre);
   const bool k_tiled = p.out_bf16 && kind == 0;
+  const bool v_tiled = p.out_bf16 && joint;   // joint bf16 values: value-MFMA operand order
 #pragma unroll
   for (int k = 0; k < kValuOuts; ++k) {
     const int idx = threadIdx.x + k * blockDim.x;
     if (idx < nt * r) {
       const int t = idx / r, j = idx - t * r;
       const int row = p.start + t0 + t;
-      const size_t off = lat_base + (k_tiled ? k_tiled_offset(row, j, r) : (size_t)row * r + j);
+      const size_t off = lat_base + (k_tiled   ? k_tiled_offset(row, j, r)
+                                     : v_tiled ? v_joint_offset(row, j, r)
+                                               : (size_t)row * r + j);
       if (p.out_bf16)
         static_cast<uint16_t*>(kind ? p.lat_v : p.lat_k)[off] = f32_to_bf16_bits(acc[k]);
       else
@@ -358,7 +361,10 @@ __global__ __launch_bounds__(128) void append_kernel(AppendParams p) {
   if (j >= r) return;
   const size_t base = (size_t)cap_rows_of(p.cap) * ((size_t)b * S + s_pre);
   const bool k_tiled = p.out_bf16 && kind == 0;
-  const size_t off = base + (k_tiled ? k_tiled_offset(pos, j, r) : (size_t)pos * r + j);
+  const bool v_tiled = p.out_bf16 && joint;
+  const size_t off = base + (k_tiled   ? k_tiled_offset(pos, j, r)
+                             : v_tiled ? v_joint_offset(pos, j, r)
+                                       : (size_t)pos * r + j);
   if (p.out_bf16)
     static_cast<uint16_t*>(kind ? p.lat_v : p.lat_k)[off] = f32_to_bf16_bits(acc);
   else

@@ -23,12 +23,10 @@
 // ~16 bits of the query. The value side (p-weighted sum of V_lat rows) runs
 // on VALU: each lane owns 8 latent channels of a subset of rows, reading 16
 // coalesced bytes per row chunk, and p comes through LDS.
-#include "kvlr_internal.hpp"
+#include "decode_common.hpp"
 
 namespace kvlr {
 namespace {
-
-constexpr float kNegInf = -__builtin_huge_valf();
 
 // Largest number of 64-lane value loads per tile of `tile` tokens over ranks r <= rb
 // (multiples of 16): a row has r/8 chunks of 8 channels, a load instruction
@@ -41,119 +39,6 @@ constexpr int value_iters_bound(int rb, int tile) {
     worst = it > worst ? it : worst;
   }
   return worst;
-}
-
-// ---------------------------------------------------------------------------
-// shared prologue: q~ = (q P_K) * scale * log2(e) for the workgroup's heads
-// ---------------------------------------------------------------------------
-// The four waves split the d rows of P_K[h]; each lane issues all of its
-// 16-byte basis loads at once (one memory round trip), forms partial dot
-// products for the 4 heads, and partials are summed across lanes with
-// shuffles and across waves through LDS. With a caller-given q~ (bases
-// folded into the query projection) the loads are of q~ itself.
-//   q_lds [4][d], red [4 waves][4 heads][RB], qt_lds [4][RB]
-template <int RB>
-__device__ __forceinline__ void project_query(const DecodeParams& p, int b, int h, int hq0, int gpw, int rk,
-                                              float* q_lds, float* red, float* qt_lds) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int d = p.d;
-  if (p.qt_in) {   // folded mode: q~ [B][Hq][qt_stride] given in latent space
-    for (int idx = tid; idx < kHeadsPerWg * RB; idx += blockDim.x) {
-      const int g = idx / RB, j = idx - g * RB;
-      qt_lds[idx] = (g < gpw && j < rk) ? p.qt_in[((size_t)b * p.Hq + hq0 + g) * p.qt_stride + j] * p.scale_log2 : 0.f;
-    }
-    __syncthreads();
-    return;
-  }
-  constexpr int NH = (RB + 63) / 64;      // 64-column halves of P
-  constexpr int RPL = 16;                 // rows per lane bound: d / 16 <= 16
-  const float* P = p.pk + (size_t)d * p.ht.rk_pre[h];
-  const int isub = lane >> 4, m = lane & 15;
-  const int rows_per_wave = d >> 2, rpl = d >> 4;
-  float4 pr[RPL];
-  auto load_half = [&](int hf) {
-    const int col = 64 * hf + 4 * m;
-#pragma unroll
-    for (int e = 0; e < RPL; ++e) {
-      const int i = wave * rows_per_wave + isub + 4 * e;
-      pr[e] = (e < rpl && col < rk) ? *reinterpret_cast<const float4*>(P + (size_t)i * rk + col)
-                                    : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  };
-  load_half(0);   // basis loads in flight together with the query rows
-  for (int idx = tid; idx < kHeadsPerWg * d; idx += blockDim.x) {
-    const int g = idx / d, i = idx - g * d;
-    q_lds[idx] = (g < gpw) ? p.q[((size_t)b * p.Hq + hq0 + g) * d + i] : 0.f;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int hf = 0; hf < NH; ++hf) {
-    const int col = 64 * hf + 4 * m;
-    if (hf > 0) load_half(hf);
-    float part[4][4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) part[g][jj] = 0.f;
-#pragma unroll
-    for (int e = 0; e < RPL; ++e) {
-      if (e < rpl) {
-        const int i = wave * rows_per_wave + isub + 4 * e;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const float qv = q_lds[g * d + i];
-          part[g][0] = fmaf(qv, pr[e].x, part[g][0]);
-          part[g][1] = fmaf(qv, pr[e].y, part[g][1]);
-          part[g][2] = fmaf(qv, pr[e].z, part[g][2]);
-          part[g][3] = fmaf(qv, pr[e].w, part[g][3]);
-        }
-      }
-    }
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        float v = part[g][jj];
-        v += __shfl_xor(v, 16, 64);
-        v += __shfl_xor(v, 32, 64);
-        part[g][jj] = v;
-      }
-    if (isub == 0 && col < RB) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<float4*>(red + (wave * 4 + g) * RB + col) =
-            make_float4(part[g][0], part[g][1], part[g][2], part[g][3]);
-    }
-  }
-  __syncthreads();
-  for (int idx = tid; idx < kHeadsPerWg * RB; idx += blockDim.x) {
-    const int g = idx / RB, j = idx - g * RB;
-    float v = 0.f;
-    if (g < gpw && j < rk)
-      v = (red[(0 * 4 + g) * RB + j] + red[(1 * 4 + g) * RB + j] + red[(2 * 4 + g) * RB + j] +
-           red[(3 * 4 + g) * RB + j]) * p.scale_log2;
-    qt_lds[idx] = v;   // zero rows for heads beyond gpw and channels beyond rk
-  }
-  __syncthreads();
-}
-
-// Split records are written and read with agent-scope relaxed atomic
-// accesses: on gfx950 these are plain stores/loads with the agent-coherence
-// bit (sc1), so a record written by one workgroup is read back coherently by
-// another workgroup on any XCD without a whole-L2 writeback.
-__device__ __forceinline__ void store_rec(float* addr, float v) {
-  __hip_atomic_store(addr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_rec(const float* addr) {
-  return __hip_atomic_load(addr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ void write_empty_records(const DecodeParams& p, int b, int hq0, int gpw, int s, int rv) {
-  for (int idx = threadIdx.x; idx < gpw * (rv + 2); idx += blockDim.x) {
-    const int g = idx / (rv + 2), j = idx - g * (rv + 2);
-    float* rec = p.ws + (((size_t)b * p.Hq + hq0 + g) * p.n_splits + s) * p.ws_stride;
-    store_rec(rec + j, (j == 0) ? kNegInf : 0.f);
-  }
 }
 
 // Merge of the 4 waves' states into one record per head.
@@ -1275,6 +1160,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge(MergeParams p) {
   }
 }
 
+
 }  // namespace
 
 hipError_t launch_decode(const DecodeParams& p, int latent_dtype, int rank_bound, int tile, hipStream_t stream) {
@@ -1327,5 +1213,6 @@ hipError_t launch_merge(const MergeParams& p, int rank_bound, hipStream_t stream
   }
   return hipGetLastError();
 }
+
 
 }  // namespace kvlr

@@ -30,6 +30,7 @@ struct DecodeParams {
   const float* q;        // [B][Hq][d]
   const float* qt_in;    // optional q~ [B][Hq][qt_stride] (bases folded into the query projection)
   int qt_stride;
+  float* qt_out;         // query projection kernel: destination of q~ [B][Hq][qt_stride]
   const float* pk;       // packed [h][d][rk(h)]
   const void* lat_k;     // latent caches
   const void* lat_v;
@@ -52,7 +53,8 @@ struct DecodeParams {
 struct MergeParams {
   const float* ws;
   const float* pv;       // packed [h][d][rv(h)]
-  float* out;            // [B][Hq][d]
+  float* out;            // [B][Hq][d], or [B][Hq][out_stride] latent rows when out_latent
+  int out_latent, out_stride;
   int B, Hq, Hkv, G, d;
   int n_splits, ws_stride, n_head_groups;
   HeadTable ht;
@@ -94,6 +96,19 @@ struct AppendParams {
 // whole 16-row MFMA blocks.
 __host__ __device__ inline int cap_rows_of(int cap) { return (cap + 15) & ~15; }
 
+// Offset (elements) of bf16 joint value latent (t, j) inside its batch row's
+// block (joint rank r, a multiple of 16). Each 16-row block holds the rows in
+// the order the value MFMA (v_mfma_f32_16x16x16_bf16, tokens as K) reads its
+// B operand: for every 32-channel pair, lane n + 16 q holds tokens 4 q .. 4 q + 3
+// of channel n, then the same tokens of channel n + 16 (16 contiguous bytes);
+// a 16-channel tail holds the tokens of channel n alone (8 bytes per lane).
+__host__ __device__ inline size_t v_joint_offset(int t, int j, int r) {
+  const size_t base = (size_t)(t >> 4) * 16 * r;
+  const int q = (t & 15) >> 2, e = t & 3, np = r >> 5;
+  if (j < 32 * np) return base + (size_t)(j >> 5) * 512 + q * 128 + (j & 15) * 8 + ((j >> 4) & 1) * 4 + e;
+  return base + (size_t)np * 512 + q * 64 + (j - 32 * np) * 4 + e;
+}
+
 // Offset (elements) of bf16 key latent (t, j) inside its (batch row, KV head)
 // block, rank rk (a multiple of 16). Each 16-row block holds the rows in the
 // order the score MFMA reads its B operand: for every 32-channel pair
@@ -125,6 +140,12 @@ __host__ __device__ constexpr int q43_row_bytes(int r) {
 hipError_t launch_decode(const DecodeParams& p, int latent_dtype, int rank_bound, int tile, hipStream_t s);
 hipError_t launch_hadamard(const float* in, float* out, size_t n_groups, hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, int rank_bound, hipStream_t s);
+// Joint bf16 values: q~ into p.qt_out, the split kernel (q~ from p.qt_in, key rank
+// bound rk_bound, `blocks` 16-token blocks per wave step: 1 or 2), and the merge
+// with one workgroup per (query head, batch row).
+hipError_t launch_project_queries(const DecodeParams& p, int rk_bound, hipStream_t s);
+hipError_t launch_decode_joint(const DecodeParams& p, int rk_bound, int blocks, hipStream_t s);
+hipError_t launch_merge_heads(const MergeParams& p, hipStream_t s);
 hipError_t launch_compress(const CompressParams& p, hipStream_t s);
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
 

@@ -191,3 +191,42 @@ def test_joint_value_mode_validation():
     with pytest.raises(kv.KvlrError) as e:
         kv.cache_elems(odd)
     assert e.value.code == -7
+
+
+def test_joint_bf16_shape_limits_and_workspace():
+    # the joint bf16 kernel holds at most 32 query heads and 8 KV heads
+    for hq, hkv in [(64, 8), (32, 16), (48, 16)]:
+        d = kv.Desc(1, hq, hkv, 64, 100, 32, [64] * hkv, kv.BF16, kv.BF16, kv.VALUES_JOINT)
+        with pytest.raises(kv.KvlrError) as e:
+            kv.cache_elems(d)
+        assert e.value.code == -2, (hq, hkv)
+    # joint values with fp32 latents run the per-head kernels: no such limit
+    kv.cache_elems(kv.Desc(1, 64, 16, 64, 100, 32, [64] * 16, kv.BF16, kv.F32, kv.VALUES_JOINT))
+    # workspace: counters, records, then the projected queries [B][Hq][max r_k]
+    d = kv.Desc(2, 32, 8, 128, 4096, [64] * 7 + [48], [128] * 8, kv.BF16, kv.BF16, kv.VALUES_JOINT)
+    rc, n = _ws(d, 512)
+    assert rc == 0
+    assert n == 256 + 2 * 32 * 8 * 132 * 4 + 2 * 32 * 64 * 4
+    ns, length = kv.decode_plan(d, 512)
+    assert (ns, length) == (8, 512)
+
+
+@pytest.mark.parametrize("r", [16, 32, 48, 64, 80, 96, 112, 128])
+def test_joint_value_tile_order(r):
+    """bf16 joint value layout: a permutation of each 16-row block, and lane 16 q + n of
+    pair p reads 16 contiguous bytes holding tokens 4 q .. 4 q + 3 of channels 32 p + n
+    and 32 p + 16 + n (the tail: 8 bytes, channel 32 np + n)."""
+    idx = kv.v_joint_index(64, r)
+    for blk in range(4):
+        sub = idx[16 * blk:16 * blk + 16]
+        assert sub.min() == 16 * r * blk and sub.max() == 16 * r * (blk + 1) - 1
+        assert len(np.unique(sub)) == 16 * r
+    np_ = r // 32
+    for lane in range(64):
+        q, n = lane // 16, lane % 16
+        for p in range(np_):
+            got = [idx[4 * q + e, 32 * p + n] for e in range(4)] + [idx[4 * q + e, 32 * p + 16 + n] for e in range(4)]
+            assert got == list(range(512 * p + 8 * lane, 512 * p + 8 * lane + 8))
+        if r % 32:
+            got = [idx[4 * q + e, 32 * np_ + n] for e in range(4)]
+            assert got == list(range(512 * np_ + 4 * lane, 512 * np_ + 4 * lane + 4))

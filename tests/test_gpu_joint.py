@@ -20,7 +20,7 @@ def _kv():
     return kv
 
 
-def _joint_case(cfg, rj, latent="bf16", n_rows=None, chunk=None):
+def _joint_case(cfg, rj, latent="bf16", n_rows=None, chunk=None, poison=False):
     import torch
     kv = _kv()
     rk, _ = host.ranks(cfg)
@@ -38,6 +38,9 @@ def _joint_case(cfg, rj, latent="bf16", n_rows=None, chunk=None):
     else:
         PK, PJ = bases32(PK), bases32([PJ])[0]
     lk, lv = kv.alloc_cache(desc)
+    if poison:   # every row not written below holds NaN bit patterns
+        lk.view(torch.int16).fill_(-1)
+        lv.view(torch.int16).fill_(-1)
     gen = KVGenerator(cfg, 0)
     n_rows = cfg.capacity if n_rows is None else n_rows
     chunk = chunk or n_rows
@@ -124,7 +127,13 @@ def test_joint_latents_match_oracle(gpu):
 @pytest.mark.parametrize("cid,extra,rj", [
     (1, dict(B=2, T=1000), 128),
     (1, dict(B=3, Hq=12, Hkv=3, T=777), 48),
-    (2, dict(B=3, T_range=(1, 600)), 64),
+    (2, dict(B=3, T_range=(1, 600)), 64),            # per-head key ranks 16..96
+    (1, dict(B=2, Hq=8, Hkv=8, T=300), 64),          # G = 1: row tiles of 4 query heads
+    (1, dict(B=2, Hq=16, Hkv=8, T=333), 80),         # G = 2; 16-channel value tail
+    (1, dict(B=1, Hq=30, Hkv=5, T=517), 112),        # G = 6: KV heads straddle the row tiles
+    (1, dict(B=2, Hq=32, Hkv=2, T=250), 16),         # G = 16; tail-only value rank
+    (3, dict(B=1, T=700), 128),                      # r_k = 48: a key pair and a tail
+    (1, dict(B=2, d=64, T=400), 96),                 # head_dim 64
 ])
 def test_joint_decode_matches_oracle(gpu, cid, extra, rj):
     cfg = CONFIGS[cid].scaled(**extra)
@@ -169,3 +178,67 @@ def test_joint_folded_latent_output(gpu):
     o_lat = o_lat.cpu().numpy().astype(np.float64)
     back = np.stack([o_lat[:, i] @ jo.joint_slice(case["PJ"], i // cfg.G, cfg.d).T for i in range(cfg.Hq)], 1)
     assert float(rel_inf_rows(back, full).max()) <= 2e-4
+
+
+def test_joint_decode_short_and_empty_rows(gpu):
+    """Sequences of 0, 1, 15, 16, 17 rows (partial and empty 16-row blocks, empty splits)."""
+    cfg = CONFIGS[1].scaled(B=6, T=260)
+    case = _joint_case(cfg, 128)
+    lens = np.array([0, 1, 15, 16, 17, 260], np.int32)
+    q = host.queries(cfg, 0, 0)
+    _check(case, _decode(case, q, lens), q, lens)
+    _check(case, _decode(case, q, lens, split=64), q, lens)
+
+
+def test_joint_decode_ignores_rows_past_the_end(gpu):
+    """Rows at and past seq_lens inside the last 16-row block hold NaN bit patterns: the
+    kernel masks them (keys through the scores, values by zeroing the operand)."""
+    cfg = CONFIGS[1].scaled(B=3, T=320)
+    case = _joint_case(cfg, 128, n_rows=290, poison=True)
+    lens = np.array([290, 123, 17], np.int32)
+    q = host.queries(cfg, 0, 0)
+    got = _decode(case, q, lens)
+    assert np.all(np.isfinite(got))
+    _check(case, got, q, lens)
+
+
+def test_joint_two_stage_matches_single_call(gpu):
+    """decode_partials + decode_combine run the same kernels as decode_attn: identical output."""
+    import torch
+    kv = _kv()
+    cfg = CONFIGS[1].scaled(B=2, T=900)
+    case = _joint_case(cfg, 128)
+    lens = np.array([900, 555], np.int32)
+    q = host.queries(cfg, 0, 0)
+    full = _decode(case, q, lens, split=128)
+    desc = case["desc"]
+    ws = kv.alloc_workspace(desc, 128)
+    lens_d = torch.as_tensor(lens).cuda()
+    kv.decode_partials(desc, torch.from_numpy(q).cuda(), case["pk"], case["lk"], case["lv"], lens_d, ws,
+                       split_tokens=128)
+    out = torch.empty((cfg.B, cfg.Hq, cfg.d), dtype=torch.float32, device="cuda")
+    kv.decode_combine(desc, case["pj"], ws, out, split_tokens=128)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), full)
+
+
+def test_joint_decode_many_splits(gpu):
+    """125 splits of 64 tokens: the per-head merge takes its records in two passes."""
+    cfg = CONFIGS[1].scaled(B=1, T=8000)
+    case = _joint_case(cfg, 128, chunk=2048)
+    lens = host.lengths(cfg)
+    q = host.queries(cfg, 0, 0)
+    _check(case, _decode(case, q, lens, split=64), q, lens)
+
+
+def test_joint_decode_two_blocks_per_step(gpu, monkeypatch):
+    """The two-block variant of the split kernel (KVLR_JOINT_BLOCKS=2, a tuning switch read
+    at each call) gives the oracle's result too, including blocks past the sequence end."""
+    cfg = CONFIGS[1].scaled(B=4, T=300)
+    case = _joint_case(cfg, 128)
+    lens = np.array([300, 17, 33, 1], np.int32)
+    q = host.queries(cfg, 0, 0)
+    monkeypatch.setenv("KVLR_JOINT_BLOCKS", "2")
+    got = _decode(case, q, lens, split=64)
+    monkeypatch.delenv("KVLR_JOINT_BLOCKS")
+    _check(case, got, q, lens)
