@@ -32,7 +32,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_split_traffic.json")
-DECODE_SRC = os.path.join(ROOT, "rank_compressed_kv_kvlr_amd", "csrc", "decode.hip")
+# sources of the dominant kernel (decode_split_bf16): the traffic counters belong to these
+DECODE_SRC = [os.path.join(ROOT, "rank_compressed_kv_kvlr_amd", "csrc", f)
+              for f in ("decode.hip", "decode_common.hpp", "kvlr_internal.hpp")]
 METRIC = "compressed-KV decode attn: tokens/sec + achieved HBM GB/s (% of peak), 1 GPU"
 
 
@@ -54,9 +56,13 @@ def parse():
     return ap.parse_args()
 
 
-def source_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(paths):
+    """sha256 (first 16 hex digits) over the concatenated sources of a kernel."""
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic():

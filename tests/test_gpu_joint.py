@@ -80,6 +80,21 @@ def _reference(case, q, b, T):
     return out
 
 
+def _reference_stored(case, q, b, T):
+    """Diagnostic: the latent order on latents rounded to bf16 as stored (keys per head,
+    the joint value latent), which separates storage rounding from kernel arithmetic."""
+    cfg = case["cfg"]
+    K, V = _rows(case, "k", b, T), _rows(case, "v", b, T)
+    V_lat = ko.bf16_round(jo.joint_latents(V.reshape(T, -1), case["PJ"]))
+    out = np.zeros((cfg.Hq, cfg.d))
+    G = cfg.G
+    for h in range(cfg.Hkv):
+        K_lat = ko.bf16_round(K[:, h] @ case["PK"][h])
+        out[h * G:(h + 1) * G] = jo.decode_joint_latent_head(q[b, h * G:(h + 1) * G], K_lat, V_lat, case["PK"][h],
+                                                             jo.joint_slice(case["PJ"], h, cfg.d), 1 / np.sqrt(cfg.d))
+    return out
+
+
 def _decode(case, q, lens, split=0):
     import torch
     kv = _kv()
@@ -89,19 +104,24 @@ def _decode(case, q, lens, split=0):
     return out.cpu().numpy().astype(np.float64)
 
 
-def _check(case, got, q, lens, bound=None):
+def _check(case, got, q, lens, bound=None, diag_bound=2e-3):
+    """Acceptance against the oracle; for bf16 latents also the storage-aware diagnostic."""
     cfg = case["cfg"]
     metric, tol = tolerance(cfg) if case["latent"] != "q43" else (rel_l2_rows, 2e-2)
     bound = tol if bound is None else bound
-    worst = 0.0
+    worst = diag = 0.0
     for b in range(cfg.B):
-        ref = _reference(case, q, b, int(lens[b]))
-        if int(lens[b]) == 0:
+        T = int(lens[b])
+        ref = _reference(case, q, b, T)
+        if T == 0:
             assert np.all(got[b] == 0)
             continue
         worst = max(worst, float(metric(got[b], ref).max()))
-    say(f"[joint check] worst {worst:.3e} (bound {bound})")
+        if case["latent"] == "bf16":
+            diag = max(diag, float(rel_l2_rows(got[b], _reference_stored(case, q, b, T)).max()))
+    say(f"[joint check] worst {worst:.3e} (bound {bound}), storage-aware {diag:.3e} (bound {diag_bound})")
     assert worst <= bound, worst
+    assert diag <= diag_bound, diag
 
 
 def test_joint_latents_match_oracle(gpu):
@@ -124,23 +144,29 @@ def test_joint_latents_match_oracle(gpu):
         assert np.all(np.abs(got - want) <= ulp + mag * 2.0 ** -14), b
 
 
-@pytest.mark.parametrize("cid,extra,rj", [
-    (1, dict(B=2, T=1000), 128),
-    (1, dict(B=3, Hq=12, Hkv=3, T=777), 48),
-    (2, dict(B=3, T_range=(1, 600)), 64),            # per-head key ranks 16..96
-    (1, dict(B=2, Hq=8, Hkv=8, T=300), 64),          # G = 1: row tiles of 4 query heads
-    (1, dict(B=2, Hq=16, Hkv=8, T=333), 80),         # G = 2; 16-channel value tail
-    (1, dict(B=1, Hq=30, Hkv=5, T=517), 112),        # G = 6: KV heads straddle the row tiles
-    (1, dict(B=2, Hq=32, Hkv=2, T=250), 16),         # G = 16; tail-only value rank
-    (3, dict(B=1, T=700), 128),                      # r_k = 48: a key pair and a tail
-    (1, dict(B=2, d=64, T=400), 96),                 # head_dim 64
+# The storage-aware diagnostic compares with latents the oracle rounds to bf16 itself.
+# Compression multiplies by the basis as a high plus a low bf16 part (about 16 bits),
+# so a few latents round to the neighbouring bf16 value; at head_dim 64 (scale 1/8,
+# full-rank keys, one token holding up to 22% of the weight) those flips move the
+# output by 4.9e-3, the same figure a CPU model of that compression gives. The kernel
+# arithmetic itself stays near 1e-4 (the other cases).
+@pytest.mark.parametrize("cid,extra,rj,diag", [
+    (1, dict(B=2, T=1000), 128, 2e-3),
+    (1, dict(B=3, Hq=12, Hkv=3, T=777), 48, 2e-3),
+    (2, dict(B=3, T_range=(1, 600)), 64, 2e-3),            # per-head key ranks 16..96
+    (1, dict(B=2, Hq=8, Hkv=8, T=300), 64, 2e-3),          # G = 1: row tiles of 4 query heads
+    (1, dict(B=2, Hq=16, Hkv=8, T=333), 80, 2e-3),         # G = 2; 16-channel value tail
+    (1, dict(B=1, Hq=30, Hkv=5, T=517), 112, 2e-3),        # G = 6: KV heads straddle the row tiles
+    (1, dict(B=2, Hq=32, Hkv=2, T=250), 16, 2e-3),         # G = 16; tail-only value rank
+    (3, dict(B=1, T=700), 128, 2e-3),                      # r_k = 48: a key pair and a tail
+    (1, dict(B=2, d=64, T=400), 96, 6e-3),                 # head_dim 64 (see above)
 ])
-def test_joint_decode_matches_oracle(gpu, cid, extra, rj):
+def test_joint_decode_matches_oracle(gpu, cid, extra, rj, diag):
     cfg = CONFIGS[cid].scaled(**extra)
     case = _joint_case(cfg, rj)
     lens = host.lengths(cfg)
     q = host.queries(cfg, 0, 0)
-    _check(case, _decode(case, q, lens), q, lens)
+    _check(case, _decode(case, q, lens), q, lens, diag_bound=diag)
 
 
 def test_joint_decode_f32(gpu):
