@@ -157,15 +157,23 @@ def measure_workloads(kv, torch, np):
         for s in range(S):
             kv.append(c["desc"], ks[s], vs[s], pos[s], c["pk"], c["pv"], c["lk"], c["lv"])
             kv.decode_attn(c["desc"], qs[s], c["pk"], c["pv"], c["lk"], c["lv"], lns[s], out=o, workspace=ws)
+    def fused_loop():   # the same steps through kvlr_append_decode_attn (one launch per step)
+        for s in range(S):
+            kv.append_decode_attn(c["desc"], ks[s], vs[s], pos[s], qs[s], c["pk"], c["pv"], c["lk"], c["lv"], lns[s],
+                                  out=o, workspace=ws)
     t_e = _timed(torch, loop, 3)
     g = _graph_of(torch, loop)
     t_g = _timed(torch, g.replay, 3)
+    t_f = _timed(torch, fused_loop, 3)
+    gf = _graph_of(torch, fused_loop)
+    t_fg = _timed(torch, gf.replay, 3)
     rk, rv = int(c["rk"][0]), int(c["rv"][0])
     nbytes = sum(T + s + 1 for s in range(S)) * cfg.B * cfg.Hkv * (rk + rv) * 2
     out[cfg.name] = {"steps": S, "eager_us_per_step": t_e / S * 1e6, "graph_us_per_step": t_g / S * 1e6,
+                     "fused_eager_us_per_step": t_f / S * 1e6, "fused_graph_us_per_step": t_fg / S * 1e6,
                      "bytes": nbytes, "graph_GBps": nbytes / t_g / 1e9, "graph_hbm_frac": nbytes / t_g / 1e9 / HBM_PEAK_GBPS,
-                     "graph_tokens_per_s": cfg.B * S / t_g}
-    del c, ws, g
+                     "graph_tokens_per_s": cfg.B * S / t_g, "fused_graph_tokens_per_s": cfg.B * S / t_fg}
+    del c, ws, g, gf
     torch.cuda.empty_cache()
 
     print("[bench] workload llama3_8b_32_layers", file=sys.stderr, flush=True)

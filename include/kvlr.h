@@ -287,6 +287,24 @@ KVLR_API int kvlr_decode_attn_latent(const kvlr_desc* desc, const float* q_lat, 
                                      void* workspace, size_t workspace_bytes, int32_t split_tokens,
                                      void* stream);
 
+/* One autoregressive decode step with its append fused in (StiefAttention
+ * technical summary, "Definição do Problema": the cache grows by one row per
+ * generated token, and the new token attends to itself): the result, in out
+ * and in the caches, is that of
+ *   kvlr_append(desc, k_new, v_new, pos, P_K, P_V, lat_k, lat_v, stream);
+ *   kvlr_decode_attn(desc, q, P_K, P_V, lat_k, lat_v, seq_lens, scale, out,
+ *                    workspace, workspace_bytes, split_tokens, stream);
+ * bit for bit. For bf16 latents with per-head values it is one launch: the
+ * workgroups whose split holds row pos[b] form the new latent rows, store
+ * them and read them back once the stores are acknowledged (no other
+ * workgroup reads that row). Other caches take the two launches above.
+ * Arguments as in kvlr_append and kvlr_decode_attn; the caller sets
+ * seq_lens[b] = pos[b] + 1 to attend to the new row. */
+KVLR_API int kvlr_append_decode_attn(const kvlr_desc* desc, const void* k_new, const void* v_new,
+                                     const int32_t* pos, const float* q, const float* P_K, const float* P_V,
+                                     void* lat_k, void* lat_v, const int32_t* seq_lens, float scale, float* out,
+                                     void* workspace, size_t workspace_bytes, int32_t split_tokens, void* stream);
+
 /* The two stages of kvlr_decode_attn, for callers that schedule them
  * separately (e.g. to time or overlap them). kvlr_decode_attn(...) is
  * exactly kvlr_decode_partials(...) followed by kvlr_decode_combine(...) on

@@ -338,6 +338,10 @@ int prepare_decode(const kvlr_desc* desc, const float* q, const float* P_K, cons
   if (!workspace || workspace_bytes < need) return KVLR_ERR_WORKSPACE;
 
   const int G = desc->n_q_heads / desc->n_kv_heads;
+  p->app_k = p->app_v = nullptr;
+  p->k_new = p->v_new = nullptr;
+  p->pos = nullptr;
+  p->in_bf16 = desc->in_dtype == KVLR_BF16;
   p->q = q;
   p->pk = P_K;
   p->lat_k = lat_k;
@@ -486,6 +490,34 @@ KVLR_API int kvlr_decode_attn_latent(const kvlr_desc* desc, const float* q_lat, 
   }
   p.out_latent = 1;
   p.out_stride = rv_max;
+  p.fuse = 1;
+  return hip_status(kvlr::launch_decode(p, desc->latent_dtype, rank_bound, decode_tile(),
+                                        static_cast<hipStream_t>(stream)));
+}
+
+KVLR_API int kvlr_append_decode_attn(const kvlr_desc* desc, const void* k_new, const void* v_new,
+                                     const int32_t* pos, const float* q, const float* P_K, const float* P_V,
+                                     void* lat_k, void* lat_v, const int32_t* seq_lens, float scale, float* out,
+                                     void* workspace, size_t workspace_bytes, int32_t split_tokens, void* stream) {
+  kvlr::DecodeParams p;
+  kvlr::MergeParams m;
+  int rank_bound = 0;
+  int rc = prepare_decode(desc, q, P_K, lat_k, lat_v, seq_lens, scale, P_V, out, true, true, workspace,
+                          workspace_bytes, split_tokens, &p, &m, &rank_bound);
+  if (rc) return rc;
+  if (!k_new || !v_new || !pos) return KVLR_ERR_NULL;
+  if (desc->latent_dtype != KVLR_BF16 || desc->value_mode != KVLR_VALUES_PER_HEAD) {
+    // other caches: the append kernel, then the decode (two launches, the same result)
+    rc = kvlr_append(desc, k_new, v_new, pos, P_K, P_V, lat_k, lat_v, stream);
+    if (rc) return rc;
+    return kvlr_decode_attn(desc, q, P_K, P_V, lat_k, lat_v, seq_lens, scale, out, workspace, workspace_bytes,
+                            split_tokens, stream);
+  }
+  p.app_k = lat_k;
+  p.app_v = lat_v;
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.pos = pos;
   p.fuse = 1;
   return hip_status(kvlr::launch_decode(p, desc->latent_dtype, rank_bound, decode_tile(),
                                         static_cast<hipStream_t>(stream)));

@@ -262,6 +262,55 @@ __device__ __forceinline__ void finish_split(const DecodeParams& p, int b, int h
 }
 
 // ---------------------------------------------------------------------------
+// fused append: new latent rows written by the workgroup that reads them
+// ---------------------------------------------------------------------------
+// One decode step of autoregressive generation appends the new token's row and
+// attends over it (StiefAttention technical summary, "Definição do Problema": the
+// cache grows by one row per generated token). In the fused form the workgroups
+// whose split holds row pos[b] form the new latent rows themselves (thread j < 128:
+// key channel j, thread 128 + j: value channel j; fp32 dot products over d in the
+// order of the append kernel, rounded to bf16), store them, and wait until the
+// stores are acknowledged before any of their waves loads a tile, so the row is
+// read back from L2. No other workgroup reads that row. With several head groups
+// per KV head every group's workgroup writes the same bytes.
+__device__ __forceinline__ bool append_owner(const DecodeParams& p, int b, int h, int s) {
+  if (p.app_k == nullptr) return false;
+  const int pos = p.pos[b];
+  return pos >= 0 && pos < p.cap && pos / p.ht.split_len[h] == s;
+}
+
+__device__ void append_rows(const DecodeParams& p, int b, int h, int rk, int rv, float* xs) {
+  const int d = p.d, tid = threadIdx.x;
+  const int pos = p.pos[b];
+  for (int i = tid; i < 2 * d; i += blockDim.x) {   // k_new row to xs[0, d), v_new row to xs[256, 256 + d)
+    const int kind = i >= d, ii = i - kind * d;
+    const void* X = kind ? p.v_new : p.k_new;
+    const size_t src = ((size_t)b * p.Hkv + h) * d + ii;
+    xs[kind * 256 + ii] = p.in_bf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(X)[src])
+                                    : static_cast<const float*>(X)[src];
+  }
+  __syncthreads();
+  const int kind = tid >> 7, j = tid & 127;
+  const int r = kind ? rv : rk;
+  if (j < r) {
+    const float* P = (kind ? p.pv : p.pk) + (size_t)d * (kind ? p.ht.rv_pre[h] : p.ht.rk_pre[h]);
+    const float* x = xs + kind * 256;
+    float acc = 0.f;
+    for (int i = 0; i < d; ++i) acc = fmaf(x[i], P[(size_t)i * r + j], acc);
+    const size_t rows = cap_rows_of(p.cap);
+    if (kind == 0) {
+      uint16_t* K = static_cast<uint16_t*>(p.app_k) + rows * ((size_t)b * p.Sk + p.ht.sk_pre[h]);
+      K[k_tiled_offset(pos, j, rk)] = f32_to_bf16_bits(acc);
+    } else {
+      uint16_t* V = static_cast<uint16_t*>(p.app_v) + rows * ((size_t)b * p.Sv + p.ht.sv_pre[h]);
+      V[(size_t)pos * rv + j] = f32_to_bf16_bits(acc);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);   // the new rows are in L2 before any wave of this workgroup loads a tile
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
 // bf16 latents: MFMA scores, VALU value mix
 // ---------------------------------------------------------------------------
 // RB: rank bound (32, 64, 96 or 128) sizing the register tiles; the actual
@@ -286,6 +335,7 @@ __global__ __launch_bounds__(256) void decode_split_bf16(DecodeParams p) {
   const int T = min(max(p.seq_lens[b], 0), p.cap);
   const int t_begin = min(s * p.ht.split_len[h], T);   // clamped: no overflow for far splits
   const int t_end = min(T, t_begin + p.ht.split_len[h]);
+  if (append_owner(p, b, h, s)) append_rows(p, b, h, rk, rv, smem);
   if (t_begin >= t_end) {
     write_empty_records(p, b, hq0, gpw, s, rv);
     BasisPrefetch<RB> pf;

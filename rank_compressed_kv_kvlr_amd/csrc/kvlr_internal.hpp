@@ -47,6 +47,15 @@ struct DecodeParams {
   int Rk, Rv;            // sum of ranks over heads
   int Sk, Sv;            // per-row storage summed over heads (elements; bytes for 4/3-bit rows)
   float scale_log2;      // scale * log2(e): scores live in the base-2 domain
+  // fused append (bf16 per-head caches): the new rows k_new, v_new [B][Hkv][d] (in_bf16
+  // says their dtype) are written at row pos[b] of app_k / app_v (the caches, writable)
+  // by the workgroups whose split holds that row, before they read it
+  void* app_k;
+  void* app_v;
+  const void* k_new;
+  const void* v_new;
+  const int* pos;
+  int in_bf16;
   HeadTable ht;
 };
 

@@ -230,3 +230,17 @@ def test_joint_value_tile_order(r):
         if r % 32:
             got = [idx[4 * q + e, 32 * np_ + n] for e in range(4)]
             assert got == list(range(512 * np_ + 4 * lane, 512 * np_ + 4 * lane + 4))
+
+
+def test_fused_step_arguments():
+    """kvlr_append_decode_attn checks every pointer, the workspace and the scale before any launch."""
+    d = _desc()
+    rc, need = _ws(d)
+    assert rc == 0
+    for k in range(10):   # k_new, v_new, pos, q, P_K, P_V, lat_k, lat_v, seq_lens, out
+        a = [FAKE] * 10
+        a[k] = None
+        assert kv.lib.kvlr_append_decode_attn(d.ptr, *a[:9], ctypes.c_float(0.1), a[9], FAKE, need, 0, None) == -1, k
+    a = [FAKE] * 9
+    assert kv.lib.kvlr_append_decode_attn(d.ptr, *a, ctypes.c_float(0.1), FAKE, FAKE, need - 1, 0, None) == -5
+    assert kv.lib.kvlr_append_decode_attn(d.ptr, *a, ctypes.c_float(float("nan")), FAKE, FAKE, need, 0, None) == -7

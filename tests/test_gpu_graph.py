@@ -66,8 +66,10 @@ def test_graph_multi_layer_step_matches_eager(gpu):
     say("[graph] 4-layer step: 3 replays equal the eager step")
 
 
-def test_graph_append_decode_loop_matches_eager(gpu):
-    """A loop of (append one token, attend over all rows) steps captured as one graph."""
+@pytest.mark.parametrize("fused", [False, True])
+def test_graph_append_decode_loop_matches_eager(gpu, fused):
+    """A loop of (append one token, attend over all rows) steps captured as one graph; with
+    fused=True each step is one kvlr_append_decode_attn call, compared with the two-call loop."""
     import torch
     kv = _kv()
     cfg = CONFIGS[3].scaled(T=2000, decode_steps=8)
@@ -80,8 +82,12 @@ def test_graph_append_decode_loop_matches_eager(gpu):
     pos = [torch.full((cfg.B,), T + s, dtype=torch.int32, device="cuda") for s in range(steps)]
     lens = [torch.full((cfg.B,), T + s + 1, dtype=torch.int32, device="cuda") for s in range(steps)]
 
-    def run(case, ws, outs):
+    def run(case, ws, outs, fused_step=False):
         for s in range(steps):
+            if fused_step:
+                kv.append_decode_attn(case.desc, ks[s], vs[s], pos[s], qs[s], case.pk, case.pv, case.lat_k,
+                                      case.lat_v, lens[s], out=outs[s], workspace=ws)
+                continue
             kv.append(case.desc, ks[s], vs[s], pos[s], case.pk, case.pv, case.lat_k, case.lat_v)
             kv.decode_attn(case.desc, qs[s], case.pk, case.pv, case.lat_k, case.lat_v, lens[s], out=outs[s],
                            workspace=ws)
@@ -95,7 +101,7 @@ def test_graph_append_decode_loop_matches_eager(gpu):
     case = build_case(cfg, n_rows=T)
     ws2 = kv.alloc_workspace(case.desc)
     outs = [torch.empty((cfg.B, cfg.Hq, cfg.d), device="cuda") for _ in range(steps)]
-    g = _capture(lambda: run(case, ws2, outs))
+    g = _capture(lambda: run(case, ws2, outs, fused))
     for rep in range(3):
         for o in outs:
             o.zero_()
@@ -104,4 +110,4 @@ def test_graph_append_decode_loop_matches_eager(gpu):
         torch.cuda.synchronize()
         for s in range(steps):
             assert torch.equal(outs[s], eager[s]), (rep, s)
-    say(f"[graph] {steps}-step append + decode loop: 3 replays equal the eager loop")
+    say(f"[graph] {steps}-step append + decode loop (fused={fused}): 3 replays equal the eager loop")
