@@ -354,3 +354,33 @@ def test_latent_guard_bands(gpu):
             for t in (0, 39, 100, 101):
                 expect_canary = t not in written
                 assert bool((rows[t] == canary).all()) == expect_canary, (b, h, t)
+
+
+@pytest.mark.parametrize("lens", [[0, 1, 2999, 17, 1500, 3000], [3000, 0, 0, 0, 0, 1], [0, 0, 0, 0, 0, 0]])
+def test_ragged_lengths_with_empty_rows(gpu, lens):
+    """Per-head ranks with very uneven lengths (empty rows, one long row): oracle parity under the
+    library's plan, and the same result with a shorter fixed split (to fp32 rounding)."""
+    cfg = CONFIGS[2].scaled(B=6, T_range=(1, 3000))
+    case = build_case(cfg)
+    q = host.queries(cfg, 0, 0)
+    got = _decode(case, q, lens)
+    _check_rows(case, got, q, lens, diag_bound=2e-3)
+    other = _decode(case, q, lens, split=256)
+    nz = [b for b in range(cfg.B) if lens[b] > 0]
+    if nz:
+        assert rel_inf_rows(got[nz], other[nz]).max() <= 1e-5
+    assert np.all(got[[b for b in range(cfg.B) if lens[b] == 0]] == 0)
+
+
+def test_single_unit_long_and_many_units(gpu):
+    """One (batch row, KV head) over 20000 rows; and 640 (batch row, KV head, head group) units."""
+    cfg = CONFIGS[0].scaled(T=20000)
+    case = build_case(cfg)
+    q = host.queries(cfg, 0, 0)
+    lens = [20000]
+    _check_rows(case, _decode(case, q, lens), q, lens)
+    cfg = CONFIGS[1].scaled(B=40, Hq=64, Hkv=4, T=300)   # 40 x 4 KV heads x 4 head groups
+    case = build_case(cfg)
+    q = host.queries(cfg, 0, 0)
+    lens = host.lengths(cfg)
+    _check_rows(case, _decode(case, q, lens), q, lens, heads=[0, 3], bs=[0, 17, 39])
