@@ -100,17 +100,19 @@ typedef enum kvlr_value_mode {
  * C16 = T_cap rounded up to a multiple of 16, the block of (b, h) starts at
  * element C16 * (b * R + R_pre(h)) and holds C16 rows of r_k[h] elements.
  * Inside a block:
- *  - value latents, fp32 key latents: row-major, (t, j) at t * r + j;
+ *  - fp32 latents: row-major, (t, j) at t * r + j;
  *  - bf16 key latents: MFMA operand order, so that the decode kernel's
  *    64-lane loads read 1 KiB contiguously. With n = t % 16 and
  *    np = r / 32, 16-row group t / 16 starts at (t / 16) * 16 * r and holds,
  *    for j < 32 np: (j / 32) * 512 + ((j % 32) / 8) * 128 + n * 8 + j % 8;
  *    for the 16-channel tail jj = j - 32 np: np * 512 + (jj / 4) * 64 + n * 4 + jj % 4.
  * Blocks are contiguous, so a split of a sequence streams one byte range.
+ *  - bf16 value latents: the operand order of the decode kernel's value
+ *    product (tokens as the reduction dimension), below.
  * Joint values: the value cache holds one block of C16 rows of r elements per
  * batch row, at element C16 * b * r, read by every head of that batch row.
- * In bf16 its rows are in the operand order of the decode kernel's value
- * product (tokens as the reduction dimension): with q = (t % 16) / 4,
+ * bf16 value latents (per head and joint) are in the operand order of the
+ * decode kernels' value product: with q = (t % 16) / 4,
  * e = t % 4 and np = r / 32, 16-row group t / 16 starts at (t / 16) * 16 * r
  * and holds, for j < 32 np:
  *   (j / 32) * 512 + q * 128 + (j % 16) * 8 + ((j % 32) / 16) * 4 + e;

@@ -259,8 +259,8 @@ def k_tiled_index(T: int, r: int):
 
 
 def v_joint_index(T: int, r: int):
-    """Element offsets [T][r] of bf16 joint value latents inside a batch row's block
-    (value-product operand order, see kvlr.h)."""
+    """Element offsets [T][r] of bf16 value latents inside a block (per head, or a batch row's
+    joint block; value-product operand order, see kvlr.h)."""
     t = np.arange(T)[:, None]
     j = np.arange(r)[None, :]
     np_ = r // 32
@@ -272,12 +272,12 @@ def v_joint_index(T: int, r: int):
 
 
 def latent_rows(lat, desc: Desc, which: str, b: int, h: int):
-    """Logical latent rows [capacity][r] of (b, h) (a gather for bf16 keys and bf16 joint
-    values, a view otherwise; [capacity][q43_row_bytes(r)] stored bytes for 4/3-bit rows)."""
+    """Logical latent rows [capacity][r] of (b, h) (a gather for bf16 latents, which are stored
+    in operand order; a view otherwise; [capacity][q43_row_bytes(r)] stored bytes for 4/3-bit rows)."""
     torch = _torch()
     r = int((desc.r_k if which == "k" else desc.r_v)[h])
     blk = block_view(lat, desc, which, b, h)
-    if desc.latent_dtype == BF16 and (which == "k" or desc.value_mode == VALUES_JOINT):
+    if desc.latent_dtype == BF16:
         index = k_tiled_index if which == "k" else v_joint_index
         idx = torch.from_numpy(index(desc.capacity, r).ravel()).to(blk.device)
         return blk[idx].view(desc.capacity, r)

@@ -180,6 +180,7 @@ __global__ __launch_bounds__(256) void compress_bf16_mfma(CompressParams p) {
   const size_t lat_base = (size_t)cap_rows_of(p.cap) * ((size_t)b * (kind ? p.Sv : p.Sk) +
                                                       (kind ? p.ht.sv_pre[h] : p.ht.sk_pre[h]));
   const bool k_tiled = kOutBf16 && kind == 0;   // bf16 key latents: MFMA operand order
+  const bool v_tiled = kOutBf16 && kind == 1;   // bf16 value latents: value-product operand order
   const int tok_wg0 = blockIdx.x * kTokensPerWg;
 
   for (int it = 0; it < kWaveIters; ++it) {
@@ -207,10 +208,36 @@ __global__ __launch_bounds__(256) void compress_bf16_mfma(CompressParams p) {
 #pragma unroll
           for (int nt = 0; nt < 4; ++nt) {
             const bf16x8_t xb = __builtin_bit_cast(bf16x8_t, xin[nt][kb]);
-            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, xb, acc[nt], 0, 0, 0);
-            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, xb, acc[nt], 0, 0, 0);
+            if (v_tiled) {   // transposed product: lane ends with 4 consecutive tokens of one channel
+              acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb, ahi, acc[nt], 0, 0, 0);
+              acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb, alo, acc[nt], 0, 0, 0);
+            } else {
+              acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, xb, acc[nt], 0, 0, 0);
+              acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, xb, acc[nt], 0, 0, 0);
+            }
           }
         }
+      }
+      if (v_tiled) {
+        // lane holds tokens tw0 + 16nt + 4q4 + i (i < 4) of latent channel 16mt + n16: one
+        // 8-byte piece when the 4 tokens are whole and aligned, single values otherwise
+        uint16_t* V = static_cast<uint16_t*>(p.lat_v) + lat_base;
+        const int j = 16 * mt + n16;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const int t = tw0 + 16 * nt + 4 * q4;
+          const int row = p.start + t;
+          if (t + 3 < p.n_tok && (row & 3) == 0) {
+            const uint32_t w0 = (uint32_t)f32_to_bf16_bits(acc[nt][0]) | ((uint32_t)f32_to_bf16_bits(acc[nt][1]) << 16);
+            const uint32_t w1 = (uint32_t)f32_to_bf16_bits(acc[nt][2]) | ((uint32_t)f32_to_bf16_bits(acc[nt][3]) << 16);
+            *reinterpret_cast<uint2*>(V + v_joint_offset(row, j, r)) = make_uint2(w0, w1);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (t + i < p.n_tok) V[v_joint_offset(row + i, j, r)] = f32_to_bf16_bits(acc[nt][i]);
+          }
+        }
+        continue;
       }
       // lane holds latent channels 16mt + 4q4 + i (i < 4) of token tw0 + 16nt + n16
 #pragma unroll
@@ -300,7 +327,7 @@ __global__ __launch_bounds__(256) void compress_valu(CompressParams p) {
   }
   const size_t lat_base = (size_t)cap_rows_of(p.cap) * ((size_t)b * S + s_pre);
   const bool k_tiled = p.out_bf16 && kind == 0;
-  const bool v_tiled = p.out_bf16 && joint;   // joint bf16 values: value-MFMA operand order
+  const bool v_tiled = p.out_bf16 && kind == 1;   // bf16 values: value-product operand order
 #pragma unroll
   for (int k = 0; k < kValuOuts; ++k) {
     const int idx = threadIdx.x + k * blockDim.x;
@@ -361,7 +388,7 @@ __global__ __launch_bounds__(128) void append_kernel(AppendParams p) {
   if (j >= r) return;
   const size_t base = (size_t)cap_rows_of(p.cap) * ((size_t)b * S + s_pre);
   const bool k_tiled = p.out_bf16 && kind == 0;
-  const bool v_tiled = p.out_bf16 && joint;
+  const bool v_tiled = p.out_bf16 && kind == 1;
   const size_t off = base + (k_tiled   ? k_tiled_offset(pos, j, r)
                              : v_tiled ? v_joint_offset(pos, j, r)
                                        : (size_t)pos * r + j);

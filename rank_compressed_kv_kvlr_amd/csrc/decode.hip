@@ -303,7 +303,7 @@ __device__ void append_rows(const DecodeParams& p, int b, int h, int rk, int rv,
       K[k_tiled_offset(pos, j, rk)] = f32_to_bf16_bits(acc);
     } else {
       uint16_t* V = static_cast<uint16_t*>(p.app_v) + rows * ((size_t)b * p.Sv + p.ht.sv_pre[h]);
-      V[(size_t)pos * rv + j] = f32_to_bf16_bits(acc);
+      V[v_joint_offset(pos, j, rv)] = f32_to_bf16_bits(acc);
     }
   }
   __builtin_amdgcn_s_waitcnt(0);   // the new rows are in L2 before any wave of this workgroup loads a tile
@@ -311,19 +311,33 @@ __device__ void append_rows(const DecodeParams& p, int b, int h, int rk, int rv,
 }
 
 // ---------------------------------------------------------------------------
-// bf16 latents: MFMA scores, VALU value mix
+// bf16 latents: scores and value mix on MFMA
 // ---------------------------------------------------------------------------
 // RB: rank bound (32, 64, 96 or 128) sizing the register tiles; the actual
 // per-head ranks are runtime values <= RB (multiples of 16).
-// TT: tokens per wave iteration (32 or 64), i.e. TT/16 MFMA column blocks.
+// TT: tokens per wave step (16 or 32), i.e. TT/16 blocks of 16 tokens.
+// Waves take TT-token steps of the split round robin. Per 16-token block:
+//  - scores transposed, S^T = K_lat q~^T (v_mfma_f32_16x16x32_bf16, key rows as
+//    the A operand straight from HBM in their operand-order layout, q~ as B with
+//    the workgroup's query heads in columns 0..3, a high and a low bf16 part);
+//    a 16-channel tail uses v_mfma_f32_16x16x16_bf16. Lane (n, q) then holds
+//    tokens 4q .. 4q + 3 of query head n;
+//  - online softmax per query head in the log2 domain (in-lane over 4 tokens,
+//    then two cross-lane steps);
+//  - value product o_lat[head][ch] += p V_lat on v_mfma_f32_16x16x16_bf16: the
+//    softmax weights are already the A operand (tokens as the reduction
+//    dimension; high and low bf16 parts), the value rows are stored in that
+//    product's B-operand order (v_joint_offset), 16 bytes per lane per channel
+//    pair. Value rows past the sequence end may hold any bits and are zeroed.
+// The waves' states meet in LDS and leave one record per query head and split.
 template <int RB, int TT>
 __global__ __launch_bounds__(256) void decode_split_bf16(DecodeParams p) {
   constexpr int NB = TT / 16;
-  constexpr int NP = RB / 32;                 // full 32-channel key pairs
-  constexpr int NIT = value_iters_bound(RB, TT);  // bound on value iterations (see n_it below)
+  constexpr int NP = RB / 32;                 // key channel pairs bound
+  constexpr int kVP = RB / 32;                // value channel pairs bound (a tail fills half a pair)
+  constexpr int kCT = RB / 16;                // value column tiles bound
   constexpr int QTS = RB;                     // q~ LDS row stride
-  constexpr int kRS = 36;   // per-lane stride of the wave reduction: 4 heads x 8 channels + 4 (bank spread)
-  __shared__ __attribute__((aligned(16))) float smem[kWaves * 64 * kRS + 64 > kTailLds ? kWaves * 64 * kRS + 64 : kTailLds];
+  __shared__ __attribute__((aligned(16))) float smem[kTailLds];
 
   const int s = blockIdx.x;
   const int h = blockIdx.y / p.n_head_groups;
@@ -344,106 +358,91 @@ __global__ __launch_bounds__(256) void decode_split_bf16(DecodeParams p) {
     return;
   }
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = lane & 15, q4 = lane >> 4;
-
-  const int np = rk >> 5;           // full 32-channel pairs
-  const int tail = (rk >> 4) & 1;   // one trailing 16-channel block
-  // ---- value-side lane mapping: C chunks of 8 channels per row
-  const int C = rv >> 3;
-  const int rpi = 64 / C;                 // rows per load instruction
-  const int ro = lane / C, cch = lane - ro * C;
-  const bool v_active = ro < rpi;
-  const int n_it = (TT + rpi - 1) / rpi;  // <= NIT
-
+  const int np = rk >> 5, ktail = (rk >> 4) & 1;
+  const int vnp = rv >> 5, vtail = (rv >> 4) & 1;
   const size_t rows = cap_rows_of(p.cap);
   const uint16_t* Kb = static_cast<const uint16_t*>(p.lat_k) + rows * ((size_t)b * p.Sk + p.ht.sk_pre[h]);
   const uint16_t* Vb = static_cast<const uint16_t*>(p.lat_v) + rows * ((size_t)b * p.Sv + p.ht.sv_pre[h]);
 
-  float* p_lds = smem + wave * (TT * 4);  // [TT tokens][4 heads] per wave
-
-  float m[4], l[4], acc[4][8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m[i] = kNegInf;
-    l[i] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
-  }
-
-  u32x4_t kreg[NB][NP];
-  u32x2_t ktail[NB];
-  u32x4_t vreg[NIT];
-
-  // key latents are stored in MFMA operand order (k_tiled_offset): lane l reads
-  // 16 contiguous bytes at 16 l within each 1 KiB pair block of a 16-row block.
-  // Blocks entirely past the valid rows re-read the last valid block; their
-  // scores are masked.
+  // blocks wholly past the valid rows re-read the last valid block; their tokens are masked
   const int last_blk = (t_end - 1) >> 4;
+  u32x4_t kreg[NB][NP];
+  u32x2_t ktl[NB];
+  u32x4_t vreg[NB][kVP];
   auto load_k = [&](int t0) {
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
-      const int kb16 = min((t0 >> 4) + blk, last_blk);
-      const uint16_t* kblk = Kb + (size_t)kb16 * 16 * rk;
+      const uint16_t* kb = Kb + (size_t)min((t0 >> 4) + blk, last_blk) * 16 * rk;
 #pragma unroll
       for (int pp = 0; pp < NP; ++pp)
-        if (pp < np) kreg[blk][pp] = load_stream16(kblk + pp * 512 + lane * 8);
-      if (tail) ktail[blk] = load_stream8(kblk + np * 512 + lane * 4);
+        if (pp < np) kreg[blk][pp] = load_stream16(kb + pp * 512 + lane * 8);
+      if (ktail) ktl[blk] = load_stream8(kb + np * 512 + lane * 4);
     }
   };
   auto load_v = [&](int t0) {
 #pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      if (it < n_it) {
-        const int r = it * rpi + ro;
-        const int t = min(t0 + min(r, TT - 1), t_end - 1);
-        vreg[it] = load_stream16(Vb + (size_t)t * rv + 8 * cch);
+    for (int blk = 0; blk < NB; ++blk) {
+      const uint16_t* vb = Vb + (size_t)min((t0 >> 4) + blk, last_blk) * 16 * rv;
+#pragma unroll
+      for (int c = 0; c < kVP; ++c) {
+        if (c < vnp) {
+          vreg[blk][c] = load_stream16(vb + c * 512 + lane * 8);
+        } else if (c == vnp && vtail) {
+          const u32x2_t t = load_stream8(vb + vnp * 512 + lane * 4);
+          vreg[blk][c] = u32x4_t{t.x, t.y, 0u, 0u};
+        } else {
+          vreg[blk][c] = u32x4_t{0u, 0u, 0u, 0u};   // channels past the rank: the products stay zero
+        }
       }
     }
   };
 
-  // the first tile's loads do not depend on q~: issue them before the prologue
+  // the first step's loads do not depend on q~: issue them before the prologue
   int t0 = t_begin + wave * TT;
   if (t0 < t_end) {
     load_k(t0);
     load_v(t0);
   }
 
-  // ---- prologue: q~ into LDS, then MFMA A operands (hi/lo) into registers
+  // ---- prologue: q~ into LDS, then this lane's query head as B operands (hi/lo)
   float* q_lds = smem;                          // [4][d]  (d <= 256)
   float* qt_lds = smem + kHeadsPerWg * 256;     // [4][QTS]
   float* qred = qt_lds + kHeadsPerWg * QTS;     // [4 waves][4][QTS]
   project_query<RB>(p, b, h, hq0, gpw, rk, q_lds, qred, qt_lds);
-
+  const bool q_ok = n16 < gpw;
+  const int qrow = q_ok ? n16 : 0;
   bf16x8_t a_hi[NP], a_lo[NP];
   bf16x4_t t_hi, t_lo;
 #pragma unroll
-  for (int pp = 0; pp < NP; ++pp) {
+  for (int pp = 0; pp < NP; ++pp)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float x = (n16 < kHeadsPerWg) ? qt_lds[n16 * QTS + 32 * pp + 8 * q4 + e] : 0.f;
-      if (32 * pp + 8 * q4 + e >= rk) x = 0.f;
+      const float x = q_ok ? qt_lds[qrow * QTS + 32 * pp + 8 * q4 + e] : 0.f;   // zero past rk
       const uint16_t hi = f32_to_bf16_bits(x);
-      const uint16_t lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
       a_hi[pp][e] = (short)hi;
-      a_lo[pp][e] = (short)lo;
+      a_lo[pp][e] = (short)f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
     }
-  }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int j = 32 * np + 4 * q4 + e;
-    float x = (n16 < kHeadsPerWg && tail && j < rk) ? qt_lds[n16 * QTS + j] : 0.f;
+    const float x = (q_ok && ktail) ? qt_lds[qrow * QTS + j] : 0.f;
     const uint16_t hi = f32_to_bf16_bits(x);
-    const uint16_t lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
     t_hi[e] = (short)hi;
-    t_lo[e] = (short)lo;
+    t_lo[e] = (short)f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
   }
   __syncthreads();   // LDS is reused below
 
+  float m = kNegInf, l = 0.f;
+  f32x4_t acc[kCT];
+#pragma unroll
+  for (int c = 0; c < kCT; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   for (; t0 < t_end; t0 += kWaves * TT) {
     const int t_next = t0 + kWaves * TT;
-    // ---- scores on MFMA
+    // ---- S^T[token][query head] per block
     f32x4_t sc[NB];
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
@@ -452,122 +451,112 @@ __global__ __launch_bounds__(256) void decode_split_bf16(DecodeParams p) {
       for (int pp = 0; pp < NP; ++pp) {
         if (pp < np) {
           const bf16x8_t kb = __builtin_bit_cast(bf16x8_t, kreg[blk][pp]);
-          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi[pp], kb, d, 0, 0, 0);
-          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo[pp], kb, d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, a_hi[pp], d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, a_lo[pp], d, 0, 0, 0);
         }
       }
-      if (tail) {
-        const bf16x4_t kb = __builtin_bit_cast(bf16x4_t, ktail[blk]);
-        d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t_hi, kb, d, 0, 0, 0);
-        d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t_lo, kb, d, 0, 0, 0);
+      if (ktail) {
+        const bf16x4_t kb = __builtin_bit_cast(bf16x4_t, ktl[blk]);
+        d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kb, t_hi, d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kb, t_lo, d, 0, 0, 0);
       }
       sc[blk] = d;
     }
     if (t_next < t_end) load_k(t_next);   // key registers are free again
 
-    // ---- online softmax (lanes 0..15 hold heads 0..3 of 16 tokens per block)
-    float alpha[4];
+    // ---- online softmax: lane (n16, q4) holds tokens t0 + 16 blk + 4 q4 + i of query head n16
+    float mx = kNegInf;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float mx = kNegInf;
+    for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
-      for (int blk = 0; blk < NB; ++blk) {
-        const bool valid = (t0 + 16 * blk + n16) < t_end;
+      for (int i = 0; i < 4; ++i) {
+        const bool valid = q_ok && (t0 + 16 * blk + 4 * q4 + i) < t_end;
         sc[blk][i] = valid ? sc[blk][i] : kNegInf;
         mx = fmaxf(mx, sc[blk][i]);
       }
-      mx = row16_allreduce<true>(mx);
-      const float m_new = fmaxf(m[i], mx);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      alpha[i] = fast_exp2(m[i] - m_use);
-      float ls = 0.f;
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m, mx);
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+    const float alpha = q_ok ? fast_exp2(m - m_use) : 1.f;
+    bf16x4_t p_hi[NB], p_lo[NB];
+    float ls = 0.f;
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pr = fast_exp2(sc[blk][i] - m_use);   // masked: exp2(-inf) = 0
+        ls += pr;
+        const uint16_t hi = f32_to_bf16_bits(pr);
+        p_hi[blk][i] = (short)hi;
+        p_lo[blk][i] = (short)f32_to_bf16_bits(pr - bf16_bits_to_f32(hi));
+      }
+    l = fmaf(l, alpha, ls);
+    m = m_new;
+    // accumulator rows are query heads 4 q4 + i; their factors sit in lanes 4 q4 + i
+    if (__ballot(alpha != 1.f)) {
+      float ar[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * q4 + i, 64);
+#pragma unroll
+      for (int c = 0; c < kCT; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[c][i] *= ar[i];
+    }
+
+    // ---- value product; rows past the sequence end hold arbitrary bits: zeroed
+    if (t0 + TT > t_end) {
 #pragma unroll
       for (int blk = 0; blk < NB; ++blk) {
-        const float pr = fast_exp2(sc[blk][i] - m_use);
-        sc[blk][i] = pr;
-        ls += pr;
-      }
-      l[i] = fmaf(l[i], alpha[i], ls);
-      m[i] = m_new;
-    }
-    if (q4 == 0) {
+        const int nv = t_end - t0 - 16 * blk - 4 * q4;   // valid tokens among this lane's 4
+        const uint32_t m01 = (nv > 0 ? 0xFFFFu : 0u) | (nv > 1 ? 0xFFFF0000u : 0u);
+        const uint32_t m23 = (nv > 2 ? 0xFFFFu : 0u) | (nv > 3 ? 0xFFFF0000u : 0u);
 #pragma unroll
-      for (int blk = 0; blk < NB; ++blk)
-        *reinterpret_cast<float4*>(p_lds + (16 * blk + n16) * 4) =
-            make_float4(sc[blk][0], sc[blk][1], sc[blk][2], sc[blk][3]);
-    }
-    // scale factors live in lane 0 (group of heads 0..3)
-    float a_s[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a_s[i] = readlane_f(alpha[i], 0);
-    if (a_s[0] != 1.f || a_s[1] != 1.f || a_s[2] != 1.f || a_s[3] != 1.f) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[i][e] *= a_s[i];
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // ---- value mix on VALU
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      if (it < n_it) {
-        const int r = it * rpi + ro;
-        if (v_active && r < TT) {
-          const float4 pw = *reinterpret_cast<const float4*>(p_lds + r * 4);
-          const u32x4_t w = vreg[it];
-          const float v[8] = {bf16lo_to_f32(w.x), bf16hi_to_f32(w.x), bf16lo_to_f32(w.y), bf16hi_to_f32(w.y),
-                              bf16lo_to_f32(w.z), bf16hi_to_f32(w.z), bf16lo_to_f32(w.w), bf16hi_to_f32(w.w)};
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            acc[0][e] = fmaf(pw.x, v[e], acc[0][e]);
-            acc[1][e] = fmaf(pw.y, v[e], acc[1][e]);
-            acc[2][e] = fmaf(pw.z, v[e], acc[2][e]);
-            acc[3][e] = fmaf(pw.w, v[e], acc[3][e]);
-          }
+        for (int c = 0; c < kVP; ++c) {
+          vreg[blk][c].x &= m01;
+          vreg[blk][c].y &= m23;
+          vreg[blk][c].z &= m01;
+          vreg[blk][c].w &= m23;
         }
       }
     }
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+      for (int c = 0; c < kVP; ++c) {
+        const bf16x4_t v0 = __builtin_bit_cast(bf16x4_t, u32x2_t{vreg[blk][c].x, vreg[blk][c].y});
+        const bf16x4_t v1 = __builtin_bit_cast(bf16x4_t, u32x2_t{vreg[blk][c].z, vreg[blk][c].w});
+        acc[2 * c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(p_hi[blk], v0, acc[2 * c], 0, 0, 0);
+        acc[2 * c + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(p_hi[blk], v1, acc[2 * c + 1], 0, 0, 0);
+        acc[2 * c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(p_lo[blk], v0, acc[2 * c], 0, 0, 0);
+        acc[2 * c + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(p_lo[blk], v1, acc[2 * c + 1], 0, 0, 0);
+      }
     if (t_next < t_end) load_v(t_next);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 
   BasisPrefetch<RB> pf;
   prefetch_basis<RB>(p, h, rv, pf);
-  // ---- workgroup merge of the 4 waves
+  // ---- workgroup merge of the 4 waves: rows 0..3 of each wave's accumulators (q4 = 0 lanes)
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  float* red = smem;                          // [wave][head][RB]
+  float* wm = smem + kWaves * kHeadsPerWg * RB;
+  float* wl = wm + kWaves * kHeadsPerWg;
+  if (q4 == 0) {
+    const int n_ct = rv >> 4;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) l[i] = row16_allreduce<false>(l[i]);
-  __syncthreads();
-  float* red = smem;                          // [wave][lane][kRS]: (head, channel) at head * 8 + channel
-  float* wm = smem + kWaves * 64 * kRS;       // [wave][head]
-  float* wl = wm + 16;
+    for (int c = 0; c < kCT; ++c)
+      if (c < n_ct)
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int e = 0; e < 8; e += 4)
-      *reinterpret_cast<float4*>(red + (wave * 64 + lane) * kRS + i * 8 + e) =
-          make_float4(acc[i][e], acc[i][e + 1], acc[i][e + 2], acc[i][e + 3]);
-  if (lane == 0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      wm[wave * 4 + i] = m[i];
-      wl[wave * 4 + i] = l[i];
+        for (int i = 0; i < kHeadsPerWg; ++i) red[(wave * kHeadsPerWg + i) * RB + 16 * c + n16] = acc[c][i];
+    if (n16 < kHeadsPerWg) {
+      wm[wave * kHeadsPerWg + n16] = m;
+      wl[wave * kHeadsPerWg + n16] = l;
     }
   }
   __syncthreads();
-  merge_waves_and_store(p, b, hq0, gpw, s, rv, wm, wl, [&](int w, int g, int j) {
-    const int c = j >> 3, e = j & 7;
-    const float* base = red + (w * 64 + c) * kRS + g * 8 + e;
-    const int step = C * kRS;
-    float sum = 0.f;
-#pragma unroll 8
-    for (int r = 0; r < rpi; ++r) sum += base[r * step];   // rows r C + c of wave w
-    return sum;
-  });
+  merge_waves_and_store(p, b, hq0, gpw, s, rv, wm, wl,
+                        [&](int w, int g, int j) { return red[(w * kHeadsPerWg + g) * RB + j]; });
   finish_split<RB>(p, b, h, hg, hq0, gpw, rv, smem, pf);
 }
 
