@@ -123,10 +123,10 @@ def measure_workloads(kv, torch, np):
     """The other workloads, each with its own algorithmic bytes: one decode over ragged
     sequences with per-head ranks; 64 x (append + decode) over 128K rows; a 32-layer decode
     step. The last two also as one captured HIP graph replayed (launch gaps removed)."""
-    from synth import CONFIGS, host
+    from synth import LLAMA3_32_LAYERS, LONG_CONTEXT_128K, PER_HEAD_RAGGED, host
     out = {}
     print("[bench] workload per_head_ranks_ragged", file=sys.stderr, flush=True)
-    cfg = CONFIGS[2]
+    cfg = PER_HEAD_RAGGED
     c = _build(kv, torch, cfg, chunk=4096)
     lens_np = host.lengths(cfg)
     lens = torch.from_numpy(lens_np).cuda()
@@ -142,7 +142,7 @@ def measure_workloads(kv, torch, np):
     torch.cuda.empty_cache()
 
     print("[bench] workload long_context_128k", file=sys.stderr, flush=True)
-    cfg = CONFIGS[3]
+    cfg = LONG_CONTEXT_128K
     T, S = cfg.T, cfg.decode_steps
     c = _build(kv, torch, cfg, n_rows=T, chunk=16384)
     ks = [c["gen"].make("k", cfg.B, 1, t0=T + s)[:, 0].contiguous() for s in range(S)]
@@ -177,7 +177,7 @@ def measure_workloads(kv, torch, np):
     torch.cuda.empty_cache()
 
     print("[bench] workload llama3_8b_32_layers", file=sys.stderr, flush=True)
-    cfg = CONFIGS[4]
+    cfg = LLAMA3_32_LAYERS
     layers = []
     for layer in range(cfg.n_layers):
         c = _build(kv, torch, cfg, layer=layer)
@@ -343,10 +343,10 @@ def main():
     import torch
 
     import rank_compressed_kv_kvlr_amd as kv
-    from synth import CONFIGS, host
+    from synth import LLAMA3_LAYER_32K, host
     from synth.device import KVGenerator
 
-    cfg = CONFIGS[1]
+    cfg = LLAMA3_LAYER_32K
     B, T, Hkv, d = cfg.B, cfg.T, cfg.Hkv, cfg.d
     rk, rv = host.ranks(cfg)
     PK, PV = host.bases(cfg)

@@ -10,4 +10,5 @@ that is implemented twice, once in numpy and once as a HIP kernel
 (``csrc/synth_gen.hip``), so that any slice of a multi-GiB workload can be
 regenerated bit for bit on the host without copying it back from the GPU.
 """
-from .configs import CONFIGS, Config, config_by_id  # noqa: F401
+from .configs import (CONFIGS, LLAMA3_32_LAYERS, LLAMA3_LAYER_32K, LONG_CONTEXT_128K,  # noqa: F401
+                      PER_HEAD_RAGGED, SINGLE_HEAD_F32, WORKLOADS, Config)

@@ -19,7 +19,7 @@ from typing import Optional, Tuple
 
 @dataclass(frozen=True)
 class Config:
-    cid: int                 # workload id 0..4 (seeds are keyed on it)
+    cid: int                 # seed key of the workload (every random stream is keyed on it)
     name: str
     B: int                   # batch
     Hq: int                  # query heads
@@ -89,5 +89,7 @@ CONFIGS = (
 )
 
 
-def config_by_id(cid: int) -> Config:
-    return CONFIGS[cid]
+SINGLE_HEAD_F32, LLAMA3_LAYER_32K, PER_HEAD_RAGGED, LONG_CONTEXT_128K, LLAMA3_32_LAYERS = CONFIGS
+
+# The workloads by name.
+WORKLOADS = {c.name: c for c in CONFIGS}

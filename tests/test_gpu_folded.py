@@ -6,7 +6,7 @@ from __future__ import annotations
 import numpy as np
 import pytest
 
-from synth import CONFIGS, host
+from synth import LLAMA3_LAYER_32K, WORKLOADS, host
 from tests.gpu_cases import build_case, rel_inf_rows, say, tolerance
 
 pytestmark = pytest.mark.gpu
@@ -47,15 +47,15 @@ def _check(case, got, q_lat, lens, bs=None, heads=None):
     return worst
 
 
-@pytest.mark.parametrize("cid,extra", [
-    (0, dict(T=2047)),
-    (1, dict(B=2, T=1000)),
-    (2, dict(B=4, T_range=(1, 700))),
-    (1, dict(B=2, Hq=10, Hkv=2, T=333, r_k=48, r_v=112)),
-    (0, dict(B=2, Hq=3, Hkv=3, T=300, r_k=12, r_v=32)),
+@pytest.mark.parametrize("wl,extra", [
+    ("single_head_f32", dict(T=2047)),
+    ("llama3_8b_layer_32k", dict(B=2, T=1000)),
+    ("per_head_ranks_ragged", dict(B=4, T_range=(1, 700))),
+    ("llama3_8b_layer_32k", dict(B=2, Hq=10, Hkv=2, T=333, r_k=48, r_v=112)),
+    ("single_head_f32", dict(B=2, Hq=3, Hkv=3, T=300, r_k=12, r_v=32)),
 ])
-def test_folded_matches_oracle(gpu, cid, extra):
-    cfg = CONFIGS[cid].scaled(**extra)
+def test_folded_matches_oracle(gpu, wl, extra):
+    cfg = WORKLOADS[wl].scaled(**extra)
     case = build_case(cfg)
     lens = host.lengths(cfg)
     q_lat = case.folded_queries(host.queries(cfg, 0, 0))
@@ -64,7 +64,7 @@ def test_folded_matches_oracle(gpu, cid, extra):
 
 @pytest.mark.parametrize("lens,split", [([0, 5], 64), ([1, 300], 64), ([257, 0], 0), ([300, 129], 128)])
 def test_folded_edge_lengths(gpu, lens, split):
-    cfg = CONFIGS[1].scaled(B=2, Hq=8, Hkv=2, T=300)
+    cfg = LLAMA3_LAYER_32K.scaled(B=2, Hq=8, Hkv=2, T=300)
     case = build_case(cfg)
     q_lat = case.folded_queries(host.queries(cfg, 0, 0))
     lens = np.array(lens, np.int32)
@@ -73,16 +73,16 @@ def test_folded_edge_lengths(gpu, lens, split):
     _check(case, got, q_lat, lens)
 
 
-@pytest.mark.parametrize("cid", [1, 2])
-def test_folded_back_projects_to_decode_attn(gpu, cid):
+@pytest.mark.parametrize("wl", ["llama3_8b_layer_32k", "per_head_ranks_ragged"])
+def test_folded_back_projects_to_decode_attn(gpu, wl):
     """o_lat P_V^T from the folded call equals kvlr_decode_attn on q with q_lat = q P_K.
 
     Both sides run the same split records; the back-projection order differs, so fp32
     rounding may differ in the last bits."""
     import torch
     kv = _kv()
-    extra = {1: dict(B=2, Hq=16, Hkv=2, T=700), 2: dict(B=3, T_range=(10, 900))}[cid]
-    cfg = CONFIGS[cid].scaled(**extra)
+    extra = {"llama3_8b_layer_32k": dict(B=2, Hq=16, Hkv=2, T=700), "per_head_ranks_ragged": dict(B=3, T_range=(10, 900))}[wl]
+    cfg = WORKLOADS[wl].scaled(**extra)
     case = build_case(cfg)
     lens = host.lengths(cfg)
     q = host.queries(cfg, 0, 0)
@@ -107,7 +107,7 @@ def test_folded_counters_left_zero(gpu):
     """A folded call leaves the merge counters at zero, so the workspace is reusable by either call."""
     import torch
     kv = _kv()
-    cfg = CONFIGS[1].scaled(B=2, Hq=8, Hkv=2, T=500)
+    cfg = LLAMA3_LAYER_32K.scaled(B=2, Hq=8, Hkv=2, T=500)
     case = build_case(cfg)
     lens = host.lengths(cfg)
     q_lat = case.folded_queries(host.queries(cfg, 0, 0))

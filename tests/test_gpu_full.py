@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import oracle
-from synth import CONFIGS, host
+from synth import LLAMA3_32_LAYERS, LLAMA3_LAYER_32K, LONG_CONTEXT_128K, PER_HEAD_RAGGED, SINGLE_HEAD_F32, host
 from synth.device import KVGenerator
 from tests.gpu_cases import build_case, rel_l2_rows, say, tolerance
 
@@ -52,7 +52,7 @@ def _check(case, got, q, lens, units):
 
 
 def test_full_single_head_f32(gpu):
-    cfg = CONFIGS[0]
+    cfg = SINGLE_HEAD_F32
     case = build_case(cfg)
     q = host.queries(cfg)
     lens = host.lengths(cfg)
@@ -60,7 +60,7 @@ def test_full_single_head_f32(gpu):
 
 
 def test_full_llama3_layer_32k(gpu):
-    cfg = CONFIGS[1]
+    cfg = LLAMA3_LAYER_32K
     case = build_case(cfg, chunk=8192)
     q = host.queries(cfg)
     lens = host.lengths(cfg)
@@ -84,7 +84,7 @@ def test_full_llama3_layer_32k(gpu):
 
 
 def test_full_per_head_ranks_ragged(gpu):
-    cfg = CONFIGS[2]
+    cfg = PER_HEAD_RAGGED
     case = build_case(cfg, chunk=4096)
     q = host.queries(cfg)
     lens = host.lengths(cfg)
@@ -100,7 +100,7 @@ def test_full_long_context_prefill_and_64_steps(gpu):
     """Prefill-compress 131072 tokens, then 64 x (append one token, attend over all rows)."""
     import torch
     kv = _kv()
-    cfg = CONFIGS[3]
+    cfg = LONG_CONTEXT_128K
     T = cfg.T
     case = build_case(cfg, n_rows=T, chunk=16384)
     gen = KVGenerator(cfg, 0)
@@ -137,7 +137,7 @@ def test_full_long_context_prefill_and_64_steps(gpu):
 def test_full_32_layers(gpu):
     """All 32 layers, each with its own bases and (r_k, r_v) from the 50%-budget profile."""
     import torch
-    cfg = CONFIGS[4]
+    cfg = LLAMA3_32_LAYERS
     prof = host.rank_profile(cfg)
     assert int(prof.sum()) == 4096
     worst = 0.0

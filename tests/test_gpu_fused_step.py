@@ -6,7 +6,7 @@ from __future__ import annotations
 import numpy as np
 import pytest
 
-from synth import CONFIGS, host
+from synth import LLAMA3_LAYER_32K, SINGLE_HEAD_F32, WORKLOADS, host
 from tests.gpu_cases import build_case, say, tolerance
 
 pytestmark = pytest.mark.gpu
@@ -57,14 +57,14 @@ def _run_steps(cfg, steps, split, pos_shift=None):
     return fused_case, q.cpu().numpy(), lens.cpu().numpy(), got.cpu().numpy().astype(np.float64)
 
 
-@pytest.mark.parametrize("cid,extra,steps,split", [
-    (3, dict(B=2, T=1000, decode_steps=6), 6, 128),        # r 48/80 (key and value tails), row mid-split
-    (1, dict(B=2, T=255, decode_steps=4), 4, 0),           # rows cross a split boundary (library plan)
-    (1, dict(B=2, Hq=32, Hkv=2, T=300, decode_steps=3), 3, 64),   # G = 16: four head groups write the row
-    (1, dict(B=1, d=64, T=90, decode_steps=3), 3, 64),     # head_dim 64
+@pytest.mark.parametrize("wl,extra,steps,split", [
+    ("long_context_128k", dict(B=2, T=1000, decode_steps=6), 6, 128),        # r 48/80 (key and value tails), row mid-split
+    ("llama3_8b_layer_32k", dict(B=2, T=255, decode_steps=4), 4, 0),           # rows cross a split boundary (library plan)
+    ("llama3_8b_layer_32k", dict(B=2, Hq=32, Hkv=2, T=300, decode_steps=3), 3, 64),   # G = 16: four head groups write the row
+    ("llama3_8b_layer_32k", dict(B=1, d=64, T=90, decode_steps=3), 3, 64),     # head_dim 64
 ])
-def test_fused_step_equals_append_then_decode(gpu, cid, extra, steps, split):
-    cfg = CONFIGS[cid].scaled(**extra)
+def test_fused_step_equals_append_then_decode(gpu, wl, extra, steps, split):
+    cfg = WORKLOADS[wl].scaled(**extra)
     case, q, lens, got = _run_steps(cfg, steps, split)
     metric, tol = tolerance(cfg)
     worst = 0.0
@@ -79,6 +79,6 @@ def test_fused_step_equals_append_then_decode(gpu, cid, extra, steps, split):
 def test_fused_step_other_rows_and_caches(gpu):
     """Rows written inside the cache (overwrites), a row outside it (nothing written), and the
     caches that take the two-launch form (fp32 latents) give the separate calls' result."""
-    cfg = CONFIGS[1].scaled(B=3, T=200, decode_steps=2)
+    cfg = LLAMA3_LAYER_32K.scaled(B=3, T=200, decode_steps=2)
     _run_steps(cfg, 2, 64, pos_shift=[0, -77, 2 - 200 + cfg.capacity])   # row T+s, T+s-77, capacity+s
-    _run_steps(CONFIGS[0].scaled(T=300, decode_steps=2), 2, 64)
+    _run_steps(SINGLE_HEAD_F32.scaled(T=300, decode_steps=2), 2, 64)

@@ -6,7 +6,7 @@ from __future__ import annotations
 import numpy as np
 import pytest
 
-from synth import CONFIGS, host
+from synth import LLAMA3_32_LAYERS, LONG_CONTEXT_128K, host
 from synth.device import KVGenerator
 from tests.gpu_cases import build_case, say
 
@@ -37,7 +37,7 @@ def test_graph_multi_layer_step_matches_eager(gpu):
     eager work in between; every replay equals the eager result bit for bit."""
     import torch
     kv = _kv()
-    cfg = CONFIGS[4].scaled(B=4, T=700)
+    cfg = LLAMA3_32_LAYERS.scaled(B=4, T=700)
     layers = []
     for layer in range(4):
         case = build_case(cfg, layer=layer)
@@ -72,7 +72,7 @@ def test_graph_append_decode_loop_matches_eager(gpu, fused):
     fused=True each step is one kvlr_append_decode_attn call, compared with the two-call loop."""
     import torch
     kv = _kv()
-    cfg = CONFIGS[3].scaled(T=2000, decode_steps=8)
+    cfg = LONG_CONTEXT_128K.scaled(T=2000, decode_steps=8)
     steps = cfg.decode_steps
     T = cfg.T
     gen = KVGenerator(cfg, 0)

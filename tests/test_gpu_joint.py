@@ -8,7 +8,7 @@ import pytest
 from oracle import joint as jo
 from oracle import kvlr_oracle as ko
 from oracle import quant as qo
-from synth import CONFIGS, host
+from synth import LLAMA3_LAYER_32K, SINGLE_HEAD_F32, WORKLOADS, host
 from synth.device import KVGenerator
 from tests.gpu_cases import bases32, rel_inf_rows, rel_l2_rows, say, tolerance
 
@@ -128,7 +128,7 @@ def test_joint_latents_match_oracle(gpu):
     """Joint value latents from prefill compression and append: sum over heads of V_h P_J[h]."""
     import torch
     kv = _kv()
-    cfg = CONFIGS[1].scaled(B=2, Hq=8, Hkv=4, T=200)
+    cfg = LLAMA3_LAYER_32K.scaled(B=2, Hq=8, Hkv=4, T=200)
     case = _joint_case(cfg, 96, n_rows=199)
     k_new = case["gen"].make("k", cfg.B, 1, t0=199)[:, 0].contiguous()
     v_new = case["gen"].make("v", cfg.B, 1, t0=199)[:, 0].contiguous()
@@ -150,19 +150,19 @@ def test_joint_latents_match_oracle(gpu):
 # full-rank keys, one token holding up to 22% of the weight) those flips move the
 # output by 4.9e-3, the same figure a CPU model of that compression gives. The kernel
 # arithmetic itself stays near 1e-4 (the other cases).
-@pytest.mark.parametrize("cid,extra,rj,diag", [
-    (1, dict(B=2, T=1000), 128, 2e-3),
-    (1, dict(B=3, Hq=12, Hkv=3, T=777), 48, 2e-3),
-    (2, dict(B=3, T_range=(1, 600)), 64, 2e-3),            # per-head key ranks 16..96
-    (1, dict(B=2, Hq=8, Hkv=8, T=300), 64, 2e-3),          # G = 1: row tiles of 4 query heads
-    (1, dict(B=2, Hq=16, Hkv=8, T=333), 80, 2e-3),         # G = 2; 16-channel value tail
-    (1, dict(B=1, Hq=30, Hkv=5, T=517), 112, 2e-3),        # G = 6: KV heads straddle the row tiles
-    (1, dict(B=2, Hq=32, Hkv=2, T=250), 16, 2e-3),         # G = 16; tail-only value rank
-    (3, dict(B=1, T=700), 128, 2e-3),                      # r_k = 48: a key pair and a tail
-    (1, dict(B=2, d=64, T=400), 96, 6e-3),                 # head_dim 64 (see above)
+@pytest.mark.parametrize("wl,extra,rj,diag", [
+    ("llama3_8b_layer_32k", dict(B=2, T=1000), 128, 2e-3),
+    ("llama3_8b_layer_32k", dict(B=3, Hq=12, Hkv=3, T=777), 48, 2e-3),
+    ("per_head_ranks_ragged", dict(B=3, T_range=(1, 600)), 64, 2e-3),            # per-head key ranks 16..96
+    ("llama3_8b_layer_32k", dict(B=2, Hq=8, Hkv=8, T=300), 64, 2e-3),          # G = 1: row tiles of 4 query heads
+    ("llama3_8b_layer_32k", dict(B=2, Hq=16, Hkv=8, T=333), 80, 2e-3),         # G = 2; 16-channel value tail
+    ("llama3_8b_layer_32k", dict(B=1, Hq=30, Hkv=5, T=517), 112, 2e-3),        # G = 6: KV heads straddle the row tiles
+    ("llama3_8b_layer_32k", dict(B=2, Hq=32, Hkv=2, T=250), 16, 2e-3),         # G = 16; tail-only value rank
+    ("long_context_128k", dict(B=1, T=700), 128, 2e-3),                      # r_k = 48: a key pair and a tail
+    ("llama3_8b_layer_32k", dict(B=2, d=64, T=400), 96, 6e-3),                 # head_dim 64 (see above)
 ])
-def test_joint_decode_matches_oracle(gpu, cid, extra, rj, diag):
-    cfg = CONFIGS[cid].scaled(**extra)
+def test_joint_decode_matches_oracle(gpu, wl, extra, rj, diag):
+    cfg = WORKLOADS[wl].scaled(**extra)
     case = _joint_case(cfg, rj)
     lens = host.lengths(cfg)
     q = host.queries(cfg, 0, 0)
@@ -170,7 +170,7 @@ def test_joint_decode_matches_oracle(gpu, cid, extra, rj, diag):
 
 
 def test_joint_decode_f32(gpu):
-    cfg = CONFIGS[0].scaled(B=2, Hq=4, Hkv=2, T=300)
+    cfg = SINGLE_HEAD_F32.scaled(B=2, Hq=4, Hkv=2, T=300)
     case = _joint_case(cfg, 40, latent="f32")
     lens = np.array([300, 133], np.int32)
     q = host.queries(cfg, 0, 0)
@@ -178,7 +178,7 @@ def test_joint_decode_f32(gpu):
 
 
 def test_joint_decode_q43(gpu):
-    cfg = CONFIGS[1].scaled(B=2, T=700)
+    cfg = LLAMA3_LAYER_32K.scaled(B=2, T=700)
     case = _joint_case(cfg, 128, latent="q43")
     lens = host.lengths(cfg)
     q = host.queries(cfg, 0, 0)
@@ -189,7 +189,7 @@ def test_joint_folded_latent_output(gpu):
     """Weight absorption: o_lat = p V_lat per query head; o = o_lat P_J[h]^T."""
     import torch
     kv = _kv()
-    cfg = CONFIGS[1].scaled(B=2, Hq=16, Hkv=4, T=500)
+    cfg = LLAMA3_LAYER_32K.scaled(B=2, Hq=16, Hkv=4, T=500)
     case = _joint_case(cfg, 64)
     lens = host.lengths(cfg)
     q = host.queries(cfg, 0, 0)
@@ -208,7 +208,7 @@ def test_joint_folded_latent_output(gpu):
 
 def test_joint_decode_short_and_empty_rows(gpu):
     """Sequences of 0, 1, 15, 16, 17 rows (partial and empty 16-row blocks, empty splits)."""
-    cfg = CONFIGS[1].scaled(B=6, T=260)
+    cfg = LLAMA3_LAYER_32K.scaled(B=6, T=260)
     case = _joint_case(cfg, 128)
     lens = np.array([0, 1, 15, 16, 17, 260], np.int32)
     q = host.queries(cfg, 0, 0)
@@ -219,7 +219,7 @@ def test_joint_decode_short_and_empty_rows(gpu):
 def test_joint_decode_ignores_rows_past_the_end(gpu):
     """Rows at and past seq_lens inside the last 16-row block hold NaN bit patterns: the
     kernel masks them (keys through the scores, values by zeroing the operand)."""
-    cfg = CONFIGS[1].scaled(B=3, T=320)
+    cfg = LLAMA3_LAYER_32K.scaled(B=3, T=320)
     case = _joint_case(cfg, 128, n_rows=290, poison=True)
     lens = np.array([290, 123, 17], np.int32)
     q = host.queries(cfg, 0, 0)
@@ -232,7 +232,7 @@ def test_joint_two_stage_matches_single_call(gpu):
     """decode_partials + decode_combine run the same kernels as decode_attn: identical output."""
     import torch
     kv = _kv()
-    cfg = CONFIGS[1].scaled(B=2, T=900)
+    cfg = LLAMA3_LAYER_32K.scaled(B=2, T=900)
     case = _joint_case(cfg, 128)
     lens = np.array([900, 555], np.int32)
     q = host.queries(cfg, 0, 0)
@@ -250,7 +250,7 @@ def test_joint_two_stage_matches_single_call(gpu):
 
 def test_joint_decode_many_splits(gpu):
     """125 splits of 64 tokens: the per-head merge takes its records in two passes."""
-    cfg = CONFIGS[1].scaled(B=1, T=8000)
+    cfg = LLAMA3_LAYER_32K.scaled(B=1, T=8000)
     case = _joint_case(cfg, 128, chunk=2048)
     lens = host.lengths(cfg)
     q = host.queries(cfg, 0, 0)
@@ -260,7 +260,7 @@ def test_joint_decode_many_splits(gpu):
 def test_joint_decode_two_blocks_per_step(gpu, monkeypatch):
     """The two-block variant of the split kernel (KVLR_JOINT_BLOCKS=2, a tuning switch read
     at each call) gives the oracle's result too, including blocks past the sequence end."""
-    cfg = CONFIGS[1].scaled(B=4, T=300)
+    cfg = LLAMA3_LAYER_32K.scaled(B=4, T=300)
     case = _joint_case(cfg, 128)
     lens = np.array([300, 17, 33, 1], np.int32)
     q = host.queries(cfg, 0, 0)

@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 import oracle
-from synth import CONFIGS, host
+from synth import LLAMA3_LAYER_32K, LONG_CONTEXT_128K, PER_HEAD_RAGGED, SINGLE_HEAD_F32, WORKLOADS, host
 from tests.gpu_cases import assert_latents_close, build_case, rel_inf_rows, rel_l2_rows, say, tolerance
 
 pytestmark = pytest.mark.gpu
@@ -56,8 +56,7 @@ def _check_rows(case, got, q, lens, heads=None, bs=None, diag_bound=None):
 def test_device_generator_matches_host(gpu):
     import torch
     from synth.device import KVGenerator
-    for cid, B, n, t0 in ((0, 1, 300, 0), (1, 3, 77, 1000), (3, 2, 50, 131072)):
-        cfg = CONFIGS[cid]
+    for cfg, B, n, t0 in ((SINGLE_HEAD_F32, 1, 300, 0), (LLAMA3_LAYER_32K, 3, 77, 1000), (LONG_CONTEXT_128K, 2, 50, 131072)):
         gen = KVGenerator(cfg, 2)
         for kind in ("k", "v"):
             dev = gen.make(kind, B, n, t0=t0)
@@ -66,19 +65,19 @@ def test_device_generator_matches_host(gpu):
             got = got.view(torch.int16).numpy().view(np.uint16) if cfg.in_dtype == "bf16" else got.numpy()
             for b in range(B):
                 ref = host.kv_rows(cfg, 2, kind, b, t0, n, stats=gen.stats)
-                assert np.array_equal(got[b], ref), (cid, kind, b)
+                assert np.array_equal(got[b], ref), (cfg.name, kind, b)
 
 
-@pytest.mark.parametrize("cid,extra", [
-    (0, {}),
-    (1, dict(B=2, T=1000)),
-    (2, dict(B=3, T_range=(100, 700))),
-    (3, dict(B=2, T=2100, decode_steps=0)),
+@pytest.mark.parametrize("wl,extra", [
+    ("single_head_f32", {}),
+    ("llama3_8b_layer_32k", dict(B=2, T=1000)),
+    ("per_head_ranks_ragged", dict(B=3, T_range=(100, 700))),
+    ("long_context_128k", dict(B=2, T=2100, decode_steps=0)),
 ])
-def test_prefill_compress_matches_oracle(gpu, cid, extra):
+def test_prefill_compress_matches_oracle(gpu, wl, extra):
     import torch
     kv = _kv()
-    cfg = CONFIGS[cid].scaled(**extra)
+    cfg = WORKLOADS[wl].scaled(**extra)
     case = build_case(cfg)
     torch.cuda.synchronize()
     rk, rv = host.ranks(cfg)
@@ -92,15 +91,15 @@ def test_prefill_compress_matches_oracle(gpu, cid, extra):
                 assert_latents_close(got, X, P, cfg.latent_dtype)
 
 
-@pytest.mark.parametrize("cid,extra,diag", [
-    (0, {}, None),
-    (0, dict(T=2047), None),
-    (1, dict(B=2, T=1000), 2e-3),
-    (2, dict(B=4, T_range=(1, 700)), 2e-3),
-    (3, dict(B=2, T=1500, decode_steps=0), 2e-3),
+@pytest.mark.parametrize("wl,extra,diag", [
+    ("single_head_f32", {}, None),
+    ("single_head_f32", dict(T=2047), None),
+    ("llama3_8b_layer_32k", dict(B=2, T=1000), 2e-3),
+    ("per_head_ranks_ragged", dict(B=4, T_range=(1, 700)), 2e-3),
+    ("long_context_128k", dict(B=2, T=1500, decode_steps=0), 2e-3),
 ])
-def test_decode_matches_oracle(gpu, cid, extra, diag):
-    cfg = CONFIGS[cid].scaled(**extra)
+def test_decode_matches_oracle(gpu, wl, extra, diag):
+    cfg = WORKLOADS[wl].scaled(**extra)
     case = build_case(cfg)
     lens = host.lengths(cfg)
     q = host.queries(cfg, 0, 0)
@@ -111,7 +110,7 @@ def test_decode_matches_oracle(gpu, cid, extra, diag):
 @pytest.mark.parametrize("rk,rv", [(16, 16), (32, 128), (48, 80), (64, 64), (80, 48), (96, 112), (112, 96),
                                    (128, 32), (128, 128)])
 def test_decode_rank_sweep_bf16(gpu, rk, rv):
-    cfg = CONFIGS[1].scaled(B=2, Hq=8, Hkv=2, T=333, r_k=rk, r_v=rv)
+    cfg = LLAMA3_LAYER_32K.scaled(B=2, Hq=8, Hkv=2, T=333, r_k=rk, r_v=rv)
     case = build_case(cfg)
     lens = np.array([333, 190], np.int32)
     q = host.queries(cfg, 0, 0)
@@ -120,7 +119,7 @@ def test_decode_rank_sweep_bf16(gpu, rk, rv):
 
 @pytest.mark.parametrize("rk,rv", [(4, 4), (12, 32), (32, 8), (96, 128), (128, 64)])
 def test_decode_rank_sweep_f32(gpu, rk, rv):
-    cfg = CONFIGS[0].scaled(B=2, Hq=3, Hkv=3, T=300, r_k=rk, r_v=rv)
+    cfg = SINGLE_HEAD_F32.scaled(B=2, Hq=3, Hkv=3, T=300, r_k=rk, r_v=rv)
     case = build_case(cfg)
     lens = np.array([300, 129], np.int32)
     q = host.queries(cfg, 0, 0)
@@ -129,7 +128,7 @@ def test_decode_rank_sweep_f32(gpu, rk, rv):
 
 @pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 8, 16])
 def test_decode_query_groups(gpu, G):
-    cfg = CONFIGS[1].scaled(B=2, Hq=2 * G, Hkv=2, T=200, r_k=32, r_v=48)
+    cfg = LLAMA3_LAYER_32K.scaled(B=2, Hq=2 * G, Hkv=2, T=200, r_k=32, r_v=48)
     case = build_case(cfg)
     lens = np.array([200, 77], np.int32)
     q = host.queries(cfg, 0, 0)
@@ -138,7 +137,7 @@ def test_decode_query_groups(gpu, G):
 
 @pytest.mark.parametrize("lens", [[0, 5], [1, 2], [17, 64], [65, 129], [257, 256], [300, 1]])
 def test_decode_edge_lengths(gpu, lens):
-    cfg = CONFIGS[1].scaled(B=2, Hq=8, Hkv=2, T=300)
+    cfg = LLAMA3_LAYER_32K.scaled(B=2, Hq=8, Hkv=2, T=300)
     case = build_case(cfg)
     q = host.queries(cfg, 0, 0)
     lens = np.array(lens, np.int32)
@@ -148,7 +147,7 @@ def test_decode_edge_lengths(gpu, lens):
 
 
 def test_decode_lengths_clamped_to_capacity(gpu):
-    cfg = CONFIGS[1].scaled(B=2, Hq=8, Hkv=2, T=128)
+    cfg = LLAMA3_LAYER_32K.scaled(B=2, Hq=8, Hkv=2, T=128)
     case = build_case(cfg)
     q = host.queries(cfg, 0, 0)
     over = _decode(case, q, np.array([10 ** 6, -5], np.int32))
@@ -156,9 +155,10 @@ def test_decode_lengths_clamped_to_capacity(gpu):
     assert np.array_equal(over, exact)
 
 
-@pytest.mark.parametrize("cid", [0, 1])
-def test_split_count_invariance(gpu, cid):
-    cfg = CONFIGS[cid].scaled(B=1, T=4096) if cid == 0 else CONFIGS[1].scaled(B=1, Hq=8, Hkv=2, T=4096)
+@pytest.mark.parametrize("wl", ["single_head_f32", "llama3_8b_layer_32k"])
+def test_split_count_invariance(gpu, wl):
+    extra = dict(B=1, T=4096) if wl == "single_head_f32" else dict(B=1, Hq=8, Hkv=2, T=4096)
+    cfg = WORKLOADS[wl].scaled(**extra)
     case = build_case(cfg)
     lens = np.array([4096], np.int32)
     q = host.queries(cfg, 0, 0)
@@ -174,7 +174,7 @@ def test_gqa_equals_mha_with_repeated_heads(gpu):
     """G query heads over one KV head == G KV heads holding copies of that head's latents."""
     import torch
     kv = _kv()
-    cfg = CONFIGS[1].scaled(B=2, Hq=8, Hkv=2, T=250, r_k=48, r_v=32)
+    cfg = LLAMA3_LAYER_32K.scaled(B=2, Hq=8, Hkv=2, T=250, r_k=48, r_v=32)
     case = build_case(cfg)
     lens = np.array([250, 111], np.int32)
     q = host.queries(cfg, 0, 0)
@@ -195,7 +195,7 @@ def test_gqa_equals_mha_with_repeated_heads(gpu):
 
 def test_ragged_equals_dense_truncated(gpu):
     import torch
-    cfg = CONFIGS[1].scaled(B=3, Hq=8, Hkv=2, T=500)
+    cfg = LLAMA3_LAYER_32K.scaled(B=3, Hq=8, Hkv=2, T=500)
     case = build_case(cfg)
     q = host.queries(cfg, 0, 0)
     ragged = _decode(case, q, np.array([500, 123, 321], np.int32))
@@ -208,7 +208,7 @@ def test_ragged_equals_dense_truncated(gpu):
 def test_per_head_ranks_equal_single_head_calls(gpu):
     import torch
     kv = _kv()
-    cfg = CONFIGS[2].scaled(B=2, T_range=(300, 300))
+    cfg = PER_HEAD_RAGGED.scaled(B=2, T_range=(300, 300))
     case = build_case(cfg)
     lens = np.array([300, 180], np.int32)
     q = host.queries(cfg, 0, 0)
@@ -228,13 +228,13 @@ def test_per_head_ranks_equal_single_head_calls(gpu):
         assert rel_inf_rows(single, full[:, h * G:(h + 1) * G]).max() <= 1e-6, h
 
 
-@pytest.mark.parametrize("cid", [0, 1, 3])
-def test_append_matches_oracle_and_prefill(gpu, cid):
+@pytest.mark.parametrize("wl", ["single_head_f32", "llama3_8b_layer_32k", "long_context_128k"])
+def test_append_matches_oracle_and_prefill(gpu, wl):
     """append of token T at row T == prefill of T+1 tokens (to one storage rounding), and == oracle."""
     import torch
     kv = _kv()
-    extra = dict(B=2, T=200, decode_steps=3) if cid != 0 else dict(T=200, decode_steps=3)
-    cfg = CONFIGS[cid].scaled(**extra)
+    extra = dict(B=2, T=200, decode_steps=3) if wl != "single_head_f32" else dict(T=200, decode_steps=3)
+    cfg = WORKLOADS[wl].scaled(**extra)
     T = cfg.T
     case = build_case(cfg, n_rows=T)
     full = build_case(cfg, n_rows=T + 3)
@@ -273,7 +273,7 @@ def test_outputs_fully_written_and_deterministic(gpu):
     """NaN-poisoned outputs and workspace are fully overwritten; guard bands stay intact; runs are bitwise equal."""
     import torch
     kv = _kv()
-    cfg = CONFIGS[2].scaled(B=3, T_range=(50, 900))
+    cfg = PER_HEAD_RAGGED.scaled(B=3, T_range=(50, 900))
     case = build_case(cfg)
     lens = host.lengths(cfg)
     q = torch.from_numpy(host.queries(cfg, 0, 0)).cuda()
@@ -299,16 +299,16 @@ def test_outputs_fully_written_and_deterministic(gpu):
     assert (ws[:nc].view(torch.int32) == 0).all(), "every call must leave the arrival counters at zero"
 
 
-@pytest.mark.parametrize("cid,split", [(1, 0), (1, 128), (0, 256), (2, 0)])
-def test_decode_attn_equals_two_stages(gpu, cid, split):
+@pytest.mark.parametrize("wl,split", [("llama3_8b_layer_32k", 0), ("llama3_8b_layer_32k", 128), ("single_head_f32", 256), ("per_head_ranks_ragged", 0)])
+def test_decode_attn_equals_two_stages(gpu, wl, split):
     """kvlr_decode_attn (one launch, merge in the last workgroup) matches partials + combine.
 
     Same split records; the merges sum them in different orders, so fp32 rounding may differ.
     """
     import torch
     kv = _kv()
-    extra = {0: dict(T=1000), 1: dict(B=2, Hq=16, Hkv=2, T=700), 2: dict(B=3, T_range=(10, 900))}[cid]
-    cfg = CONFIGS[cid].scaled(**extra)
+    extra = {"single_head_f32": dict(T=1000), "llama3_8b_layer_32k": dict(B=2, Hq=16, Hkv=2, T=700), "per_head_ranks_ragged": dict(B=3, T_range=(10, 900))}[wl]
+    cfg = WORKLOADS[wl].scaled(**extra)
     case = build_case(cfg)
     lens_t = torch.from_numpy(host.lengths(cfg)).cuda()
     q = torch.from_numpy(host.queries(cfg, 0, 0)).cuda()
@@ -327,7 +327,7 @@ def test_latent_guard_bands(gpu):
     import torch
     kv = _kv()
     from synth.device import KVGenerator
-    cfg = CONFIGS[2].scaled(B=2, T_range=(100, 100), decode_steps=2)
+    cfg = PER_HEAD_RAGGED.scaled(B=2, T_range=(100, 100), decode_steps=2)
     rk, rv = host.ranks(cfg)
     PK, PV = host.bases(cfg)
     desc = kv.Desc(cfg.B, cfg.Hq, cfg.Hkv, cfg.d, cfg.capacity, rk, rv, kv.BF16, kv.BF16)
@@ -360,7 +360,7 @@ def test_latent_guard_bands(gpu):
 def test_ragged_lengths_with_empty_rows(gpu, lens):
     """Per-head ranks with very uneven lengths (empty rows, one long row): oracle parity under the
     library's plan, and the same result with a shorter fixed split (to fp32 rounding)."""
-    cfg = CONFIGS[2].scaled(B=6, T_range=(1, 3000))
+    cfg = PER_HEAD_RAGGED.scaled(B=6, T_range=(1, 3000))
     case = build_case(cfg)
     q = host.queries(cfg, 0, 0)
     got = _decode(case, q, lens)
@@ -374,12 +374,12 @@ def test_ragged_lengths_with_empty_rows(gpu, lens):
 
 def test_single_unit_long_and_many_units(gpu):
     """One (batch row, KV head) over 20000 rows; and 640 (batch row, KV head, head group) units."""
-    cfg = CONFIGS[0].scaled(T=20000)
+    cfg = SINGLE_HEAD_F32.scaled(T=20000)
     case = build_case(cfg)
     q = host.queries(cfg, 0, 0)
     lens = [20000]
     _check_rows(case, _decode(case, q, lens), q, lens)
-    cfg = CONFIGS[1].scaled(B=40, Hq=64, Hkv=4, T=300)   # 40 x 4 KV heads x 4 head groups
+    cfg = LLAMA3_LAYER_32K.scaled(B=40, Hq=64, Hkv=4, T=300)   # 40 x 4 KV heads x 4 head groups
     case = build_case(cfg)
     q = host.queries(cfg, 0, 0)
     lens = host.lengths(cfg)

@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 from oracle import quant as qo
-from synth import CONFIGS, host
+from synth import LLAMA3_LAYER_32K, PER_HEAD_RAGGED, WORKLOADS, host
 from synth.device import KVGenerator
 from tests.gpu_cases import bases32, say
 
@@ -85,7 +85,7 @@ def test_quantised_compression_matches_oracle(gpu):
     one quantisation step of the oracle's, and almost every code is identical."""
     import torch
     kv = _kv()
-    cfg = CONFIGS[2].scaled(B=2, T_range=(300, 300))
+    cfg = PER_HEAD_RAGGED.scaled(B=2, T_range=(300, 300))
     rk, rv = host.ranks(cfg)
     PK, PV = host.bases(cfg)
     desc = kv.Desc(cfg.B, cfg.Hq, cfg.Hkv, cfg.d, cfg.capacity, rk, rv, kv.BF16, kv.Q43)
@@ -194,15 +194,15 @@ def _q43_check(case, got, q, lens, units=None, bound=2e-2, long_bound=2e-3, long
     return worst
 
 
-@pytest.mark.parametrize("cid,extra", [
-    (1, dict(B=2, T=1000)),
-    (2, dict(B=3, T_range=(1, 700))),
-    (1, dict(B=2, Hq=10, Hkv=2, T=333, r_k=128, r_v=16)),
-    (1, dict(B=2, Hq=8, Hkv=2, T=300, r_k=16, r_v=128)),
-    (1, dict(B=2, Hq=6, Hkv=2, T=257, r_k=112, r_v=48)),
+@pytest.mark.parametrize("wl,extra", [
+    ("llama3_8b_layer_32k", dict(B=2, T=1000)),
+    ("per_head_ranks_ragged", dict(B=3, T_range=(1, 700))),
+    ("llama3_8b_layer_32k", dict(B=2, Hq=10, Hkv=2, T=333, r_k=128, r_v=16)),
+    ("llama3_8b_layer_32k", dict(B=2, Hq=8, Hkv=2, T=300, r_k=16, r_v=128)),
+    ("llama3_8b_layer_32k", dict(B=2, Hq=6, Hkv=2, T=257, r_k=112, r_v=48)),
 ])
-def test_q43_decode_matches_oracle(gpu, cid, extra):
-    cfg = CONFIGS[cid].scaled(**extra)
+def test_q43_decode_matches_oracle(gpu, wl, extra):
+    cfg = WORKLOADS[wl].scaled(**extra)
     case = _q43_case(cfg)
     lens = host.lengths(cfg)
     q = host.queries(cfg, 0, 0)
@@ -211,7 +211,7 @@ def test_q43_decode_matches_oracle(gpu, cid, extra):
 
 @pytest.mark.parametrize("lens,split", [([0, 5], 64), ([1, 300], 64), ([257, 256], 0), ([300, 129], 128)])
 def test_q43_decode_edge_lengths(gpu, lens, split):
-    cfg = CONFIGS[1].scaled(B=2, Hq=8, Hkv=2, T=300)
+    cfg = LLAMA3_LAYER_32K.scaled(B=2, Hq=8, Hkv=2, T=300)
     case = _q43_case(cfg)
     q = host.queries(cfg, 0, 0)
     lens = np.array(lens, np.int32)
@@ -261,7 +261,7 @@ def test_q43_folded_and_two_stage(gpu):
     """The folded entry point and partials + combine run the same kernel on 4/3-bit caches."""
     import torch
     kv = _kv()
-    cfg = CONFIGS[1].scaled(B=2, Hq=16, Hkv=2, T=700)
+    cfg = LLAMA3_LAYER_32K.scaled(B=2, Hq=16, Hkv=2, T=700)
     case = _q43_case(cfg)
     lens = host.lengths(cfg)
     q = host.queries(cfg, 0, 0)

@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 import torch
 
-from synth import CONFIGS, host
+from synth import LLAMA3_32_LAYERS, LLAMA3_LAYER_32K, LONG_CONTEXT_128K, PER_HEAD_RAGGED, WORKLOADS, host
 
 
 def _exact_bf16(x: float) -> float:
@@ -27,7 +27,7 @@ def _exact_bf16(x: float) -> float:
 
 
 def test_splitmix_vector_matches_scalar_definition():
-    key = host.stream_key(CONFIGS[1], 3, host.KIND_K)
+    key = host.stream_key(LLAMA3_LAYER_32K, 3, host.KIND_K)
     n = np.array([1, 2, 3, 1000, 2 ** 40 + 7], dtype=np.uint64)
     vec = host.word(key, n)
     ref = [host.mix64_scalar(key + int(i) * host.GAMMA) for i in n]
@@ -53,7 +53,7 @@ def test_bf16_encoder_is_exact_nearest_even():
 
 
 def test_slices_regenerate_identically():
-    cfg = CONFIGS[3].scaled(T=64)
+    cfg = LONG_CONTEXT_128K.scaled(T=64)
     full = host.kv_values_f64(cfg, 0, "k", 1, 0, 40)
     part = host.kv_values_f64(cfg, 0, "k", 1, 17, 9, heads=[2, 5])
     assert np.array_equal(full[17:26][:, [2, 5]], part)
@@ -65,7 +65,7 @@ def test_slices_regenerate_identically():
 
 
 def test_channel_statistics_and_outliers():
-    cfg = CONFIGS[1]
+    cfg = LLAMA3_LAYER_32K
     st = host.kv_stats(cfg, 0)
     x = host.kv_values_f64(cfg, 0, "v", 0, 0, 20000, heads=[3], stats=st)[:, 0, :]
     assert np.allclose(x.mean(0), st["mu_v"][3], atol=0.06)
@@ -74,9 +74,9 @@ def test_channel_statistics_and_outliers():
     assert np.all((st["sigma_k"] >= 0.5) & (st["sigma_k"] <= 2))
 
 
-@pytest.mark.parametrize("cid", [0, 1, 2, 3])
-def test_bases_orthonormal(cid):
-    cfg = CONFIGS[cid]
+@pytest.mark.parametrize("wl", ["single_head_f32", "llama3_8b_layer_32k", "per_head_ranks_ragged", "long_context_128k"])
+def test_bases_orthonormal(wl):
+    cfg = WORKLOADS[wl]
     PK, PV = host.bases(cfg)
     rk, rv = host.ranks(cfg)
     for h in range(cfg.Hkv):
@@ -88,16 +88,16 @@ def test_bases_orthonormal(cid):
 
 
 def test_rank_tables():
-    rk, rv = host.ranks(CONFIGS[2])
-    assert set(rk) | set(rv) <= set(CONFIGS[2].rank_choices)
-    prof = host.rank_profile(CONFIGS[4])
+    rk, rv = host.ranks(PER_HEAD_RAGGED)
+    assert set(rk) | set(rv) <= set(PER_HEAD_RAGGED.rank_choices)
+    prof = host.rank_profile(LLAMA3_32_LAYERS)
     assert prof.shape == (32, 2) and prof.sum() == 4096
     assert np.all(prof % 16 == 0) and prof.min() >= 16 and prof.max() <= 128
-    lens = host.lengths(CONFIGS[2])
+    lens = host.lengths(PER_HEAD_RAGGED)
     assert lens.min() >= 4096 and lens.max() <= 16384 and len(lens) == 16
 
 
 def test_queries_fresh_per_step():
-    cfg = CONFIGS[3]
+    cfg = LONG_CONTEXT_128K
     a, b = host.queries(cfg, 0, 0), host.queries(cfg, 0, 1)
     assert a.dtype == np.float32 and a.shape == (2, 32, 128) and not np.array_equal(a, b)
