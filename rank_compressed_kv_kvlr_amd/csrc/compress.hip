@@ -261,10 +261,11 @@ __global__ __launch_bounds__(256) void compress_bf16_mfma(CompressParams p) {
   }
 }
 
-// Plain VALU compression (fp32 inputs, 4/3-bit latents, joint values): one
-// workgroup per (64-token tile, KV head x {K, V}, batch row); the tile is staged
-// in LDS as fp32 and each thread forms latent channels as fp32 dot products,
-// kept in registers (at most 64 * 128 / 256 = 32 per thread). Joint values
+// Plain VALU compression (fp32 inputs, ranks that are not whole 16-channel
+// tiles, 4/3-bit latents, joint values): one workgroup per (64-token tile,
+// KV head x {K, V}, batch row); the tile is staged in LDS as fp32 and each
+// thread forms latent channels as fp32 dot products, kept in registers (at
+// most 64 * 128 / 256 = 32 per thread). Joint values
 // (STAR-KV technical summary, "Metodologia" section 2) sum the contributions of
 // every KV head's rows, V_all P_J = sum_h V_h P_J[h d .. (h+1) d), staging one
 // head's tile at a time.
@@ -403,11 +404,15 @@ __global__ __launch_bounds__(128) void append_kernel(AppendParams p) {
 hipError_t launch_compress(const CompressParams& p_in, hipStream_t stream) {
   if (p_in.n_tok <= 0) return hipSuccess;
   int max_r = 0;
-  for (int h = 0; h < p_in.Hkv; ++h) max_r = max(max_r, max(p_in.ht.rk[h], p_in.ht.rv[h]));
+  bool tiles16 = true;   // the MFMA kernel writes whole 16-channel tiles (fp32 latents allow ranks of 4 k)
+  for (int h = 0; h < p_in.Hkv; ++h) {
+    max_r = max(max_r, max(p_in.ht.rk[h], p_in.ht.rv[h]));
+    tiles16 = tiles16 && p_in.ht.rk[h] % 16 == 0 && (p_in.joint_v || p_in.ht.rv[h] % 16 == 0);
+  }
   CompressParams p = p_in;
   p.only_kind = p.joint_v ? 0 : -1;   // joint values get a launch of their own below
   const int ykinds = p.joint_v ? 1 : 2;
-  if (p.in_bf16 && !p.out_q43) {
+  if (p.in_bf16 && !p.out_q43 && tiles16) {
     const size_t lds = (size_t)4 * max_r * p.d;   // hi + lo operand tiles
     const dim3 grid((p.n_tok + kTokensPerWg - 1) / kTokensPerWg, ykinds * p.Hkv, p.B);
 #define KVLR_COMPRESS_CASE(NKB)                                                              \

@@ -117,9 +117,12 @@ def test_decode_rank_sweep_bf16(gpu, rk, rv):
     _check_rows(case, _decode(case, q, lens), q, lens, diag_bound=2e-3)
 
 
-@pytest.mark.parametrize("rk,rv", [(4, 4), (12, 32), (32, 8), (96, 128), (128, 64)])
-def test_decode_rank_sweep_f32(gpu, rk, rv):
-    cfg = SINGLE_HEAD_F32.scaled(B=2, Hq=3, Hkv=3, T=300, r_k=rk, r_v=rv)
+@pytest.mark.parametrize("in_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rk,rv", [(4, 4), (12, 32), (32, 8), (96, 128), (128, 64), (60, 20)])
+def test_decode_rank_sweep_f32(gpu, rk, rv, in_dtype):
+    """fp32 latents take any rank that is a multiple of 4, from fp32 or bf16 rows (ranks that
+    are not whole 16-channel tiles are compressed on VALU)."""
+    cfg = SINGLE_HEAD_F32.scaled(B=2, Hq=3, Hkv=3, T=300, r_k=rk, r_v=rv, in_dtype=in_dtype)
     case = build_case(cfg)
     lens = np.array([300, 129], np.int32)
     q = host.queries(cfg, 0, 0)

@@ -1,0 +1,86 @@
+"""GPU parity on seeded random shapes: head dims 32 to 256, per-head ranks, GQA groups of 1 to
+16 query heads, ragged lengths with empty rows, explicit split lengths, fp32 / bf16 / 4/3-bit
+latents, per-head and joint values. Every case is checked against the float64 oracle with the
+same acceptance bounds as the fixed cases; bf16 per-head caches also take a fused decode step
+that must equal append followed by decode bit for bit."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from synth import LLAMA3_LAYER_32K, host
+from tests.gpu_cases import build_case, say
+from tests.test_gpu_fused_step import _run_steps
+from tests.test_gpu_joint import _check as joint_check
+from tests.test_gpu_joint import _decode as joint_decode
+from tests.test_gpu_joint import _joint_case
+from tests.test_gpu_parity import _check_rows, _decode
+from tests.test_gpu_quant import _q43_case, _q43_check, _q43_decode
+
+pytestmark = pytest.mark.gpu
+
+# storage of each case: latent dtype, and "joint" for one value latent shared by every KV head
+KINDS = ["bf16", "f32", "q43", "joint_bf16", "bf16", "f32", "bf16", "joint_bf16", "q43", "bf16",
+         "joint_q43", "bf16", "f32", "joint_bf16", "bf16", "q43", "joint_f32", "bf16", "f32", "joint_bf16",
+         "bf16", "q43", "joint_bf16", "bf16"]
+HEAD_DIMS = [32, 64, 96, 128, 160, 192, 256]
+GROUPS = [1, 2, 3, 4, 5, 6, 8, 16]
+SPLITS = [0, 64, 128, 256, 512]
+
+
+def draw(i: int):
+    """Shape of case i: (kind, cfg, lens, split, joint rank or None), from its own seed."""
+    g = np.random.default_rng(np.random.SeedSequence([9100, i]))
+    kind = KINDS[i]
+    joint = kind.startswith("joint")
+    lat = kind.split("_")[-1]
+    d = int(g.choice(HEAD_DIMS))
+    Hkv = int(g.integers(1, 7))
+    G = int(g.choice(GROUPS))
+    if joint and lat == "bf16":   # the joint bf16 kernel holds at most 32 query heads of 8 KV heads
+        G = min(G, 32 // Hkv)
+    B = int(g.integers(1, 5))
+    T = int(g.integers(1, 700))
+    gran = 4 if lat == "f32" else 16
+    rmax = min(d, 128)
+    choices = tuple(sorted({int(x) for x in g.choice(np.arange(gran, rmax + 1, gran), size=3)}))
+    in_dtype = str(g.choice(["bf16", "f32"])) if kind != "q43" else "bf16"   # the 4/3-bit builder takes bf16 rows
+    cfg = LLAMA3_LAYER_32K.scaled(B=B, Hq=Hkv * G, Hkv=Hkv, d=d, T=T, rank_mode="per_head", rank_choices=choices,
+                                  n_outliers=min(4, d), in_dtype=in_dtype,
+                                  latent_dtype="f32" if lat == "f32" else "bf16")
+    lens = g.integers(0, T + 1, size=B).astype(np.int32)
+    lens[g.integers(0, B)] = T
+    if B > 1:
+        lens[g.integers(0, B)] = 0
+    split = int(g.choice(SPLITS))
+    rj = None
+    if joint:
+        jmax = min(Hkv * d, 128)
+        rj = int(g.choice(np.arange(gran, jmax + 1, gran)))
+    return kind, cfg, lens, split, rj
+
+
+@pytest.mark.parametrize("i", range(len(KINDS)))
+def test_random_shape_matches_oracle(gpu, i):
+    kind, cfg, lens, split, rj = draw(i)
+    say(f"[random {i}] {kind} B={cfg.B} Hq={cfg.Hq} Hkv={cfg.Hkv} d={cfg.d} T={cfg.T} ranks={cfg.rank_choices} "
+        f"in={cfg.in_dtype} lens={lens.tolist()} split={split} r_joint={rj}")
+    q = host.queries(cfg, 0, 0)
+    if kind.startswith("joint"):
+        case = _joint_case(cfg, rj, latent=kind.split("_")[1])
+        joint_check(case, joint_decode(case, q, lens, split), q, lens, diag_bound=1e-2)
+    elif kind == "q43":
+        case = _q43_case(cfg)
+        _q43_check(case, _q43_decode(case, q, lens, split), q, lens)
+    else:
+        case = build_case(cfg, layer=1 + i)
+        q = host.queries(cfg, 1 + i, 0)
+        _check_rows(case, _decode(case, q, lens, split=split), q, lens,
+                    diag_bound=5e-3 if cfg.latent_dtype == "bf16" else None)
+
+
+@pytest.mark.parametrize("i", [i for i, k in enumerate(KINDS) if k == "bf16"][:4])
+def test_random_shape_fused_step(gpu, i):
+    """Two fused steps (append + attend in one launch) equal the two-call form bit for bit."""
+    _, cfg, _, split, _ = draw(i)
+    _run_steps(cfg.scaled(decode_steps=2), 2, split)
