@@ -1,15 +1,18 @@
 """GPU parity on seeded random shapes: head dims 32 to 256, per-head ranks, GQA groups of 1 to
 16 query heads, ragged lengths with empty rows, explicit split lengths, fp32 / bf16 / 4/3-bit
 latents, per-head and joint values. Every case is checked against the float64 oracle with the
-same acceptance bounds as the fixed cases; bf16 per-head caches also take a fused decode step
-that must equal append followed by decode bit for bit."""
+same acceptance bounds as the fixed cases. On the same caches the one-launch, two-stage and folded
+entry points must agree, and bf16 per-head caches take fused decode steps that must equal append
+followed by decode bit for bit."""
 from __future__ import annotations
 
 import numpy as np
 import pytest
 
+from oracle import joint as jo
+from oracle import quant as qo
 from synth import LLAMA3_LAYER_32K, host
-from tests.gpu_cases import build_case, say
+from tests.gpu_cases import bases32, build_case, rel_inf_rows, say
 from tests.test_gpu_fused_step import _run_steps
 from tests.test_gpu_joint import _check as joint_check
 from tests.test_gpu_joint import _decode as joint_decode
@@ -18,6 +21,11 @@ from tests.test_gpu_parity import _check_rows, _decode
 from tests.test_gpu_quant import _q43_case, _q43_check, _q43_decode
 
 pytestmark = pytest.mark.gpu
+
+
+def _kv():
+    import rank_compressed_kv_kvlr_amd as kv
+    return kv
 
 # storage of each case: latent dtype, and "joint" for one value latent shared by every KV head
 KINDS = ["bf16", "f32", "q43", "joint_bf16", "bf16", "f32", "bf16", "joint_bf16", "q43", "bf16",
@@ -77,6 +85,63 @@ def test_random_shape_matches_oracle(gpu, i):
         q = host.queries(cfg, 1 + i, 0)
         _check_rows(case, _decode(case, q, lens, split=split), q, lens,
                     diag_bound=5e-3 if cfg.latent_dtype == "bf16" else None)
+
+
+def _handles(kind, cfg, case):
+    """(desc, P_K, P_V, lat_k, lat_v, host P_K per head as the kernels apply it, host value basis
+    rows per head) of a case of any storage."""
+    if kind.startswith("joint"):
+        PV = [jo.joint_slice(case["PJ"], h, cfg.d) for h in range(cfg.Hkv)]
+        return case["desc"], case["pk"], case["pj"], case["lk"], case["lv"], case["PK"], PV
+    if kind == "q43":
+        PK = [qo.fuse_bases(P) for P in bases32(case["PK"])]
+        PV = [qo.fuse_bases(P) for P in bases32(case["PV"])]
+        return case["desc"], case["pk"], case["pv"], case["lk"], case["lv"], PK, PV
+    return case.desc, case.pk, case.pv, case.lat_k, case.lat_v, case.P32K, case.P32V
+
+
+@pytest.mark.parametrize("i", range(len(KINDS)))
+def test_random_shape_entry_points_agree(gpu, i):
+    """On the same caches: decode_attn writes every output element (NaN-poisoned buffer) and
+    zero rows for empty sequences; decode_partials + decode_combine give its result; the folded
+    entry point, back-projected on the host, gives it too."""
+    import torch
+    kv = _kv()
+    kind, cfg, lens, split, rj = draw(i)
+    say(f"[random entry points {i}] {kind} B={cfg.B} Hq={cfg.Hq} Hkv={cfg.Hkv} d={cfg.d} split={split}")
+    if kind.startswith("joint"):
+        case = _joint_case(cfg, rj, latent=kind.split("_")[1])
+    elif kind == "q43":
+        case = _q43_case(cfg)
+    else:
+        case = build_case(cfg)
+    desc, pk, pv, lk, lv, PK, PV = _handles(kind, cfg, case)
+    q = host.queries(cfg, 0, 0)
+    qd = torch.from_numpy(q).cuda()
+    lens_t = torch.from_numpy(lens).cuda()
+    out = torch.full((cfg.B, cfg.Hq, cfg.d), float("nan"), device="cuda")
+    kv.decode_attn(desc, qd, pk, pv, lk, lv, lens_t, out=out, split_tokens=split)
+    ws = kv.alloc_workspace(desc, split)
+    kv.decode_partials(desc, qd, pk, lk, lv, lens_t, ws, split_tokens=split)
+    two = kv.decode_combine(desc, pv, ws, torch.full_like(out, float("nan")), split_tokens=split)
+    rk_max = max(P.shape[1] for P in PK)
+    q_lat = np.zeros((cfg.B, cfg.Hq, rk_max), np.float32)
+    for qh in range(cfg.Hq):
+        P = PK[qh // cfg.G]
+        q_lat[:, qh, :P.shape[1]] = (q[:, qh].astype(np.float64) @ P).astype(np.float32)
+    o_lat = kv.decode_attn_latent(desc, torch.from_numpy(q_lat).cuda(), lk, lv, lens_t, split_tokens=split)
+    torch.cuda.synchronize()
+    a = out.cpu().numpy().astype(np.float64)
+    assert np.isfinite(a).all(), "every output element is written"
+    assert np.all(a[lens == 0] == 0), "empty sequences give zero rows"
+    live = lens > 0
+    err_two = float(rel_inf_rows(two.cpu().numpy().astype(np.float64)[live], a[live]).max()) if live.any() else 0.0
+    ol = o_lat.cpu().numpy().astype(np.float64)
+    folded = np.stack([ol[:, qh, :PV[qh // cfg.G].shape[1]] @ PV[qh // cfg.G].T for qh in range(cfg.Hq)], axis=1)
+    err_fold = float(rel_inf_rows(folded[live], a[live]).max()) if live.any() else 0.0
+    say(f"[random entry points {i}] two-stage {err_two:.2e} folded {err_fold:.2e}")
+    assert err_two <= 1e-6, err_two
+    assert err_fold <= (1e-5 if kind.endswith("f32") else 1e-4), err_fold
 
 
 @pytest.mark.parametrize("i", [i for i, k in enumerate(KINDS) if k == "bf16"][:4])
