@@ -2,8 +2,8 @@
 16 query heads, ragged lengths with empty rows, explicit split lengths, fp32 / bf16 / 4/3-bit
 latents, per-head and joint values. Every case is checked against the float64 oracle with the
 same acceptance bounds as the fixed cases. On the same caches the one-launch, two-stage and folded
-entry points must agree, and bf16 per-head caches take fused decode steps that must equal append
-followed by decode bit for bit."""
+entry points must agree; caches grown by kvlr_append decode like prefilled ones; and bf16 per-head
+caches take fused decode steps that must equal append followed by decode bit for bit."""
 from __future__ import annotations
 
 import numpy as np
@@ -142,6 +142,39 @@ def test_random_shape_entry_points_agree(gpu, i):
     say(f"[random entry points {i}] two-stage {err_two:.2e} folded {err_fold:.2e}")
     assert err_two <= 1e-6, err_two
     assert err_fold <= (1e-5 if kind.endswith("f32") else 1e-4), err_fold
+
+
+@pytest.mark.parametrize("i", range(len(KINDS)))
+def test_random_shape_append(gpu, i):
+    """Prefill all but the last two rows, append those two (kvlr_append, one call per row), then
+    decode over the whole cache against the oracle, which regenerates every row."""
+    import torch
+    kv = _kv()
+    kind, cfg, lens, split, rj = draw(i)
+    T = cfg.T
+    n_pre = max(T - 2, 0)
+    say(f"[random append {i}] {kind} B={cfg.B} Hq={cfg.Hq} Hkv={cfg.Hkv} d={cfg.d} rows {n_pre} + {T - n_pre}")
+    if kind.startswith("joint"):
+        case = _joint_case(cfg, rj, latent=kind.split("_")[1], n_rows=n_pre, chunk=1024)
+    elif kind == "q43":
+        case = _q43_case(cfg, n_rows=n_pre, chunk=1024)
+    else:
+        case = build_case(cfg, n_rows=n_pre, chunk=1024)
+    desc, pk, pv, lk, lv, _, _ = _handles(kind, cfg, case)
+    from synth.device import KVGenerator
+    gen = KVGenerator(cfg, 0)
+    for t in range(n_pre, T):
+        pos = torch.full((cfg.B,), t, dtype=torch.int32, device="cuda")
+        kv.append(desc, gen.make("k", cfg.B, 1, t0=t)[:, 0].contiguous(), gen.make("v", cfg.B, 1, t0=t)[:, 0].contiguous(),
+                  pos, pk, pv, lk, lv)
+    q = host.queries(cfg, 0, 0)
+    if kind.startswith("joint"):
+        joint_check(case, joint_decode(case, q, lens, split), q, lens, diag_bound=1e-2)
+    elif kind == "q43":
+        _q43_check(case, _q43_decode(case, q, lens, split), q, lens)
+    else:
+        _check_rows(case, _decode(case, q, lens, split=split), q, lens,
+                    diag_bound=5e-3 if cfg.latent_dtype == "bf16" else None)
 
 
 @pytest.mark.parametrize("i", [i for i, k in enumerate(KINDS) if k == "bf16"][:4])
