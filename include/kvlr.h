@@ -27,6 +27,10 @@
  *    is complete when that stream is.
  *  - Pointers named "device" must be device memory (or memory the device
  *    can read/write); descriptor rank arrays are host memory.
+ *  - Buffers the kernels access with 16-byte vector loads or stores must
+ *    start on a 16-byte boundary: K, V, the latent caches, the bases, the
+ *    workspace and q_lat (KVLR_ERR_ARG otherwise). q, out, o_lat, k_new,
+ *    v_new, pos and seq_lens need only their element alignment.
  *  - Calls are re-entrant and thread-safe on disjoint output buffers.
  *  - Device-resident indices (seq_lens, pos) are trusted preconditions;
  *    kernels clamp them to [0, capacity] and never access memory out of
@@ -55,7 +59,8 @@ typedef enum kvlr_status {
   KVLR_ERR_DTYPE = -4,     /* unsupported dtype code */
   KVLR_ERR_WORKSPACE = -5, /* workspace NULL or smaller than kvlr_decode_workspace_bytes() */
   KVLR_ERR_HIP = -6,       /* a kernel launch failed (hipGetLastError) */
-  KVLR_ERR_ARG = -7        /* other invalid scalar argument (split_tokens, scale, start) */
+  KVLR_ERR_ARG = -7        /* other invalid argument (split_tokens, scale, start, a buffer not
+                              16-byte aligned) */
 } kvlr_status;
 
 /* Element types. */
@@ -140,8 +145,7 @@ typedef enum kvlr_value_mode {
  * (b, h) starts at byte C16 * (b * RB + RB_pre(h)) and row t at t * rb(r).
  * The bases used with such a cache must have the block-wise Hadamard folded
  * in (kvlr_hadamard_bases); compression, append and decode all take those
- * folded bases. The cache base addresses must be 16-byte aligned (checked:
- * KVLR_ERR_ARG otherwise).
+ * folded bases.
  *
  * Basis layout: P_K is fp32, heads packed back to back, head h a row-major
  * [d][r_k[h]] block starting at element d * R_pre(h); P_V likewise. */
@@ -308,9 +312,11 @@ KVLR_API int kvlr_append_decode_attn(const kvlr_desc* desc, const void* k_new, c
                                      void* workspace, size_t workspace_bytes, int32_t split_tokens, void* stream);
 
 /* The two stages of kvlr_decode_attn, for callers that schedule them
- * separately (e.g. to time or overlap them). kvlr_decode_attn(...) is
- * exactly kvlr_decode_partials(...) followed by kvlr_decode_combine(...) on
- * the same stream with the same workspace and split_tokens.
+ * separately (e.g. to time or overlap them). kvlr_decode_partials(...)
+ * followed by kvlr_decode_combine(...) on the same stream with the same
+ * workspace and split_tokens gives kvlr_decode_attn's result: the same split
+ * records, merged in another order (per-head values: fp32 rounding of the
+ * merge may differ; joint bf16 values: bit for bit, the launches are the same).
  *
  * kvlr_decode_partials: query projection q~ = q P_K, latent scores, online
  * softmax and the p-weighted sum of value latents for every split of every

@@ -3,6 +3,8 @@
 // never synchronises. Every check runs before the first HIP call.
 #include <math.h>
 #include <stdlib.h>
+
+#include <initializer_list>
 #include <stdint.h>
 #include <string.h>
 
@@ -45,9 +47,13 @@ int rk_max_of(const kvlr_desc* d) {
   return m;
 }
 
-// 4/3-bit caches are streamed with 16-byte loads: their base addresses must be 16-byte aligned.
-bool q43_aligned(int latent_dtype, const void* a, const void* b) {
-  return latent_dtype != KVLR_Q43 || (((uintptr_t)a | (uintptr_t)b) & 15) == 0;
+// Buffers the kernels access with 16-byte vector loads or stores (K/V rows, latent
+// caches, bases, workspace) must start on a 16-byte boundary. NULLs pass (they are
+// checked separately).
+bool aligned16(std::initializer_list<const void*> ptrs) {
+  uintptr_t bits = 0;
+  for (const void* ptr : ptrs) bits |= (uintptr_t)ptr;
+  return (bits & 15) == 0;
 }
 bool valid_latent_dtype(int t) { return valid_dtype(t) || t == KVLR_Q43; }
 
@@ -249,7 +255,7 @@ KVLR_API int kvlr_prefill_compress(const kvlr_desc* desc, const void* K, const v
   if ((long long)start + n_tok > desc->capacity) return KVLR_ERR_SHAPE;
   if (n_tok == 0) return KVLR_OK;
   if (!K || !V || !P_K || !P_V || !lat_k || !lat_v) return KVLR_ERR_NULL;
-  if (!q43_aligned(desc->latent_dtype, lat_k, lat_v)) return KVLR_ERR_ARG;
+  if (!aligned16({K, V, P_K, P_V, lat_k, lat_v})) return KVLR_ERR_ARG;
   if ((long long)desc->batch * n_tok * desc->n_kv_heads * desc->head_dim > (1LL << 40)) return KVLR_ERR_SHAPE;
   p.x_k = K;
   p.x_v = V;
@@ -277,7 +283,7 @@ KVLR_API int kvlr_append(const kvlr_desc* desc, const void* k_new, const void* v
   const int rc = check_desc(desc, &p.ht, &p.Rk, &p.Rv, nullptr, &p.Sk, &p.Sv);
   if (rc) return rc;
   if (!k_new || !v_new || !pos || !P_K || !P_V || !lat_k || !lat_v) return KVLR_ERR_NULL;
-  if (!q43_aligned(desc->latent_dtype, lat_k, lat_v)) return KVLR_ERR_ARG;
+  if (!aligned16({P_K, P_V, lat_k, lat_v})) return KVLR_ERR_ARG;
   p.k_new = k_new;
   p.v_new = v_new;
   p.pos = pos;
@@ -302,6 +308,7 @@ KVLR_API int kvlr_hadamard_bases(const kvlr_desc* desc, const float* P_K, const 
   const int rc = check_desc(desc, nullptr, &Rk, &Rv, nullptr);
   if (rc) return rc;
   if (!P_K || !P_V || !out_K || !out_V) return KVLR_ERR_NULL;
+  if (!aligned16({P_K, P_V, out_K, out_V})) return KVLR_ERR_ARG;
   // every head's block is row-major [d][r(h)] with r(h) a multiple of 16, so the
   // transform acts on consecutive runs of 16 floats of the packed arrays
   if (Rk % 16 || Rv % 16) return KVLR_ERR_RANK;
@@ -327,7 +334,7 @@ int prepare_decode(const kvlr_desc* desc, const float* q, const float* P_K, cons
   if (need_partials && (!q || !P_K || !lat_k || !lat_v || !seq_lens)) return KVLR_ERR_NULL;
   if (need_combine && (!P_V || !out)) return KVLR_ERR_NULL;
   if (need_partials && !isfinite(scale)) return KVLR_ERR_ARG;
-  if (need_partials && !q43_aligned(desc->latent_dtype, lat_k, lat_v)) return KVLR_ERR_ARG;
+  if (!aligned16({P_K, lat_k, lat_v, P_V, workspace})) return KVLR_ERR_ARG;
   int ns = 0, len = 0;
   rc = plan_split(desc, split_tokens, &ns, &len, p->ht.split_len);
   if (rc) return rc;

@@ -244,3 +244,33 @@ def test_fused_step_arguments():
     a = [FAKE] * 9
     assert kv.lib.kvlr_append_decode_attn(d.ptr, *a, ctypes.c_float(0.1), FAKE, FAKE, need - 1, 0, None) == -5
     assert kv.lib.kvlr_append_decode_attn(d.ptr, *a, ctypes.c_float(float("nan")), FAKE, FAKE, need, 0, None) == -7
+
+
+def test_misaligned_buffers_rejected():
+    """Buffers read or written with 16-byte vector accesses must be 16-byte aligned, for every
+    latent dtype: the entry points return KVLR_ERR_ARG before any launch."""
+    odd = ctypes.c_void_p(0x1008)
+    for lat in (kv.BF16, kv.F32, kv.Q43):
+        d = _desc(latent_dtype=lat)
+        rc, need = _ws(d)
+        assert rc == 0
+        for k in range(6):   # K, V, P_K, P_V, lat_k, lat_v
+            a = [FAKE] * 6
+            a[k] = odd
+            K, V, pk, pv, lk, lv = a
+            assert kv.lib.kvlr_prefill_compress(d.ptr, K, V, 0, 10, pk, pv, lk, lv, None) == -7, (lat, k)
+        for k in range(4):   # P_K, P_V, lat_k, lat_v
+            a = [FAKE] * 4
+            a[k] = odd
+            pk, pv, lk, lv = a
+            assert kv.lib.kvlr_append(d.ptr, FAKE, FAKE, FAKE, pk, pv, lk, lv, None) == -7, (lat, k)
+        for k in range(5):   # P_K, P_V, lat_k, lat_v, workspace
+            a = [FAKE] * 5
+            a[k] = odd
+            pk, pv, lk, lv, ws = a
+            assert kv.lib.kvlr_decode_attn(d.ptr, FAKE, pk, pv, lk, lv, FAKE, ctypes.c_float(0.1), FAKE, ws, need, 0,
+                                           None) == -7, (lat, k)
+        # q, out and seq_lens need only element alignment: those calls get past the check
+        # (and are stopped by the workspace size instead, still before any launch)
+        assert kv.lib.kvlr_decode_attn(d.ptr, ctypes.c_void_p(0x1004), FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p(0x1004),
+                                       ctypes.c_float(0.1), ctypes.c_void_p(0x1004), FAKE, need - 1, 0, None) == -5
