@@ -87,6 +87,39 @@ def test_random_shape_matches_oracle(gpu, i):
                     diag_bound=5e-3 if cfg.latent_dtype == "bf16" else None)
 
 
+# shapes at the limits of the descriptor: 64 KV heads, 16 query heads per KV head at
+# head_dim 256 and rank 128, a one-row cache, the joint bf16 kernel's 32 x 8 heads
+EXTREMES = [
+    ("bf16", dict(B=1, Hq=64, Hkv=64, d=32, T=70, rank_choices=(16, 32)), [70]),
+    ("f32", dict(B=1, Hq=64, Hkv=64, d=32, T=70, rank_choices=(4, 32), in_dtype="f32", latent_dtype="f32"), [70]),
+    ("q43", dict(B=1, Hq=64, Hkv=64, d=64, T=70, rank_choices=(16, 64)), [70]),
+    ("bf16", dict(B=1, Hq=64, Hkv=4, d=256, T=130, rank_choices=(128,)), [130]),
+    ("f32", dict(B=1, Hq=64, Hkv=4, d=256, T=130, rank_choices=(128,), latent_dtype="f32"), [130]),
+    ("bf16", dict(B=2, Hq=8, Hkv=2, d=128, T=1, rank_choices=(64,)), [1, 0]),
+    ("q43", dict(B=2, Hq=8, Hkv=2, d=128, T=1, rank_choices=(64,)), [1, 0]),
+    ("joint_bf16", dict(B=2, Hq=32, Hkv=8, d=256, T=150, rank_choices=(128,)), [150, 77]),
+    ("joint_bf16", dict(B=1, Hq=8, Hkv=8, d=128, T=1, rank_choices=(16,)), [1]),
+]
+
+
+@pytest.mark.parametrize("n", range(len(EXTREMES)))
+def test_extreme_shapes_match_oracle(gpu, n):
+    kind, extra, lens = EXTREMES[n]
+    lens = np.asarray(lens, np.int32)
+    cfg = LLAMA3_LAYER_32K.scaled(rank_mode="per_head", n_outliers=4, **extra)
+    say(f"[extreme {n}] {kind} {extra} lens={lens.tolist()}")
+    q = host.queries(cfg, 0, 0)
+    if kind.startswith("joint"):
+        case = _joint_case(cfg, 128 if cfg.T > 1 else 16, latent=kind.split("_")[1])
+        joint_check(case, joint_decode(case, q, lens), q, lens, diag_bound=1e-2)
+    elif kind == "q43":
+        case = _q43_case(cfg)
+        _q43_check(case, _q43_decode(case, q, lens), q, lens)
+    else:
+        case = build_case(cfg)
+        _check_rows(case, _decode(case, q, lens), q, lens, diag_bound=5e-3 if cfg.latent_dtype == "bf16" else None)
+
+
 def _handles(kind, cfg, case):
     """(desc, P_K, P_V, lat_k, lat_v, host P_K per head as the kernels apply it, host value basis
     rows per head) of a case of any storage."""
