@@ -111,3 +111,48 @@ def test_graph_append_decode_loop_matches_eager(gpu, fused):
         for s in range(steps):
             assert torch.equal(outs[s], eager[s]), (rep, s)
     say(f"[graph] {steps}-step append + decode loop (fused={fused}): 3 replays equal the eager loop")
+
+
+def test_graph_other_paths_match_eager(gpu):
+    """Joint bf16 values (three launches, q~ through the workspace), 4/3-bit latents, the folded
+    entry point and the two-stage form, captured together and replayed 3 times: every replay
+    equals the eager calls bit for bit."""
+    import torch
+    kv = _kv()
+    from synth import LLAMA3_LAYER_32K
+    from tests.test_gpu_joint import _joint_case
+    from tests.test_gpu_quant import _q43_case
+    cfg = LLAMA3_LAYER_32K.scaled(B=3, T=900)
+    lens = torch.from_numpy(np.array([900, 311, 0], np.int32)).cuda()
+    q = torch.from_numpy(host.queries(cfg, 0, 0)).cuda()
+    joint = _joint_case(cfg, 128)
+    q43 = _q43_case(cfg)
+    per_head = build_case(cfg)
+    q_lat = torch.randn((cfg.B, cfg.Hq, 64), generator=torch.Generator().manual_seed(5)).cuda()
+    ws = [kv.alloc_workspace(joint["desc"]), kv.alloc_workspace(q43["desc"]), kv.alloc_workspace(per_head.desc),
+          kv.alloc_workspace(per_head.desc, 128)]
+    outs = [torch.empty((cfg.B, cfg.Hq, cfg.d), device="cuda") for _ in range(3)] + \
+           [torch.empty((cfg.B, cfg.Hq, 64), device="cuda")]
+
+    def step():
+        kv.decode_attn(joint["desc"], q, joint["pk"], joint["pj"], joint["lk"], joint["lv"], lens, out=outs[0],
+                       workspace=ws[0])
+        kv.decode_attn(q43["desc"], q, q43["pk"], q43["pv"], q43["lk"], q43["lv"], lens, out=outs[1], workspace=ws[1])
+        kv.decode_partials(per_head.desc, q, per_head.pk, per_head.lat_k, per_head.lat_v, lens, ws[3], split_tokens=128)
+        kv.decode_combine(per_head.desc, per_head.pv, ws[3], outs[2], split_tokens=128)
+        kv.decode_attn_latent(per_head.desc, q_lat, per_head.lat_k, per_head.lat_v, lens, o_lat=outs[3],
+                              workspace=ws[2])
+
+    step()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    g = _capture(step)
+    for rep in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, (o, e) in enumerate(zip(outs, eager)):
+            assert torch.equal(o, e), (rep, k)
+    say("[graph] joint, 4/3-bit, two-stage and folded calls: 3 replays equal the eager calls")
