@@ -14,9 +14,14 @@
 // fp32 accumulator), so products carry ~16 bits of the basis and the only
 // rounding of note is the final one to the latent dtype. The basis operands
 // are staged once per workgroup in LDS, pre-arranged in operand order.
+// bf16 value latents take the product the other way round (A = the token
+// rows), so that each lane ends with 4 consecutive tokens of one latent
+// channel: the decode kernels' value-product operand order, stored as one
+// 8-byte piece.
 //
-// fp32 inputs (and any other combination) use a plain VALU kernel; append
-// uses one workgroup per (batch row, KV head, K or V).
+// fp32 inputs, ranks that are not whole 16-channel tiles, 4/3-bit latents and
+// joint value latents use a plain VALU kernel; append uses one workgroup per
+// (batch row, KV head, K or V).
 //
 // Mixed 4/3-bit latents (STAR-KV technical summary, "Metodologia" section 3)
 // are quantised from the fp32 latents of a row by one thread per row; the

@@ -8,21 +8,22 @@
 // back-projected once by P_V^T after the splits are merged.
 //
 // Work decomposition: one workgroup (4 waves) per (split of the sequence,
-// KV head, group of <= 4 query heads sharing it, batch row). Each wave walks
-// 64-token tiles of the split; waves keep a running max / sum / weighted
-// latent sum (online softmax, base-2 domain) and the workgroup merges its 4
-// waves into one partial record (m, l, o_lat[r_v]) per query head. A second
-// kernel merges the records of all splits with log-sum-exp weights and
-// applies P_V^T.
+// KV head, group of <= 4 query heads sharing it, batch row). The waves take
+// the split's token steps round robin and keep a running max / sum /
+// weighted latent sum (online softmax, base-2 domain); the workgroup merges
+// its 4 waves into one partial record (m, l, o_lat[r_v]) per query head. In
+// the single-launch form the workgroup that finishes last for its group
+// merges the records of all splits with log-sum-exp weights and applies
+// P_V^T (finish_split); the two-stage form leaves the records to decode_merge.
 //
-// bf16 latents: the score tile S[head][token] = q~ . K_lat is one MFMA chain
-// per 16 tokens (v_mfma_f32_16x16x32_bf16, query heads as rows, tokens as
-// columns, the key latent rows loaded straight from HBM into the B operand,
-// 16 contiguous bytes per lane). q~ is fp32; it enters the MFMA as a high
-// and a low bf16 part (two MFMAs into one fp32 accumulator), so scores keep
-// ~16 bits of the query. The value side (p-weighted sum of V_lat rows) runs
-// on VALU: each lane owns 8 latent channels of a subset of rows, reading 16
-// coalesced bytes per row chunk, and p comes through LDS.
+// bf16 latents (decode_split_bf16): both products on MFMA. Scores are formed
+// transposed, S^T = K_lat q~^T, with the key rows as the A operand straight
+// from HBM (operand-order layout, 16 contiguous bytes per lane) and q~ as B
+// in a high and a low bf16 part, so a lane ends with 4 consecutive tokens of
+// one query head: the A operand of the value product, whose value rows are
+// stored in its B-operand order. 4/3-bit latents (decode_split_q43): keys on
+// MFMA from the stored codes, values on VALU. fp32 latents
+// (decode_split_f32): VALU throughout.
 #include "decode_common.hpp"
 
 namespace kvlr {

@@ -12,7 +12,7 @@ namespace kvlr {
 constexpr int kMaxKvHeads = 64;   // per-head tables travel in the kernel argument block
 constexpr int kMaxRank = 128;     // rank bound of the decode kernels' register tiles
 constexpr int kHeadsPerWg = 4;    // query heads sharing one KV head handled by one workgroup
-constexpr int kTile = 64;         // tokens per wave iteration in decode
+constexpr int kTile = 64;         // tokens per wave iteration of the fp32 decode kernel; splits are multiples of it
 constexpr int kWaves = 4;         // waves per decode workgroup
 
 // Per-KV-head tables: ranks and prefix sums of ranks (latent and basis offsets).
@@ -120,7 +120,9 @@ __host__ __device__ inline size_t v_joint_offset(int t, int j, int r) {
 
 // Offset (elements) of bf16 key latent (t, j) inside its (batch row, KV head)
 // block, rank rk (a multiple of 16). Each 16-row block holds the rows in the
-// order the score MFMA reads its B operand: for every 32-channel pair
+// order the score MFMA reads its key operand (lane n + 16 q: token n, channels
+// 8 q .. 8 q + 7 of a pair; the A operand of the transposed score product):
+// for every 32-channel pair
 // [lane group q][token n][8 channels], then a 16-channel tail as
 // [q][n][4 channels]; a 64-lane load then reads 1 KiB (512 B for the tail)
 // contiguously.
