@@ -63,6 +63,9 @@ typedef enum kvlr_status {
                               16-byte aligned) */
 } kvlr_status;
 
+/* split_tokens value that asks kvlr_decode_attn for the balanced plan. */
+#define KVLR_SPLIT_BALANCED (-1)
+
 /* Element types. */
 typedef enum kvlr_dtype {
   KVLR_F32 = 0,  /* IEEE binary32 */
@@ -177,10 +180,13 @@ KVLR_API int kvlr_cache_elems(const kvlr_desc* desc, size_t* k_elems, size_t* v_
 /* Bytes of decode workspace that kvlr_decode_attn needs for this
  * descriptor and split length (split_tokens as in kvlr_decode_attn; 0 picks
  * the library's choice, the same one kvlr_decode_attn makes for 0).
- * Layout: int32 arrival counters (kvlr_decode_counter_bytes bytes), then one
- * fp32 record [B][Hq][n_splits][round_up(max_h r_v[h] + 2, 4)] per split,
- * then (joint values with bf16 latents only) the projected queries, fp32
- * [B][Hq][max_h r_k[h]]. */
+ * Layout: int32 arrival counters (kvlr_decode_counter_bytes bytes), then the
+ * fp32 split records of round_up(max_h r_v[h] + 2, 4) floats each:
+ * [B][Hq][n_splits] for a fixed split length; with split_tokens 0 or -1 on
+ * caches that allow the balanced plan, the region also fits that plan's
+ * (n_wg + B Hkv ceil(G / 4)) slots of 4 records (n_wg = its workgroups), so one
+ * workspace serves both plans; then (joint values with bf16 latents only) the
+ * projected queries, fp32 [B][Hq][max_h r_k[h]]. */
 KVLR_API int kvlr_decode_workspace_bytes(const kvlr_desc* desc, int32_t split_tokens, size_t* bytes);
 
 /* Size of the counter region at the start of a decode workspace:
@@ -189,7 +195,8 @@ KVLR_API int kvlr_decode_counter_bytes(const kvlr_desc* desc, size_t* bytes);
 
 /* Splits that kvlr_decode_attn uses per (batch row, KV head) for
  * split_tokens (0 = library choice: one round of workgroups over the
- * device), and the tokens per split. */
+ * device), and the tokens per split. For the balanced plan: n_splits is its
+ * number of workgroups (one round over the device) and tokens_per_split 0. */
 KVLR_API int kvlr_decode_plan(const kvlr_desc* desc, int32_t split_tokens, int32_t* n_splits,
                               int32_t* tokens_per_split);
 
@@ -254,12 +261,20 @@ KVLR_API int kvlr_append(const kvlr_desc* desc, const void* k_new, const void* v
  *             first kvlr_decode_attn call that uses it; every completed call
  *             leaves it zero again. The records need no initialisation.
  *             Calls sharing one workspace must be ordered on one stream.
- *   split_tokens 0 for the library's choice (see kvlr_decode_plan), or a
+ *   split_tokens 0 for the library's choice (see kvlr_decode_plan), a
  *             multiple of 64: tokens per split of the sequence (every split
- *             yields a partial
- *             softmax state; the workgroup that finishes last for a group of
- *             query heads merges the states and back-projects with P_V^T,
- *             all in one kernel launch)
+ *             yields a partial softmax state; the workgroup that finishes
+ *             last for a group of query heads merges the states and
+ *             back-projects with P_V^T, all in one kernel launch), or
+ *             KVLR_SPLIT_BALANCED (-1): the balanced plan (bf16 latents with
+ *             per-head values; other caches take the library's choice). The
+ *             kernel reads seq_lens and gives every workgroup an equal share
+ *             of the work, each token counting a fixed part plus its latent
+ *             elements, cut across (batch row, KV head) units where needed;
+ *             the last workgroup to finish a unit merges it. The plan depends
+ *             only on seq_lens, so results are reproducible. The library's
+ *             choice is the balanced plan when the KV heads' ranks differ
+ *             (batches of 4096 rows at most), the fixed one otherwise.
  * Scores and the softmax are computed in fp32; bf16 latents are read as
  * stored and multiplied in fp32 (the key side on MFMA with the query split
  * into a high and a low bf16 part).
@@ -314,9 +329,15 @@ KVLR_API int kvlr_append_decode_attn(const kvlr_desc* desc, const void* k_new, c
 /* The two stages of kvlr_decode_attn, for callers that schedule them
  * separately (e.g. to time or overlap them). kvlr_decode_partials(...)
  * followed by kvlr_decode_combine(...) on the same stream with the same
- * workspace and split_tokens gives kvlr_decode_attn's result: the same split
- * records, merged in another order (per-head values: fp32 rounding of the
- * merge may differ; joint bf16 values: bit for bit, the launches are the same).
+ * workspace and split_tokens gives kvlr_decode_attn's result: with a fixed
+ * split length the same split records, merged in another order (per-head
+ * values: fp32 rounding of the merge may differ; joint bf16 values: bit for
+ * bit, the launches are the same); where kvlr_decode_attn takes the balanced
+ * plan, other cuts of the sequences, so the softmax weights round differently
+ * (about 1e-5 relative).
+ *
+ * The two stages always take a fixed split length (split_tokens -1 means the
+ * library's fixed choice here).
  *
  * kvlr_decode_partials: query projection q~ = q P_K, latent scores, online
  * softmax and the p-weighted sum of value latents for every split of every

@@ -39,6 +39,7 @@ __all__ = [
 
 F32, BF16, Q43 = 0, 1, 2
 VALUES_PER_HEAD, VALUES_JOINT = 0, 1
+SPLIT_BALANCED = -1   # split_tokens asking kvlr_decode_attn for the balanced plan
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvlr.so")
 

@@ -40,6 +40,56 @@ bool joint_bf16(const kvlr_desc* d) {
 
 int rank_bound_of(int r) { return r <= 32 ? 32 : r <= 64 ? 64 : r <= 96 ? 96 : 128; }
 
+// Balanced plan (bf16 latents, per-head values, single-launch decode): the kernel
+// reads seq_lens and gives every workgroup an equal share of the bytes. Taken on
+// request (split_tokens = -1) and by default when the KV heads' ranks differ; the
+// batch's prefix sums live in LDS (int64) and the kernel's 64-bit work positions
+// times the workgroup count must not overflow.
+constexpr int kSplitBalanced = -1;
+constexpr int kTokenFixedCost = 512;   // measured on ragged per-head ranks 16..96 (256..2048 within 3%)
+constexpr int kMaxBalancedBatch = 4096;
+
+int head_groups_of(const kvlr_desc* d) {
+  return (d->n_q_heads / d->n_kv_heads + kvlr::kHeadsPerWg - 1) / kvlr::kHeadsPerWg;
+}
+
+// Work of one token of KV head h in the balanced plan: its latent elements plus a
+// fixed part for the arithmetic every token costs whatever its rank (softmax,
+// masks, loop control); KVLR_BALANCE_FIXED overrides the fixed part for tuning.
+int token_fixed_cost() {
+  const char* env = getenv("KVLR_BALANCE_FIXED");
+  const int v = env ? atoi(env) : kTokenFixedCost;
+  return v < 0 ? 0 : v > 4096 ? 4096 : v;
+}
+int token_cost(const kvlr_desc* d, int h) { return token_fixed_cost() + d->r_k[h] + d->r_v[h]; }
+
+long long row_cost_of(const kvlr_desc* d) {
+  long long c = 0;
+  for (int h = 0; h < d->n_kv_heads; ++h) c += token_cost(d, h);
+  return c * head_groups_of(d);
+}
+
+bool ranks_differ(const kvlr_desc* d) {
+  for (int h = 1; h < d->n_kv_heads; ++h)
+    if (d->r_k[h] != d->r_k[0] || d->r_v[h] != d->r_v[0]) return true;
+  return false;
+}
+
+bool supports_balanced(const kvlr_desc* d) {
+  if (d->latent_dtype != KVLR_BF16 || d->value_mode != KVLR_VALUES_PER_HEAD) return false;
+  if (d->batch > kMaxBalancedBatch) return false;
+  return (long long)d->batch * d->capacity * row_cost_of(d) <= (1LL << 46);   // row_cost <= 2^20 x 4 groups
+}
+
+bool balanced_plan(const kvlr_desc* d, int32_t split_tokens) {
+  return supports_balanced(d) && (split_tokens == kSplitBalanced || (split_tokens == 0 && ranks_differ(d)));
+}
+
+// Workgroups of the balanced plan: one round over the device.
+int balanced_wgs(const kvlr_desc* d, int rank_bound) {
+  return kComputeUnits * resident_wgs_per_cu(d->latent_dtype, rank_bound);
+}
+
 // Largest key rank and its kernel bound.
 int rk_max_of(const kvlr_desc* d) {
   int m = 0;
@@ -121,6 +171,7 @@ int plan_split(const kvlr_desc* d, int32_t split_tokens, int* n_splits, int* len
   const int G = d->n_q_heads / d->n_kv_heads;
   const int groups = (G + kvlr::kHeadsPerWg - 1) / kvlr::kHeadsPerWg;
   int len;
+  if (split_tokens == kSplitBalanced) split_tokens = 0;   // the fixed plan behind a balanced request
   if (split_tokens < 0 || split_tokens % kSplitGranule != 0) return KVLR_ERR_ARG;
   if (split_tokens > 0) {
     len = split_tokens;
@@ -152,6 +203,21 @@ int ws_stride_of(const HeadTable& ht, int Hkv) {
   int m = 0;
   for (int h = 0; h < Hkv; ++h) m = ht.rv[h] > m ? ht.rv[h] : m;
   return (m + 2 + 3) / 4 * 4;
+}
+
+// Record region of the workspace: [B][Hq][n_splits][stride] fp32 for the fixed
+// plan; with split_tokens 0 or -1 on caches that allow the balanced plan, also
+// room for its (n_wg + B Hkv head_groups) slots of 4 records, so that one
+// workspace serves both plans.
+size_t record_bytes_of(const kvlr_desc* d, const HeadTable& ht, int32_t split_tokens, int n_splits, int rank_bound) {
+  const size_t stride = ws_stride_of(ht, d->n_kv_heads);
+  size_t bytes = (size_t)d->batch * d->n_q_heads * n_splits * stride * sizeof(float);
+  if ((split_tokens == 0 || split_tokens == kSplitBalanced) && supports_balanced(d)) {
+    const size_t slots = (size_t)balanced_wgs(d, rank_bound) + (size_t)d->batch * d->n_kv_heads * head_groups_of(d);
+    const size_t bal = slots * kvlr::kHeadsPerWg * stride * sizeof(float);
+    bytes = bal > bytes ? bal : bytes;
+  }
+  return bytes;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? KVLR_OK : KVLR_ERR_HIP; }
@@ -218,6 +284,12 @@ KVLR_API int kvlr_decode_plan(const kvlr_desc* desc, int32_t split_tokens, int32
   int ns = 0, len = 0;
   rc = plan_split(desc, split_tokens, &ns, &len);
   if (rc) return rc;
+  if (balanced_plan(desc, split_tokens)) {   // workgroups of equal shares; no fixed split length
+    int rank_bound = 0;
+    check_desc(desc, nullptr, nullptr, nullptr, &rank_bound);
+    ns = balanced_wgs(desc, rank_bound);
+    len = 0;
+  }
   *n_splits = ns;
   *tokens_per_split = len;
   return KVLR_OK;
@@ -225,15 +297,14 @@ KVLR_API int kvlr_decode_plan(const kvlr_desc* desc, int32_t split_tokens, int32
 
 KVLR_API int kvlr_decode_workspace_bytes(const kvlr_desc* desc, int32_t split_tokens, size_t* bytes) {
   HeadTable ht;
-  int rc = check_desc(desc, &ht, nullptr, nullptr, nullptr);
+  int rank_bound = 0;
+  int rc = check_desc(desc, &ht, nullptr, nullptr, &rank_bound);
   if (rc) return rc;
   if (!bytes) return KVLR_ERR_NULL;
   int ns = 0, len = 0;
   rc = plan_split(desc, split_tokens, &ns, &len);
   if (rc) return rc;
-  *bytes = counter_bytes_of(desc) +
-           (size_t)desc->batch * desc->n_q_heads * ns * ws_stride_of(ht, desc->n_kv_heads) * sizeof(float) +
-           qt_bytes_of(desc);
+  *bytes = counter_bytes_of(desc) + record_bytes_of(desc, ht, split_tokens, ns, rank_bound) + qt_bytes_of(desc);
   return KVLR_OK;
 }
 
@@ -323,10 +394,12 @@ KVLR_API int kvlr_hadamard_bases(const kvlr_desc* desc, const float* P_K, const 
 namespace {
 
 // Shared checks of the decode stages; fills the kernel parameter blocks.
+// single_launch: decode_attn and its folded and fused forms, which may take the
+// balanced plan; the two stages always take the fixed plan.
 int prepare_decode(const kvlr_desc* desc, const float* q, const float* P_K, const void* lat_k, const void* lat_v,
                    const int32_t* seq_lens, float scale, const float* P_V, float* out, bool need_partials,
                    bool need_combine, void* workspace, size_t workspace_bytes, int32_t split_tokens,
-                   kvlr::DecodeParams* p, kvlr::MergeParams* m, int* rank_bound) {
+                   kvlr::DecodeParams* p, kvlr::MergeParams* m, int* rank_bound, bool single_launch = false) {
   int rc = check_desc(desc, &p->ht, &p->Rk, &p->Rv, rank_bound, &p->Sk, &p->Sv);
   p->qt_in = nullptr;
   p->qt_stride = 0;
@@ -340,8 +413,16 @@ int prepare_decode(const kvlr_desc* desc, const float* q, const float* P_K, cons
   if (rc) return rc;
   const int stride = ws_stride_of(p->ht, desc->n_kv_heads);
   const size_t cbytes = counter_bytes_of(desc);
-  const size_t rec_bytes = (size_t)desc->batch * desc->n_q_heads * ns * stride * sizeof(float);
+  const size_t rec_bytes = record_bytes_of(desc, p->ht, split_tokens, ns, *rank_bound);
   const size_t need = cbytes + rec_bytes + qt_bytes_of(desc);
+  p->balanced = single_launch && balanced_plan(desc, split_tokens);
+  p->n_wg = p->balanced ? balanced_wgs(desc, *rank_bound) : 0;
+  p->row_cost = p->balanced ? (int)row_cost_of(desc) : 0;
+  for (int h = 0, c = 0; h < desc->n_kv_heads; ++h) {
+    p->ht.cost[h] = token_cost(desc, h);
+    p->ht.cost_pre[h] = c;
+    c += p->ht.cost[h];
+  }
   if (!workspace || workspace_bytes < need) return KVLR_ERR_WORKSPACE;
 
   const int G = desc->n_q_heads / desc->n_kv_heads;
@@ -451,7 +532,7 @@ KVLR_API int kvlr_decode_attn(const kvlr_desc* desc, const float* q, const float
   kvlr::MergeParams m;
   int rank_bound = 0;
   const int rc = prepare_decode(desc, q, P_K, lat_k, lat_v, seq_lens, scale, P_V, out, true, true, workspace,
-                                workspace_bytes, split_tokens, &p, &m, &rank_bound);
+                                workspace_bytes, split_tokens, &p, &m, &rank_bound, true);
   if (rc) return rc;
   if (joint_bf16(desc)) {   // projection, split and merge launches
     const hipStream_t s = static_cast<hipStream_t>(stream);
@@ -473,7 +554,7 @@ KVLR_API int kvlr_decode_attn_latent(const kvlr_desc* desc, const float* q_lat, 
   int rank_bound = 0;
   // q_lat stands in for q and P_K (checked non-NULL through the same slots); no P_V is read
   const int rc = prepare_decode(desc, q_lat, q_lat, lat_k, lat_v, seq_lens, scale, q_lat, o_lat, true, true,
-                                workspace, workspace_bytes, split_tokens, &p, &m, &rank_bound);
+                                workspace, workspace_bytes, split_tokens, &p, &m, &rank_bound, true);
   if (rc) return rc;
   int rk_max = 0, rv_max = 0;
   for (int h = 0; h < desc->n_kv_heads; ++h) {
@@ -513,8 +594,9 @@ KVLR_API int kvlr_append_decode_attn(const kvlr_desc* desc, const void* k_new, c
                           workspace_bytes, split_tokens, &p, &m, &rank_bound);
   if (rc) return rc;
   if (!k_new || !v_new || !pos) return KVLR_ERR_NULL;
-  if (desc->latent_dtype != KVLR_BF16 || desc->value_mode != KVLR_VALUES_PER_HEAD) {
-    // other caches: the append kernel, then the decode (two launches, the same result)
+  if (desc->latent_dtype != KVLR_BF16 || desc->value_mode != KVLR_VALUES_PER_HEAD ||
+      balanced_plan(desc, split_tokens)) {
+    // other caches and the balanced plan: the append kernel, then the decode (two launches, the same result)
     rc = kvlr_append(desc, k_new, v_new, pos, P_K, P_V, lat_k, lat_v, stream);
     if (rc) return rc;
     return kvlr_decode_attn(desc, q, P_K, P_V, lat_k, lat_v, seq_lens, scale, out, workspace, workspace_bytes,

@@ -47,9 +47,9 @@ constexpr int value_iters_bound(int rb, int tile) {
 //   the caller; value(w, g, j) returns wave w's unnormalised latent sum for
 //   head g, channel j.
 template <typename ValueFn>
-__device__ __forceinline__ void merge_waves_and_store(const DecodeParams& p, int b, int hq0, int gpw, int s,
-                                                      int rv, const float* wm, const float* wl, ValueFn value) {
-  for (int idx = threadIdx.x; idx < gpw * rv; idx += blockDim.x) {
+__device__ __forceinline__ void merge_waves_and_store(const RecLayout& rl, int k, int gpw, int rv, const float* wm,
+                                                      const float* wl, ValueFn value) {
+  for (int idx = thread_id(); idx < gpw * rv; idx += blockDim.x) {
     const int g = idx / rv, j = idx - g * rv;
     float M = kNegInf;
 #pragma unroll
@@ -63,7 +63,7 @@ __device__ __forceinline__ void merge_waves_and_store(const DecodeParams& p, int
         o = fmaf(f, value(w, g, j), o);
       }
     }
-    float* rec = p.ws + (((size_t)b * p.Hq + hq0 + g) * p.n_splits + s) * p.ws_stride;
+    float* rec = rec_at(rl, k, g);
     store_rec(rec + 2 + j, o);
     if (j == 0) {
       store_rec(rec, M);
@@ -101,7 +101,7 @@ template <int RB>
 __device__ __forceinline__ void prefetch_basis(const DecodeParams& p, int h, int rv, BasisPrefetch<RB>& pf) {
   if (!p.fuse || p.out_latent || p.d > 128) return;
   const float* P = p.pv + (size_t)p.d * p.ht.rv_pre[h];
-  const int m = threadIdx.x & 15, rg = threadIdx.x >> 4;
+  const int m = thread_id() & 15, rg = thread_id() >> 4;
   const int per_row4 = rv >> 2;
 #pragma unroll
   for (int k = 0; k < 8; ++k)
@@ -115,18 +115,19 @@ __device__ __forceinline__ void prefetch_basis(const DecodeParams& p, int h, int
 
 template <int RB>
 __device__ __forceinline__ void finish_split(const DecodeParams& p, int b, int h, int hg, int hq0, int gpw,
-                                             int rv, float* scratch, const BasisPrefetch<RB>& pf) {
+                                             int rv, float* scratch, const BasisPrefetch<RB>& pf,
+                                             const RecLayout& rl, int n_rec) {
   if (!p.fuse) return;
   int* flag = reinterpret_cast<int*>(scratch + kTailLds - 1);
   int* counter = p.counters + ((size_t)b * p.Hkv + h) * p.n_head_groups + hg;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (threadIdx.x == 0)
-    *flag = (__hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == p.n_splits - 1);
+  if (thread_id() == 0)
+    *flag = (__hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n_rec - 1);
   __syncthreads();
   if (*flag == 0) return;
 
-  const int tid = threadIdx.x, lane = tid & 63, g = tid >> 6;
+  const int tid = thread_id(), lane = tid & 63, g = tid >> 6;
   const int d = p.d;
   const bool reg_basis = d <= 128;              // P_V already in registers (see BasisPrefetch)
   float* olat = scratch;                        // [RB][4] head-minor
@@ -147,13 +148,12 @@ __device__ __forceinline__ void finish_split(const DecodeParams& p, int b, int h
   // wave g folds the records of head g in one pass with a running maximum
   float M = kNegInf, L = 0.f, o0 = 0.f, o1 = 0.f;
   if (g < gpw) {
-    const float* r0 = p.ws + ((size_t)b * p.Hq + hq0 + g) * p.n_splits * p.ws_stride;
-    for (int s0 = 0; s0 < p.n_splits; s0 += 8) {
+    for (int s0 = 0; s0 < n_rec; s0 += 8) {
       float ms[8], ls[8], v0[8], v1[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const bool ok = s0 + u < p.n_splits;
-        const float* r = r0 + (size_t)(s0 + u) * p.ws_stride;
+        const bool ok = s0 + u < n_rec;
+        const float* r = rec_at(rl, ok ? s0 + u : 0, g);
         ms[u] = ok ? load_rec(r) : kNegInf;
         ls[u] = ok ? load_rec(r + 1) : 0.f;
         v0[u] = (ok && lane < rv) ? load_rec(r + 2 + lane) : 0.f;
@@ -281,7 +281,7 @@ __device__ __forceinline__ bool append_owner(const DecodeParams& p, int b, int h
 }
 
 __device__ void append_rows(const DecodeParams& p, int b, int h, int rk, int rv, float* xs) {
-  const int d = p.d, tid = threadIdx.x;
+  const int d = p.d, tid = thread_id();
   const int pos = p.pos[b];
   for (int i = tid; i < 2 * d; i += blockDim.x) {   // k_new row to xs[0, d), v_new row to xs[256, 256 + d)
     const int kind = i >= d, ii = i - kind * d;
@@ -331,35 +331,30 @@ __device__ void append_rows(const DecodeParams& p, int b, int h, int rk, int rv,
 //    product's B-operand order (v_joint_offset), 16 bytes per lane per channel
 //    pair. Value rows past the sequence end may hold any bits and are zeroed.
 // The waves' states meet in LDS and leave one record per query head and split.
+// One segment [t_begin, t_end) of the sequence of (batch row b, KV head h, head
+// group hg): stream it, leave record k of the group's records rl, and, in the
+// single-launch form, take part in the group's merge of its n_rec records.
 template <int RB, int TT>
-__global__ __launch_bounds__(256) void decode_split_bf16(DecodeParams p) {
+__device__ __forceinline__ void bf16_segment(const DecodeParams& p, int b, int h, int hg, int t_begin, int t_end,
+                                             const RecLayout& rl, int k, int n_rec, float* smem) {
   constexpr int NB = TT / 16;
   constexpr int NP = RB / 32;                 // key channel pairs bound
   constexpr int kVP = RB / 32;                // value channel pairs bound (a tail fills half a pair)
   constexpr int kCT = RB / 16;                // value column tiles bound
   constexpr int QTS = RB;                     // q~ LDS row stride
-  __shared__ __attribute__((aligned(16))) float smem[kTailLds];
 
-  const int s = blockIdx.x;
-  const int h = blockIdx.y / p.n_head_groups;
-  const int hg = blockIdx.y - h * p.n_head_groups;
-  const int b = blockIdx.z;
   const int hq0 = h * p.G + hg * kHeadsPerWg;
   const int gpw = min(kHeadsPerWg, p.G - hg * kHeadsPerWg);
   const int rk = p.ht.rk[h], rv = p.ht.rv[h];
-  const int T = min(max(p.seq_lens[b], 0), p.cap);
-  const int t_begin = min(s * p.ht.split_len[h], T);   // clamped: no overflow for far splits
-  const int t_end = min(T, t_begin + p.ht.split_len[h]);
-  if (append_owner(p, b, h, s)) append_rows(p, b, h, rk, rv, smem);
   if (t_begin >= t_end) {
-    write_empty_records(p, b, hq0, gpw, s, rv);
+    write_empty_records(rl, k, gpw, rv);
     BasisPrefetch<RB> pf;
     prefetch_basis<RB>(p, h, rv, pf);
-    finish_split<RB>(p, b, h, hg, hq0, gpw, rv, smem, pf);
+    finish_split<RB>(p, b, h, hg, hq0, gpw, rv, smem, pf, rl, n_rec);
     return;
   }
 
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = thread_id(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = lane & 15, q4 = lane >> 4;
   const int np = rk >> 5, ktail = (rk >> 4) & 1;
@@ -556,9 +551,198 @@ __global__ __launch_bounds__(256) void decode_split_bf16(DecodeParams p) {
     }
   }
   __syncthreads();
-  merge_waves_and_store(p, b, hq0, gpw, s, rv, wm, wl,
+  merge_waves_and_store(rl, k, gpw, rv, wm, wl,
                         [&](int w, int g, int j) { return red[(w * kHeadsPerWg + g) * RB + j]; });
-  finish_split<RB>(p, b, h, hg, hq0, gpw, rv, smem, pf);
+  finish_split<RB>(p, b, h, hg, hq0, gpw, rv, smem, pf, rl, n_rec);
+}
+
+// Values equal in every lane, made wave-uniform for the compiler (scalar registers).
+__device__ __forceinline__ int uniform32(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// floor(a / b) for 0 <= a < 2^62 and 0 < b: a double-precision quotient (within one
+// of the exact one for every operand here) corrected with the remainder; far fewer
+// instructions than a 64-bit integer division.
+__device__ __forceinline__ long long div64(long long a, long long b) {
+  long long q = (long long)((double)a / (double)b);
+  long long r = a - q * b;
+  while (r < 0) {
+    --q;
+    r += b;
+  }
+  while (r >= b) {
+    ++q;
+    r -= b;
+  }
+  return q;
+}
+
+// Lane `src` (wave-uniform) of a 64-bit value, as a wave-uniform value.
+__device__ __forceinline__ long long readlane64(long long x, int src) {
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(x & 0xFFFFFFFFll), src);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(x >> 32), src);
+  return (long long)(((unsigned long long)hi << 32) | lo);
+}
+
+// 64-bit shuffle up by d lanes (two 32-bit halves).
+__device__ __forceinline__ long long shfl_up64(long long x, int d) {
+  const int lo = __shfl_up((int)(unsigned)(x & 0xFFFFFFFFll), d, 64);
+  const int hi = __shfl_up((int)(x >> 32), d, 64);
+  return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
+}
+
+// Balanced plan: the call's work W = sum_b T_b * row_cost (row_cost = sum over the
+// (KV head, head group) units of a batch row of cost[h], the work of one token:
+// its latent elements r_k + r_v plus a fixed part for the per-step arithmetic)
+// is cut into P = gridDim.x equal shares [w W / P, (w + 1) W / P) along
+// the units in (b, h, hg) order. A share may span several units and a unit
+// several shares; inside a unit the cuts fall on multiples of kBalancedTokens
+// tokens, computed the same way by both neighbours. Workgroup w streams its
+// segment of every unit it meets and leaves a record in slot w_first(u) + u + k,
+// where w_first(u) is the first workgroup whose share meets unit u; the last
+// workgroup to arrive for a unit merges its records. Batch rows without tokens
+// get zero output rows from workgroup b % P. The plan reads seq_lens on the
+// device and depends on nothing else, so every run gives the same result.
+constexpr int kBalancedTokens = 128;
+
+template <int RB, int TT>
+__device__ __forceinline__ void decode_balanced(const DecodeParams& p, float* smem) {
+  const int tid = thread_id(), lane = tid & 63;
+  const int B = p.B, w = blockIdx.x;
+  const long long C = p.row_cost;
+  // Every wave works out the plan on its own, from the clamped lengths 64 rows at a
+  // time (an inclusive scan across the lanes), so the plan needs no LDS and no barrier.
+  auto len_of = [&](int bi) { return bi < B ? (long long)min(max(p.seq_lens[bi], 0), p.cap) : 0ll; };
+  auto scan = [&](long long v) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const long long y = shfl_up64(v, off);
+      if (lane >= off) v += y;
+    }
+    return v;
+  };
+  long long total = 0;
+  for (int c0 = 0; c0 < B; c0 += 64) total += readlane64(scan(len_of(c0 + lane)), 63);
+  const long long W = total * C;
+  for (int b = w; b < B; b += gridDim.x) {   // rows without tokens: zero outputs
+    if (len_of(b) == 0) {
+      const int n = p.Hq * p.out_stride;
+      float* o = p.out + (size_t)b * n;
+      for (int i = tid; i < n; i += blockDim.x) o[i] = 0.f;
+    }
+  }
+  const long long P = min((long long)gridDim.x, W);   // every share non-empty
+  if (w >= P) return;
+  const long long x0 = div64(w * W, P), x1 = div64((w + 1) * W, P);
+  // the unit holding x0: its batch row is the last one whose rows before it hold
+  // at most x0 / C work (a row with tokens, since x0 < W)
+  int b = -1;
+  long long row0 = 0;
+  int T = 0;
+  long long carry = 0;
+  for (int c0 = 0; c0 < B; c0 += 64) {
+    const long long v = len_of(c0 + lane);
+    const long long incl = scan(v);
+    const long long excl = carry + incl - v;
+    const unsigned long long m = __ballot(c0 + lane < B && excl * C <= x0);
+    if (m) {
+      const int last = 63 - __builtin_clzll(m);
+      b = c0 + last;
+      row0 = readlane64(excl, last) * C;
+      T = (int)readlane64(v, last);
+    }
+    carry += readlane64(incl, 63);
+  }
+  b = uniform32(b);
+  T = uniform32(T);
+  const int n_hg = p.n_head_groups;
+  const long long v0 = div64(x0 - row0, T);   // position along the row's per-token cost axis
+  // its KV head: the last h with n_hg cost_pre[h] <= v0 (one load per lane, then a ballot)
+  const unsigned long long hm =
+      __ballot(lane < p.Hkv && (long long)n_hg * p.ht.cost_pre[lane < p.Hkv ? lane : 0] <= v0);
+  int h = uniform32(63 - __builtin_clzll(hm));
+  int hg = (int)div64(v0 - (long long)n_hg * p.ht.cost_pre[h], p.ht.cost[h]);
+  hg = min(hg, n_hg - 1);
+  // The walk over units keeps its state in LDS between segments: held in registers
+  // across the whole segment body, it would push the kernel past its scalar registers.
+  __shared__ long long st_row0, st_x[4];   // st_x: x0, x1, W, P
+  __shared__ int st_b, st_T, st_h, st_hg;
+  if (tid == 0) {
+    st_x[0] = x0;
+    st_x[1] = x1;
+    st_x[2] = W;
+    st_x[3] = P;
+    st_row0 = row0;
+    st_b = b;
+    st_T = T;
+    st_h = h;
+    st_hg = hg;
+  }
+  __syncthreads();
+  for (;;) {
+    b = st_b;
+    T = st_T;
+    h = st_h;
+    hg = st_hg;
+    row0 = st_row0;
+    const long long x0 = st_x[0], x1 = st_x[1], W = st_x[2], P = st_x[3];
+    const int ch = p.ht.cost[h];
+    const long long S = row0 + (long long)T * ((long long)n_hg * p.ht.cost_pre[h] + (long long)hg * ch);
+    if (S >= x1) return;
+    const long long Wu = (long long)T * ch;
+    auto tok = [&](long long x) {   // token boundary of work position x inside this unit
+      if (x <= S) return 0;
+      long long t = div64(x - S + ch - 1, ch);
+      t = (t + kBalancedTokens - 1) / kBalancedTokens * kBalancedTokens;
+      return (int)min(t, (long long)T);
+    };
+    const int ta = tok(max(x0, S)), te = tok(min(x1, S + Wu));
+    const long long wf = div64((S + 1) * P - 1, W), wl = div64((S + Wu) * P - 1, W);
+    const long long u = ((long long)b * p.Hkv + h) * n_hg + hg;
+    const RecLayout rl{p.ws + (size_t)(wf + u) * kHeadsPerWg * p.ws_stride, (size_t)kHeadsPerWg * p.ws_stride,
+                       (size_t)p.ws_stride};
+    __syncthreads();   // every thread has read the state; the previous segment's LDS reads are done
+    if (tid == 0) {    // the next unit: head group, KV head, then the next batch row with tokens
+      int nb = b, nT = T, nh = h, nhg = hg + 1;
+      long long nrow0 = row0;
+      if (nhg == n_hg) {
+        nhg = 0;
+        if (++nh == p.Hkv) {
+          nh = 0;
+          do {
+            nrow0 += (long long)nT * C;
+            if (++nb >= B) break;
+            nT = min(max(p.seq_lens[nb], 0), p.cap);
+          } while (nT == 0);
+          if (nb >= B) nrow0 = x1;   // past the end: the next S >= x1 stops the walk
+        }
+      }
+      st_b = min(nb, B - 1);
+      st_T = nT;
+      st_h = nh;
+      st_hg = nhg;
+      st_row0 = nrow0;
+    }
+    bf16_segment<RB, TT>(p, b, h, hg, ta, te, rl, (int)(w - wf), (int)(wl - wf + 1), smem);
+  }
+}
+
+template <int RB, int TT, bool kBalanced>
+__global__ __launch_bounds__(256) void decode_split_bf16(DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) float smem[kTailLds];
+  if constexpr (kBalanced) {
+    decode_balanced<RB, TT>(p, smem);
+  } else {
+    const int s = blockIdx.x;
+    const int h = blockIdx.y / p.n_head_groups;
+    const int hg = blockIdx.y - h * p.n_head_groups;
+    const int b = blockIdx.z;
+    const int T = min(max(p.seq_lens[b], 0), p.cap);
+    const int t_begin = min(s * p.ht.split_len[h], T);   // clamped: no overflow for far splits
+    const int t_end = min(T, t_begin + p.ht.split_len[h]);
+    if (append_owner(p, b, h, s)) append_rows(p, b, h, p.ht.rk[h], p.ht.rv[h], smem);
+    bf16_segment<RB, TT>(p, b, h, hg, t_begin, t_end, fixed_records(p, b, h * p.G + hg * kHeadsPerWg), s,
+                         p.n_splits, smem);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -609,14 +793,14 @@ __global__ __launch_bounds__(256) void decode_split_q43(DecodeParams p) {
   const int t_begin = min(s * p.ht.split_len[h], T);
   const int t_end = min(T, t_begin + p.ht.split_len[h]);
   if (t_begin >= t_end) {
-    write_empty_records(p, b, hq0, gpw, s, rv);
+    write_empty_records(fixed_records(p, b, hq0), s, gpw, rv);
     BasisPrefetch<RB> pf;
     prefetch_basis<RB>(p, h, rv, pf);
-    finish_split<RB>(p, b, h, hg, hq0, gpw, rv, smem, pf);
+    finish_split<RB>(p, b, h, hg, hq0, gpw, rv, smem, pf, fixed_records(p, b, hq0), p.n_splits);
     return;
   }
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = thread_id(), lane = tid & 63, wave = tid >> 6;
   const int n16 = lane & 15, q4 = lane >> 4;
 
   // ---- key row geometry and this lane's byte offsets inside a row
@@ -926,7 +1110,7 @@ __global__ __launch_bounds__(256) void decode_split_q43(DecodeParams p) {
     }
   }
   __syncthreads();
-  merge_waves_and_store(p, b, hq0, gpw, s, rv, wm, wl, [&](int w, int g, int j) {
+  merge_waves_and_store(fixed_records(p, b, hq0), s, gpw, rv, wm, wl, [&](int w, int g, int j) {
     const int c = j >> 3, e = j & 7;
     const float* base = red + (w * 64 + c) * kRS + g * 8 + e;
     const int step = C * kRS;
@@ -935,7 +1119,7 @@ __global__ __launch_bounds__(256) void decode_split_q43(DecodeParams p) {
     for (int r = 0; r < rpi; ++r) sum += base[r * step];
     return sum;
   });
-  finish_split<RB>(p, b, h, hg, hq0, gpw, rv, smem, pf);
+  finish_split<RB>(p, b, h, hg, hq0, gpw, rv, smem, pf, fixed_records(p, b, hq0), p.n_splits);
 }
 
 // ---------------------------------------------------------------------------
@@ -961,13 +1145,13 @@ __global__ __launch_bounds__(256) void decode_split_f32(DecodeParams p) {
   const int t_begin = min(s * p.ht.split_len[h], T);   // clamped: no overflow for far splits
   const int t_end = min(T, t_begin + p.ht.split_len[h]);
   if (t_begin >= t_end) {
-    write_empty_records(p, b, hq0, gpw, s, rv);
+    write_empty_records(fixed_records(p, b, hq0), s, gpw, rv);
     BasisPrefetch<RB> pf;
     prefetch_basis<RB>(p, h, rv, pf);
-    finish_split<RB>(p, b, h, hg, hq0, gpw, rv, smem, pf);
+    finish_split<RB>(p, b, h, hg, hq0, gpw, rv, smem, pf, fixed_records(p, b, hq0), p.n_splits);
     return;
   }
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = thread_id(), lane = tid & 63, wave = tid >> 6;
 
   float* red = smem;                                  // [wave][4 heads][RB] at the end
   float* q_lds = smem + RED;                          // [4][d]
@@ -1067,9 +1251,9 @@ __global__ __launch_bounds__(256) void decode_split_f32(DecodeParams p) {
     }
   }
   __syncthreads();
-  merge_waves_and_store(p, b, hq0, gpw, s, rv, wm, wl,
+  merge_waves_and_store(fixed_records(p, b, hq0), s, gpw, rv, wm, wl,
                         [&](int w, int g, int j) { return red[(w * 4 + g) * RB + j]; });
-  finish_split<RB>(p, b, h, hg, hq0, gpw, rv, smem, pf);
+  finish_split<RB>(p, b, h, hg, hq0, gpw, rv, smem, pf, fixed_records(p, b, hq0), p.n_splits);
 }
 
 // ---------------------------------------------------------------------------
@@ -1097,7 +1281,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge(MergeParams p) {
   const int hq0 = h * p.G + hg * kHeadsPerWg;
   const int gpw = min(kHeadsPerWg, p.G - hg * kHeadsPerWg);
   const int rv = p.ht.rv[h];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = thread_id(), lane = tid & 63, wave = tid >> 6;
   const int ns = p.n_splits, stride = p.ws_stride, d = p.d;
   const size_t head_stride = (size_t)ns * stride;
   const float* recs = p.ws + ((size_t)b * p.Hq + hq0) * head_stride;
@@ -1217,19 +1401,27 @@ hipError_t launch_decode(const DecodeParams& p, int latent_dtype, int rank_bound
     return hipGetLastError();
   }
   if (latent_bf16) {
-    if (tile == 32) {
+    if (p.balanced) {   // one workgroup per share of the balanced plan
+      const dim3 grid_b(p.n_wg);
       switch (rank_bound) {
-        case 32: hipLaunchKernelGGL((decode_split_bf16<32, 32>), grid, block, 0, stream, p); break;
-        case 64: hipLaunchKernelGGL((decode_split_bf16<64, 32>), grid, block, 0, stream, p); break;
-        case 96: hipLaunchKernelGGL((decode_split_bf16<96, 32>), grid, block, 0, stream, p); break;
-        default: hipLaunchKernelGGL((decode_split_bf16<128, 32>), grid, block, 0, stream, p); break;
+        case 32: hipLaunchKernelGGL((decode_split_bf16<32, 32, true>), grid_b, block, 0, stream, p); break;
+        case 64: hipLaunchKernelGGL((decode_split_bf16<64, 32, true>), grid_b, block, 0, stream, p); break;
+        case 96: hipLaunchKernelGGL((decode_split_bf16<96, 32, true>), grid_b, block, 0, stream, p); break;
+        default: hipLaunchKernelGGL((decode_split_bf16<128, 32, true>), grid_b, block, 0, stream, p); break;
+      }
+    } else if (tile == 32) {
+      switch (rank_bound) {
+        case 32: hipLaunchKernelGGL((decode_split_bf16<32, 32, false>), grid, block, 0, stream, p); break;
+        case 64: hipLaunchKernelGGL((decode_split_bf16<64, 32, false>), grid, block, 0, stream, p); break;
+        case 96: hipLaunchKernelGGL((decode_split_bf16<96, 32, false>), grid, block, 0, stream, p); break;
+        default: hipLaunchKernelGGL((decode_split_bf16<128, 32, false>), grid, block, 0, stream, p); break;
       }
     } else {
       switch (rank_bound) {
-        case 32: hipLaunchKernelGGL((decode_split_bf16<32, 64>), grid, block, 0, stream, p); break;
-        case 64: hipLaunchKernelGGL((decode_split_bf16<64, 64>), grid, block, 0, stream, p); break;
-        case 96: hipLaunchKernelGGL((decode_split_bf16<96, 64>), grid, block, 0, stream, p); break;
-        default: hipLaunchKernelGGL((decode_split_bf16<128, 64>), grid, block, 0, stream, p); break;
+        case 32: hipLaunchKernelGGL((decode_split_bf16<32, 64, false>), grid, block, 0, stream, p); break;
+        case 64: hipLaunchKernelGGL((decode_split_bf16<64, 64, false>), grid, block, 0, stream, p); break;
+        case 96: hipLaunchKernelGGL((decode_split_bf16<96, 64, false>), grid, block, 0, stream, p); break;
+        default: hipLaunchKernelGGL((decode_split_bf16<128, 64, false>), grid, block, 0, stream, p); break;
       }
     }
   } else {

@@ -7,6 +7,16 @@
 namespace kvlr {
 namespace {
 
+// threadIdx.x through an empty asm: a value the compiler cannot hoist out of a
+// loop. Without it, the balanced decode kernel (a loop over segments, each the
+// whole split body) keeps every lane-derived address of the body live across
+// the loop and runs out of registers.
+__device__ __forceinline__ int thread_id() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 constexpr float kNegInf = -__builtin_huge_valf();
 
 // ---------------------------------------------------------------------------
@@ -21,7 +31,7 @@ constexpr float kNegInf = -__builtin_huge_valf();
 template <int RB>
 __device__ __forceinline__ void project_query(const DecodeParams& p, int b, int h, int hq0, int gpw, int rk,
                                               float* q_lds, float* red, float* qt_lds) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = thread_id(), lane = tid & 63, wave = tid >> 6;
   const int d = p.d;
   if (p.qt_in) {   // folded mode: q~ [B][Hq][qt_stride] given in latent space
     for (int idx = tid; idx < kHeadsPerWg * RB; idx += blockDim.x) {
@@ -114,12 +124,30 @@ __device__ __forceinline__ float load_rec(const float* addr) {
   return __hip_atomic_load(addr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ void write_empty_records(const DecodeParams& p, int b, int hq0, int gpw, int s, int rv) {
-  for (int idx = threadIdx.x; idx < gpw * (rv + 2); idx += blockDim.x) {
+// Where a workgroup's split records live: record k of the group's head g
+// (m, l, o_lat[r_v]) starts at base + k * k_stride + g * g_stride floats.
+struct RecLayout {
+  float* base;
+  size_t k_stride, g_stride;
+};
+__device__ __forceinline__ float* rec_at(const RecLayout& rl, int k, int g) {
+  return rl.base + (size_t)k * rl.k_stride + (size_t)g * rl.g_stride;
+}
+// Fixed split plan: records [B][Hq][n_splits][ws_stride], heads hq0 .. of batch row b.
+__device__ __forceinline__ RecLayout fixed_records(const DecodeParams& p, int b, int hq0) {
+  return RecLayout{p.ws + ((size_t)b * p.Hq + hq0) * p.n_splits * p.ws_stride, (size_t)p.ws_stride,
+                   (size_t)p.n_splits * p.ws_stride};
+}
+
+// Record k of an empty split (m = -inf, l = 0, o_lat = 0) for heads 0 .. gpw-1.
+__device__ __forceinline__ void write_empty_records(const RecLayout& rl, int k, int gpw, int rv) {
+  for (int idx = thread_id(); idx < gpw * (rv + 2); idx += blockDim.x) {
     const int g = idx / (rv + 2), j = idx - g * (rv + 2);
-    float* rec = p.ws + (((size_t)b * p.Hq + hq0 + g) * p.n_splits + s) * p.ws_stride;
-    store_rec(rec + j, (j == 0) ? kNegInf : 0.f);
+    store_rec(rec_at(rl, k, g) + j, (j == 0) ? kNegInf : 0.f);
   }
+}
+__device__ __forceinline__ void write_empty_records(const DecodeParams& p, int b, int hq0, int gpw, int s, int rv) {
+  write_empty_records(fixed_records(p, b, hq0), s, gpw, rv);
 }
 
 }  // namespace

@@ -22,6 +22,8 @@ struct HeadTable {
   int rk_pre[kMaxKvHeads];
   int rv_pre[kMaxKvHeads];
   int split_len[kMaxKvHeads];   // decode: tokens per split of KV head h (splits past the sequence are empty)
+  int cost[kMaxKvHeads];        // decode, balanced plan: work per token of KV head h (a fixed part + r_k + r_v)
+  int cost_pre[kMaxKvHeads];    // decode, balanced plan: sum of cost[h'] over KV heads h' < h
   int sk_pre[kMaxKvHeads];      // prefix sums of per-row storage (elements; bytes for 4/3-bit rows)
   int sv_pre[kMaxKvHeads];
 };
@@ -40,6 +42,9 @@ struct DecodeParams {
   const float* pv;       // single-launch merge: packed [h][d][rv(h)]
   float* out;            // single-launch merge: [B][Hq][d]
   int fuse;              // 1: the last split workgroup of a group merges and back-projects
+  int balanced;          // bf16 latents: balanced plan, n_wg workgroups with equal shares of the work
+  int n_wg;
+  int row_cost;          // balanced plan: n_head_groups * sum_h cost[h], work per token of a batch row
   int out_latent;        // 1: write the normalised latent output o_lat [B][Hq][out_stride] (no P_V^T)
   int out_stride;
   int B, Hq, Hkv, G, d, cap;

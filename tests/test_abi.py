@@ -274,3 +274,25 @@ def test_misaligned_buffers_rejected():
         # (and are stopped by the workspace size instead, still before any launch)
         assert kv.lib.kvlr_decode_attn(d.ptr, ctypes.c_void_p(0x1004), FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p(0x1004),
                                        ctypes.c_float(0.1), ctypes.c_void_p(0x1004), FAKE, need - 1, 0, None) == -5
+
+
+def test_balanced_plan_queries():
+    """split_tokens = -1 (KVLR_SPLIT_BALANCED): the balanced plan for bf16 per-head caches (one round of
+    workgroups, no fixed split length), the library's fixed plan elsewhere; its default when the KV
+    heads' ranks differ; one workspace size serves both plans."""
+    uniform = _desc(batch=8, n_q_heads=32, n_kv_heads=8, capacity=32768, r_k=64, r_v=64)
+    ns, length = kv.decode_plan(uniform, -1)
+    assert length == 0 and ns >= 256
+    assert kv.decode_plan(uniform, 0)[1] > 0            # fixed plan by default: uniform ranks
+    ragged = kv.Desc(16, 32, 8, 128, 16384, [16, 32, 48, 64, 80, 96, 16, 32], [96, 80, 64, 48, 32, 16, 96, 80],
+                     kv.BF16, kv.BF16)
+    assert kv.decode_plan(ragged, 0)[1] == 0            # balanced by default: ranks differ
+    assert kv.decode_plan(ragged, 256) == (64, 256)     # an explicit length stays fixed
+    assert kv.decode_workspace_bytes(ragged, 0) == kv.decode_workspace_bytes(ragged, -1)
+    assert kv.decode_workspace_bytes(ragged, 0) >= kv.decode_workspace_bytes(ragged, 4096)
+    for other in (_desc(latent_dtype=kv.F32), _desc(latent_dtype=kv.Q43),
+                  _desc(n_q_heads=8, n_kv_heads=8, value_mode=kv.VALUES_JOINT)):
+        assert kv.decode_plan(other, -1) == kv.decode_plan(other, 0)   # the fixed choice
+    assert kv.decode_plan(_desc(batch=5000, capacity=64), -1)[1] > 0   # too many rows for the balanced plan
+    with pytest.raises(kv.KvlrError):
+        kv.decode_plan(uniform, -2)
