@@ -395,17 +395,23 @@ def test_single_unit_long_and_many_units(gpu):
 
 # ---------------------------------------------------------------------------
 # balanced plan (split_tokens = -1; the library's default when the KV heads' ranks differ)
-@pytest.mark.parametrize("wl,extra,lens", [
-    ("per_head_ranks_ragged", dict(B=6, T_range=(1, 3000)), None),              # per-head ranks, ragged
-    ("llama3_8b_layer_32k", dict(B=3, Hq=8, Hkv=2, T=2000), [2000, 17, 0]),     # a tiny and an empty row
-    ("llama3_8b_layer_32k", dict(B=1, Hq=4, Hkv=1, T=1, r_k=16, r_v=16), [1]),  # less work than workgroups
-    ("long_context_128k", dict(B=2, T=3000, decode_steps=0), [3000, 2999]),     # ranks 48/80: tails
-    ("llama3_8b_layer_32k", dict(B=5, Hq=64, Hkv=4, T=700), None),              # 4 head groups per KV head
-    ("per_head_ranks_ragged", dict(B=40, T_range=(0, 400)), None),              # many short rows, some empty
+@pytest.mark.parametrize("wl,extra,lens,diag", [
+    ("per_head_ranks_ragged", dict(B=6, T_range=(1, 3000)), None, 2e-3),              # per-head ranks, ragged
+    ("llama3_8b_layer_32k", dict(B=3, Hq=8, Hkv=2, T=2000), [2000, 17, 0], 2e-3),     # a tiny and an empty row
+    ("llama3_8b_layer_32k", dict(B=1, Hq=4, Hkv=1, T=1, r_k=16, r_v=16), [1], 2e-3),  # less work than workgroups
+    ("long_context_128k", dict(B=2, T=3000, decode_steps=0), [3000, 2999], 2e-3),     # ranks 48/80: tails
+    ("llama3_8b_layer_32k", dict(B=5, Hq=64, Hkv=4, T=700), None, 2e-3),              # 4 head groups per KV head
+    ("per_head_ranks_ragged", dict(B=40, T_range=(0, 400)), None, 2e-3),              # many short rows, some empty
+    # 2000 rows (the input generator's limit): 32 chunks of the length scan
+    ("llama3_8b_layer_32k", dict(B=2000, Hq=4, Hkv=2, T=16, r_k=16, r_v=16), [(7 * i) % 17 for i in range(2000)], 6e-3),
 ])
-def test_balanced_plan_matches_oracle_and_fixed_plan(gpu, wl, extra, lens):
-    """Equal shares of the bytes per workgroup, cut across (batch row, KV head) units: the oracle's
-    result, the fixed plan's to fp32 rounding, and the same bits on every run."""
+def test_balanced_plan_matches_oracle_and_fixed_plan(gpu, wl, extra, lens, diag):
+    """Equal shares of the work per workgroup, cut across (batch row, KV head) units: the oracle's
+    result, the fixed plan's to the rounding of the softmax weights, and the same bits on every run.
+    The storage-aware diagnostic is looser for rank 16 over at most 16 tokens: compression rounds
+    its fp32 latents to bf16, and an element on a rounding boundary can come out one ulp (2^-8)
+    from the float64 oracle's rounding; with 16 channels and a few tokens one such element moves
+    an output by a few 1e-3."""
     import torch
     cfg = WORKLOADS[wl].scaled(**extra)
     case = build_case(cfg)
@@ -414,7 +420,7 @@ def test_balanced_plan_matches_oracle_and_fixed_plan(gpu, wl, extra, lens):
     kv = _kv()
     say(f"[balanced] plan {kv.decode_plan(case.desc, -1)} lens={lens.tolist()[:8]}")
     bal = _decode(case, q, lens, split=-1)
-    _check_rows(case, bal, q, lens, diag_bound=2e-3)
+    _check_rows(case, bal, q, lens, diag_bound=diag)
     assert np.array_equal(_decode(case, q, lens, split=-1), bal)
     fixed = _decode(case, q, lens, split=256)
     live = lens > 0
