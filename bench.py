@@ -478,7 +478,7 @@ def main():
         "step_hbm_GBps": alg_bytes / (elapsed / args.steps) / 1e9,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "kernel": "decode_split_bf16<64, 32, false> (kvlr_decode_attn, fixed split plan, merge fused)", "bytes_per_launch": alg_bytes,
+                     "kernel": "decode_split_bf16<64, 32> (kvlr_decode_attn, fixed split plan, merge fused)", "bytes_per_launch": alg_bytes,
                      "launch_us_mean": float(split_us.mean()), "launch_us_p10": float(np.percentile(split_us, 10)),
                      "launch_us_p90": float(np.percentile(split_us, 90))},
     }

@@ -726,23 +726,27 @@ __device__ __forceinline__ void decode_balanced(const DecodeParams& p, float* sm
   }
 }
 
-template <int RB, int TT, bool kBalanced>
+// Fixed plan: one workgroup per (split, KV head and head group, batch row).
+template <int RB, int TT>
 __global__ __launch_bounds__(256) void decode_split_bf16(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) float smem[kTailLds];
-  if constexpr (kBalanced) {
-    decode_balanced<RB, TT>(p, smem);
-  } else {
-    const int s = blockIdx.x;
-    const int h = blockIdx.y / p.n_head_groups;
-    const int hg = blockIdx.y - h * p.n_head_groups;
-    const int b = blockIdx.z;
-    const int T = min(max(p.seq_lens[b], 0), p.cap);
-    const int t_begin = min(s * p.ht.split_len[h], T);   // clamped: no overflow for far splits
-    const int t_end = min(T, t_begin + p.ht.split_len[h]);
-    if (append_owner(p, b, h, s)) append_rows(p, b, h, p.ht.rk[h], p.ht.rv[h], smem);
-    bf16_segment<RB, TT>(p, b, h, hg, t_begin, t_end, fixed_records(p, b, h * p.G + hg * kHeadsPerWg), s,
-                         p.n_splits, smem);
-  }
+  const int s = blockIdx.x;
+  const int h = blockIdx.y / p.n_head_groups;
+  const int hg = blockIdx.y - h * p.n_head_groups;
+  const int b = blockIdx.z;
+  const int T = min(max(p.seq_lens[b], 0), p.cap);
+  const int t_begin = min(s * p.ht.split_len[h], T);   // clamped: no overflow for far splits
+  const int t_end = min(T, t_begin + p.ht.split_len[h]);
+  if (append_owner(p, b, h, s)) append_rows(p, b, h, p.ht.rk[h], p.ht.rv[h], smem);
+  bf16_segment<RB, TT>(p, b, h, hg, t_begin, t_end, fixed_records(p, b, h * p.G + hg * kHeadsPerWg), s,
+                       p.n_splits, smem);
+}
+
+// Balanced plan: one workgroup per share.
+template <int RB, int TT>
+__global__ __launch_bounds__(256) void decode_balanced_bf16(DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) float smem[kTailLds];
+  decode_balanced<RB, TT>(p, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -1403,25 +1407,25 @@ hipError_t launch_decode(const DecodeParams& p, int latent_dtype, int rank_bound
   if (latent_bf16) {
     if (p.balanced) {   // one workgroup per share of the balanced plan
       const dim3 grid_b(p.n_wg);
-      switch (rank_bound) {
-        case 32: hipLaunchKernelGGL((decode_split_bf16<32, 32, true>), grid_b, block, 0, stream, p); break;
-        case 64: hipLaunchKernelGGL((decode_split_bf16<64, 32, true>), grid_b, block, 0, stream, p); break;
-        case 96: hipLaunchKernelGGL((decode_split_bf16<96, 32, true>), grid_b, block, 0, stream, p); break;
-        default: hipLaunchKernelGGL((decode_split_bf16<128, 32, true>), grid_b, block, 0, stream, p); break;
+      switch (rank_bound) {   // 32-token steps (64 would leave one wave per SIMD at bound 96)
+        case 32: hipLaunchKernelGGL((decode_balanced_bf16<32, 32>), grid_b, block, 0, stream, p); break;
+        case 64: hipLaunchKernelGGL((decode_balanced_bf16<64, 32>), grid_b, block, 0, stream, p); break;
+        case 96: hipLaunchKernelGGL((decode_balanced_bf16<96, 32>), grid_b, block, 0, stream, p); break;
+        default: hipLaunchKernelGGL((decode_balanced_bf16<128, 32>), grid_b, block, 0, stream, p); break;
       }
     } else if (tile == 32) {
       switch (rank_bound) {
-        case 32: hipLaunchKernelGGL((decode_split_bf16<32, 32, false>), grid, block, 0, stream, p); break;
-        case 64: hipLaunchKernelGGL((decode_split_bf16<64, 32, false>), grid, block, 0, stream, p); break;
-        case 96: hipLaunchKernelGGL((decode_split_bf16<96, 32, false>), grid, block, 0, stream, p); break;
-        default: hipLaunchKernelGGL((decode_split_bf16<128, 32, false>), grid, block, 0, stream, p); break;
+        case 32: hipLaunchKernelGGL((decode_split_bf16<32, 32>), grid, block, 0, stream, p); break;
+        case 64: hipLaunchKernelGGL((decode_split_bf16<64, 32>), grid, block, 0, stream, p); break;
+        case 96: hipLaunchKernelGGL((decode_split_bf16<96, 32>), grid, block, 0, stream, p); break;
+        default: hipLaunchKernelGGL((decode_split_bf16<128, 32>), grid, block, 0, stream, p); break;
       }
     } else {
       switch (rank_bound) {
-        case 32: hipLaunchKernelGGL((decode_split_bf16<32, 64, false>), grid, block, 0, stream, p); break;
-        case 64: hipLaunchKernelGGL((decode_split_bf16<64, 64, false>), grid, block, 0, stream, p); break;
-        case 96: hipLaunchKernelGGL((decode_split_bf16<96, 64, false>), grid, block, 0, stream, p); break;
-        default: hipLaunchKernelGGL((decode_split_bf16<128, 64, false>), grid, block, 0, stream, p); break;
+        case 32: hipLaunchKernelGGL((decode_split_bf16<32, 64>), grid, block, 0, stream, p); break;
+        case 64: hipLaunchKernelGGL((decode_split_bf16<64, 64>), grid, block, 0, stream, p); break;
+        case 96: hipLaunchKernelGGL((decode_split_bf16<96, 64>), grid, block, 0, stream, p); break;
+        default: hipLaunchKernelGGL((decode_split_bf16<128, 64>), grid, block, 0, stream, p); break;
       }
     }
   } else {
