@@ -173,7 +173,10 @@ def test_random_shape_entry_points_agree(gpu, i):
     folded = np.stack([ol[:, qh, :PV[qh // cfg.G].shape[1]] @ PV[qh // cfg.G].T for qh in range(cfg.Hq)], axis=1)
     err_fold = float(rel_inf_rows(folded[live], a[live]).max()) if live.any() else 0.0
     say(f"[random entry points {i}] two-stage {err_two:.2e} folded {err_fold:.2e}")
-    assert err_two <= 1e-6, err_two
+    # the two stages keep the fixed plan; where the one-launch call takes the balanced plan
+    # (per-head ranks that differ) the sequences are cut elsewhere: weights round differently
+    balanced = kv.decode_plan(desc, split)[1] == 0
+    assert err_two <= (2e-5 if balanced else 1e-6), err_two
     assert err_fold <= (1e-5 if kind.endswith("f32") else 1e-4), err_fold
 
 
