@@ -136,8 +136,13 @@ def measure_workloads(kv, torch, np):
     nbytes = int(lens_np.astype(np.int64).sum()) * int((c["rk"] + c["rv"]).sum()) * 2
     call = lambda: kv.decode_attn(c["desc"], q, c["pk"], c["pv"], c["lk"], c["lv"], lens, out=o, workspace=ws)  # noqa: E731
     t = _timed(torch, lambda: [call() for _ in range(20)], 3) / 20
+    fixed = lambda: kv.decode_attn(c["desc"], q, c["pk"], c["pv"], c["lk"], c["lv"], lens, out=o,  # noqa: E731
+                                   workspace=ws, split_tokens=4096)
+    t_fixed = _timed(torch, lambda: [fixed() for _ in range(20)], 3) / 20
     out[cfg.name] = {"us_per_call": t * 1e6, "bytes": nbytes, "GBps": nbytes / t / 1e9,
-                     "hbm_frac": nbytes / t / 1e9 / HBM_PEAK_GBPS, "tokens_per_s": cfg.B / t}
+                     "hbm_frac": nbytes / t / 1e9 / HBM_PEAK_GBPS, "tokens_per_s": cfg.B / t,
+                     "plan": "balanced (the library's choice: the KV heads' ranks differ)",
+                     "fixed_plan_4096_us_per_call": t_fixed * 1e6}
     del c, ws
     torch.cuda.empty_cache()
 
