@@ -248,6 +248,30 @@ def measure_joint(kv, torch, np, cfg, gen, q, lens, steps, warmup, r_joint=128):
             "note": "the value latent is read once per KV head (from L2 / the last-level cache after the first)"}
 
 
+def measure_stream_ceiling(torch, np):
+    """Achievable HBM read bandwidth on this device: a non-temporal streaming read of a 1 GiB
+    buffer (above the 256 MB last-level cache) in 1, 2, 4 or 8 contiguous chunks per compute
+    unit; the best launch shape's median over 7 event-timed passes."""
+    from synth.device import stream_read
+    src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+    src.fill_(1.0)
+    sink = torch.zeros(2048, dtype=torch.int32, device="cuda")
+    best = 0.0
+    for wgs in (256, 512, 1024, 2048):
+        for _ in range(2):
+            stream_read(src, sink, wgs)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(7)]
+        for e in evs:
+            e[0].record()
+            stream_read(src, sink, wgs)
+            e[1].record()
+        torch.cuda.synchronize()
+        us = float(np.median([e[0].elapsed_time(e[1]) * 1e3 for e in evs]))
+        best = max(best, (1 << 30) / (us * 1e-6) / 1e9)
+    del src, sink
+    return best
+
+
 def measure_q43(kv, torch, np, cfg, gen, q, lens, steps, warmup):
     """The same workload with mixed 4/3-bit latents (4-bit outlier, 3-bit inlier block per
     token, block-wise Hadamard folded into the bases): kvlr_decode_attn launches timed with
@@ -452,6 +476,8 @@ def main():
     if not args.no_q43:
         q43 = measure_q43(kv, torch, np, cfg, gen, q, lens, args.steps, args.warmup)
 
+    stream_ceiling = measure_stream_ceiling(torch, np)
+
     if args.traffic_reference:
         from synth.device import copy as device_copy
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
@@ -490,6 +516,7 @@ def main():
         "step_hbm_GBps": alg_bytes / (elapsed / args.steps) / 1e9,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "stream_read_ceiling_GBps": stream_ceiling, "frac_of_stream_read": achieved / stream_ceiling,
                      "kernel": "decode_split_bf16<64, 32> (kvlr_decode_attn, fixed split plan, merge fused)", "bytes_per_launch": alg_bytes,
                      "launch_us_mean": launch_us,
                      "timing": "one HIP event pair on the launch stream around the K timed launches",

@@ -32,6 +32,9 @@ def lib():
         _lib.synth_touch.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_void_p]
         _lib.synth_copy.restype = ctypes.c_int
         _lib.synth_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]
+        _lib.synth_stream_read.restype = ctypes.c_int
+        _lib.synth_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int,
+                                           ctypes.c_void_p]
     return _lib
 
 
@@ -91,3 +94,17 @@ def copy(src, dst):
                           ctypes.c_uint64(nbytes), _stream_ptr(torch))
     if rc != 0:
         raise RuntimeError(f"synth_copy failed with {rc}")
+
+
+def stream_read(src, sink, workgroups: int = 512):
+    """Non-temporal streaming read of all of src (a byte size that is a multiple of 16), in
+    `workgroups` contiguous chunks: the achievable read bandwidth. sink: an int32 device
+    tensor of at least 2048 elements."""
+    import torch
+    nbytes = src.numel() * src.element_size()
+    assert nbytes % 16 == 0 and sink.dtype == torch.int32 and sink.numel() >= 2048
+    assert 1 <= workgroups <= 2048
+    rc = lib().synth_stream_read(ctypes.c_void_p(src.data_ptr()), ctypes.c_uint64(nbytes),
+                                 ctypes.c_void_p(sink.data_ptr()), ctypes.c_int(workgroups), _stream_ptr(torch))
+    if rc != 0:
+        raise RuntimeError(f"synth_stream_read failed with {rc}")
