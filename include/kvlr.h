@@ -94,7 +94,7 @@ typedef enum kvlr_value_mode {
  *   capacity    T_cap in [1, 2^30]: usable rows per (batch row, KV head)
  *   r_k, r_v    host arrays [Hkv]: ranks of each KV head (uniform per-layer
  *               ranks repeat one value); 1 <= r <= min(d, 128), a multiple of 16
- *               for bf16 latents and of 4 for fp32 latents
+ *               for bf16 and 4/3-bit latents and of 4 for fp32 latents
  *   in_dtype    dtype of the full-width K/V rows given to compression and append
  *   latent_dtype dtype of the latent cache
  *   value_mode  KVLR_VALUES_PER_HEAD or KVLR_VALUES_JOINT. Joint values: every
