@@ -359,7 +359,21 @@ def cpu_baseline(cfg, seconds):
                    f"scaled x{cfg.Hkv} KV heads to one token"),
         "definition_order_tokens_per_s": 1.0 / (per_head_def * cfg.Hkv),
         "blas": blas,
+        "cpu_model": _cpu_model(),
+        "host_threads_available": len(os.sched_getaffinity(0)),
     }
+
+
+def _cpu_model():
+    """The host CPU's model name (first entry of /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def main():
