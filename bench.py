@@ -245,7 +245,7 @@ def measure_joint(kv, torch, np, cfg, gen, q, lens, steps, warmup, r_joint=128):
     return {"entry": "kvlr_decode_attn, value_mode KVLR_VALUES_JOINT", "r_k": int(rk[0]), "r_joint": r_joint,
             "bytes_per_launch": nbytes, "launch_us_mean": us, "GBps": nbytes / (us * 1e-6) / 1e9,
             "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, "tokens_per_s": B * steps / elapsed,
-            "note": "the value latent is read once per KV head (from L2 / the last-level cache after the first)"}
+            "note": "three launches: query projection, one split kernel per (split, batch row) that streams every head's keys and the shared value latent once, and a merge per (query head, batch row)"}
 
 
 def measure_stream_ceiling(torch, np):
