@@ -36,6 +36,19 @@
  *    kernels clamp them to [0, capacity] and never access memory out of
  *    bounds.
  *  - The library never prints.
+ *  - Tuning overrides are read from the environment at each call. They exist
+ *    for measurement; every setting keeps results within the same bounds.
+ *    Values outside the listed ones are ignored.
+ *      KVLR_SPLIT_TOKENS   tokens per split when the library's choice is the
+ *                          fixed plan (a positive multiple of 64)
+ *      KVLR_TILE=64        64-token wave steps in the bf16 split kernel
+ *                          (default 32)
+ *      KVLR_BALANCE_FIXED  fixed work per token in the balanced plan, 0..4096
+ *                          (default 512; the latent elements are added to it)
+ *      KVLR_JOINT_BLOCKS=2 two 16-token blocks per step of the joint-values
+ *                          split kernel (default 1)
+ *    The workspace size follows the plan, so the same overrides must be set
+ *    when kvlr_decode_workspace_bytes is called.
  */
 #ifndef KVLR_H
 #define KVLR_H
