@@ -756,9 +756,12 @@ __global__ __launch_bounds__(256) void decode_balanced_bf16(DecodeParams p) {
 // A wave streams ST consecutive rows of keys and of values per iteration with
 // 16-byte loads (the rows of a (batch row, KV head) block are contiguous and a
 // tile starts 16-byte aligned), parks them in its own LDS region while the
-// next ST rows are in flight, and reads the codes it needs from LDS. Compressed
-// rows are short, so a tile of ST = 128 rows keeps as many bytes in flight per
-// wave as the bf16 kernel's 32-row tile.
+// next ST rows are in flight, and reads the codes it needs from LDS. For ranks
+// up to 64 the tile is one 32-token step (ST = 32), which keeps the kernel
+// within 168 registers, i.e. 3 waves per SIMD and 3 workgroups per CU. The
+// kernel is bound by VALU work and latency, so the third workgroup gains more
+// than the deeper tile. Larger ranks would spill at that size and keep
+// 64-row tiles at 2 waves per SIMD.
 // Scores: a code c enters the MFMA as the bf16 number 128 + c (bits 0x4300 | c,
 // exact), so per token and block of channels
 //   sum_j q~_j (step c_j + base) = step (acc - 128 Q) + base Q,
@@ -769,10 +772,11 @@ __global__ __launch_bounds__(256) void decode_balanced_bf16(DecodeParams p) {
 // accumulates sum_t p_t step_t c_t per channel and sum_t p_t base_t once per
 // head; the two are added when the split ends.
 template <int RB>
-__global__ __launch_bounds__(256) void decode_split_q43(DecodeParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB <= 64 ? 3 : 1)))
+void decode_split_q43(DecodeParams p) {
   constexpr int TT = 32;                     // tokens per score/softmax/value step
   constexpr int NB = TT / 16;
-  constexpr int ST = RB <= 64 ? 128 : 64;    // rows per wave iteration
+  constexpr int ST = RB <= 64 ? 32 : 64;     // rows per wave iteration
   constexpr int NSUB = ST / TT;
   constexpr int RBM = q43_row_bytes(RB);     // bytes of the longest row
   constexpr int CH = (ST * RBM + 1023) / 1024;   // 16-byte chunks per lane per tile (keys or values)
