@@ -209,6 +209,24 @@ def test_q43_decode_matches_oracle(gpu, wl, extra):
     _q43_check(case, _q43_decode(case, q, lens), q, lens)
 
 
+def test_q43_full_llama3_layer_32k(gpu):
+    """The 4/3-bit decode at the benchmark's size and launch configuration: 8 sequences of
+    32768 tokens, rank 64, the library's plan (12 splits of 2752 tokens, 3 workgroups per
+    CU). Seeded (batch row, KV head) units against the oracle's decode over its own
+    quantised latents."""
+    kv = _kv()
+    cfg = LLAMA3_LAYER_32K
+    case = _q43_case(cfg, chunk=8192)
+    assert kv.decode_plan(case["desc"], 0) == (12, 2752)
+    q = host.queries(cfg)
+    lens = host.lengths(cfg)
+    got = _q43_decode(case, q, lens)
+    assert np.isfinite(got).all()
+    g = np.random.default_rng(np.random.SeedSequence([7100, cfg.cid]))
+    units = sorted({(int(g.integers(cfg.B)), int(g.integers(cfg.Hkv))) for _ in range(3)})
+    _q43_check(case, got, q, lens, units=units)
+
+
 @pytest.mark.parametrize("lens,split", [([0, 5], 64), ([1, 300], 64), ([257, 256], 0), ([300, 129], 128)])
 def test_q43_decode_edge_lengths(gpu, lens, split):
     cfg = LLAMA3_LAYER_32K.scaled(B=2, Hq=8, Hkv=2, T=300)
