@@ -169,6 +169,29 @@ def test_joint_decode_matches_oracle(gpu, wl, extra, rj, diag):
     _check(case, _decode(case, q, lens), q, lens, diag_bound=diag)
 
 
+def test_joint_full_llama3_layer_32k(gpu):
+    """Joint values at the benchmark's size and launch configuration: 8 sequences of 32768
+    tokens, key rank 64, joint value rank 128, the library's plan. Two seeded batch rows
+    (every query head) against the oracle, with the storage-aware diagnostic."""
+    cfg = LLAMA3_LAYER_32K
+    case = _joint_case(cfg, 128, chunk=8192)
+    q = host.queries(cfg)
+    lens = host.lengths(cfg)
+    got = _decode(case, q, lens)
+    assert np.isfinite(got).all()
+    metric, bound = tolerance(cfg)
+    g = np.random.default_rng(np.random.SeedSequence([7200, cfg.cid]))
+    rows = sorted({int(g.integers(cfg.B)) for _ in range(2)})
+    worst = diag = 0.0
+    for b in rows:
+        T = int(lens[b])
+        worst = max(worst, float(metric(got[b], _reference(case, q, b, T)).max()))
+        diag = max(diag, float(rel_l2_rows(got[b], _reference_stored(case, q, b, T)).max()))
+    say(f"[joint full] rows {rows}: worst {worst:.3e} (bound {bound}), storage-aware {diag:.3e} (bound 2e-3)")
+    assert worst <= bound, worst
+    assert diag <= 2e-3, diag
+
+
 def test_joint_decode_f32(gpu):
     cfg = SINGLE_HEAD_F32.scaled(B=2, Hq=4, Hkv=2, T=300)
     case = _joint_case(cfg, 40, latent="f32")
