@@ -4,6 +4,7 @@
 #include <math.h>
 #include <stdlib.h>
 
+#include <atomic>
 #include <initializer_list>
 #include <stdint.h>
 #include <string.h>
@@ -16,7 +17,43 @@ using kvlr::HeadTable;
 
 constexpr int kVersion = 10000;   // 1.0.0
 constexpr int kSplitGranule = kvlr::kTile;
-constexpr int kComputeUnits = 256;   // MI355X
+
+// Compute units of the current device, queried once per device and cached. The
+// plans size one round of workgroups over them, so a partitioned device (fewer
+// CUs per logical device) gets plans for what it has. Without a device (size
+// queries on a host with no GPU) the MI355X count is assumed.
+constexpr int kDefaultComputeUnits = 256;
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_compute_units[kMaxDevices];   // 0: not queried yet
+
+int compute_units() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return kDefaultComputeUnits;
+  int n = g_compute_units[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = kDefaultComputeUnits;
+  g_compute_units[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Tuning overrides from the environment, read once, the first time a plan is
+// made (see kvlr.h); later changes to the environment have no effect.
+struct Tuning {
+  long long split_tokens;   // KVLR_SPLIT_TOKENS: tokens per split of the fixed plan (0: library choice)
+  int balance_fixed;        // KVLR_BALANCE_FIXED: fixed work per token of the balanced plan (-1: default)
+  int tile;                 // KVLR_TILE: 64-token wave steps of the bf16 split kernel (default 32)
+};
+const Tuning& tuning() {
+  static const Tuning t = [] {
+    Tuning r{0, -1, 32};
+    if (const char* e = getenv("KVLR_SPLIT_TOKENS")) r.split_tokens = atoll(e);
+    if (const char* e = getenv("KVLR_BALANCE_FIXED")) r.balance_fixed = atoi(e);
+    if (const char* e = getenv("KVLR_TILE")) r.tile = atoi(e) == 64 ? 64 : 32;
+    return r;
+  }();
+  return t;
+}
 
 // Resident split workgroups per CU for each kernel variant (4 waves each;
 // limited by the variant's register count on gfx950). The default split
@@ -57,9 +94,9 @@ int head_groups_of(const kvlr_desc* d) {
 // fixed part for the arithmetic every token costs whatever its rank (softmax,
 // masks, loop control); KVLR_BALANCE_FIXED overrides the fixed part for tuning.
 int token_fixed_cost() {
-  const char* env = getenv("KVLR_BALANCE_FIXED");
-  const int v = env ? atoi(env) : kTokenFixedCost;
-  return v < 0 ? 0 : v > 4096 ? 4096 : v;
+  const int v = tuning().balance_fixed;
+  if (v < 0) return kTokenFixedCost;
+  return v > 4096 ? 4096 : v;
 }
 int token_cost(const kvlr_desc* d, int h) { return token_fixed_cost() + d->r_k[h] + d->r_v[h]; }
 
@@ -87,7 +124,7 @@ bool balanced_plan(const kvlr_desc* d, int32_t split_tokens) {
 
 // Workgroups of the balanced plan: one round over the device.
 int balanced_wgs(const kvlr_desc* d, int rank_bound) {
-  return kComputeUnits * resident_wgs_per_cu(d->latent_dtype, rank_bound);
+  return compute_units() * resident_wgs_per_cu(d->latent_dtype, rank_bound);
 }
 
 // Largest key rank and its kernel bound.
@@ -176,13 +213,12 @@ int plan_split(const kvlr_desc* d, int32_t split_tokens, int* n_splits, int* len
   if (split_tokens > 0) {
     len = split_tokens;
   } else {
-    const char* env = getenv("KVLR_SPLIT_TOKENS");   // tuning override
-    long long want = env ? atoll(env) : 0;
+    long long want = tuning().split_tokens;   // tuning override
     if (want <= 0 || want % kSplitGranule) {
       const bool jd = joint_bf16(d);   // one workgroup per (split, batch row)
       const long long units = jd ? (long long)d->batch : (long long)d->batch * d->n_kv_heads * groups;
       const long long slots =
-          (long long)kComputeUnits * (jd ? kJointResident : resident_wgs_per_cu(d->latent_dtype, rank_bound));
+          (long long)compute_units() * (jd ? kJointResident : resident_wgs_per_cu(d->latent_dtype, rank_bound));
       want = (units * d->capacity + slots - 1) / slots;
       // whole tiles for every wave; the 4/3-bit kernel steps 32 rows at a time, so any
       // multiple of the granule keeps whole steps (measured: 2752 against 2816 tokens,
@@ -228,11 +264,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? KVLR_OK : KVLR_ERR_HIP; 
 // Tokens per wave iteration of the bf16 split kernel (32 or 64; 32 measured
 // faster: fewer registers, 3 waves per SIMD at rank 64); KVLR_TILE overrides
 // for tuning.
-int decode_tile() {
-  const char* env = getenv("KVLR_TILE");
-  if (env && atoi(env) == 64) return 64;
-  return 32;
-}
+int decode_tile() { return tuning().tile; }
 
 // Workspace layout: arrival counters [B][Hkv][head groups] int32, padded to
 // 256 bytes, then the split records [B][Hq][n_splits][stride] fp32, then (joint
@@ -476,12 +508,8 @@ int prepare_decode(const kvlr_desc* desc, const float* q, const float* P_K, cons
 }
 
 // 16-token blocks per wave step of the joint split kernel: one (measured faster
-// than two at rank 64/128, which doubles the loads in flight and the registers);
-// KVLR_JOINT_BLOCKS=2 selects two for tuning.
-int joint_blocks() {
-  const char* env = getenv("KVLR_JOINT_BLOCKS");
-  return env && atoi(env) == 2 ? 2 : 1;
-}
+// than two at rank 64/128, which doubles the loads in flight and the registers).
+constexpr int kJointBlocks = 1;
 
 // Joint bf16 values: q~ = q P_K into the workspace, then the split kernel over it.
 hipError_t joint_partials(const kvlr_desc* desc, kvlr::DecodeParams p, hipStream_t s) {
@@ -494,7 +522,7 @@ hipError_t joint_partials(const kvlr_desc* desc, kvlr::DecodeParams p, hipStream
   if (e != hipSuccess) return e;
   p.qt_in = p.qt_out;
   p.qt_stride = rk_max;
-  return kvlr::launch_decode_joint(p, rank_bound_of(rk_max), joint_blocks(), s);
+  return kvlr::launch_decode_joint(p, rank_bound_of(rk_max), kJointBlocks, s);
 }
 
 }  // namespace
@@ -575,7 +603,7 @@ KVLR_API int kvlr_decode_attn_latent(const kvlr_desc* desc, const float* q_lat, 
     m.out = o_lat;
     m.out_latent = 1;
     m.out_stride = rv_max;
-    hipError_t e = kvlr::launch_decode_joint(p, rank_bound_of(rk_max), joint_blocks(), s);
+    hipError_t e = kvlr::launch_decode_joint(p, rank_bound_of(rk_max), kJointBlocks, s);
     if (e == hipSuccess) e = kvlr::launch_merge_heads(m, s);
     return hip_status(e);
   }

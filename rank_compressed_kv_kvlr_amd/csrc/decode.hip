@@ -120,6 +120,17 @@ __device__ __forceinline__ void finish_split(const DecodeParams& p, int b, int h
   if (!p.fuse) return;
   int* flag = reinterpret_cast<int*>(scratch + kTailLds - 1);
   int* counter = p.counters + ((size_t)b * p.Hkv + h) * p.n_head_groups + hg;
+  // Hand-off between workgroups without a release/acquire fence. This relies on
+  // gfx950 behaviour that the HIP memory model does not promise at relaxed order:
+  //  - the records are agent-scope relaxed stores (store_rec), which compile to
+  //    global stores with the sc1 bit: they write through to the device-coherent
+  //    level rather than staying in this XCD's L2;
+  //  - s_waitcnt(0) returns only once every such store is acknowledged, and the
+  //    barrier makes that true for all waves before thread 0 counts the arrival;
+  //  - the merging workgroup reads the records with agent-scope relaxed loads
+  //    (load_rec, sc1: they bypass non-coherent cached copies).
+  // A release fence per workgroup (buffer_wbl2 sc1, a writeback of the whole L2)
+  // gives the same ordering at a measured cost of 16-63 us per call.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (thread_id() == 0)

@@ -278,16 +278,3 @@ def test_joint_decode_many_splits(gpu):
     lens = host.lengths(cfg)
     q = host.queries(cfg, 0, 0)
     _check(case, _decode(case, q, lens, split=64), q, lens)
-
-
-def test_joint_decode_two_blocks_per_step(gpu, monkeypatch):
-    """The two-block variant of the split kernel (KVLR_JOINT_BLOCKS=2, a tuning switch read
-    at each call) gives the oracle's result too, including blocks past the sequence end."""
-    cfg = LLAMA3_LAYER_32K.scaled(B=4, T=300)
-    case = _joint_case(cfg, 128)
-    lens = np.array([300, 17, 33, 1], np.int32)
-    q = host.queries(cfg, 0, 0)
-    monkeypatch.setenv("KVLR_JOINT_BLOCKS", "2")
-    got = _decode(case, q, lens, split=64)
-    monkeypatch.delenv("KVLR_JOINT_BLOCKS")
-    _check(case, got, q, lens)
