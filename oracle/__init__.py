@@ -47,6 +47,7 @@ from .kvlr_oracle import (  # noqa: F401
     compress,
     reconstruct,
     softmax,
+    attend,
     attend_reconstructed,
     attend_latent,
     decode,

@@ -52,6 +52,20 @@ def softmax(s) -> np.ndarray:
     return w / w.sum(axis=-1, keepdims=True)
 
 
+def attend(q, Kt, Vt, scale) -> np.ndarray:
+    """Standard softmax attention of one query q [d] over full-dimension rows
+    Kt, Vt [T][d]: o = softmax(Kt q * scale) Vt, the attention that follows the
+    reconstruction (Mecanismo Central, item 5). Zero row when T = 0.
+    """
+    Kt = np.asarray(Kt, np.float64)
+    Vt = np.asarray(Vt, np.float64)
+    if Kt.shape[0] == 0:
+        return np.zeros(Vt.shape[1])
+    s = (Kt @ np.asarray(q, np.float64)) * scale
+    p = softmax(s)
+    return p @ Vt
+
+
 def attend_reconstructed(q, K, V, P_K, P_V, scale) -> np.ndarray:
     """Definition mode for one query vector q [d] over one KV head.
 
@@ -65,9 +79,7 @@ def attend_reconstructed(q, K, V, P_K, P_V, scale) -> np.ndarray:
         return np.zeros(d)
     Kt = reconstruct(compress(K, P_K), P_K)
     Vt = reconstruct(compress(V, P_V), P_V)
-    s = (Kt @ np.asarray(q, np.float64)) * scale
-    p = softmax(s)
-    return p @ Vt
+    return attend(q, Kt, Vt, scale)
 
 
 def attend_latent(q, K_lat, V_lat, P_K, P_V, scale) -> np.ndarray:
@@ -93,8 +105,17 @@ def kv_head_of(i: int, Hq: int, Hkv: int) -> int:
 
 
 def decode_head_reconstructed(q_heads, K, V, P_K, P_V, scale) -> np.ndarray:
-    """Definition mode for the G query heads [G][d] that share one KV head's K, V [T][d]."""
-    return np.stack([attend_reconstructed(qi, K, V, P_K, P_V, scale) for qi in np.asarray(q_heads)])
+    """Definition mode for the G query heads [G][d] that share one KV head's K, V [T][d]:
+    the head's rows are reconstructed once and every query head attends over them
+    (the same arithmetic as attend_reconstructed per head)."""
+    q_heads = np.asarray(q_heads, np.float64)
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    if K.shape[0] == 0:
+        return np.zeros((q_heads.shape[0], np.asarray(P_V).shape[0]))
+    Kt = reconstruct(compress(K, P_K), P_K)
+    Vt = reconstruct(compress(V, P_V), P_V)
+    return np.stack([attend(qi, Kt, Vt, scale) for qi in q_heads])
 
 
 def decode_head_latent(q_heads, K_lat, V_lat, P_K, P_V, scale) -> np.ndarray:

@@ -4,6 +4,7 @@ from __future__ import annotations
 import types
 
 import numpy as np
+import scipy.special
 import pytest
 import torch
 
@@ -63,6 +64,26 @@ def test_decode_latents_matches_decode():
     a = oracle.decode(q, K, V, P_K, P_V, lens, 0.25)
     b = oracle.decode_latents(q, lat_k, lat_v, P_K, P_V, lens, 0.25)
     assert np.abs(a - b).max() <= 1e-12 * np.abs(a).max()
+
+
+def test_grouped_head_decode_equals_per_head_definition():
+    """decode_head_reconstructed (rows reconstructed once for the G query heads of a KV
+    head) gives attend_reconstructed's result for every head, bit for bit, and the
+    textbook attention over the reconstructed rows."""
+    rng = np.random.default_rng(5)
+    d, T, G = 16, 40, 3
+    P_K = np.linalg.qr(rng.standard_normal((d, 5)))[0]
+    P_V = np.linalg.qr(rng.standard_normal((d, 7)))[0]
+    K, V = rng.standard_normal((T, d)), rng.standard_normal((T, d))
+    q = rng.standard_normal((G, d))
+    got = oracle.decode_head_reconstructed(q, K, V, P_K, P_V, 0.4)
+    ref = np.stack([oracle.attend_reconstructed(qi, K, V, P_K, P_V, 0.4) for qi in q])
+    assert np.array_equal(got, ref)
+    Kt, Vt = K @ P_K @ P_K.T, V @ P_V @ P_V.T
+    text = np.stack([scipy.special.softmax(Kt @ qi * 0.4) @ Vt for qi in q])
+    assert np.abs(got - text).max() <= 1e-12 * np.abs(text).max()
+    assert np.all(oracle.decode_head_reconstructed(q, K[:0], V[:0], P_K, P_V, 0.4) == 0)
+    assert oracle.decode_head_reconstructed(q, K[:0], V[:0], P_K, P_V, 0.4).shape == (G, d)
 
 
 # --------------------------------------------------------------------------
