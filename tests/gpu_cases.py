@@ -8,6 +8,7 @@ the oracle.
 """
 from __future__ import annotations
 
+import os
 import sys
 from dataclasses import dataclass, field
 
@@ -102,15 +103,16 @@ def dtype_code(kv, name):
 
 
 def build_case(cfg: Config, layer: int = 0, n_rows: int = None, capacity: int = None, ranks=None,
-               chunk: int = None) -> Case:
-    """Generate K, V on the device and prefill-compress rows 0..n_rows-1 of every (b, h)."""
+               chunk: int = None, bases=None) -> Case:
+    """Generate K, V on the device and prefill-compress rows 0..n_rows-1 of every (b, h).
+    `bases` (per-head lists PK, PV of float64 [d][r] arrays) replaces the seeded bases."""
     import torch
 
     import rank_compressed_kv_kvlr_amd as kv
     from synth.device import KVGenerator
 
     rk, rv = host.ranks(cfg, layer) if ranks is None else ranks
-    PK, PV = host.bases(cfg, layer)
+    PK, PV = host.bases(cfg, layer) if bases is None else bases
     n_rows = cfg.capacity if n_rows is None else n_rows
     cap = cfg.capacity if capacity is None else capacity
     desc = kv.Desc(cfg.B, cfg.Hq, cfg.Hkv, cfg.d, cap, rk, rv, dtype_code(kv, cfg.in_dtype),
@@ -172,3 +174,54 @@ def tolerance(cfg: Config):
     if cfg.latent_dtype == "f32":
         return rel_inf_rows, 1e-5
     return rel_l2_rows, 2e-2
+
+
+# ---------------------------------------------------------------------------
+# float64 references in worker processes. Regenerating the checked rows on the
+# host dominates the full-size checks, so (batch row, KV head) units go to a
+# pool of spawned workers (one BLAS thread each); the oracle is called as is.
+# ---------------------------------------------------------------------------
+def _one_blas_thread():
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(1)
+
+
+def oracle_pool(max_workers: int = 16):
+    """A process pool for unit references, sized to the host's CPUs (at most max_workers)."""
+    import multiprocessing as mp
+    n = max(1, min(max_workers, len(os.sched_getaffinity(0))))
+    return mp.get_context("spawn").Pool(n, initializer=_one_blas_thread)
+
+
+def _rows_f64(cfg: Config, layer: int, kind: str, b: int, h: int, n: int) -> np.ndarray:
+    return host.decode_to_f64(host.kv_rows(cfg, layer, kind, b, 0, n, heads=[h]), cfg.in_dtype)[:, 0, :]
+
+
+def unit_reference(job):
+    """Oracle output [G][d] of the query heads q_heads [G][d] of KV head h, batch row b,
+    over rows t < T (definition order, float64)."""
+    cfg, layer, b, h, T, q_heads, PK, PV, scale = job
+    K = _rows_f64(cfg, layer, "k", b, h, T)
+    V = _rows_f64(cfg, layer, "v", b, h, T)
+    return oracle.decode_head_reconstructed(np.asarray(q_heads, np.float64), K, V, PK, PV, scale)
+
+
+def unit_reference_folded(job):
+    """Oracle folded output [G][r_v]: q_lat [G][r_k] in, o_lat out, over rows t < T."""
+    cfg, layer, b, h, T, q_lat, PK, PV, scale = job
+    lk = oracle.compress(_rows_f64(cfg, layer, "k", b, h, T), PK)
+    lv = oracle.compress(_rows_f64(cfg, layer, "v", b, h, T), PV)
+    return np.stack([oracle.attend_folded(np.asarray(qi, np.float64), lk, lv, scale) for qi in q_lat])
+
+
+def unit_reference_steps(job):
+    """Oracle outputs [S][G][d] of S decode steps of KV head h, batch row b: step s attends
+    over rows t < T0 + s + 1 (the prefill rows and the tokens appended up to step s) with
+    its own queries q_steps[s] [G][d]. The rows are reconstructed once (definition order)."""
+    cfg, layer, b, h, T0, q_steps, PK, PV, scale = job
+    S = len(q_steps)
+    Kt = oracle.reconstruct(oracle.compress(_rows_f64(cfg, layer, "k", b, h, T0 + S), PK), PK)
+    Vt = oracle.reconstruct(oracle.compress(_rows_f64(cfg, layer, "v", b, h, T0 + S), PV), PV)
+    return np.stack([np.stack([oracle.attend(np.asarray(qi, np.float64), Kt[:T0 + s + 1], Vt[:T0 + s + 1], scale)
+                               for qi in q_steps[s]]) for s in range(S)])
+
