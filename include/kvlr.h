@@ -19,8 +19,8 @@
  *
  * Conventions for every entry point:
  *  - Every function returns 0 (KVLR_OK) or a negative kvlr_status.
- *    Argument checks run on the host before any HIP call; on failure nothing
- *    is launched and no buffer is touched.
+ *    Argument checks run on the host before any work is enqueued; on failure
+ *    nothing is launched and no buffer is touched.
  *  - The caller owns every buffer. The library allocates nothing, keeps no
  *    pointer after returning and never synchronises: work is enqueued on
  *    `stream` (a hipStream_t passed as void*; NULL is the null stream) and
@@ -73,9 +73,14 @@ typedef enum kvlr_status {
   KVLR_ERR_DTYPE = -4,     /* unsupported dtype code */
   KVLR_ERR_WORKSPACE = -5, /* workspace NULL or smaller than kvlr_decode_workspace_bytes() */
   KVLR_ERR_HIP = -6,       /* a kernel launch failed (hipGetLastError) */
-  KVLR_ERR_ARG = -7        /* other invalid argument (split_tokens, scale, start, a buffer not
+  KVLR_ERR_ARG = -7,       /* other invalid argument (split_tokens, scale, start, a buffer not
                               16-byte aligned) */
+  KVLR_ERR_SCRATCH = -8    /* kvlr_decode_attn_noalloc: the call needs more decode workspace than
+                              KVLR_STATIC_SCRATCH_BYTES */
 } kvlr_status;
+
+/* Size of the library's static decode scratch (kvlr_decode_attn_noalloc). */
+#define KVLR_STATIC_SCRATCH_BYTES (16u << 20)
 
 /* split_tokens value that asks kvlr_decode_attn for the balanced plan. */
 #define KVLR_SPLIT_BALANCED (-1)
@@ -339,6 +344,23 @@ KVLR_API int kvlr_append_decode_attn(const kvlr_desc* desc, const void* k_new, c
                                      const int32_t* pos, const float* q, const float* P_K, const float* P_V,
                                      void* lat_k, void* lat_v, const int32_t* seq_lens, float scale, float* out,
                                      void* workspace, size_t workspace_bytes, int32_t split_tokens, void* stream);
+
+/* kvlr_decode_attn for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Arguments and result are those of kvlr_decode_attn without the workspace:
+ * the workspace is a static device array owned by the library,
+ * KVLR_STATIC_SCRATCH_BYTES (16 MiB) per device, held until the process ends.
+ * A call whose kvlr_decode_workspace_bytes(desc, split_tokens) exceeds that
+ * returns KVLR_ERR_SCRATCH and launches nothing. The call allocates nothing.
+ * The first call on a device does a one-time set-up with that device current
+ * (looks up the array's device address, and zeroes the array on `stream`);
+ * make that first call outside graph capture. Every call on a device shares
+ * that device's array and leaves its counters zero: calls that overlap on one
+ * device (concurrent streams or threads) race and must not be made; calls
+ * ordered on one stream are safe. */
+KVLR_API int kvlr_decode_attn_noalloc(const kvlr_desc* desc, const float* q, const float* P_K, const float* P_V,
+                                      const void* lat_k, const void* lat_v, const int32_t* seq_lens, float scale,
+                                      float* out, int32_t split_tokens, void* stream);
 
 /* The two stages of kvlr_decode_attn, for callers that schedule them
  * separately (e.g. to time or overlap them). kvlr_decode_partials(...)

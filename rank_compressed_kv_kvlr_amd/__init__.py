@@ -31,7 +31,7 @@ import numpy as np
 __all__ = [
     "KvlrError", "Desc", "F32", "BF16", "Q43", "VALUES_PER_HEAD", "VALUES_JOINT", "lib", "version", "status_string",
     "cache_elems", "decode_workspace_bytes", "decode_plan", "decode_counter_bytes",
-    "prefill_compress", "append", "decode_attn", "append_decode_attn", "decode_partials", "decode_combine", "decode_attn_latent",
+    "prefill_compress", "append", "decode_attn", "decode_attn_noalloc", "append_decode_attn", "decode_partials", "decode_combine", "decode_attn_latent",
     "hadamard_bases", "q43_outlier", "q43_row_bytes",
     "alloc_cache", "alloc_workspace", "pack_bases", "block_view", "latent_rows", "cap_rows", "k_tiled_index",
     "v_joint_index",
@@ -40,6 +40,7 @@ __all__ = [
 F32, BF16, Q43 = 0, 1, 2
 VALUES_PER_HEAD, VALUES_JOINT = 0, 1
 SPLIT_BALANCED = -1   # split_tokens asking kvlr_decode_attn for the balanced plan
+STATIC_SCRATCH_BYTES = 16 << 20   # the library's static decode scratch (kvlr_decode_attn_noalloc)
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvlr.so")
 
@@ -76,6 +77,7 @@ lib.kvlr_prefill_compress.argtypes = [_D, _P, _P, ctypes.c_int32, ctypes.c_int32
 lib.kvlr_append.argtypes = [_D, _P, _P, _P, _P, _P, _P, _P, _P]
 lib.kvlr_decode_attn.argtypes = [_D, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, ctypes.c_size_t,
                                  ctypes.c_int32, _P]
+lib.kvlr_decode_attn_noalloc.argtypes = [_D, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, ctypes.c_int32, _P]
 lib.kvlr_decode_partials.argtypes = [_D, _P, _P, _P, _P, _P, ctypes.c_float, _P, ctypes.c_size_t, ctypes.c_int32, _P]
 lib.kvlr_decode_combine.argtypes = [_D, _P, _P, ctypes.c_size_t, ctypes.c_int32, _P, _P]
 lib.kvlr_decode_attn_latent.argtypes = [_D, _P, _P, _P, _P, ctypes.c_float, _P, _P, ctypes.c_size_t,
@@ -85,7 +87,7 @@ lib.kvlr_append_decode_attn.argtypes = [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P, 
 lib.kvlr_hadamard_bases.argtypes = [_D, _P, _P, _P, _P, _P]
 for _f in ("kvlr_cache_elems", "kvlr_decode_workspace_bytes", "kvlr_decode_plan", "kvlr_decode_counter_bytes", "kvlr_prefill_compress",
            "kvlr_append", "kvlr_decode_attn", "kvlr_decode_partials", "kvlr_decode_combine",
-           "kvlr_decode_attn_latent", "kvlr_hadamard_bases", "kvlr_append_decode_attn"):
+           "kvlr_decode_attn_latent", "kvlr_hadamard_bases", "kvlr_append_decode_attn", "kvlr_decode_attn_noalloc"):
     getattr(lib, _f).restype = ctypes.c_int
 
 
@@ -345,6 +347,29 @@ def decode_attn(desc: Desc, q, P_K, P_V, lat_k, lat_v, seq_lens, scale: Optional
             _need(out, "out", torch.float32, nq), _need(workspace, "workspace", workspace.dtype),
             ctypes.c_size_t(ws_bytes), split_tokens)
     _check(lib.kvlr_decode_attn(desc.ptr, *args, _stream()), "kvlr_decode_attn")
+    return out
+
+
+def decode_attn_noalloc(desc: Desc, q, P_K, P_V, lat_k, lat_v, seq_lens, scale: Optional[float] = None,
+                        out=None, split_tokens: int = 0):
+    """decode_attn without a workspace argument: the library's static device scratch
+    (STATIC_SCRATCH_BYTES per device) serves as the workspace; nothing is allocated
+    by the call when `out` is given."""
+    torch = _torch()
+    if scale is None:
+        scale = 1.0 / math.sqrt(desc.head_dim)
+    nq = desc.batch * desc.n_q_heads * desc.head_dim
+    if out is None:
+        out = torch.empty((desc.batch, desc.n_q_heads, desc.head_dim), dtype=torch.float32, device=q.device)
+    nk, nv = cache_elems(desc)
+    lad = _dtype_of(desc.latent_dtype)
+    args = (_need(q, "q", torch.float32, nq),
+            _need(P_K, "P_K", torch.float32, _basis_numel(desc, "k")),
+            _need(P_V, "P_V", torch.float32, _basis_numel(desc, "v")),
+            _need(lat_k, "lat_k", lad, nk), _need(lat_v, "lat_v", lad, nv),
+            _need(seq_lens, "seq_lens", torch.int32, desc.batch), ctypes.c_float(scale),
+            _need(out, "out", torch.float32, nq), split_tokens)
+    _check(lib.kvlr_decode_attn_noalloc(desc.ptr, *args, _stream()), "kvlr_decode_attn_noalloc")
     return out
 
 

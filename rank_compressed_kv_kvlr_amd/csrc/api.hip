@@ -1,11 +1,14 @@
 // Host side of the libkvlr C ABI: argument validation, split planning and
-// kernel launches on the caller's stream. Allocates nothing, keeps no state,
-// never synchronises. Every check runs before the first HIP call.
+// kernel launches on the caller's stream. Allocates nothing and never
+// synchronises; the only state is per-device caches (the compute-unit count,
+// the address of the static decode scratch). Every check runs before any
+// work is enqueued.
 #include <math.h>
 #include <stdlib.h>
 
 #include <atomic>
 #include <initializer_list>
+#include <mutex>
 #include <stdint.h>
 #include <string.h>
 
@@ -296,6 +299,7 @@ KVLR_API const char* kvlr_status_string(int status) {
     case KVLR_ERR_WORKSPACE: return "workspace missing or too small";
     case KVLR_ERR_HIP: return "HIP launch failed";
     case KVLR_ERR_ARG: return "invalid scalar argument";
+    case KVLR_ERR_SCRATCH: return "the call needs more decode scratch than the library's static array holds";
     default: return "unknown status";
   }
 }
@@ -641,6 +645,75 @@ KVLR_API int kvlr_append_decode_attn(const kvlr_desc* desc, const void* k_new, c
   p.fuse = 1;
   return hip_status(kvlr::launch_decode(p, desc->latent_dtype, rank_bound, decode_tile(),
                                         static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// decode without a caller workspace: the library's static scratch
+// ---------------------------------------------------------------------------
+// For callers that cannot allocate device memory. The decode workspace (arrival
+// counters, split records, projected queries) lives in a file-scope device
+// array of KVLR_STATIC_SCRATCH_BYTES. Host code never passes the array's name
+// to a kernel: its device address is looked up once per device with
+// hipGetSymbolAddress (each device holds its own copy) and cached.
+namespace {
+
+static __device__ __align__(256) uint32_t scratch[KVLR_STATIC_SCRATCH_BYTES / 4];
+
+__global__ void zero_words(uint32_t* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];   // device address of `scratch`, per device
+
+// Set-up on the first call on a device (with that device current): the array's
+// device address, and the array zeroed on the caller's stream (the arrival
+// counters must start at zero; every completed decode leaves them zero again).
+int static_scratch(hipStream_t s, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KVLR_ERR_HIP;
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!ptr) {
+      if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return KVLR_ERR_HIP;
+      hipLaunchKernelGGL(zero_words, dim3(256), dim3(256), 0, s, static_cast<uint32_t*>(ptr),
+                         (size_t)KVLR_STATIC_SCRATCH_BYTES / 4);
+      if (hipGetLastError() != hipSuccess) return KVLR_ERR_HIP;
+      g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return KVLR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+KVLR_API int kvlr_decode_attn_noalloc(const kvlr_desc* desc, const float* q, const float* P_K, const float* P_V,
+                                      const void* lat_k, const void* lat_v, const int32_t* seq_lens, float scale,
+                                      float* out, int32_t split_tokens, void* stream) {
+  size_t need = 0;
+  int rc = kvlr_decode_workspace_bytes(desc, split_tokens, &need);
+  if (rc) return rc;
+  if (need > (size_t)KVLR_STATIC_SCRATCH_BYTES) return KVLR_ERR_SCRATCH;
+  {   // every other argument check, with a stand-in for the scratch (no memory is read)
+    kvlr::DecodeParams p;
+    kvlr::MergeParams m;
+    int rank_bound = 0;
+    rc = prepare_decode(desc, q, P_K, lat_k, lat_v, seq_lens, scale, P_V, out, true, true,
+                        reinterpret_cast<void*>(uintptr_t{256}), need, split_tokens, &p, &m, &rank_bound, true);
+    if (rc) return rc;
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  rc = static_scratch(s, &ws);
+  if (rc) return rc;
+  return kvlr_decode_attn(desc, q, P_K, P_V, lat_k, lat_v, seq_lens, scale, out, ws, need, split_tokens, stream);
 }
 
 }  // extern "C"

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     assert kv.status_string(0) == "ok"
-    for code in range(-7, 0):
+    for code in range(-8, 0):
         assert kv.status_string(code) not in ("ok", "unknown status")
     assert kv.status_string(-99) == "unknown status"
 
@@ -296,3 +296,17 @@ def test_balanced_plan_queries():
     assert kv.decode_plan(_desc(batch=5000, capacity=64), -1)[1] > 0   # too many rows for the balanced plan
     with pytest.raises(kv.KvlrError):
         kv.decode_plan(uniform, -2)
+
+
+def test_noalloc_entry_checks_on_the_host():
+    """kvlr_decode_attn_noalloc rejects a call whose workspace would exceed the static scratch
+    (KVLR_ERR_SCRATCH) and bad arguments, before any device work."""
+    big = kv.Desc(64, 32, 8, 128, 1 << 20, 64, 64)
+    assert kv.decode_workspace_bytes(big, 64) > kv.STATIC_SCRATCH_BYTES
+    f = kv.lib.kvlr_decode_attn_noalloc
+    assert f(big.ptr, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, 64, None) == -8
+    small = _desc()
+    assert f(small.ptr, None, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, 0, None) == -1
+    assert f(small.ptr, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, float("nan"), FAKE, 0, None) == -7
+    assert f(small.ptr, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, 100, None) == -7   # split not a multiple of 64
+
