@@ -28,13 +28,31 @@ Readings where the page leaves a step open:
   `quantize_block`, so any fp32 implementation takes the same decision;
 * dequantised value: step * code + minimum.
 
-Storage of one token row of rank r (little-endian bytes):
+Storage (the cache layout of kvlr.h, written out here as plain loops). A
+block of rows (one KV head of one batch row) is cut into tiles of 32
+consecutive tokens; a tile of rank r takes 32 * row_bytes(r) bytes, with
+row_bytes(r) = 8 + n_o / 2 + 3 n_i / 8 (n_o outlier, n_i = r - n_o inlier
+channels, both multiples of 16). Token u of a tile (0 <= u < 32) sits in
+"slot" 8 ((u mod 16) div 4) + 4 (u div 16) + (u mod 4). Inside a tile:
 
-  [0:2] step of the outlier block, [2:4] its minimum, [4:6] step of the
-  inlier block, [6:8] its minimum (fp16; both zero when there is no inlier
-  block), then the outlier codes, two per byte (channel 2k in the low
-  nibble of byte k), then the inlier codes as one bit stream (channel c in
-  bits 3c .. 3c+2), zero padding to a multiple of 4 bytes.
+* bytes [0, 256): the block parameters as half floats, parameter P of the
+  token in slot s at byte 64 (s div 8) + 16 P + 2 (s mod 8); P = 0 outlier
+  step, 1 outlier minimum, 2 inlier step, 3 inlier minimum (the inlier pair
+  is zero when there is no inlier block);
+* then n_o / 16 outlier groups of 16 channels, 256 bytes each: 64 words, word
+  w = n + 16 kq (0 <= n < 16, 0 <= kq < 4); byte i (0..3) of word w holds two
+  4-bit codes, block 0 in the low nibble and block 1 in the high nibble;
+* then n_i / 16 inlier groups of 16 channels, 192 bytes each: position w
+  owns bytes 3w .. 3w + 2 as a little-endian 24-bit field that holds 8 codes
+  of 3 bits, code e at bits 3e .. 3e + 2, where e names (block, i) as
+  e = 0..7 -> (0,0) (0,2) (1,0) (1,2) (0,1) (0,3) (1,1) (1,3).
+
+What (block, n, kq, i) means depends on the kind of latent, so that every
+position holds what one lane of the decode kernel feeds to its matrix
+products:
+
+* keys:   token 16 block + n, channel (of the group) 4 kq + i;
+* values: token 16 block + 4 kq + i, channel (of the group) n.
 """
 from __future__ import annotations
 
@@ -124,48 +142,123 @@ def dequantize_row(codes, meta, r: int = None) -> np.ndarray:
     return out
 
 
+TILE = 32
+KINDS = ("k", "v")
+# (block, i) of the code at position e of a 24-bit inlier field
+INLIER_FIELD = ((0, 0), (0, 2), (1, 0), (1, 2), (0, 1), (0, 3), (1, 1), (1, 3))
+
+
 def row_bytes(r: int) -> int:
-    """Bytes of one stored row of rank r."""
+    """Bytes one token takes in the cache at rank r (meta, outlier nibbles, inlier 3-bit codes)."""
     no = n_outlier(r)
-    n = 8 + no // 2 + (3 * (r - no) + 7) // 8
-    return (n + 3) // 4 * 4
+    return 8 + no // 2 + 3 * (r - no) // 8
 
 
-def pack_row(codes, meta, r: int = None) -> np.ndarray:
-    """Codes and block parameters -> the stored bytes of one row (uint8 [row_bytes(r)])."""
+def tile_bytes(r: int) -> int:
+    """Bytes of one tile of 32 tokens."""
+    return TILE * row_bytes(r)
+
+
+def slot(u: int) -> int:
+    """Position of tile token u (0..31) in the parameter arrays."""
+    return 8 * ((u % 16) // 4) + 4 * (u // 16) + (u % 4)
+
+
+def lane_code(kind: str, n: int, kq: int, block: int, i: int):
+    """(token in the tile, channel in the 16-channel group) held at (block, n, kq, i)."""
+    if kind == "k":
+        return 16 * block + n, 4 * kq + i
+    return 16 * block + 4 * kq + i, n
+
+
+def pack_tile(codes, meta, r: int, kind: str) -> np.ndarray:
+    """Codes [32][r] and block parameters [32][4] (float16) of one tile -> its bytes."""
     codes = np.asarray(codes, np.int64)
-    r = codes.shape[0] if r is None else r
+    meta = np.asarray(meta, np.float16)
     no = n_outlier(r)
-    out = np.zeros(row_bytes(r), np.uint8)
-    out[0:8] = np.array(meta, dtype=np.float16).view(np.uint8)
-    for c in range(no):
-        out[8 + c // 2] |= np.uint8((codes[c] & 0xF) << (4 * (c % 2)))
-    base = 8 + no // 2
-    for c in range(r - no):
-        v = int(codes[no + c]) & 0x7
-        for bit in range(3):
-            pos = 3 * c + bit
-            if (v >> bit) & 1:
-                out[base + pos // 8] |= np.uint8(1 << (pos % 8))
+    out = np.zeros(tile_bytes(r), np.uint8)
+    for u in range(TILE):
+        s = slot(u)
+        for P in range(4):
+            off = 64 * (s // 8) + 16 * P + 2 * (s % 8)
+            out[off:off + 2] = np.array([meta[u, P]], np.float16).view(np.uint8)
+    for g in range(no // BLOCK):
+        base = 256 + 256 * g
+        for n in range(16):
+            for kq in range(4):
+                w = n + 16 * kq
+                for i in range(4):
+                    for block in range(2):
+                        tok, ch = lane_code(kind, n, kq, block, i)
+                        out[base + 4 * w + i] |= np.uint8((int(codes[tok, BLOCK * g + ch]) & 0xF) << (4 * block))
+    for g in range((r - no) // BLOCK):
+        base = 256 + 256 * (no // BLOCK) + 192 * g
+        for n in range(16):
+            for kq in range(4):
+                w = n + 16 * kq
+                field = 0
+                for e, (block, i) in enumerate(INLIER_FIELD):
+                    tok, ch = lane_code(kind, n, kq, block, i)
+                    field |= (int(codes[tok, no + BLOCK * g + ch]) & 0x7) << (3 * e)
+                out[base + 3 * w:base + 3 * w + 3] = np.frombuffer(field.to_bytes(3, "little"), np.uint8)
     return out
 
 
-def unpack_row(raw, r: int):
-    """Stored bytes of one row -> (codes [r] uint8, (step_o, base_o, step_i, base_i) as float16)."""
+def unpack_tile(raw, r: int, kind: str):
+    """Bytes of one tile -> (codes [32][r] uint8, meta [32][4] float16)."""
     raw = np.asarray(raw, np.uint8)
     no = n_outlier(r)
-    meta = tuple(raw[0:8].view(np.float16))
-    codes = np.zeros(r, np.uint8)
-    for c in range(no):
-        codes[c] = (raw[8 + c // 2] >> (4 * (c % 2))) & 0xF
-    base = 8 + no // 2
-    for c in range(r - no):
-        v = 0
-        for bit in range(3):
-            pos = 3 * c + bit
-            v |= ((int(raw[base + pos // 8]) >> (pos % 8)) & 1) << bit
-        codes[no + c] = v
+    codes = np.zeros((TILE, r), np.uint8)
+    meta = np.zeros((TILE, 4), np.float16)
+    for u in range(TILE):
+        s = slot(u)
+        for P in range(4):
+            off = 64 * (s // 8) + 16 * P + 2 * (s % 8)
+            meta[u, P] = raw[off:off + 2].copy().view(np.float16)[0]
+    for g in range(no // BLOCK):
+        base = 256 + 256 * g
+        for n in range(16):
+            for kq in range(4):
+                w = n + 16 * kq
+                for i in range(4):
+                    for block in range(2):
+                        tok, ch = lane_code(kind, n, kq, block, i)
+                        codes[tok, BLOCK * g + ch] = (int(raw[base + 4 * w + i]) >> (4 * block)) & 0xF
+    for g in range((r - no) // BLOCK):
+        base = 256 + 256 * (no // BLOCK) + 192 * g
+        for n in range(16):
+            for kq in range(4):
+                w = n + 16 * kq
+                field = int.from_bytes(bytes(raw[base + 3 * w:base + 3 * w + 3]), "little")
+                for e, (block, i) in enumerate(INLIER_FIELD):
+                    tok, ch = lane_code(kind, n, kq, block, i)
+                    codes[tok, no + BLOCK * g + ch] = (field >> (3 * e)) & 0x7
     return codes, meta
+
+
+def unpack_block(raw, T: int, r: int, kind: str):
+    """The first T tokens of a block (its bytes, whole tiles) -> (codes [T][r], meta [T][4])."""
+    raw = np.asarray(raw, np.uint8)
+    n_tiles = (T + TILE - 1) // TILE
+    codes = np.zeros((n_tiles * TILE, r), np.uint8)
+    meta = np.zeros((n_tiles * TILE, 4), np.float16)
+    tb = tile_bytes(r)
+    for k in range(n_tiles):
+        codes[k * TILE:(k + 1) * TILE], meta[k * TILE:(k + 1) * TILE] = unpack_tile(raw[k * tb:(k + 1) * tb], r, kind)
+    return codes[:T], meta[:T]
+
+
+def pack_block(codes, meta, r: int, kind: str) -> np.ndarray:
+    """Codes [T][r] and meta [T][4] of the first T tokens -> the bytes of whole tiles (tokens
+    past T zero)."""
+    codes = np.asarray(codes)
+    T = codes.shape[0]
+    n_tiles = (T + TILE - 1) // TILE
+    c = np.zeros((n_tiles * TILE, r), np.int64)
+    m = np.zeros((n_tiles * TILE, 4), np.float16)
+    c[:T], m[:T] = codes, meta
+    return np.concatenate([pack_tile(c[k * TILE:(k + 1) * TILE], m[k * TILE:(k + 1) * TILE], r, kind)
+                           for k in range(n_tiles)]) if n_tiles else np.zeros(0, np.uint8)
 
 
 def quantize_rows(X32):

@@ -66,11 +66,23 @@ def pin_golden(m) -> bool:
         if "dequantized" in c:   # a block on its own: dequantised with its own step and base
             deq = float(step) * np.asarray(codes, np.float64) + float(base)
             ok &= np.array_equal(deq, np.array(c["dequantized"]))
-    p = g["pack_row"]
-    raw = m.pack_row(np.array(p["codes"]), tuple(np.float16(v) for v in p["meta"]), p["r"])
-    ok &= list(map(int, raw)) == p["bytes"] and len(raw) == m.row_bytes(p["r"])
-    codes, meta = m.unpack_row(np.array(p["bytes"], np.uint8), p["r"])
-    ok &= list(map(int, codes)) == p["codes"] and [float(v) for v in meta] == p["meta"]
+    for t in g["pack_tile"]:
+        r, kind = t["r"], t["kind"]
+        codes = np.zeros((m.TILE, r), np.int64)
+        meta = np.zeros((m.TILE, 4), np.float16)
+        for tok, ch, c in t["codes"]:
+            codes[tok, ch] = c
+        for tok, P, v in t["meta"]:
+            meta[tok, P] = v
+        want = np.zeros(t["tile_bytes"], np.uint8)
+        for off, v in t["bytes"].items():
+            want[int(off)] = v
+        raw = m.pack_tile(codes, meta, r, kind)
+        ok &= len(raw) == m.tile_bytes(r) and np.array_equal(raw, want)
+        c2, m2 = m.unpack_tile(want, r, kind)
+        ok &= np.array_equal(c2, codes) and np.array_equal(m2.view(np.uint16), meta.view(np.uint16))
+    rb = g["row_bytes"]
+    ok &= all(m.row_bytes(int(r)) == v for r, v in rb.items() if r != "note")
     return bool(ok)
 
 
@@ -98,19 +110,28 @@ def pin_quantizer_properties(m) -> bool:
     return bool(ok)
 
 
-def pin_row_round_trip(m) -> bool:
-    """pack/unpack are inverse on random codes for every rank; the outlier block is
-    quantised with 4 bits and the inlier block with 3 (a row whose inlier block spans
-    many steps never stores a code above 7 there)."""
+def pin_tile_round_trip(m) -> bool:
+    """pack/unpack are inverse on random codes and parameters for every rank and both kinds,
+    every byte of a tile is used (a tile holds exactly 32 rows of 3.2-bit-class codes), the
+    outlier block is quantised with 4 bits and the inlier block with 3 (a row whose inlier
+    block spans many steps never stores a code above 7 there)."""
     rng = np.random.default_rng(33)
     ok = True
     for r in range(16, 129, 16):
         no = m.n_outlier(r)
-        codes = np.concatenate([rng.integers(0, 16, no), rng.integers(0, 8, r - no)]).astype(np.uint8)
-        meta = tuple(np.float16(v) for v in rng.standard_normal(4))
-        raw = m.pack_row(codes, meta, r)
-        c2, m2 = m.unpack_row(raw, r)
-        ok &= np.array_equal(c2, codes) and all(float(a) == float(b) for a, b in zip(m2, meta))
+        ok &= m.tile_bytes(r) * 8 == m.TILE * (64 + 4 * no + 3 * (r - no))
+        for kind in ("k", "v"):
+            T = 45
+            codes = np.concatenate([rng.integers(0, 16, (T, no)), rng.integers(0, 8, (T, r - no))], 1).astype(np.uint8)
+            meta = rng.standard_normal((T, 4)).astype(np.float16)
+            raw = m.pack_block(codes, meta, r, kind)
+            ok &= len(raw) == 2 * m.tile_bytes(r)
+            c2, m2 = m.unpack_block(raw, T, r, kind)
+            ok &= np.array_equal(c2, codes) and np.array_equal(m2.view(np.uint16), meta.view(np.uint16))
+            # all-ones codes and parameters fill every bit of a tile
+            full = m.pack_tile(np.concatenate([np.full((32, no), 15), np.full((32, r - no), 7)], 1),
+                               np.full((32, 4), np.float16(np.frombuffer(b"\xff\x7b", np.float16)[0])), r, kind)
+            ok &= bool(np.all(full[256:] == 255)) and bool(np.all(full[:256].view(np.uint16) == 0x7BFF))
         x = np.linspace(-4, 4, r).astype(np.float32)
         cq, _ = m.quantize_row(x, r)
         ok &= int(cq[:no].max()) == 15 and (r == no or int(cq[no:].max()) == 7)
@@ -149,7 +170,7 @@ PINS = {
     "block_sizes": pin_block_sizes,
     "golden": pin_golden,
     "quantizer_properties": pin_quantizer_properties,
-    "row_round_trip": pin_row_round_trip,
+    "tile_round_trip": pin_tile_round_trip,
     "decode_quantized": pin_decode_quantized,
 }
 
@@ -191,12 +212,25 @@ def _no_clamp_block(x, bits):
     return np.rint(t).astype(np.int64).astype(np.uint8), step, base
 
 
-def _swapped_nibbles(codes, meta, r=None):
-    raw = qo.pack_row(codes, meta, r)
-    no = qo.n_outlier(len(codes) if r is None else r)
-    seg = raw[8:8 + no // 2]
-    raw[8:8 + no // 2] = ((seg & 0xF) << 4) | (seg >> 4)
+def _swapped_nibbles(codes, meta, r, kind):
+    raw = qo.pack_tile(codes, meta, r, kind)
+    seg = raw[256:256 + 256 * (qo.n_outlier(r) // 16)]
+    raw[256:256 + len(seg)] = ((seg & 0xF) << 4) | (seg >> 4)
     return raw
+
+
+def _meta_in_token_order(codes, meta, r, kind):
+    raw = qo.pack_tile(codes, np.zeros((32, 4), np.float16), r, kind)
+    meta = np.asarray(meta, np.float16)
+    for u in range(32):
+        for P in range(4):
+            off = 64 * (u // 8) + 16 * P + 2 * (u % 8)
+            raw[off:off + 2] = np.array([meta[u, P]], np.float16).view(np.uint8)
+    return raw
+
+
+def _kinds_swapped(codes, meta, r, kind):
+    return qo.pack_tile(codes, meta, r, "v" if kind == "k" else "k")
 
 
 def _unnormalised_hadamard(n):
@@ -215,7 +249,9 @@ def _three_bit_outliers(x, r=None):
 MUTANTS = {
     "floor_instead_of_round": _variant(quantize_block=_floor_block),
     "no_clamp": _variant(quantize_block=_no_clamp_block),
-    "swapped_nibbles": _variant(pack_row=_swapped_nibbles),
+    "swapped_nibbles": _variant(pack_tile=_swapped_nibbles),
+    "key_value_layouts_swapped": _variant(pack_tile=_kinds_swapped),
+    "parameters_in_token_order": _variant(pack_tile=_meta_in_token_order),
     "unnormalised_hadamard": _variant(hadamard=_unnormalised_hadamard),
     "quarter_outliers": _variant(n_outlier=lambda r: 16 * max(1, int(np.floor(r / 64 + 0.5)))),
     "three_bit_outliers": _variant(quantize_row=_three_bit_outliers),
