@@ -150,21 +150,36 @@ typedef enum kvlr_value_mode {
  * Mixed-precision latents (latent_dtype KVLR_Q43; STAR-KV technical summary,
  * "Metodologia" section 3): the leading n_o(r) = 16 * max(1, (r + 40) / 80)
  * latent channels form the outlier block (20% of the channels, in whole
- * 16-channel Hadamard blocks), the rest the inlier block. Each block of each
- * token is quantised on its own: asymmetric round-to-nearest between its
- * minimum and maximum, 15 steps (4 bits) for the outlier block, 7 steps
- * (3 bits) for the inlier block, with the step and the minimum kept as IEEE
- * half floats; the stored value is step * code + minimum. In fp32 the code is
+ * 16-channel Hadamard blocks), the rest (n_i = r - n_o) the inlier block. Each
+ * block of each token is quantised on its own: asymmetric round-to-nearest
+ * between its minimum and maximum, 15 steps (4 bits) for the outlier block, 7
+ * steps (3 bits) for the inlier block, with the step and the minimum kept as
+ * IEEE half floats; the stored value is step * code + minimum. In fp32 the code is
  *   step = half((max - min) / (2^bits - 1)), base = half(min),
  *   code = clamp(rint((x - base) * (1 / step)), 0, 2^bits - 1)   (0 if step == 0).
- * The caches are byte arrays; a row of rank r takes
- *   rb(r) = round_up(8 + n_o / 2 + ceil(3 (r - n_o) / 8), 4) bytes:
- *   [0:2] outlier step, [2:4] outlier minimum, [4:6] inlier step,
- *   [6:8] inlier minimum (half floats), then the outlier codes two per byte
- *   (channel 2k in the low nibble of byte k), then the inlier codes as one
- *   little-endian bit stream (channel c at bits 3c .. 3c+2), zero padding.
- * With RB = sum_h rb(r_k[h]) and RB_pre(h) its prefix sum, the block of
- * (b, h) starts at byte C16 * (b * RB + RB_pre(h)) and row t at t * rb(r).
+ * The caches are byte arrays. A token of rank r takes
+ *   rb(r) = 8 + n_o / 2 + 3 n_i / 8 bytes
+ * and tokens are stored in tiles of 32: with RB = sum_h rb(r_k[h]), RB_pre(h)
+ * its prefix sum and C32 = T_cap rounded up to a multiple of 32, the block of
+ * (b, h) starts at byte C32 * (b * RB + RB_pre(h)) and tile k (rows 32 k ..
+ * 32 k + 31) at 32 k rb(r) inside it. Token u of a tile sits in slot
+ * s(u) = 8 ((u % 16) / 4) + 4 (u / 16) + u % 4. Inside a tile:
+ *   [0, 256)  block parameters as half floats: parameter P of the token in slot
+ *             s at byte 64 (s / 8) + 16 P + 2 (s % 8), with P = 0 outlier step,
+ *             1 outlier minimum, 2 inlier step, 3 inlier minimum;
+ *   then n_o / 16 groups of 16 outlier channels, 256 bytes each: 64 words,
+ *             word w = n + 16 kq (n < 16, kq < 4), byte i of word w holds code
+ *             (block 0, i) in its low nibble and (block 1, i) in its high nibble;
+ *   then n_i / 16 groups of 16 inlier channels, 192 bytes each: bytes 3 w ..
+ *             3 w + 2 form a little-endian 24-bit field of eight 3-bit codes,
+ *             bits 3 e .. 3 e + 2 holding (block, i) = (0,0) (0,2) (1,0) (1,2)
+ *             (0,1) (0,3) (1,1) (1,3) for e = 0 .. 7.
+ * (block, n, kq, i) names token 16 block + n, channel 4 kq + i of the group in
+ * the key cache, and token 16 block + 4 kq + i, channel n of the group in the
+ * value cache: every word or field is what one lane of the decode kernel feeds
+ * to the score product (keys) or the value product (values), so no code is
+ * moved before use. Rows past a sequence's length may hold any bits. Joint
+ * values: one block of C32 rows per batch row, at byte C32 * b * rb(r).
  * The bases used with such a cache must have the block-wise Hadamard folded
  * in (kvlr_hadamard_bases); compression, append and decode all take those
  * folded bases.
@@ -192,8 +207,8 @@ KVLR_API const char* kvlr_status_string(int status);
 
 /* Validates `desc` and returns, through k_elems / v_elems, the number of
  * latent elements of lat_k and lat_v: B * C16 * sum_h r(h), C16 = T_cap
- * rounded up to a multiple of 16 (bytes, B * C16 * sum_h rb(r(h)), for
- * KVLR_Q43 latents). */
+ * rounded up to a multiple of 16 (bytes, B * C32 * sum_h rb(r(h)), for
+ * KVLR_Q43 latents, C32 = T_cap rounded up to a multiple of 32). */
 KVLR_API int kvlr_cache_elems(const kvlr_desc* desc, size_t* k_elems, size_t* v_elems);
 
 /* Bytes of decode workspace that kvlr_decode_attn needs for this

@@ -174,10 +174,9 @@ def q43_outlier(r: int) -> int:
 
 
 def q43_row_bytes(r: int) -> int:
-    """Bytes of one stored 4/3-bit row of rank r (layout in kvlr.h)."""
+    """Bytes one token takes in a 4/3-bit cache of rank r (tiles of 32 tokens, layout in kvlr.h)."""
     no = q43_outlier(r)
-    n = 8 + no // 2 + (3 * (r - no) + 7) // 8
-    return (n + 3) // 4 * 4
+    return 8 + no // 2 + 3 * (r - no) // 8
 
 
 def _row_storage(desc, r: int) -> int:
@@ -232,8 +231,10 @@ def pack_bases(bases: Sequence, device="cuda"):
 
 
 def cap_rows(desc: Desc) -> int:
-    """Rows allocated per (batch row, KV head) block: capacity rounded up to 16."""
-    return (desc.capacity + 15) // 16 * 16
+    """Rows allocated per (batch row, KV head) block: capacity rounded up to 16 (to 32 for
+    4/3-bit caches, which store tiles of 32 tokens)."""
+    g = 32 if desc.latent_dtype == Q43 else 16
+    return (desc.capacity + g - 1) // g * g
 
 
 def block_view(lat, desc: Desc, which: str, b: int, h: int):
@@ -276,7 +277,8 @@ def v_joint_index(T: int, r: int):
 
 def latent_rows(lat, desc: Desc, which: str, b: int, h: int):
     """Logical latent rows [capacity][r] of (b, h) (a gather for bf16 latents, which are stored
-    in operand order; a view otherwise; [capacity][q43_row_bytes(r)] stored bytes for 4/3-bit rows)."""
+    in operand order; a view otherwise). 4/3-bit caches store tiles of 32 tokens, not rows: this
+    returns the block's bytes (cap_rows * q43_row_bytes(r)) as they are."""
     torch = _torch()
     r = int((desc.r_k if which == "k" else desc.r_v)[h])
     blk = block_view(lat, desc, which, b, h)
@@ -284,8 +286,9 @@ def latent_rows(lat, desc: Desc, which: str, b: int, h: int):
         index = k_tiled_index if which == "k" else v_joint_index
         idx = torch.from_numpy(index(desc.capacity, r).ravel()).to(blk.device)
         return blk[idx].view(desc.capacity, r)
-    w = _row_storage(desc, r)
-    return blk[:desc.capacity * w].view(desc.capacity, w)
+    if desc.latent_dtype == Q43:
+        return blk
+    return blk[:desc.capacity * r].view(desc.capacity, r)
 
 
 def _basis_numel(desc: Desc, which: str) -> int:

@@ -309,7 +309,8 @@ KVLR_API int kvlr_cache_elems(const kvlr_desc* desc, size_t* k_elems, size_t* v_
   const int rc = check_desc(desc, nullptr, nullptr, nullptr, nullptr, &Sk, &Sv);
   if (rc) return rc;
   if (!k_elems || !v_elems) return KVLR_ERR_NULL;
-  const size_t rows = (size_t)kvlr::cap_rows_of(desc->capacity);
+  const size_t rows = (size_t)(desc->latent_dtype == KVLR_Q43 ? kvlr::cap_rows_q43(desc->capacity)
+                                                               : kvlr::cap_rows_of(desc->capacity));
   *k_elems = (size_t)desc->batch * rows * Sk;
   *v_elems = (size_t)desc->batch * rows * Sv;
   return KVLR_OK;

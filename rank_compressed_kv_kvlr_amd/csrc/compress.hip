@@ -58,43 +58,61 @@ __device__ __forceinline__ uint32_t q43_code(float x, float base, float inv, flo
   return (uint32_t)fminf(fmaxf(t, 0.f), levels);
 }
 
-// Quantise one row of r fp32 latents x[] (LDS) and store its rb(r) bytes at dst
-// (4-byte aligned). NO = outlier channels (16 or 32); the word indices of the
-// unrolled loops are compile-time constants, so the row is built in registers.
-template <int NO>
-__device__ void q43_store_row(const float* x, int r, uint32_t* dst) {
-  constexpr int kWords = 15;               // q43_row_bytes(128) / 4
-  constexpr int kInBase = (8 + NO / 2) / 4;  // first word of the inlier bit stream
-  uint32_t w[kWords];
-#pragma unroll
-  for (int k = 0; k < kWords; ++k) w[k] = 0;
+// Quantise one row of r fp32 latents x[] into codes[] (one byte per channel) and its
+// 4 block parameters (half-float bits: outlier step, minimum, inlier step, minimum).
+__device__ void q43_quantise_row(const float* x, int r, uint8_t* codes, uint16_t* prm) {
+  const int no = q43_outlier(r);
   float base, inv;
-  q43_block_params(x, 0, NO, 15.f, base, inv, w[0]);
-#pragma unroll
-  for (int c = 0; c < NO; ++c) w[2 + c / 8] |= q43_code(x[c], base, inv, 15.f) << (4 * (c % 8));
-  if (r > NO) {
-    q43_block_params(x, NO, r, 7.f, base, inv, w[1]);
-#pragma unroll
-    for (int c = 0; c < kMaxRank - NO; ++c) {
-      if (NO + c < r) {
-        const uint32_t v = q43_code(x[NO + c], base, inv, 7.f);
-        const int pos = 3 * c;
-        w[kInBase + pos / 32] |= v << (pos % 32);
-        if (pos % 32 > 29) w[kInBase + pos / 32 + 1] |= v >> (32 - pos % 32);
-      }
-    }
+  uint32_t meta;
+  q43_block_params(x, 0, no, 15.f, base, inv, meta);
+  prm[0] = (uint16_t)(meta & 0xFFFFu);
+  prm[1] = (uint16_t)(meta >> 16);
+  for (int c = 0; c < no; ++c) codes[c] = (uint8_t)q43_code(x[c], base, inv, 15.f);
+  if (r > no) {
+    q43_block_params(x, no, r, 7.f, base, inv, meta);
+    for (int c = no; c < r; ++c) codes[c] = (uint8_t)q43_code(x[c], base, inv, 7.f);
+  } else {
+    meta = 0;
   }
-  const int words = q43_row_bytes(r) / 4;
-#pragma unroll
-  for (int k = 0; k < kWords; ++k)
-    if (k < words) dst[k] = w[k];
+  prm[2] = (uint16_t)(meta & 0xFFFFu);
+  prm[3] = (uint16_t)(meta >> 16);
 }
 
-__device__ __forceinline__ void q43_store_row_any(const float* x, int r, uint32_t* dst) {
-  if (q43_outlier(r) == 16)
-    q43_store_row<16>(x, r, dst);
-  else
-    q43_store_row<32>(x, r, dst);
+// Tile layout (kvlr.h): what (block, n, kq, i) of a lane position means, as
+// (token in the tile, channel in the 16-channel group).
+__device__ __forceinline__ int q43_token(int kind, int n, int kq, int blk, int i) {
+  return kind == 0 ? 16 * blk + n : 16 * blk + 4 * kq + i;
+}
+__device__ __forceinline__ int q43_channel(int kind, int n, int kq, int i) { return kind == 0 ? 4 * kq + i : n; }
+// (block, i) of position e of a 24-bit 3-bit field, and the inverse
+__device__ __forceinline__ int q43_field_blk(int e) { return (e >> 1) & 1; }
+__device__ __forceinline__ int q43_field_i(int e) { return 2 * (e & 1) + (e >> 2); }
+__device__ __forceinline__ int q43_field_pos(int blk, int i) { return 2 * blk + (i >> 1) + 4 * (i & 1); }
+
+// Byte offset in a tile and bit shift of code (token u, channel c), rank r.
+__device__ __forceinline__ void q43_code_pos(int kind, int u, int c, int r, int& byte, int& shift) {
+  const int no = q43_outlier(r);
+  const int blk = u >> 4;
+  const bool four = c < no;
+  const int g = four ? c >> 4 : (c - no) >> 4, cc = four ? c & 15 : (c - no) & 15;
+  int n, kq, i;
+  if (kind == 0) {
+    n = u & 15;
+    kq = cc >> 2;
+    i = cc & 3;
+  } else {
+    n = cc;
+    kq = (u & 15) >> 2;
+    i = u & 3;
+  }
+  const int w = n + 16 * kq;
+  if (four) {
+    byte = kQ43MetaBytes + kQ43OutGroupBytes * g + 4 * w + i;
+    shift = 4 * blk;
+  } else {
+    byte = kQ43MetaBytes + kQ43OutGroupBytes * (no >> 4) + kQ43InGroupBytes * g + 3 * w;
+    shift = 3 * q43_field_pos(blk, i);
+  }
 }
 
 // Block-wise Hadamard fold: every run of 16 floats becomes x H16 / 4 (a fast
@@ -317,20 +335,6 @@ __global__ __launch_bounds__(256) void compress_valu(CompressParams p) {
   }
   const int S = kind ? p.Sv : p.Sk;
   const int s_pre = kind ? p.ht.sv_pre[h] : p.ht.sk_pre[h];
-  if (p.out_q43) {   // latents of the tile into LDS, then one thread per row quantises and stores
-    float* lat = xs + kValuTile * d;
-#pragma unroll
-    for (int k = 0; k < kValuOuts; ++k) {
-      const int idx = threadIdx.x + k * blockDim.x;
-      if (idx < nt * r) lat[idx] = acc[k];
-    }
-    __syncthreads();
-    const int rb = q43_row_bytes(r);
-    uint8_t* blk = static_cast<uint8_t*>(kind ? p.lat_v : p.lat_k) + (size_t)cap_rows_of(p.cap) * ((size_t)b * S + s_pre);
-    for (int t = threadIdx.x; t < nt; t += blockDim.x)
-      q43_store_row_any(lat + t * r, r, reinterpret_cast<uint32_t*>(blk + (size_t)(p.start + t0 + t) * rb));
-    return;
-  }
   const size_t lat_base = (size_t)cap_rows_of(p.cap) * ((size_t)b * S + s_pre);
   const bool k_tiled = p.out_bf16 && kind == 0;
   const bool v_tiled = p.out_bf16 && kind == 1;   // bf16 values: value-product operand order
@@ -347,6 +351,129 @@ __global__ __launch_bounds__(256) void compress_valu(CompressParams p) {
         static_cast<uint16_t*>(kind ? p.lat_v : p.lat_k)[off] = f32_to_bf16_bits(acc[k]);
       else
         static_cast<float*>(kind ? p.lat_v : p.lat_k)[off] = acc[k];
+    }
+  }
+}
+
+// LDS of the 4/3-bit compression: the inputs [64][d] (later the codes [64][128] and
+// parameters [64][4]), then the fp32 latents [64][r]; offset of the latents in floats.
+__host__ __device__ constexpr int q43_lat_offset(int d) {
+  return kValuTile * d > (kValuTile * kMaxRank + kValuTile * 8) / 4 ? kValuTile * d
+                                                                     : (kValuTile * kMaxRank + kValuTile * 8) / 4;
+}
+
+// 4/3-bit latents (tile layout in kvlr.h): one workgroup per (64 rows starting on a
+// 32-row tile, KV head x {K, V}, batch row), so that no tile is shared between
+// workgroups. The chunk's rows inside [start, start + n_tok) get fp32 latents as in
+// compress_valu, one thread per row quantises them (codes and block parameters into
+// LDS), and one thread per 4-bit word or 24-bit field assembles it; words that also
+// hold rows outside the range keep those rows' bits.
+__global__ __launch_bounds__(256) void compress_q43(CompressParams p) {
+  extern __shared__ __attribute__((aligned(16))) float xs[];   // [64][d], then latents [64][r]
+  const int kind = p.only_kind >= 0 ? p.only_kind : (int)(blockIdx.y & 1);
+  const int h = p.only_kind >= 0 ? (int)blockIdx.y : (int)(blockIdx.y >> 1);
+  const bool joint = kind == 1 && p.joint_v;
+  const int b = blockIdx.z;
+  const int d = p.d;
+  const int r = kind ? p.ht.rv[h] : p.ht.rk[h];
+  const void* X = kind ? p.x_v : p.x_k;
+  const int T0 = (p.start & ~(kQ43Tile - 1)) + kValuTile * (int)blockIdx.x;   // first row of the chunk
+  const int lo = max(T0, p.start), hi = min(T0 + kValuTile, p.start + p.n_tok);  // rows written
+  const size_t row_stride = (size_t)p.Hkv * d;
+  float acc[kValuOuts];
+#pragma unroll
+  for (int k = 0; k < kValuOuts; ++k) acc[k] = 0.f;
+  const int heads = joint ? p.Hkv : 1;
+  for (int hs = 0; hs < heads; ++hs) {
+    const int hh = joint ? hs : h;
+    if (hs > 0) __syncthreads();
+    for (int idx = threadIdx.x; idx < kValuTile * d; idx += blockDim.x) {
+      const int t = idx / d, i = idx - t * d;
+      const int row = T0 + t;
+      float v = 0.f;
+      if (row >= lo && row < hi) {
+        const size_t src = ((size_t)b * p.n_tok + (row - p.start)) * row_stride + (size_t)hh * d + i;
+        v = p.in_bf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(X)[src]) : static_cast<const float*>(X)[src];
+      }
+      xs[idx] = v;
+    }
+    __syncthreads();
+    const float* P = (kind ? p.pv : p.pk) + (size_t)d * (kind ? p.ht.rv_pre[hh] : p.ht.rk_pre[hh]);
+#pragma unroll
+    for (int k = 0; k < kValuOuts; ++k) {
+      const int idx = threadIdx.x + k * blockDim.x;
+      if (idx < kValuTile * r) {
+        const int t = idx / r, j = idx - t * r;
+        const float* x = xs + t * d;
+        float a = acc[k];
+        for (int i = 0; i < d; ++i) a = fmaf(x[i], P[(size_t)i * r + j], a);
+        acc[k] = a;
+      }
+    }
+  }
+  float* lat = xs + q43_lat_offset(d);
+#pragma unroll
+  for (int k = 0; k < kValuOuts; ++k) {
+    const int idx = threadIdx.x + k * blockDim.x;
+    if (idx < kValuTile * r) lat[idx] = acc[k];
+  }
+  __syncthreads();
+  uint8_t* codes = reinterpret_cast<uint8_t*>(xs);                                // [64][r]; inputs no longer read
+  uint16_t* prm = reinterpret_cast<uint16_t*>(codes + kValuTile * kMaxRank);      // [64][4]
+  for (int t = threadIdx.x; t < kValuTile; t += blockDim.x)
+    if (T0 + t >= lo && T0 + t < hi) q43_quantise_row(lat + t * r, r, codes + t * r, prm + 4 * t);
+  __syncthreads();
+
+  const int S = kind ? p.Sv : p.Sk;
+  const int s_pre = kind ? p.ht.sv_pre[h] : p.ht.sk_pre[h];
+  uint8_t* blk = static_cast<uint8_t*>(kind ? p.lat_v : p.lat_k) + (size_t)cap_rows_q43(p.cap) * ((size_t)b * S + s_pre);
+  const size_t tb = (size_t)kQ43Tile * q43_row_bytes(r);
+  const int no = q43_outlier(r), go = no >> 4, gi = (r - no) >> 4;
+  const int per_tile = 128 + 64 * (go + gi);   // parameter halves (4 x 32), then one unit per lane and group
+  for (int idx = threadIdx.x; idx < 2 * per_tile; idx += blockDim.x) {
+    const int k = idx / per_tile, x = idx - k * per_tile;
+    const int t_lo = T0 + kQ43Tile * k;          // rows of this tile: [t_lo, t_lo + 32)
+    if (t_lo >= hi || t_lo + kQ43Tile <= lo) continue;
+    uint8_t* tile = blk + (size_t)(t_lo / kQ43Tile) * tb;
+    auto live = [&](int u) { return t_lo + u >= lo && t_lo + u < hi; };
+    auto code = [&](int u, int c) { return (uint32_t)codes[(kQ43Tile * k + u) * r + c]; };
+    if (x < 128) {                              // parameter P of tile token u
+      const int u = x >> 2, P = x & 3;
+      if (live(u)) {
+        const int sl = q43_slot(u);
+        reinterpret_cast<uint16_t*>(tile + 64 * (sl >> 3) + 16 * P)[sl & 7] = prm[4 * (kQ43Tile * k + u) + P];
+      }
+      continue;
+    }
+    const int unit = x - 128, g = unit >> 6, w = unit & 63, n = w & 15, kq = w >> 4;
+    if (g < go) {                               // 4-bit word: byte i, nibble = block
+      uint32_t bits = 0, keep = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) {
+          const int u = q43_token(kind, n, kq, bb, i);
+          const int sh = 8 * i + 4 * bb;
+          if (live(u)) bits |= code(u, 16 * g + q43_channel(kind, n, kq, i)) << sh;
+          else keep |= 0xFu << sh;
+        }
+      uint32_t* dst = reinterpret_cast<uint32_t*>(tile + kQ43MetaBytes + kQ43OutGroupBytes * g) + w;
+      *dst = keep ? ((*dst & keep) | bits) : bits;
+    } else {                                    // 24-bit field of 8 3-bit codes
+      const int gg = g - go;
+      uint32_t bits = 0, keep = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int bb = q43_field_blk(e), i = q43_field_i(e);
+        const int u = q43_token(kind, n, kq, bb, i);
+        if (live(u)) bits |= code(u, no + 16 * gg + q43_channel(kind, n, kq, i)) << (3 * e);
+        else keep |= 0x7u << (3 * e);
+      }
+      uint8_t* dst = tile + kQ43MetaBytes + kQ43OutGroupBytes * go + kQ43InGroupBytes * gg + 3 * w;
+      if (keep) bits = ((dst[0] | (uint32_t)dst[1] << 8 | (uint32_t)dst[2] << 16) & keep) | bits;
+      dst[0] = (uint8_t)bits;
+      dst[1] = (uint8_t)(bits >> 8);
+      dst[2] = (uint8_t)(bits >> 16);
     }
   }
 }
@@ -382,12 +509,50 @@ __global__ __launch_bounds__(128) void append_kernel(AppendParams p) {
   }
   const int S = kind ? p.Sv : p.Sk;
   const int s_pre = kind ? p.ht.sv_pre[h] : p.ht.sk_pre[h];
-  if (p.out_q43) {
+  if (p.out_q43) {   // thread 0 finds the block parameters; thread j quantises channel j
+    __shared__ float qb[4];   // outlier base, 1/step, inlier base, 1/step
+    __shared__ uint16_t qp[4];
     if (j < r) lat[j] = acc;
     __syncthreads();
+    const int no = q43_outlier(r);
     if (threadIdx.x == 0) {
-      uint8_t* blk = static_cast<uint8_t*>(kind ? p.lat_v : p.lat_k) + (size_t)cap_rows_of(p.cap) * ((size_t)b * S + s_pre);
-      q43_store_row_any(lat, r, reinterpret_cast<uint32_t*>(blk + (size_t)pos * q43_row_bytes(r)));
+      uint32_t meta = 0;
+      q43_block_params(lat, 0, no, 15.f, qb[0], qb[1], meta);
+      qp[0] = (uint16_t)(meta & 0xFFFFu);
+      qp[1] = (uint16_t)(meta >> 16);
+      meta = 0;
+      qb[2] = qb[3] = 0.f;
+      if (r > no) q43_block_params(lat, no, r, 7.f, qb[2], qb[3], meta);
+      qp[2] = (uint16_t)(meta & 0xFFFFu);
+      qp[3] = (uint16_t)(meta >> 16);
+    }
+    __syncthreads();
+    uint8_t* tile = static_cast<uint8_t*>(kind ? p.lat_v : p.lat_k) +
+                    (size_t)cap_rows_q43(p.cap) * ((size_t)b * S + s_pre) +
+                    (size_t)(pos / kQ43Tile) * kQ43Tile * q43_row_bytes(r);
+    const int u = pos & (kQ43Tile - 1);
+    if (j < 4) {
+      const int sl = q43_slot(u);
+      reinterpret_cast<uint16_t*>(tile + 64 * (sl >> 3) + 16 * j)[sl & 7] = qp[j];
+    }
+    if (j < r) {
+      const bool four = j < no;
+      const uint32_t c = q43_code(lat[j], qb[four ? 0 : 2], qb[four ? 1 : 3], four ? 15.f : 7.f);
+      int byte, shift;
+      q43_code_pos(kind, u, j, r, byte, shift);
+      // the code's bits inside the tile's dwords (tiles start on 32-byte boundaries); other
+      // threads change other bits of the same dwords, hence the atomic AND / OR
+      const int bit = 8 * byte + shift, width = four ? 4 : 3;
+      uint32_t* wd = reinterpret_cast<uint32_t*>(tile) + (bit >> 5);
+      const int b0 = bit & 31;
+      const uint32_t m0 = ((1u << width) - 1u) << b0;
+      __hip_atomic_fetch_and(wd, ~m0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_or(wd, c << b0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (b0 + width > 32) {
+        const int hi_bits = b0 + width - 32;
+        __hip_atomic_fetch_and(wd + 1, ~((1u << hi_bits) - 1u), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_or(wd + 1, c >> (width - hi_bits), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
     return;
   }
@@ -405,6 +570,16 @@ __global__ __launch_bounds__(128) void append_kernel(AppendParams p) {
 }
 
 }  // namespace
+
+// 4/3-bit compression: chunks of 64 rows from the tile holding row `start`, and their LDS
+// (inputs [64][d] then latents [64][r]; codes and parameters reuse the input area).
+int q43_chunks(const CompressParams& p) {
+  const int t0 = p.start & ~(kQ43Tile - 1);
+  return (p.start + p.n_tok - t0 + kValuTile - 1) / kValuTile;
+}
+size_t q43_lds(const CompressParams& p, int max_r) {
+  return ((size_t)q43_lat_offset(p.d) + (size_t)kValuTile * max_r) * sizeof(float);
+}
 
 hipError_t launch_compress(const CompressParams& p_in, hipStream_t stream) {
   if (p_in.n_tok <= 0) return hipSuccess;
@@ -438,17 +613,24 @@ hipError_t launch_compress(const CompressParams& p_in, hipStream_t stream) {
       default: KVLR_COMPRESS_CASE(8)
     }
 #undef KVLR_COMPRESS_CASE
+  } else if (p.out_q43) {
+    const dim3 grid(q43_chunks(p), ykinds * p.Hkv, p.B);
+    hipLaunchKernelGGL(compress_q43, grid, dim3(256), q43_lds(p, max_r), stream, p);
   } else {
-    const size_t lds = (size_t)kValuTile * (p.d + (p.out_q43 ? max_r : 0)) * sizeof(float);
+    const size_t lds = (size_t)kValuTile * p.d * sizeof(float);
     const dim3 grid((p.n_tok + kValuTile - 1) / kValuTile, ykinds * p.Hkv, p.B);
     hipLaunchKernelGGL(compress_valu, grid, dim3(256), lds, stream, p);
   }
   if (p.joint_v) {   // joint values: one workgroup per (tile, batch row) sums over every head
     CompressParams pv = p_in;
     pv.only_kind = 1;
-    const size_t lds = (size_t)kValuTile * (p.d + (p.out_q43 ? max_r : 0)) * sizeof(float);
-    const dim3 grid((p.n_tok + kValuTile - 1) / kValuTile, 1, p.B);
-    hipLaunchKernelGGL(compress_valu, grid, dim3(256), lds, stream, pv);
+    if (p.out_q43) {
+      hipLaunchKernelGGL(compress_q43, dim3(q43_chunks(pv), 1, p.B), dim3(256), q43_lds(pv, max_r), stream, pv);
+    } else {
+      const size_t lds = (size_t)kValuTile * p.d * sizeof(float);
+      const dim3 grid((p.n_tok + kValuTile - 1) / kValuTile, 1, p.B);
+      hipLaunchKernelGGL(compress_valu, grid, dim3(256), lds, stream, pv);
+    }
   }
   return hipGetLastError();
 }

@@ -21,26 +21,13 @@
 // from HBM (operand-order layout, 16 contiguous bytes per lane) and q~ as B
 // in a high and a low bf16 part, so a lane ends with 4 consecutive tokens of
 // one query head: the A operand of the value product, whose value rows are
-// stored in its B-operand order. 4/3-bit latents (decode_split_q43): keys on
-// MFMA from the stored codes, values on VALU. fp32 latents
-// (decode_split_f32): VALU throughout.
+// stored in its B-operand order. 4/3-bit latents (decode_split_q43): the same
+// two products on MFMA, fed from the stored codes (tiles in operand order).
+// fp32 latents (decode_split_f32): VALU throughout.
 #include "decode_common.hpp"
 
 namespace kvlr {
 namespace {
-
-// Largest number of 64-lane value loads per tile of `tile` tokens over ranks r <= rb
-// (multiples of 16): a row has r/8 chunks of 8 channels, a load instruction
-// covers floor(64 / (r/8)) rows.
-constexpr int value_iters_bound(int rb, int tile) {
-  int worst = 0;
-  for (int r = 16; r <= rb; r += 16) {
-    const int rpi = 64 / (r / 8);
-    const int it = (tile + rpi - 1) / rpi;
-    worst = it > worst ? it : worst;
-  }
-  return worst;
-}
 
 // Merge of the 4 waves' states into one record per head.
 //   wm, wl: [4 waves][4 heads]; red: per-wave per-lane partial sums laid out by
@@ -761,45 +748,88 @@ __global__ __launch_bounds__(256) void decode_balanced_bf16(DecodeParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// 4/3-bit latents (STAR-KV technical summary, "Metodologia" section 3): keys on
-// MFMA, values on VALU, both read as stored codes
+// 4/3-bit latents (STAR-KV technical summary, "Metodologia" section 3): both
+// products on MFMA, straight from the stored codes
 // ---------------------------------------------------------------------------
-// A wave streams ST consecutive rows of keys and of values per iteration with
-// 16-byte loads (the rows of a (batch row, KV head) block are contiguous and a
-// tile starts 16-byte aligned), parks them in its own LDS region while the
-// next ST rows are in flight, and reads the codes it needs from LDS. For ranks
-// up to 64 the tile is one 32-token step (ST = 32), which keeps the kernel
-// within 168 registers, i.e. 3 waves per SIMD and 3 workgroups per CU. The
-// kernel is bound by VALU work and latency, so the third workgroup gains more
-// than the deeper tile. Larger ranks would spill at that size and keep
-// 64-row tiles at 2 waves per SIMD.
-// Scores: a code c enters the MFMA as the bf16 number 128 + c (bits 0x4300 | c,
-// exact), so per token and block of channels
-//   sum_j q~_j (step c_j + base) = step (acc - 128 Q) + base Q,
-// with acc = sum_j q~_j (128 + c_j) from the MFMA and Q = sum_j q~_j over the
-// block, q~ as the MFMA sees it (high plus low bf16 part). Outlier slices hold
-// 16 channels (16x16x16), inlier slices 32 (16x16x32) plus a 16-channel tail.
-// Values: a lane owns 8 channels of a row, all inside one block, and
-// accumulates sum_t p_t step_t c_t per channel and sum_t p_t base_t once per
-// head; the two are added when the split ends.
+// The cache holds tiles of 32 tokens whose words are already in the operand
+// order of the two products (layout in kvlr.h): one 32-bit word or 24-bit field
+// per lane and 16-channel group holds the 8 codes that lane feeds to them. A
+// wave takes one tile per step; the waves of a workgroup take the split's tiles
+// round robin. A code c enters an MFMA as the bf16 number 128 + c (bits
+// 0x4300 | c, exact).
+//  - Scores, transposed: S^T = K q~^T per 16-token block and group of 16 key
+//    channels (v_mfma_f32_16x16x16_bf16, key codes as A, q~ as B in a high and a
+//    low bf16 part), outlier and inlier groups into separate accumulators that
+//    start at -128 Q (Q = sum of q~ over the block, as the MFMA sees it), so
+//    they end as sum_j q~_j c_j. Lane (n, q) then holds tokens 4 q .. 4 q + 3 of
+//    query head n and applies the tokens' block parameters:
+//      s = step_o acc_o + base_o Q_o + step_i acc_i + base_i Q_i.
+//  - Online softmax per query head in the log2 domain, as in the bf16 kernel.
+//  - Values: o_lat[head][ch] += sum_t w_t (128 + c_t,ch) on
+//    v_mfma_f32_16x16x32_bf16 over the tile's 32 tokens, with w = p step_o or
+//    p step_i (high and low bf16 parts, already the A operand in registers) and
+//    the value codes as B. Two more MFMAs against a B operand of ones give
+//    sum_t w_t (the 128 offset), and each lane keeps sum_t p_t base_t; the
+//    three are combined when the split ends.
+// Codes are turned into MFMA operands with a handful of bit operations: a
+// 4-bit word splits into its low and high nibbles (blocks 0 and 1) and v_perm
+// interleaves them with the exponent byte 0x43; a 24-bit 3-bit field is
+// rotated so that codes e and e + 4 sit 16 bits apart, and each pair is one
+// shift and one AND-OR.
+constexpr uint32_t kBf16Code = 0x43434343u;   // bf16 exponent bytes of 128 + c (keys)
+constexpr uint32_t kF16Code = 0x64646464u;    // f16 exponent bytes of 1024 + c (values)
+
+// v_perm selectors: bytes 0 and 1 (2 and 3) of x, each followed by the exponent byte
+__device__ __forceinline__ u32x2_t nibbles_to_num(uint32_t x, uint32_t ebytes) {
+  return u32x2_t{__builtin_amdgcn_perm(ebytes, x, 0x04010400u), __builtin_amdgcn_perm(ebytes, x, 0x04030402u)};
+}
+
+// One 4-bit group word of a lane -> the 8 codes as 16-bit pairs (exponent byte ebytes):
+// dwords 0, 1 block 0 (positions i = 0..3), dwords 2, 3 block 1.
+__device__ __forceinline__ u32x4_t codes4_to_num(uint32_t w, uint32_t ebytes) {
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+  const u32x2_t a = nibbles_to_num(lo, ebytes), b = nibbles_to_num(hi, ebytes);
+  return u32x4_t{a.x, a.y, b.x, b.y};
+}
+
+// One 24-bit 3-bit field (bits 0..23 of x) -> the same order: field position e
+// holds (block, i) = (0,0) (0,2) (1,0) (1,2) (0,1) (0,3) (1,1) (1,3), so after
+// moving bits 12..23 to 16..27 the pairs (e, e + 4) are (block e / 2, i = 2 (e % 2) + {0, 1}).
+__device__ __forceinline__ u32x4_t codes3_to_num(uint32_t x, uint32_t ebytes) {
+  const uint32_t rot = __builtin_amdgcn_alignbit(x, x, 28);   // rotate left by 4
+  const uint32_t y = (x & 0xFFFFu) | (rot & 0xFFFF0000u);
+  const uint32_t e2 = ebytes & 0xFF00FF00u;
+  u32x4_t o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = ((y >> (3 * e)) & 0x00070007u) | e2;
+  return o;
+}
+
+// The lane's 24-bit field of an inlier group: bytes 3 lane .. 3 lane + 2 of the group,
+// from the two dwords that hold them (the same dword when they do not straddle).
+__device__ __forceinline__ uint32_t field24(uint32_t w_a, uint32_t w_b, int shift) {
+  return __builtin_amdgcn_alignbit(w_b, w_a, shift);
+}
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+// A vector element is copied to a scalar before it is bit-cast: clang's __builtin_bit_cast
+// applied straight to an element of an ext_vector_type value reads element 0 whatever
+// the index (found in the ISA of this file; the copy is compiled as intended).
+__device__ __forceinline__ float half_at(const u32x4_t& v, int k) {   // half float k (0..7) of a 16-byte piece
+  const uint32_t w = v[k >> 1];
+  return (float)__builtin_bit_cast(half2_t, w)[k & 1];
+}
+__device__ __forceinline__ half2_t half2_of(uint32_t w) { return __builtin_bit_cast(half2_t, w); }
+
 template <int RB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB <= 64 ? 3 : 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB <= 64 ? 3 : 2)))
 void decode_split_q43(DecodeParams p) {
-  constexpr int TT = 32;                     // tokens per score/softmax/value step
-  constexpr int NB = TT / 16;
-  constexpr int ST = RB <= 64 ? 32 : 64;     // rows per wave iteration
-  constexpr int NSUB = ST / TT;
-  constexpr int RBM = q43_row_bytes(RB);     // bytes of the longest row
-  constexpr int CH = (ST * RBM + 1023) / 1024;   // 16-byte chunks per lane per tile (keys or values)
-  constexpr int MSO = RB == 128 ? 2 : 1;     // outlier 16-channel slices (bound)
-  constexpr int MSI = RB > 32 ? (RB - 16) / 32 : 1;   // full 32-channel inlier slices (bound; >= 1)
-  constexpr int NIT = value_iters_bound(RB, TT);
+  constexpr int GO = RB == 128 ? 2 : 1;                    // 4-bit groups (bound): group 0 always is one
+  constexpr int GI = RB == 128 ? 6 : (RB - 16) / 16;       // 3-bit groups (bound)
+  constexpr int NG = GO + GI;                              // groups from GO on are always 3-bit
   constexpr int QTS = RB;
-  constexpr int kRS = 36;                    // per-lane stride of the wave reduction
-  constexpr int kStageF = kWaves * ST * 2 * RBM / 4;   // floats of LDS for the staged rows
-  static_assert(kStageF + kWaves * TT * 4 <= kTailLds, "staged rows and p tiles must fit the LDS block");
-  __shared__ __attribute__((aligned(16))) float smem[kWaves * 64 * kRS + 64 > kTailLds ? kWaves * 64 * kRS + 64 : kTailLds];
-  __shared__ float qsum[2][kHeadsPerWg];     // Q of the outlier and inlier key blocks per head
+  __shared__ __attribute__((aligned(16))) float smem[kTailLds];
 
   const int s = blockIdx.x;
   const int h = blockIdx.y / p.n_head_groups;
@@ -811,334 +841,243 @@ void decode_split_q43(DecodeParams p) {
   const int T = min(max(p.seq_lens[b], 0), p.cap);
   const int t_begin = min(s * p.ht.split_len[h], T);
   const int t_end = min(T, t_begin + p.ht.split_len[h]);
+  const RecLayout rl = fixed_records(p, b, hq0);
   if (t_begin >= t_end) {
-    write_empty_records(fixed_records(p, b, hq0), s, gpw, rv);
+    write_empty_records(rl, s, gpw, rv);
     BasisPrefetch<RB> pf;
     prefetch_basis<RB>(p, h, rv, pf);
-    finish_split<RB>(p, b, h, hg, hq0, gpw, rv, smem, pf, fixed_records(p, b, hq0), p.n_splits);
+    finish_split<RB>(p, b, h, hg, hq0, gpw, rv, smem, pf, rl, p.n_splits);
     return;
   }
 
-  const int tid = thread_id(), lane = tid & 63, wave = tid >> 6;
+  const int tid = thread_id(), lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = lane & 15, q4 = lane >> 4;
-
-  // ---- key row geometry and this lane's byte offsets inside a row
-  const int nok = q43_outlier(rk), nik = rk - nok;
-  const int nso = nok >> 4, nsi = nik >> 5, ktail = (nik >> 4) & 1;
-  const int rbk = q43_row_bytes(rk);
-  const int kib = 8 + nok / 2;                          // inlier bit stream
-  const int ko_off = 8 + 4 * (q4 >> 1), ko_sh = 16 * (q4 & 1);
-  const int ki_off = kib + 4 * ((24 * q4) >> 5), ki_sh = (24 * q4) & 31;
-  const bool ki_two = ki_sh > 8;
-  const int kt_off = kib + 4 * (3 * nsi + ((12 * q4) >> 5)), kt_sh = (12 * q4) & 31;
-  const bool kt_two = kt_sh > 20;
-  // ---- value row geometry: C chunks of 8 channels per row
-  const int nov = q43_outlier(rv);
-  const int rbv = q43_row_bytes(rv);
-  const int C = rv >> 3;
-  const int rpi = 64 / C;
-  const int ro = lane / C, cch = lane - ro * C;
-  const bool v_active = ro < rpi;
-  const int n_it = (TT + rpi - 1) / rpi;
-  const bool v_out = cch < (nov >> 3);                 // chunk in the 4-bit outlier block
-  const int v_meta = v_out ? 0 : 4;
-  const int v_bits = v_out ? 4 : 3;
-  const int v_bit0 = v_out ? 0 : 24 * (cch - (nov >> 3));
-  const int v_off = v_out ? 8 + 4 * cch : 8 + nov / 2 + 4 * (v_bit0 >> 5);
-  const int v_sh = v_out ? 0 : v_bit0 & 31;
-  const bool v_two = v_sh > 8;
-
-  const size_t rows = cap_rows_of(p.cap);
+  const bool q_ok = n16 < gpw;
+  const int gok = q43_outlier(rk) >> 4, ngk = rk >> 4;   // 4-bit groups and all groups of the keys
+  const int gov = q43_outlier(rv) >> 4, ngv = rv >> 4;
+  const size_t tbk = (size_t)kQ43Tile * q43_row_bytes(rk), tbv = (size_t)kQ43Tile * q43_row_bytes(rv);
+  const size_t rows = cap_rows_q43(p.cap);
   const uint8_t* Kb = static_cast<const uint8_t*>(p.lat_k) + rows * ((size_t)b * p.Sk + p.ht.sk_pre[h]);
   const uint8_t* Vb = static_cast<const uint8_t*>(p.lat_v) + rows * ((size_t)b * p.Sv + p.ht.sv_pre[h]);
+  // this lane's 24-bit fields: bytes 3 lane .. 3 lane + 2 of a 3-bit group, inside 2 dwords
+  const int off_a = (3 * lane) & ~3, off_b = (3 * lane + 2) & ~3, f_shift = 8 * ((3 * lane) & 3);
 
-  // this wave's LDS: staged key rows, staged value rows, then (after all staging) its p tile
-  uint8_t* kst = reinterpret_cast<uint8_t*>(smem) + (size_t)wave * ST * 2 * RBM;
-  uint8_t* vst = kst + ST * RBM;
-  float* p_lds = smem + kStageF + wave * (TT * 4);     // [TT tokens][4 heads]
+  // One tile of one kind in registers: the 4 parameter arrays (this lane's 8 slots each,
+  // only lanes of a live query head load them) and, per 16-channel group in channel
+  // order, the lane's 4-bit word (wa) or the two dwords of its 24-bit field (wa, wb).
+  u32x4_t km[4], vm[4];
+  uint32_t kwa[NG], kwb[NG], vwa[NG], vwb[NG];
+  auto load_tile = [&](const uint8_t* tile, int go, int ng, u32x4_t* meta, uint32_t* wa, uint32_t* wb) {
+#pragma unroll
+    for (int P = 0; P < 4; ++P)
+      meta[P] = q_ok ? load_stream16(tile + 64 * q4 + 16 * P) : u32x4_t{0u, 0u, 0u, 0u};
+    const uint8_t* in = tile + kQ43MetaBytes + kQ43OutGroupBytes * go;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const bool four = g == 0 || (GO == 2 && g == 1 && go == 2);
+      if (four) {
+        wa[g] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(tile + kQ43MetaBytes + kQ43OutGroupBytes * g) + lane);
+      } else if (g < ng) {
+        const uint8_t* grp = in + kQ43InGroupBytes * (g - go);
+        wa[g] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(grp + off_a));
+        wb[g] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(grp + off_b));
+      }
+    }
+  };
+  // operands of group g: 16-bit pairs with exponent bytes eb, block 0 then block 1
+  auto group_codes = [&](int g, int go, const uint32_t* wa, const uint32_t* wb, uint32_t eb) -> u32x4_t {
+    if (g == 0) return codes4_to_num(wa[0], eb);
+    if (g >= GO) return codes3_to_num(field24(wa[g], wb[g], f_shift), eb);
+    return go == 2 ? codes4_to_num(wa[g], eb) : codes3_to_num(field24(wa[g], wb[g], f_shift), eb);
+  };
 
-  float m[4], l[4], acc[4][8], accb[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m[i] = kNegInf;
-    l[i] = 0.f;
-    accb[i] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
+  int t0 = t_begin + wave * kQ43Tile;   // split starts are multiples of 64 tokens: whole tiles
+  if (t0 < t_end) {
+    load_tile(Kb + (size_t)(t0 / kQ43Tile) * tbk, gok, ngk, km, kwa, kwb);
+    load_tile(Vb + (size_t)(t0 / kQ43Tile) * tbv, gov, ngv, vm, vwa, vwb);
   }
 
-  // ---- tile streaming: rows [t0, t0 + ST) of keys and values as 16-byte chunks.
-  // Chunks past the last valid row's bytes are not read (they never cross the end
-  // of the block: it is a multiple of 16 bytes, as is every tile start).
-  u32x4_t kraw[CH], vraw[CH];
-  int nk_ch = 0, nv_ch = 0;
-  auto load_raw = [&](int t0) {
-    const int n = min(ST, t_end - t0);
-    nk_ch = (n * rbk + 15) >> 4;
-    nv_ch = (n * rbv + 15) >> 4;
-    const uint8_t* ks = Kb + (size_t)t0 * rbk;
-    const uint8_t* vs = Vb + (size_t)t0 * rbv;
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int ch = c * 64 + lane;
-      if (ch < nk_ch) kraw[c] = load_stream16(ks + 16 * ch);
-      if (ch < nv_ch) vraw[c] = load_stream16(vs + 16 * ch);
-    }
-  };
-  auto stage_raw = [&]() {
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int ch = c * 64 + lane;
-      if (ch < nk_ch) *reinterpret_cast<u32x4_t*>(kst + 16 * ch) = kraw[c];
-      if (ch < nv_ch) *reinterpret_cast<u32x4_t*>(vst + 16 * ch) = vraw[c];
-    }
-  };
-  auto lds32 = [](const uint8_t* ptr) { return *reinterpret_cast<const uint32_t*>(ptr); };
-
-  // the first tile's loads do not depend on q~: issue them before the prologue
-  int t0 = t_begin + wave * ST;
-  if (t0 < t_end) load_raw(t0);
-
-  // ---- prologue: q~ into LDS, block sums Q, MFMA A operands (hi/lo) into registers
-  float* q_lds = smem;                          // [4][d]  (d <= 256)
+  // ---- prologue: q~ (scaled to log2 units) and, per key group, this lane's column as B (hi/lo)
+  float* q_lds = smem;                          // [4][d]
   float* qt_lds = smem + kHeadsPerWg * 256;     // [4][QTS]
   float* qred = qt_lds + kHeadsPerWg * QTS;     // [4 waves][4][QTS]
   project_query<RB>(p, b, h, hq0, gpw, rk, q_lds, qred, qt_lds);
-  if (tid < 2 * kHeadsPerWg) {
-    const int g = tid & 3, region = tid >> 2;
-    const int j1 = region ? rk : nok;
-    float Q = 0.f;
-    for (int j = region ? nok : 0; j < j1; ++j) {
-      const float x = qt_lds[g * QTS + j];
+  bf16x4_t qh[NG], ql[NG];
+  float Qo = 0.f, Qi = 0.f;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const bool four = g < gok;
+    const bool ok = g < ngk;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ch = 16 * g + 4 * q4 + i;   // 4-bit groups first, then 3-bit: channels in order
+      const float x = (q_ok && ok) ? qt_lds[n16 * QTS + ch] : 0.f;
       const uint16_t hi = f32_to_bf16_bits(x);
       const uint16_t lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
-      Q += bf16_bits_to_f32(hi) + bf16_bits_to_f32(lo);
+      qh[g][i] = (short)hi;
+      ql[g][i] = (short)lo;
+      const float seen = bf16_bits_to_f32(hi) + bf16_bits_to_f32(lo);
+      if (four) Qo += seen; else Qi += seen;
     }
-    qsum[region][g] = Q;
   }
-  auto qt_at = [&](int j, bool valid) { return (n16 < kHeadsPerWg && valid) ? qt_lds[n16 * QTS + j] : 0.f; };
-  auto bf_hi = [](float x) { return (short)f32_to_bf16_bits(x); };
-  auto bf_lo = [](float x) { return (short)f32_to_bf16_bits(x - bf16_bits_to_f32(f32_to_bf16_bits(x))); };
-  bf16x4_t ao_hi[MSO], ao_lo[MSO], at_hi, at_lo;
-  bf16x8_t ai_hi[MSI], ai_lo[MSI];
-#pragma unroll
-  for (int sl = 0; sl < MSO; ++sl)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float x = qt_at(16 * sl + 4 * q4 + e, sl < nso);
-      ao_hi[sl][e] = bf_hi(x);
-      ao_lo[sl][e] = bf_lo(x);
-    }
-#pragma unroll
-  for (int sl = 0; sl < MSI; ++sl)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float x = qt_at(nok + 32 * sl + 8 * q4 + e, sl < nsi);
-      ai_hi[sl][e] = bf_hi(x);
-      ai_lo[sl][e] = bf_lo(x);
-    }
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float x = qt_at(nok + 32 * nsi + 4 * q4 + e, ktail != 0);
-    at_hi[e] = bf_hi(x);
-    at_lo[e] = bf_lo(x);
-  }
+  Qo += __shfl_xor(Qo, 16, 64);
+  Qo += __shfl_xor(Qo, 32, 64);
+  Qi += __shfl_xor(Qi, 16, 64);
+  Qi += __shfl_xor(Qi, 32, 64);
+  const float c_o = -128.f * Qo, c_i = -128.f * Qi;
   __syncthreads();   // LDS is reused below
-  float Qo[4], Qi[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    Qo[i] = qsum[0][i];
-    Qi[i] = qsum[1][i];
-  }
-  if (t0 < t_end) stage_raw();
 
-  for (; t0 < t_end; t0 += kWaves * ST) {
-    const int t_next = t0 + kWaves * ST;
-    const int n_valid = min(ST, t_end - t0);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (t_next < t_end) load_raw(t_next);   // in flight while this tile is processed from LDS
+  const half8_t ones = __builtin_bit_cast(half8_t, u32x4_t{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u});
+  float m = kNegInf, l = 0.f;
+  // value accumulators (rows: query heads 4 q4 + i) and the sums over tokens of w_o, w_i,
+  // p base_o and p base_i (the same rows, every column alike)
+  f32x4_t acc[NG], sw_o = {0.f, 0.f, 0.f, 0.f}, sw_i = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t sb_o = {0.f, 0.f, 0.f, 0.f}, sb_i = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int g = 0; g < NG; ++g) acc[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    for (int sub = 0; sub < NSUB; ++sub) {
-      const int ts = 32 * sub;                 // first row of the step inside the tile
-      if (ts >= n_valid) break;
-      // ---- scores on MFMA from the codes (128 + c as bf16)
-      f32x4_t sc[NB];
+  for (; t0 < t_end; t0 += kWaves * kQ43Tile) {
+    const int t_next = t0 + kWaves * kQ43Tile;
+    // ---- scores S^T[token][head], both 16-token blocks; accumulators start at -128 Q
+    f32x4_t ao[2] = {{c_o, c_o, c_o, c_o}, {c_o, c_o, c_o, c_o}};
+    f32x4_t ai[2] = {{c_i, c_i, c_i, c_i}, {c_i, c_i, c_i, c_i}};
 #pragma unroll
-      for (int blk = 0; blk < NB; ++blk) {
-        const uint8_t* row = kst + min(ts + 16 * blk + n16, n_valid - 1) * rbk;
-        f32x4_t ao = {0.f, 0.f, 0.f, 0.f}, ai = {0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < NG; ++g) {
+      if (g < ngk) {
+        const u32x4_t kc = group_codes(g, gok, kwa, kwb, kBf16Code);
 #pragma unroll
-        for (int sl = 0; sl < MSO; ++sl) {
-          if (sl < nso) {
-            const uint32_t x = lds32(row + ko_off + 8 * sl) >> ko_sh;   // 4 nibbles: channels 4 q4 ..
-            const uint32_t lo = x & 0x0F0Fu, hi = (x >> 4) & 0x0F0Fu;
-            u32x2_t w;
-            w.x = __builtin_amdgcn_perm(hi, lo, 0x0C040C00u) | 0x43004300u;
-            w.y = __builtin_amdgcn_perm(hi, lo, 0x0C050C01u) | 0x43004300u;
-            const bf16x4_t kb = __builtin_bit_cast(bf16x4_t, w);
-            ao = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ao_hi[sl], kb, ao, 0, 0, 0);
-            ao = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ao_lo[sl], kb, ao, 0, 0, 0);
+        for (int blk = 0; blk < 2; ++blk) {
+          const bf16x4_t a = __builtin_bit_cast(bf16x4_t, u32x2_t{kc[2 * blk], kc[2 * blk + 1]});
+          if (g == 0 || (GO == 2 && g == 1 && gok == 2)) {
+            ao[blk] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, qh[g], ao[blk], 0, 0, 0);
+            ao[blk] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ql[g], ao[blk], 0, 0, 0);
+          } else {
+            ai[blk] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, qh[g], ai[blk], 0, 0, 0);
+            ai[blk] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ql[g], ai[blk], 0, 0, 0);
           }
         }
-#pragma unroll
-        for (int sl = 0; sl < MSI; ++sl) {
-          if (sl < nsi) {
-            const uint32_t w0 = lds32(row + ki_off + 12 * sl);
-            const uint32_t w1 = ki_two ? lds32(row + ki_off + 12 * sl + 4) : 0u;
-            const uint32_t bits = __builtin_amdgcn_alignbit(w1, w0, ki_sh);
-            u32x4_t w;
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-              w[k] = __builtin_amdgcn_ubfe(bits, 6 * k, 3) | (__builtin_amdgcn_ubfe(bits, 6 * k + 3, 3) << 16) |
-                     0x43004300u;
-            const bf16x8_t kb = __builtin_bit_cast(bf16x8_t, w);
-            ai = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ai_hi[sl], kb, ai, 0, 0, 0);
-            ai = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ai_lo[sl], kb, ai, 0, 0, 0);
-          }
-        }
-        if (ktail) {
-          const uint32_t w0 = lds32(row + kt_off);
-          const uint32_t w1 = kt_two ? lds32(row + kt_off + 4) : 0u;
-          const uint32_t bits = __builtin_amdgcn_alignbit(w1, w0, kt_sh);
-          u32x2_t w;
-          w.x = __builtin_amdgcn_ubfe(bits, 0, 3) | (__builtin_amdgcn_ubfe(bits, 3, 3) << 16) | 0x43004300u;
-          w.y = __builtin_amdgcn_ubfe(bits, 6, 3) | (__builtin_amdgcn_ubfe(bits, 9, 3) << 16) | 0x43004300u;
-          const bf16x4_t kb = __builtin_bit_cast(bf16x4_t, w);
-          ai = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(at_hi, kb, ai, 0, 0, 0);
-          ai = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(at_lo, kb, ai, 0, 0, 0);
-        }
-        // block parameters of this lane's token (lanes 0..15 hold heads 0..3)
-        const uint32_t m0 = lds32(row), m1 = lds32(row + 4);
-        const float so = half_bits_to_f32(m0 & 0xFFFFu), bo = half_bits_to_f32(m0 >> 16);
-        const float si = half_bits_to_f32(m1 & 0xFFFFu), bi = half_bits_to_f32(m1 >> 16);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sc[blk][i] = so * (ao[i] - 128.f * Qo[i]) + bo * Qo[i] + si * (ai[i] - 128.f * Qi[i]) + bi * Qi[i];
       }
-
-      // ---- online softmax (as in the bf16 kernel)
-      const int tb = t0 + ts;
-      float alpha[4];
+    }
+    // the keys' block parameters: s = step_o acc_o + base_o Q_o + step_i acc_i + base_i Q_i
+    const bool tail = t0 + kQ43Tile > t_end;   // rows past the end may hold any bits
+    float sc[2][4];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float mx = kNegInf;
-#pragma unroll
-        for (int blk = 0; blk < NB; ++blk) {
-          const bool valid = (tb + 16 * blk + n16) < t_end;
-          sc[blk][i] = valid ? sc[blk][i] : kNegInf;
-          mx = fmaxf(mx, sc[blk][i]);
-        }
-        mx = row16_allreduce<true>(mx);
-        const float m_new = fmaxf(m[i], mx);
-        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-        alpha[i] = fast_exp2(m[i] - m_use);
-        float ls = 0.f;
-#pragma unroll
-        for (int blk = 0; blk < NB; ++blk) {
-          const float pr = fast_exp2(sc[blk][i] - m_use);
-          sc[blk][i] = pr;
-          ls += pr;
-        }
-        l[i] = fmaf(l[i], alpha[i], ls);
-        m[i] = m_new;
+        const int k = 4 * blk + i;
+        float x = half_at(km[0], k) * ao[blk][i] + half_at(km[1], k) * Qo + half_at(km[2], k) * ai[blk][i] +
+                  half_at(km[3], k) * Qi;
+        if (!q_ok) x = kNegInf;
+        if (tail && t0 + 16 * blk + 4 * q4 + i >= t_end) x = kNegInf;
+        sc[blk][i] = x;
       }
-      if (q4 == 0) {
-#pragma unroll
-        for (int blk = 0; blk < NB; ++blk)
-          *reinterpret_cast<float4*>(p_lds + (16 * blk + n16) * 4) =
-              make_float4(sc[blk][0], sc[blk][1], sc[blk][2], sc[blk][3]);
-      }
-      float a_s[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a_s[i] = readlane_f(alpha[i], 0);
-      if (a_s[0] != 1.f || a_s[1] != 1.f || a_s[2] != 1.f || a_s[3] != 1.f) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          accb[i] *= a_s[i];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[i][e] *= a_s[i];
-        }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (t_next < t_end) load_tile(Kb + (size_t)(t_next / kQ43Tile) * tbk, gok, ngk, km, kwa, kwb);
 
-      // ---- value mix on VALU from the codes
+    // ---- online softmax (lane: head n16, tokens 16 blk + 4 q4 + i)
+    float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m, mx);
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+    const float alpha = q_ok ? fast_exp2(m - m_use) : 1.f;
+    float pr[2][4], ls = 0.f;
 #pragma unroll
-      for (int it = 0; it < NIT; ++it) {
-        if (it < n_it) {
-          const int r = it * rpi + ro;
-          if (v_active && r < TT) {
-            const uint8_t* row = vst + min(ts + r, n_valid - 1) * rbv;
-            const float4 pw = *reinterpret_cast<const float4*>(p_lds + r * 4);
-            const uint32_t mt = lds32(row + v_meta);
-            const float step = half_bits_to_f32(mt & 0xFFFFu), base = half_bits_to_f32(mt >> 16);
-            const uint32_t c0 = lds32(row + v_off);
-            const uint32_t c1 = v_two ? lds32(row + v_off + 4) : 0u;
-            const uint32_t bits = __builtin_amdgcn_alignbit(c1, c0, v_sh);
-            accb[0] = fmaf(pw.x, base, accb[0]);
-            accb[1] = fmaf(pw.y, base, accb[1]);
-            accb[2] = fmaf(pw.z, base, accb[2]);
-            accb[3] = fmaf(pw.w, base, accb[3]);
-            const float w0 = pw.x * step, w1 = pw.y * step, w2 = pw.z * step, w3 = pw.w * step;
+    for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float c = (float)__builtin_amdgcn_ubfe(bits, e * v_bits, v_bits);
-              acc[0][e] = fmaf(w0, c, acc[0][e]);
-              acc[1][e] = fmaf(w1, c, acc[1][e]);
-              acc[2][e] = fmaf(w2, c, acc[2][e]);
-              acc[3][e] = fmaf(w3, c, acc[3][e]);
-            }
-          }
-        }
+      for (int i = 0; i < 4; ++i) {
+        pr[blk][i] = fast_exp2(sc[blk][i] - m_use);   // masked: exp2(-inf) = 0
+        ls += pr[blk][i];
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    l = fmaf(l, alpha, ls);
+    m = m_new;
+    if (__ballot(alpha != 1.f)) {
+      // accumulator rows are query heads 4 q4 + i; their factors sit in lanes 4 q4 + i
+      float ar[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * q4 + i, 64);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int g = 0; g < NG; ++g) acc[g][i] *= ar[i];
+        sw_o[i] *= ar[i];
+        sw_i[i] *= ar[i];
+        sb_o[i] *= ar[i];
+        sb_i[i] *= ar[i];
+      }
     }
-    if (t_next < t_end) stage_raw();   // this tile's LDS reads are done (in order within the wave)
+
+    // ---- value weights in half floats, two tokens per operation: w = p step, and p base;
+    // lane (n16, q4) holds K slots k = 4 blk + i of head n16, whose parameters are the
+    // halves of its 16-byte pieces. In the last tile the parameters of rows past the end
+    // are zeroed (they may hold any bits).
+    if (tail) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int k = 2 * j, t_k = t0 + 16 * (k >> 2) + 4 * q4 + (k & 3);
+        const uint32_t msk = (t_k < t_end ? 0xFFFFu : 0u) | (t_k + 1 < t_end ? 0xFFFF0000u : 0u);
+#pragma unroll
+        for (int P = 0; P < 4; ++P) vm[P][j] &= msk;
+      }
+    }
+    u32x4_t wo, wi, bo, bi;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const half2_t pk = __builtin_convertvector(
+          (float __attribute__((ext_vector_type(2)))){pr[j >> 1][2 * (j & 1)], pr[j >> 1][2 * (j & 1) + 1]}, half2_t);
+      wo[j] = __builtin_bit_cast(uint32_t, pk * half2_of(vm[0][j]));
+      bo[j] = __builtin_bit_cast(uint32_t, pk * half2_of(vm[1][j]));
+      wi[j] = __builtin_bit_cast(uint32_t, pk * half2_of(vm[2][j]));
+      bi[j] = __builtin_bit_cast(uint32_t, pk * half2_of(vm[3][j]));
+    }
+    const half8_t awo = __builtin_bit_cast(half8_t, wo), awi = __builtin_bit_cast(half8_t, wi);
+
+    // ---- value product per group of 16 channels (codes as 1024 + c), and the four sums
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      if (g < ngv) {
+        const half8_t bv = __builtin_bit_cast(half8_t, group_codes(g, gov, vwa, vwb, kF16Code));
+        const bool four = g == 0 || (GO == 2 && g == 1 && gov == 2);
+        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(four ? awo : awi, bv, acc[g], 0, 0, 0);
+      }
+    }
+    sw_o = __builtin_amdgcn_mfma_f32_16x16x32_f16(awo, ones, sw_o, 0, 0, 0);
+    sw_i = __builtin_amdgcn_mfma_f32_16x16x32_f16(awi, ones, sw_i, 0, 0, 0);
+    sb_o = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, bo), ones, sb_o, 0, 0, 0);
+    sb_i = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, bi), ones, sb_i, 0, 0, 0);
+    if (t_next < t_end) load_tile(Vb + (size_t)(t_next / kQ43Tile) * tbv, gov, ngv, vm, vwa, vwb);
   }
-  // the block minimum enters every channel of this lane's chunk once per unit of weight
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[i][e] += accb[i];
 
   BasisPrefetch<RB> pf;
   prefetch_basis<RB>(p, h, rv, pf);
-  // ---- workgroup merge of the 4 waves
+  // ---- per head: l over the lane groups; rows 0..3 (lanes q4 = 0) hold heads 0..3:
+  // o_lat = sum_t w_t (1024 + c_t) - 1024 sum_t w_t + sum_t p_t base_t
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  float* red = smem;                          // [wave][head][RB]
+  float* wm = smem + kWaves * kHeadsPerWg * RB;
+  float* wl = wm + kWaves * kHeadsPerWg;
+  if (q4 == 0) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) l[i] = row16_allreduce<false>(l[i]);
-  __syncthreads();
-  float* red = smem;                          // [wave][lane][kRS]
-  float* wm = smem + kWaves * 64 * kRS;       // [wave][head]
-  float* wl = wm + 16;
+    for (int g = 0; g < NG; ++g)
+      if (g < ngv) {
+        const bool four = g == 0 || (GO == 2 && g == 1 && gov == 2);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int e = 0; e < 8; e += 4)
-      *reinterpret_cast<float4*>(red + (wave * 64 + lane) * kRS + i * 8 + e) =
-          make_float4(acc[i][e], acc[i][e + 1], acc[i][e + 2], acc[i][e + 3]);
-  if (lane == 0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      wm[wave * 4 + i] = m[i];
-      wl[wave * 4 + i] = l[i];
+        for (int i = 0; i < kHeadsPerWg; ++i)
+          red[(wave * kHeadsPerWg + i) * RB + 16 * g + n16] =
+              acc[g][i] - 1024.f * (four ? sw_o[i] : sw_i[i]) + (four ? sb_o[i] : sb_i[i]);
+      }
+    if (n16 < kHeadsPerWg) {
+      wm[wave * kHeadsPerWg + n16] = m;
+      wl[wave * kHeadsPerWg + n16] = l;
     }
   }
   __syncthreads();
-  merge_waves_and_store(fixed_records(p, b, hq0), s, gpw, rv, wm, wl, [&](int w, int g, int j) {
-    const int c = j >> 3, e = j & 7;
-    const float* base = red + (w * 64 + c) * kRS + g * 8 + e;
-    const int step = C * kRS;
-    float sum = 0.f;
-#pragma unroll 8
-    for (int r = 0; r < rpi; ++r) sum += base[r * step];
-    return sum;
-  });
-  finish_split<RB>(p, b, h, hg, hq0, gpw, rv, smem, pf, fixed_records(p, b, hq0), p.n_splits);
+  merge_waves_and_store(rl, s, gpw, rv, wm, wl,
+                        [&](int w, int g, int j) { return red[(w * kHeadsPerWg + g) * RB + j]; });
+  finish_split<RB>(p, b, h, hg, hq0, gpw, rv, smem, pf, rl, p.n_splits);
 }
 
 // ---------------------------------------------------------------------------

@@ -107,8 +107,9 @@ struct AppendParams {
 };
 
 // Rows allocated per (batch row, KV head) block: the capacity rounded up to
-// whole 16-row MFMA blocks.
+// whole 16-row MFMA blocks (whole 32-row tiles for 4/3-bit latents).
 __host__ __device__ inline int cap_rows_of(int cap) { return (cap + 15) & ~15; }
+__host__ __device__ inline int cap_rows_q43(int cap) { return (cap + 31) & ~31; }
 
 // Offset (elements) of bf16 joint value latent (t, j) inside its batch row's
 // block (joint rank r, a multiple of 16). Each 16-row block holds the rows in
@@ -139,18 +140,22 @@ __host__ __device__ inline size_t k_tiled_offset(int t, int j, int rk) {
   return base + (size_t)np * 512 + (jj >> 2) * 64 + n * 4 + (jj & 3);
 }
 
-// Mixed 4/3-bit latent rows (STAR-KV technical summary, "Metodologia" section 3):
+// Mixed 4/3-bit latents (STAR-KV technical summary, "Metodologia" section 3):
 // channels in the 4-bit outlier block (20% of r in whole 16-channel blocks) and
-// bytes per stored row.
+// bytes per stored token: 4 half-float block parameters, n_o 4-bit and
+// r - n_o 3-bit codes. Tokens are stored in tiles of 32 (layout in kvlr.h).
 __host__ __device__ constexpr int q43_outlier(int r) {
   const int n = (r + 40) / 80;
   return 16 * (n > 1 ? n : 1);
 }
 __host__ __device__ constexpr int q43_row_bytes(int r) {
-  const int no = q43_outlier(r);
-  const int n = 8 + no / 2 + (3 * (r - no) + 7) / 8;
-  return (n + 3) / 4 * 4;
+  return 8 + q43_outlier(r) / 2 + 3 * (r - q43_outlier(r)) / 8;
 }
+constexpr int kQ43Tile = 32;            // tokens per 4/3-bit tile
+constexpr int kQ43MetaBytes = 256;      // block parameters of a tile: [4 slot groups][4 params][8 slots] fp16
+constexpr int kQ43OutGroupBytes = 256;  // one 16-channel 4-bit group of a tile
+constexpr int kQ43InGroupBytes = 192;   // one 16-channel 3-bit group of a tile
+__host__ __device__ inline int q43_slot(int u) { return 8 * ((u & 15) >> 2) + 4 * (u >> 4) + (u & 3); }
 
 // Launchers (return hipGetLastError() of their launches).
 hipError_t launch_decode(const DecodeParams& p, int latent_dtype, int rank_bound, int tile, hipStream_t s);
