@@ -50,7 +50,11 @@ def parse():
     ap.add_argument("--no-q43", action="store_true", help="skip the 4/3-bit latent measurement")
     ap.add_argument("--no-joint", action="store_true", help="skip the joint-value measurement")
     ap.add_argument("--no-workloads", action="store_true",
-                    help="skip the other workloads (ragged per-head ranks, 128K steps, 32 layers)")
+                    help="skip the other workloads (single head fp32, ragged per-head ranks, 128K, 32 layers)")
+    ap.add_argument("--workload", default="all",
+                    choices=["all", "headline", "single_head_f32", "per_head_ranks_ragged", "long_context_128k",
+                             "llama3_8b_32_layers", "q43", "joint"],
+                    help="run only this part (for profiling one workload at a time); default: everything")
     ap.add_argument("--traffic-reference", action="store_true",
                     help="also run a plain 1 GiB device copy (a known-size reference for HBM traffic counters)")
     return ap.parse_args()
@@ -94,16 +98,46 @@ def _build(kv, torch, cfg, layer=0, n_rows=None, chunk=8192):
     return dict(desc=desc, pk=pk, pv=pv, lk=lk, lv=lv, rk=rk, rv=rv, gen=gen)
 
 
-def _timed(torch, fn, reps):
-    fn()
+def event_times(torch, np, fn, n, warmup=3):
+    """n calls fn(k), each bracketed by its own HIP event pair on the current stream (the stream
+    the library launches on); returns the durations in microseconds."""
+    for k in range(warmup):
+        fn(k)
     torch.cuda.synchronize()
-    times = []
-    for _ in range(reps):
-        t0 = time.perf_counter()
-        fn()
-        torch.cuda.synchronize()
-        times.append(time.perf_counter() - t0)
-    return min(times)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+    for k in range(n):
+        evs[k][0].record()
+        fn(k)
+        evs[k][1].record()
+    torch.cuda.synchronize()
+    return np.array([e[0].elapsed_time(e[1]) * 1e3 for e in evs])
+
+
+def region_us(torch, fn, n):
+    """One event pair around n back-to-back calls fn(k): the average duration per call (us)."""
+    fn(0)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for k in range(n):
+        fn(k)
+    ev[1].record()
+    torch.cuda.synchronize()
+    return ev[0].elapsed_time(ev[1]) * 1e3 / n
+
+
+def spread(np, us):
+    """Median, p10, p90 and mean of event-pair durations (us)."""
+    return {"median_us": float(np.median(us)), "p10_us": float(np.percentile(us, 10)),
+            "p90_us": float(np.percentile(us, 90)), "mean_us": float(np.mean(us)), "calls": int(len(us))}
+
+
+def with_rates(np, st, nbytes, tokens):
+    """Add GB/s, fraction of the HBM peak and tokens/s at the median duration."""
+    t = st["median_us"] * 1e-6
+    st.update({"bytes": int(nbytes), "GBps": nbytes / t / 1e9, "hbm_frac": nbytes / t / 1e9 / HBM_PEAK_GBPS,
+               "tokens_per_s": tokens / t})
+    return st
 
 
 def _graph_of(torch, fn):
@@ -119,68 +153,125 @@ def _graph_of(torch, fn):
     return g
 
 
-def measure_workloads(kv, torch, np):
-    """The other workloads, each with its own algorithmic bytes: one decode over ragged
-    sequences with per-head ranks; 64 x (append + decode) over 128K rows; a 32-layer decode
-    step. The last two also as one captured HIP graph replayed (launch gaps removed)."""
-    from synth import LLAMA3_32_LAYERS, LONG_CONTEXT_128K, PER_HEAD_RAGGED, host
-    out = {}
+def measure_single_head(kv, torch, np):
+    """single_head_f32: B=1, one head, T=2048, r=32/32, fp32 latents (0.5 MiB, cache-resident):
+    decode latency per call."""
+    from synth import SINGLE_HEAD_F32, host
+    from synth.device import KVGenerator
+    cfg = SINGLE_HEAD_F32
+    print("[bench] workload single_head_f32", file=sys.stderr, flush=True)
+    rk, rv = host.ranks(cfg)
+    PK, PV = host.bases(cfg)
+    desc = kv.Desc(cfg.B, cfg.Hq, cfg.Hkv, cfg.d, cfg.capacity, rk, rv, kv.F32, kv.F32)
+    pk, pv = kv.pack_bases(PK), kv.pack_bases(PV)
+    lk, lv = kv.alloc_cache(desc)
+    gen = KVGenerator(cfg, 0)
+    K, V = gen.make("k", cfg.B, cfg.T), gen.make("v", cfg.B, cfg.T)
+    comp = event_times(torch, np, lambda k: kv.prefill_compress(desc, K, V, 0, pk, pv, lk, lv), 50)
+    q = torch.from_numpy(host.queries(cfg)).cuda()
+    lens = torch.from_numpy(host.lengths(cfg)).cuda()
+    ws = kv.alloc_workspace(desc)
+    o = torch.empty((cfg.B, cfg.Hq, cfg.d), device="cuda")
+    us = event_times(torch, np, lambda k: kv.decode_attn(desc, q, pk, pv, lk, lv, lens, out=o, workspace=ws), 200)
+    st = with_rates(np, spread(np, us), cfg.T * (int(rk[0]) + int(rv[0])) * 4, cfg.B)
+    st["note"] = "latency-bound (0.5 MiB of latents, cache-resident): reported in us, not as a share of HBM"
+    st["prefill_compress_median_us"] = float(np.median(comp))
+    return st
+
+
+def measure_ragged(kv, torch, np, n_rep=3):
+    """per_head_ranks_ragged: one decode over ragged sequences with per-head ranks, the library's
+    plan (balanced), rotating n_rep cache replicas (n_rep x 290 MB, above the 256 MB last-level
+    cache) so that no call finds its bytes in cache; the fixed plan beside it."""
+    from synth import PER_HEAD_RAGGED, host
     print("[bench] workload per_head_ranks_ragged", file=sys.stderr, flush=True)
     cfg = PER_HEAD_RAGGED
     c = _build(kv, torch, cfg, chunk=4096)
+    reps = [(c["lk"], c["lv"])] + [(c["lk"].clone(), c["lv"].clone()) for _ in range(n_rep - 1)]
     lens_np = host.lengths(cfg)
     lens = torch.from_numpy(lens_np).cuda()
     q = torch.from_numpy(host.queries(cfg)).cuda()
     ws = kv.alloc_workspace(c["desc"])
     o = torch.empty((cfg.B, cfg.Hq, cfg.d), device="cuda")
     nbytes = int(lens_np.astype(np.int64).sum()) * int((c["rk"] + c["rv"]).sum()) * 2
-    call = lambda: kv.decode_attn(c["desc"], q, c["pk"], c["pv"], c["lk"], c["lv"], lens, out=o, workspace=ws)  # noqa: E731
-    t = _timed(torch, lambda: [call() for _ in range(20)], 3) / 20
-    fixed = lambda: kv.decode_attn(c["desc"], q, c["pk"], c["pv"], c["lk"], c["lv"], lens, out=o,  # noqa: E731
-                                   workspace=ws, split_tokens=4096)
-    t_fixed = _timed(torch, lambda: [fixed() for _ in range(20)], 3) / 20
-    out[cfg.name] = {"us_per_call": t * 1e6, "bytes": nbytes, "GBps": nbytes / t / 1e9,
-                     "hbm_frac": nbytes / t / 1e9 / HBM_PEAK_GBPS, "tokens_per_s": cfg.B / t,
-                     "plan": "balanced (the library's choice: the KV heads' ranks differ)",
-                     "fixed_plan_4096_us_per_call": t_fixed * 1e6}
-    del c, ws
-    torch.cuda.empty_cache()
 
+    def call(k, split=0):
+        lk, lv = reps[k % n_rep]
+        kv.decode_attn(c["desc"], q, c["pk"], c["pv"], lk, lv, lens, out=o, workspace=ws, split_tokens=split)
+    st = with_rates(np, spread(np, event_times(torch, np, call, 60)), nbytes, cfg.B)
+    st["region_us_per_call"] = region_us(torch, call, 60)
+    st["plan"] = "balanced (the library's choice: the KV heads' ranks differ)"
+    st["replicas"] = n_rep
+    st["fixed_plan_4096"] = spread(np, event_times(torch, np, lambda k: call(k, 4096), 60))
+    del c, reps, ws
+    torch.cuda.empty_cache()
+    return st
+
+
+def measure_long_context(kv, torch, np):
+    """long_context_128k: prefill compression of 2 x 131072 tokens (r_k = 48, r_v = 80), then
+    64 x (append one token + decode over all rows), eager as two calls and as the fused step, and
+    each loop also as one captured HIP graph."""
+    from synth import LONG_CONTEXT_128K, host
+    from synth.device import KVGenerator
     print("[bench] workload long_context_128k", file=sys.stderr, flush=True)
     cfg = LONG_CONTEXT_128K
-    T, S = cfg.T, cfg.decode_steps
-    c = _build(kv, torch, cfg, n_rows=T, chunk=16384)
-    ks = [c["gen"].make("k", cfg.B, 1, t0=T + s)[:, 0].contiguous() for s in range(S)]
-    vs = [c["gen"].make("v", cfg.B, 1, t0=T + s)[:, 0].contiguous() for s in range(S)]
+    T, S, B, Hkv, d = cfg.T, cfg.decode_steps, cfg.B, cfg.Hkv, cfg.d
+    rk, rv = host.ranks(cfg)
+    PK, PV = host.bases(cfg)
+    desc = kv.Desc(B, cfg.Hq, Hkv, d, cfg.capacity, rk, rv, kv.BF16, kv.BF16)
+    pk, pv = kv.pack_bases(PK), kv.pack_bases(PV)
+    lk, lv = kv.alloc_cache(desc)
+    gen = KVGenerator(cfg, 0)
+    K, V = gen.make("k", B, T), gen.make("v", B, T)
+    out = {}
+    pre = event_times(torch, np, lambda k: kv.prefill_compress(desc, K, V, 0, pk, pv, lk, lv), 20, warmup=2)
+    r_sum = int(rk[0]) + int(rv[0])
+    pbytes = B * T * Hkv * (2 * d * 2 + r_sum * 2)
+    flops = 2.0 * B * T * Hkv * d * r_sum
+    st = with_rates(np, spread(np, pre), pbytes, B * T)
+    st["useful_TFLOPs"] = flops / (st["median_us"] * 1e-6) / 1e12
+    st["mfma_useful_frac"] = st["useful_TFLOPs"] / BF16_MFMA_PEAK_TFLOPS
+    st["kernel"] = "compress_bf16_mfma"
+    st["note"] = ("bytes: K and V read (bf16) plus latents written; flops 2 d (r_k + r_v) per token and head; "
+                  "MFMA busy share from counters in profiles/")
+    out["prefill"] = st
+    del K, V
+    ks = [gen.make("k", B, 1, t0=T + s)[:, 0].contiguous() for s in range(S)]
+    vs = [gen.make("v", B, 1, t0=T + s)[:, 0].contiguous() for s in range(S)]
     qs = [torch.from_numpy(host.queries(cfg, 0, s)).cuda() for s in range(S)]
-    pos = [torch.full((cfg.B,), T + s, dtype=torch.int32, device="cuda") for s in range(S)]
-    lns = [torch.full((cfg.B,), T + s + 1, dtype=torch.int32, device="cuda") for s in range(S)]
-    ws = kv.alloc_workspace(c["desc"])
-    o = torch.empty((cfg.B, cfg.Hq, cfg.d), device="cuda")
+    pos = [torch.full((B,), T + s, dtype=torch.int32, device="cuda") for s in range(S)]
+    lns = [torch.full((B,), T + s + 1, dtype=torch.int32, device="cuda") for s in range(S)]
+    ws = kv.alloc_workspace(desc)
+    o = torch.empty((B, cfg.Hq, d), device="cuda")
 
-    def loop():
-        for s in range(S):
-            kv.append(c["desc"], ks[s], vs[s], pos[s], c["pk"], c["pv"], c["lk"], c["lv"])
-            kv.decode_attn(c["desc"], qs[s], c["pk"], c["pv"], c["lk"], c["lv"], lns[s], out=o, workspace=ws)
-    def fused_loop():   # the same steps through kvlr_append_decode_attn (one launch per step)
-        for s in range(S):
-            kv.append_decode_attn(c["desc"], ks[s], vs[s], pos[s], qs[s], c["pk"], c["pv"], c["lk"], c["lv"], lns[s],
-                                  out=o, workspace=ws)
-    t_e = _timed(torch, loop, 3)
-    g = _graph_of(torch, loop)
-    t_g = _timed(torch, g.replay, 3)
-    t_f = _timed(torch, fused_loop, 3)
-    gf = _graph_of(torch, fused_loop)
-    t_fg = _timed(torch, gf.replay, 3)
-    rk, rv = int(c["rk"][0]), int(c["rv"][0])
-    nbytes = sum(T + s + 1 for s in range(S)) * cfg.B * cfg.Hkv * (rk + rv) * 2
-    out[cfg.name] = {"steps": S, "eager_us_per_step": t_e / S * 1e6, "graph_us_per_step": t_g / S * 1e6,
-                     "fused_eager_us_per_step": t_f / S * 1e6, "fused_graph_us_per_step": t_fg / S * 1e6,
-                     "bytes": nbytes, "graph_GBps": nbytes / t_g / 1e9, "graph_hbm_frac": nbytes / t_g / 1e9 / HBM_PEAK_GBPS,
-                     "graph_tokens_per_s": cfg.B * S / t_g, "fused_graph_tokens_per_s": cfg.B * S / t_fg}
-    del c, ws, g, gf
+    def two_calls(s):
+        kv.append(desc, ks[s], vs[s], pos[s], pk, pv, lk, lv)
+        kv.decode_attn(desc, qs[s], pk, pv, lk, lv, lns[s], out=o, workspace=ws)
+
+    def fused(s):
+        kv.append_decode_attn(desc, ks[s], vs[s], pos[s], qs[s], pk, pv, lk, lv, lns[s], out=o, workspace=ws)
+    step_bytes = np.array([(T + s + 1) * B * Hkv * r_sum * 2 for s in range(S)])
+    nbytes = int(step_bytes.mean())
+    for name, fn in (("two_calls", two_calls), ("fused", fused)):
+        st = with_rates(np, spread(np, event_times(torch, np, lambda k: fn(k % S), S, warmup=2)), nbytes, B)
+        g = _graph_of(torch, lambda: [fn(s) for s in range(S)])
+        gt = event_times(torch, np, lambda k: g.replay(), 5, warmup=1)
+        st["graph_us_per_step"] = float(np.median(gt)) / S
+        st["graph_tokens_per_s"] = B * S / (float(np.median(gt)) * 1e-6)
+        out[name] = st
+        del g
+    out["steps"] = S
+    out["bytes_per_step_mean"] = nbytes
+    del lk, lv, ws
     torch.cuda.empty_cache()
+    return out
 
+
+def measure_32_layers(kv, torch, np):
+    """llama3_8b_32_layers: 32 back-to-back decodes (one per layer, each with its own bases and
+    ranks), timed per whole step; eager and as one captured HIP graph."""
+    from synth import LLAMA3_32_LAYERS, host
     print("[bench] workload llama3_8b_32_layers", file=sys.stderr, flush=True)
     cfg = LLAMA3_32_LAYERS
     layers = []
@@ -193,19 +284,18 @@ def measure_workloads(kv, torch, np):
         layers.append(c)
     lens = torch.from_numpy(host.lengths(cfg)).cuda()
 
-    def step():
+    def step(k=0):
         for c in layers:
             kv.decode_attn(c["desc"], c["q"], c["pk"], c["pv"], c["lk"], c["lv"], lens, out=c["o"], workspace=c["ws"])
-    t_e = _timed(torch, step, 5)
-    g = _graph_of(torch, step)
-    t_g = _timed(torch, g.replay, 5)
     nbytes = sum(cfg.B * cfg.T * int((c["rk"] + c["rv"]).sum()) * 2 for c in layers)
-    out[cfg.name] = {"layers": cfg.n_layers, "eager_ms_per_step": t_e * 1e3, "graph_ms_per_step": t_g * 1e3,
-                     "bytes": nbytes, "graph_GBps": nbytes / t_g / 1e9, "graph_hbm_frac": nbytes / t_g / 1e9 / HBM_PEAK_GBPS,
-                     "graph_tokens_per_s": cfg.B / t_g}
+    st = with_rates(np, spread(np, event_times(torch, np, step, 7, warmup=2)), nbytes, cfg.B)
+    g = _graph_of(torch, step)
+    gst = spread(np, event_times(torch, np, lambda k: g.replay(), 7, warmup=2))
+    st["graph"] = with_rates(np, gst, nbytes, cfg.B)
+    st["layers"] = cfg.n_layers
     del layers, g
     torch.cuda.empty_cache()
-    return out
+    return st
 
 
 def measure_joint(kv, torch, np, cfg, gen, q, lens, steps, warmup, r_joint=128):
@@ -227,25 +317,15 @@ def measure_joint(kv, torch, np, cfg, gen, q, lens, steps, warmup, r_joint=128):
         reps.append((lk, lv))
     ws = kv.alloc_workspace(desc)
     out = torch.empty((B, cfg.Hq, d), dtype=torch.float32, device="cuda")
-    for k in range(warmup):
+
+    def call(k):
         lk, lv = reps[k % 2]
         kv.decode_attn(desc, q, pk, pj, lk, lv, lens, out=out, workspace=ws)
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-    t_start = time.perf_counter()
-    for k in range(steps):
-        lk, lv = reps[k % 2]
-        evs[k][0].record()
-        kv.decode_attn(desc, q, pk, pj, lk, lv, lens, out=out, workspace=ws)
-        evs[k][1].record()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
-    us = float(np.mean([e[0].elapsed_time(e[1]) * 1e3 for e in evs]))
     nbytes = B * T * (int(rk.sum()) + r_joint) * 2
-    return {"entry": "kvlr_decode_attn, value_mode KVLR_VALUES_JOINT", "r_k": int(rk[0]), "r_joint": r_joint,
-            "bytes_per_launch": nbytes, "launch_us_mean": us, "GBps": nbytes / (us * 1e-6) / 1e9,
-            "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, "tokens_per_s": B * steps / elapsed,
-            "note": "three launches: query projection, one split kernel per (split, batch row) that streams every head's keys and the shared value latent once, and a merge per (query head, batch row)"}
+    st = with_rates(np, spread(np, event_times(torch, np, call, steps, warmup)), nbytes, B)
+    st.update({"entry": "kvlr_decode_attn, value_mode KVLR_VALUES_JOINT", "r_k": int(rk[0]), "r_joint": r_joint,
+               "region_us_per_call": region_us(torch, call, steps)})
+    return st
 
 
 def measure_stream_ceiling(torch, np):
@@ -293,27 +373,18 @@ def measure_q43(kv, torch, np, cfg, gen, q, lens, steps, warmup):
         reps.append((lk, lv))
     ws = kv.alloc_workspace(desc)
     out = torch.empty((B, cfg.Hq, d), dtype=torch.float32, device="cuda")
-    for k in range(warmup):
+
+    def call(k):
         lk, lv = reps[k % 2]
         kv.decode_attn(desc, q, pk, pv, lk, lv, lens, out=out, workspace=ws)
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-    t_start = time.perf_counter()
-    for k in range(steps):
-        lk, lv = reps[k % 2]
-        evs[k][0].record()
-        kv.decode_attn(desc, q, pk, pv, lk, lv, lens, out=out, workspace=ws)
-        evs[k][1].record()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
-    us = float(np.mean([e[0].elapsed_time(e[1]) * 1e3 for e in evs]))
     row_k = sum(kv.q43_row_bytes(int(r)) for r in rk)
     row_v = sum(kv.q43_row_bytes(int(r)) for r in rv)
     nbytes = B * T * (row_k + row_v)
-    return {"entry": "kvlr_decode_attn on KVLR_Q43 caches", "kernel": "decode_split_q43<64>",
-            "bytes_per_launch": nbytes, "launch_us_mean": us, "GBps": nbytes / (us * 1e-6) / 1e9,
-            "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, "tokens_per_s": B * steps / elapsed,
-            "bytes_vs_bf16": nbytes / (B * T * int((rk + rv).sum()) * 2)}
+    st = with_rates(np, spread(np, event_times(torch, np, call, steps, warmup)), nbytes, B)
+    st.update({"entry": "kvlr_decode_attn on KVLR_Q43 caches", "kernel": "decode_split_q43",
+               "region_us_per_call": region_us(torch, call, steps),
+               "bytes_vs_bf16": nbytes / (B * T * int((rk + rv).sum()) * 2)})
+    return st
 
 
 def cpu_baseline(cfg, seconds):
@@ -389,6 +460,8 @@ def main():
     from synth import LLAMA3_LAYER_32K, host
     from synth.device import KVGenerator
 
+    want = args.workload
+    run = lambda part: want == "all" or want == part   # noqa: E731
     cfg = LLAMA3_LAYER_32K
     B, T, Hkv, d = cfg.B, cfg.T, cfg.Hkv, cfg.d
     rk, rv = host.ranks(cfg)
@@ -396,101 +469,116 @@ def main():
     desc = kv.Desc(B, cfg.Hq, Hkv, d, cfg.capacity, rk, rv, kv.BF16, kv.BF16)
     pk, pv = kv.pack_bases(PK), kv.pack_bases(PV)
     gen = KVGenerator(cfg, 0)
-    print(f"[bench] building 2 cache replicas of {cfg.name}", file=sys.stderr, flush=True)
-
-    replicas = []
-    prefill = None
-    for rep in range(2):
-        lat_k, lat_v = kv.alloc_cache(desc)
-        K = gen.make("k", B, T)
-        V = gen.make("v", B, T)
-        kv.prefill_compress(desc, K, V, 0, pk, pv, lat_k, lat_v)
-        if rep == 0 and not args.no_prefill:
-            # prefill compression of all 32768 tokens (both K and V), timed with HIP events
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-            times = []
-            for _ in range(5):
-                ev[0].record()
-                kv.prefill_compress(desc, K, V, 0, pk, pv, lat_k, lat_v)
-                ev[1].record()
-                torch.cuda.synchronize()
-                times.append(ev[0].elapsed_time(ev[1]) * 1e-3)
-            t = float(np.median(times))
-            nbytes = B * T * Hkv * (2 * d * 2 + (int(rk[0]) + int(rv[0])) * 2)
-            flops = 2.0 * B * T * Hkv * d * (int(rk[0]) + int(rv[0]))
-            prefill = {"tokens": B * T, "us": t * 1e6, "GBps": nbytes / t / 1e9,
-                       "hbm_frac": nbytes / t / 1e9 / HBM_PEAK_GBPS,
-                       "mfma_util": flops / t / 1e12 / BF16_MFMA_PEAK_TFLOPS,
-                       "note": "MFMA utilisation counts useful flops; the kernel issues 2x (basis high/low parts)"}
-        del K, V
-        replicas.append((lat_k, lat_v))
-    torch.cuda.synchronize()
-
     q = torch.from_numpy(host.queries(cfg, 0, 0)).cuda()
     lens = torch.full((B,), T, dtype=torch.int32, device="cuda")
-    split = args.split_tokens
-    ws = kv.alloc_workspace(desc, split)
-    out = torch.empty((B, cfg.Hq, d), dtype=torch.float32, device="cuda")
-    n_splits, split_len = kv.decode_plan(desc, split)
+    alg_bytes = B * T * int((rk + rv).sum()) * 2     # latent bytes read per launch
+    result = {"metric": METRIC, "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+              "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",
+              "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+              "config": {"workload": cfg.name, "batch": B, "cached_tokens": T, "q_heads": cfg.Hq, "kv_heads": Hkv,
+                         "head_dim": d, "r_k": int(rk[0]), "r_v": int(rv[0]), "latents": "bf16"}}
 
-    def step(k, evs=None):
-        # one kvlr_decode_attn call = one kernel launch (split workgroups merge in the last arrival)
-        lk, lv = replicas[k % 2]
-        if evs is not None:
-            evs[0].record()
-        kv.decode_attn(desc, q, pk, pv, lk, lv, lens, out=out, workspace=ws, split_tokens=split)
-        if evs is not None:
-            evs[1].record()
+    if run("headline"):
+        print(f"[bench] building 2 cache replicas of {cfg.name}", file=sys.stderr, flush=True)
+        replicas = []
+        prefill = None
+        for rep in range(2):
+            lat_k, lat_v = kv.alloc_cache(desc)
+            K = gen.make("k", B, T)
+            V = gen.make("v", B, T)
+            kv.prefill_compress(desc, K, V, 0, pk, pv, lat_k, lat_v)
+            if rep == 0 and not args.no_prefill:
+                # prefill compression of all 32768 tokens (both K and V), timed with HIP events
+                pre = event_times(torch, np, lambda k: kv.prefill_compress(desc, K, V, 0, pk, pv, lat_k, lat_v), 10, 1)
+                nbytes = B * T * Hkv * (2 * d * 2 + (int(rk[0]) + int(rv[0])) * 2)
+                flops = 2.0 * B * T * Hkv * d * (int(rk[0]) + int(rv[0]))
+                prefill = with_rates(np, spread(np, pre), nbytes, B * T)
+                prefill["useful_TFLOPs"] = flops / (prefill["median_us"] * 1e-6) / 1e12
+                prefill["mfma_useful_frac"] = prefill["useful_TFLOPs"] / BF16_MFMA_PEAK_TFLOPS
+            del K, V
+            replicas.append((lat_k, lat_v))
+        torch.cuda.synchronize()
+        split = args.split_tokens
+        ws = kv.alloc_workspace(desc, split)
+        out = torch.empty((B, cfg.Hq, d), dtype=torch.float32, device="cuda")
+        n_splits, split_len = kv.decode_plan(desc, split)
 
-    for k in range(args.warmup):
-        step(k)
-    torch.cuda.synchronize()
-    # headline: exactly K steps, nothing between the launches; a HIP event pair on the launch
-    # stream around the same region gives the kernel's average duration (region / K)
-    region = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    t0 = time.perf_counter()
-    region[0].record()
-    for k in range(args.steps):
-        step(k)
-    region[1].record()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    region_us = region[0].elapsed_time(region[1]) * 1e3
-    # spread: the same K steps again, each launch bracketed by its own event pair (which adds the
-    # events' own overhead to every launch, so these durations run a few microseconds long)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for k in range(args.steps):
-        step(k, evs[k])
-    torch.cuda.synchronize()
+        def step(k):
+            # one kvlr_decode_attn call = one kernel launch (split workgroups merge in the last arrival)
+            lk, lv = replicas[k % 2]
+            kv.decode_attn(desc, q, pk, pv, lk, lv, lens, out=out, workspace=ws, split_tokens=split)
 
-    # folded form (q_lat = q P_K in, o_lat out, P_V^T left to the caller's output projection)
-    q_lat = torch.zeros((B, cfg.Hq, int(rk.max())), dtype=torch.float32, device="cuda")
-    rk_pre = np.concatenate([[0], np.cumsum(rk)])
-    for i in range(cfg.Hq):
-        h = i // cfg.G
-        q_lat[:, i, :int(rk[h])] = q[:, i] @ pk[d * int(rk_pre[h]): d * int(rk_pre[h + 1])].view(d, int(rk[h]))
-    o_lat = torch.empty((B, cfg.Hq, int(rv.max())), dtype=torch.float32, device="cuda")
-    fevs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    for k in range(args.steps):
-        lk, lv = replicas[k % 2]
-        fevs[k][0].record()
-        kv.decode_attn_latent(desc, q_lat, lk, lv, lens, o_lat=o_lat, workspace=ws, split_tokens=split)
-        fevs[k][1].record()
-    torch.cuda.synchronize()
-    folded_us = float(np.mean([e[0].elapsed_time(e[1]) * 1e3 for e in fevs]))
+        for k in range(args.warmup):
+            step(k)
+        torch.cuda.synchronize()
+        # headline: exactly K steps, nothing between the launches; a HIP event pair on the launch
+        # stream around the same region gives the kernel's average duration (region / K)
+        region = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        t0 = time.perf_counter()
+        region[0].record()
+        for k in range(args.steps):
+            step(k)
+        region[1].record()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        launch_us = region[0].elapsed_time(region[1]) * 1e3 / args.steps
+        # spread: the same K steps again, each launch bracketed by its own event pair (which adds the
+        # events' own overhead to every launch, so these durations run a few microseconds long)
+        split_us = event_times(torch, np, step, args.steps, 0)
 
-    workloads = None
+        # folded form (q_lat = q P_K in, o_lat out, P_V^T left to the caller's output projection)
+        q_lat = torch.zeros((B, cfg.Hq, int(rk.max())), dtype=torch.float32, device="cuda")
+        rk_pre = np.concatenate([[0], np.cumsum(rk)])
+        for i in range(cfg.Hq):
+            h = i // cfg.G
+            q_lat[:, i, :int(rk[h])] = q[:, i] @ pk[d * int(rk_pre[h]): d * int(rk_pre[h + 1])].view(d, int(rk[h]))
+        o_lat = torch.empty((B, cfg.Hq, int(rv.max())), dtype=torch.float32, device="cuda")
+
+        def folded(k):
+            lk, lv = replicas[k % 2]
+            kv.decode_attn_latent(desc, q_lat, lk, lv, lens, o_lat=o_lat, workspace=ws, split_tokens=split)
+        fst = with_rates(np, spread(np, event_times(torch, np, folded, args.steps, 0)), alg_bytes, B)
+        fst["entry"] = "kvlr_decode_attn_latent"
+        fst["region_us_per_call"] = region_us(torch, folded, args.steps)
+        del replicas, ws
+        torch.cuda.empty_cache()
+
+        achieved = alg_bytes / (launch_us * 1e-6) / 1e9
+        result.update({"value": B * args.steps / elapsed, "ms_per_step": elapsed / args.steps * 1e3})
+        result["config"].update({"splits": n_splits, "split_tokens": split_len})
+        result["step_hbm_GBps"] = alg_bytes / (elapsed / args.steps) / 1e9
+        result["roofline"] = {
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS, "traffic": load_traffic(),
+            "kernel": "decode_split_bf16<64, 32> (kvlr_decode_attn, fixed split plan, merge fused)",
+            "bytes_per_launch": alg_bytes, "launch_us_mean": launch_us,
+            "timing": "one HIP event pair on the launch stream around the K timed launches",
+            "bracketed_launch": spread(np, split_us)}
+        result["folded"] = fst
+        if prefill is not None:
+            result["prefill"] = prefill
+
+    workloads = {}
     if not args.no_workloads:
-        workloads = measure_workloads(kv, torch, np)
-    joint = None
-    if not args.no_joint:
-        joint = measure_joint(kv, torch, np, cfg, gen, q, lens, args.steps, args.warmup)
-    q43 = None
-    if not args.no_q43:
-        q43 = measure_q43(kv, torch, np, cfg, gen, q, lens, args.steps, args.warmup)
+        if run("single_head_f32"):
+            workloads["single_head_f32"] = measure_single_head(kv, torch, np)
+        if run("per_head_ranks_ragged"):
+            workloads["per_head_ranks_ragged"] = measure_ragged(kv, torch, np)
+        if run("long_context_128k"):
+            workloads["long_context_128k"] = measure_long_context(kv, torch, np)
+        if run("llama3_8b_32_layers"):
+            workloads["llama3_8b_32_layers"] = measure_32_layers(kv, torch, np)
+    if workloads:
+        result["workloads"] = workloads
+    if run("joint") and not args.no_joint:
+        result["joint_values"] = measure_joint(kv, torch, np, cfg, gen, q, lens, args.steps, args.warmup)
+    if run("q43") and not args.no_q43:
+        result["q43"] = measure_q43(kv, torch, np, cfg, gen, q, lens, args.steps, args.warmup)
 
-    stream_ceiling = measure_stream_ceiling(torch, np)
+    if run("headline"):
+        ceiling = measure_stream_ceiling(torch, np)
+        result["roofline"]["stream_read_ceiling_GBps"] = ceiling
+        result["roofline"]["frac_of_stream_read"] = result["roofline"]["achieved"] / ceiling
 
     if args.traffic_reference:
         from synth.device import copy as device_copy
@@ -502,53 +590,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    split_us = np.array([e[0].elapsed_time(e[1]) * 1e3 for e in evs])
-    alg_bytes = B * T * int((rk + rv).sum()) * 2     # latent bytes read per launch
-    launch_us = region_us / args.steps               # average launch duration over the timed region
-    split_mean_s = launch_us * 1e-6
-    achieved = alg_bytes / split_mean_s / 1e9
-    ms_per_step = elapsed / args.steps * 1e3
-    tokens_per_s = B * args.steps / elapsed
-    traffic = load_traffic()
-
-    result = {
-        "metric": METRIC,
-        "value": tokens_per_s,
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": cfg.name, "batch": B, "cached_tokens": T, "q_heads": cfg.Hq, "kv_heads": Hkv,
-                   "head_dim": d, "r_k": int(rk[0]), "r_v": int(rv[0]), "latents": "bf16",
-                   "splits": n_splits, "split_tokens": split_len},
-        "step_hbm_GBps": alg_bytes / (elapsed / args.steps) / 1e9,
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "stream_read_ceiling_GBps": stream_ceiling, "frac_of_stream_read": achieved / stream_ceiling,
-                     "kernel": "decode_split_bf16<64, 32> (kvlr_decode_attn, fixed split plan, merge fused)", "bytes_per_launch": alg_bytes,
-                     "launch_us_mean": launch_us,
-                     "timing": "one HIP event pair on the launch stream around the K timed launches",
-                     "bracketed_launch_us_mean": float(split_us.mean()),
-                     "bracketed_launch_us_p10": float(np.percentile(split_us, 10)),
-                     "bracketed_launch_us_p90": float(np.percentile(split_us, 90))},
-    }
-    result["folded"] = {"entry": "kvlr_decode_attn_latent", "launch_us_mean": folded_us,
-                        "GBps": alg_bytes / (folded_us * 1e-6) / 1e9}
-    if q43 is not None:
-        result["q43"] = q43
-    if joint is not None:
-        result["joint_values"] = joint
-    if workloads is not None:
-        result["workloads"] = workloads
-    if prefill is not None:
-        result["prefill"] = prefill
-    if not args.no_cpu_baseline:
+    if run("headline") and not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
     else:
