@@ -795,13 +795,13 @@ __device__ __forceinline__ u32x4_t codes4_to_num(uint32_t w, uint32_t ebytes) {
 // One 24-bit 3-bit field (bits 0..23 of x) -> the same order: field position e
 // holds (block, i) = (0,0) (0,2) (1,0) (1,2) (0,1) (0,3) (1,1) (1,3), so after
 // moving bits 12..23 to 16..27 the pairs (e, e + 4) are (block e / 2, i = 2 (e % 2) + {0, 1}).
-__device__ __forceinline__ u32x4_t codes3_to_num(uint32_t x, uint32_t ebytes) {
-  const uint32_t rot = __builtin_amdgcn_alignbit(x, x, 28);   // rotate left by 4
-  const uint32_t y = (x & 0xFFFFu) | (rot & 0xFFFF0000u);
-  const uint32_t e2 = ebytes & 0xFF00FF00u;
+// m7 = 0x00070007 and e2 = the exponent bytes in the high byte of each half come in
+// registers: the AND-OR of two of them is then one instruction.
+__device__ __forceinline__ u32x4_t codes3_to_num(uint32_t x, uint32_t m7, uint32_t e2) {
+  const uint32_t y = (x & 0xFFFFu) | ((x << 4) & 0xFFFF0000u);   // bits 12..23 to 16..27
   u32x4_t o;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) o[e] = ((y >> (3 * e)) & 0x00070007u) | e2;
+  for (int e = 0; e < 4; ++e) o[e] = ((y >> (3 * e)) & m7) | e2;
   return o;
 }
 
@@ -822,7 +822,40 @@ __device__ __forceinline__ float half_at(const u32x4_t& v, int k) {   // half fl
 }
 __device__ __forceinline__ half2_t half2_of(uint32_t w) { return __builtin_bit_cast(half2_t, w); }
 
-template <int RB>
+// Reductions over the lanes n, n + 16, n + 32, n + 48 (the four 16-lane rows of a wave)
+// with gfx950's row swaps: after swapping rows 1 <-> 0 and 3 <-> 2 of two copies of x,
+// the two results hold, lane by lane, x and its partner 16 lanes away; likewise for the
+// 32-lane halves.
+__device__ __forceinline__ float max_over_rows(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_over_rows(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Raw buffer access to one (batch row, KV head) block of a 4/3-bit cache: base and size
+// in a resource (word 3 = 0x00020000: the raw 32-bit data format of gfx9 buffers), a
+// per-lane offset in a VGPR and the tile offset in an SGPR; loads stream (non-temporal).
+typedef __amdgpu_buffer_rsrc_t q43_rsrc_t;
+constexpr int kBufNonTemporal = 2;
+__device__ __forceinline__ q43_rsrc_t q43_block_rsrc(const uint8_t* base, int nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, nbytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4_t q43_load16(q43_rsrc_t rs, int voff, int soff) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, kBufNonTemporal));
+}
+__device__ __forceinline__ uint32_t q43_load4(q43_rsrc_t rs, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, kBufNonTemporal);
+}
+
+// EXACT: every KV head has r_k = r_v = RB, so the group structure is known at compile time.
+template <int RB, bool EXACT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB <= 64 ? 3 : 2)))
 void decode_split_q43(DecodeParams p) {
   constexpr int GO = RB == 128 ? 2 : 1;                    // 4-bit groups (bound): group 0 always is one
@@ -837,7 +870,7 @@ void decode_split_q43(DecodeParams p) {
   const int b = blockIdx.z;
   const int hq0 = h * p.G + hg * kHeadsPerWg;
   const int gpw = min(kHeadsPerWg, p.G - hg * kHeadsPerWg);
-  const int rk = p.ht.rk[h], rv = p.ht.rv[h];
+  const int rk = EXACT ? RB : p.ht.rk[h], rv = EXACT ? RB : p.ht.rv[h];
   const int T = min(max(p.seq_lens[b], 0), p.cap);
   const int t_begin = min(s * p.ht.split_len[h], T);
   const int t_end = min(T, t_begin + p.ht.split_len[h]);
@@ -854,48 +887,59 @@ void decode_split_q43(DecodeParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = lane & 15, q4 = lane >> 4;
   const bool q_ok = n16 < gpw;
-  const int gok = q43_outlier(rk) >> 4, ngk = rk >> 4;   // 4-bit groups and all groups of the keys
-  const int gov = q43_outlier(rv) >> 4, ngv = rv >> 4;
-  const size_t tbk = (size_t)kQ43Tile * q43_row_bytes(rk), tbv = (size_t)kQ43Tile * q43_row_bytes(rv);
+  const int gok = EXACT ? GO : q43_outlier(rk) >> 4, ngk = EXACT ? NG : rk >> 4;   // 4-bit and all groups of the keys
+  const int gov = EXACT ? GO : q43_outlier(rv) >> 4, ngv = EXACT ? NG : rv >> 4;
+  const int tbk = kQ43Tile * q43_row_bytes(rk), tbv = kQ43Tile * q43_row_bytes(rv);
   const size_t rows = cap_rows_q43(p.cap);
-  const uint8_t* Kb = static_cast<const uint8_t*>(p.lat_k) + rows * ((size_t)b * p.Sk + p.ht.sk_pre[h]);
-  const uint8_t* Vb = static_cast<const uint8_t*>(p.lat_v) + rows * ((size_t)b * p.Sv + p.ht.sv_pre[h]);
-  // this lane's 24-bit fields: bytes 3 lane .. 3 lane + 2 of a 3-bit group, inside 2 dwords
+  // Buffer resources over this (batch row, KV head) block of each cache; the tile offset
+  // travels in the scalar offset, so per-lane offsets stay fixed across tiles.
+  const q43_rsrc_t rs_k = q43_block_rsrc(static_cast<const uint8_t*>(p.lat_k) + rows * ((size_t)b * p.Sk + p.ht.sk_pre[h]),
+                                         (int)rows / kQ43Tile * tbk);
+  const q43_rsrc_t rs_v = q43_block_rsrc(static_cast<const uint8_t*>(p.lat_v) + rows * ((size_t)b * p.Sv + p.ht.sv_pre[h]),
+                                         (int)rows / kQ43Tile * tbv);
+  // this lane's offsets: its 8 parameter slots, its 4-bit word, and the two dwords that
+  // hold bytes 3 lane .. 3 lane + 2 of a 3-bit group (its 24-bit field)
+  const int vo_meta = 64 * q4, vo_4 = 4 * lane;
   const int off_a = (3 * lane) & ~3, off_b = (3 * lane + 2) & ~3, f_shift = 8 * ((3 * lane) & 3);
 
-  // One tile of one kind in registers: the 4 parameter arrays (this lane's 8 slots each,
-  // only lanes of a live query head load them) and, per 16-channel group in channel
-  // order, the lane's 4-bit word (wa) or the two dwords of its 24-bit field (wa, wb).
+  // One tile of one kind in registers: the 4 parameter arrays (this lane's 8 slots each)
+  // and, per 16-channel group in channel order, the lane's 4-bit word (wa) or the two
+  // dwords of its 24-bit field (wa, wb). Group g starts at byte 256 + 256 g while g is a
+  // 4-bit group, at 256 + 64 go + 192 g once it is a 3-bit one (go 4-bit groups first).
   u32x4_t km[4], vm[4];
   uint32_t kwa[NG], kwb[NG], vwa[NG], vwb[NG];
-  auto load_tile = [&](const uint8_t* tile, int go, int ng, u32x4_t* meta, uint32_t* wa, uint32_t* wb) {
+  auto load_tile = [&](q43_rsrc_t rs, int so, int go, int ng, u32x4_t* meta, uint32_t* wa, uint32_t* wb) {
 #pragma unroll
-    for (int P = 0; P < 4; ++P)
-      meta[P] = q_ok ? load_stream16(tile + 64 * q4 + 16 * P) : u32x4_t{0u, 0u, 0u, 0u};
-    const uint8_t* in = tile + kQ43MetaBytes + kQ43OutGroupBytes * go;
+    for (int P = 0; P < 4; ++P) meta[P] = q43_load16(rs, vo_meta, so + 16 * P);
+    const int so_in = so + kQ43MetaBytes + (kQ43OutGroupBytes - kQ43InGroupBytes) * go;
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       const bool four = g == 0 || (GO == 2 && g == 1 && go == 2);
       if (four) {
-        wa[g] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(tile + kQ43MetaBytes + kQ43OutGroupBytes * g) + lane);
+        wa[g] = q43_load4(rs, vo_4, so + kQ43MetaBytes + kQ43OutGroupBytes * g);
       } else if (g < ng) {
-        const uint8_t* grp = in + kQ43InGroupBytes * (g - go);
-        wa[g] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(grp + off_a));
-        wb[g] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(grp + off_b));
+        wa[g] = q43_load4(rs, off_a, so_in + kQ43InGroupBytes * g);
+        wb[g] = q43_load4(rs, off_b, so_in + kQ43InGroupBytes * g);
       }
     }
   };
   // operands of group g: 16-bit pairs with exponent bytes eb, block 0 then block 1
+  // constants of the 3-bit conversion, held in registers (see codes3_to_num)
+  uint32_t m7 = 0x00070007u, e2_k = kBf16Code & 0xFF00FF00u, e2_v = kF16Code & 0xFF00FF00u;
+  asm volatile("" : "+v"(m7), "+s"(e2_k), "+s"(e2_v));
   auto group_codes = [&](int g, int go, const uint32_t* wa, const uint32_t* wb, uint32_t eb) -> u32x4_t {
+    const uint32_t e2 = eb == kBf16Code ? e2_k : e2_v;
     if (g == 0) return codes4_to_num(wa[0], eb);
-    if (g >= GO) return codes3_to_num(field24(wa[g], wb[g], f_shift), eb);
-    return go == 2 ? codes4_to_num(wa[g], eb) : codes3_to_num(field24(wa[g], wb[g], f_shift), eb);
+    if (g >= GO) return codes3_to_num(field24(wa[g], wb[g], f_shift), m7, e2);
+    return go == 2 ? codes4_to_num(wa[g], eb) : codes3_to_num(field24(wa[g], wb[g], f_shift), m7, e2);
   };
 
+  // Each wave takes every kWaves-th tile of the split. The next tile's loads are issued
+  // unconditionally: past the split's end they re-read the current tile (cached, unused).
   int t0 = t_begin + wave * kQ43Tile;   // split starts are multiples of 64 tokens: whole tiles
   if (t0 < t_end) {
-    load_tile(Kb + (size_t)(t0 / kQ43Tile) * tbk, gok, ngk, km, kwa, kwb);
-    load_tile(Vb + (size_t)(t0 / kQ43Tile) * tbv, gov, ngv, vm, vwa, vwb);
+    load_tile(rs_k, t0 / kQ43Tile * tbk, gok, ngk, km, kwa, kwb);
+    load_tile(rs_v, t0 / kQ43Tile * tbv, gov, ngv, vm, vwa, vwb);
   }
 
   // ---- prologue: q~ (scaled to log2 units) and, per key group, this lane's column as B (hi/lo)
@@ -939,6 +983,7 @@ void decode_split_q43(DecodeParams p) {
 
   for (; t0 < t_end; t0 += kWaves * kQ43Tile) {
     const int t_next = t0 + kWaves * kQ43Tile;
+    const int t_ld = t_next < t_end ? t_next : t0;
     // ---- scores S^T[token][head], both 16-token blocks; accumulators start at -128 Q
     f32x4_t ao[2] = {{c_o, c_o, c_o, c_o}, {c_o, c_o, c_o, c_o}};
     f32x4_t ai[2] = {{c_i, c_i, c_i, c_i}, {c_i, c_i, c_i, c_i}};
@@ -967,19 +1012,23 @@ void decode_split_q43(DecodeParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int k = 4 * blk + i;
-        float x = half_at(km[0], k) * ao[blk][i] + half_at(km[1], k) * Qo + half_at(km[2], k) * ai[blk][i] +
-                  half_at(km[3], k) * Qi;
-        if (!q_ok) x = kNegInf;
-        if (tail && t0 + 16 * blk + 4 * q4 + i >= t_end) x = kNegInf;
-        sc[blk][i] = x;
+        sc[blk][i] = fmaf(half_at(km[0], k), ao[blk][i],
+                          fmaf(half_at(km[2], k), ai[blk][i],
+                               fmaf(half_at(km[1], k), Qo, fmaf(half_at(km[3], k), Qi, 0.f))));
       }
-    if (t_next < t_end) load_tile(Kb + (size_t)(t_next / kQ43Tile) * tbk, gok, ngk, km, kwa, kwb);
+    if (__builtin_expect(tail, 0)) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (t0 + 16 * blk + 4 * q4 + i >= t_end) sc[blk][i] = kNegInf;
+    }
+    load_tile(rs_k, t_ld / kQ43Tile * tbk, gok, ngk, km, kwa, kwb);
 
     // ---- online softmax (lane: head n16, tokens 16 blk + 4 q4 + i)
     float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
                      fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = max_over_rows(mx);
     const float m_new = fmaxf(m, mx);
     const float m_use = (m_new == kNegInf) ? 0.f : m_new;
     const float alpha = q_ok ? fast_exp2(m - m_use) : 1.f;
@@ -1022,17 +1071,17 @@ void decode_split_q43(DecodeParams p) {
         for (int P = 0; P < 4; ++P) vm[P][j] &= msk;
       }
     }
-    u32x4_t wo, wi, bo, bi;
+    u32x4_t pw, wo, wi;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const half2_t pk = __builtin_convertvector(
           (float __attribute__((ext_vector_type(2)))){pr[j >> 1][2 * (j & 1)], pr[j >> 1][2 * (j & 1) + 1]}, half2_t);
+      pw[j] = __builtin_bit_cast(uint32_t, pk);
       wo[j] = __builtin_bit_cast(uint32_t, pk * half2_of(vm[0][j]));
-      bo[j] = __builtin_bit_cast(uint32_t, pk * half2_of(vm[1][j]));
       wi[j] = __builtin_bit_cast(uint32_t, pk * half2_of(vm[2][j]));
-      bi[j] = __builtin_bit_cast(uint32_t, pk * half2_of(vm[3][j]));
     }
     const half8_t awo = __builtin_bit_cast(half8_t, wo), awi = __builtin_bit_cast(half8_t, wi);
+    const half8_t ap = __builtin_bit_cast(half8_t, pw);
 
     // ---- value product per group of 16 channels (codes as 1024 + c), and the four sums
 #pragma unroll
@@ -1045,17 +1094,17 @@ void decode_split_q43(DecodeParams p) {
     }
     sw_o = __builtin_amdgcn_mfma_f32_16x16x32_f16(awo, ones, sw_o, 0, 0, 0);
     sw_i = __builtin_amdgcn_mfma_f32_16x16x32_f16(awi, ones, sw_i, 0, 0, 0);
-    sb_o = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, bo), ones, sb_o, 0, 0, 0);
-    sb_i = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, bi), ones, sb_i, 0, 0, 0);
-    if (t_next < t_end) load_tile(Vb + (size_t)(t_next / kQ43Tile) * tbv, gov, ngv, vm, vwa, vwb);
+    // the B operand of lane (n, q) holds slots 8 q .. 8 q + 7 for column n: its own parameters
+    sb_o = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap, __builtin_bit_cast(half8_t, vm[1]), sb_o, 0, 0, 0);
+    sb_i = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap, __builtin_bit_cast(half8_t, vm[3]), sb_i, 0, 0, 0);
+    load_tile(rs_v, t_ld / kQ43Tile * tbv, gov, ngv, vm, vwa, vwb);
   }
 
   BasisPrefetch<RB> pf;
   prefetch_basis<RB>(p, h, rv, pf);
   // ---- per head: l over the lane groups; rows 0..3 (lanes q4 = 0) hold heads 0..3:
   // o_lat = sum_t w_t (1024 + c_t) - 1024 sum_t w_t + sum_t p_t base_t
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
+  l = sum_over_rows(l);
   float* red = smem;                          // [wave][head][RB]
   float* wm = smem + kWaves * kHeadsPerWg * RB;
   float* wl = wm + kWaves * kHeadsPerWg;
@@ -1350,12 +1399,18 @@ hipError_t launch_decode(const DecodeParams& p, int latent_dtype, int rank_bound
   const dim3 grid(p.n_splits, p.Hkv * p.n_head_groups, p.B);
   const dim3 block(kWaves * 64);
   if (latent_dtype == KVLR_Q43) {
+    bool exact = true;   // every head at r_k = r_v = the bound: no per-head group conditions
+    for (int h = 0; h < p.Hkv; ++h) exact = exact && p.ht.rk[h] == rank_bound && p.ht.rv[h] == rank_bound;
+#define KVLR_Q43_LAUNCH(RB)                                                     \
+  if (exact) hipLaunchKernelGGL((decode_split_q43<RB, true>), grid, block, 0, stream, p); \
+  else hipLaunchKernelGGL((decode_split_q43<RB, false>), grid, block, 0, stream, p)
     switch (rank_bound) {
-      case 32: hipLaunchKernelGGL(decode_split_q43<32>, grid, block, 0, stream, p); break;
-      case 64: hipLaunchKernelGGL(decode_split_q43<64>, grid, block, 0, stream, p); break;
-      case 96: hipLaunchKernelGGL(decode_split_q43<96>, grid, block, 0, stream, p); break;
-      default: hipLaunchKernelGGL(decode_split_q43<128>, grid, block, 0, stream, p); break;
+      case 32: KVLR_Q43_LAUNCH(32); break;
+      case 64: KVLR_Q43_LAUNCH(64); break;
+      case 96: KVLR_Q43_LAUNCH(96); break;
+      default: KVLR_Q43_LAUNCH(128); break;
     }
+#undef KVLR_Q43_LAUNCH
     return hipGetLastError();
   }
   if (latent_bf16) {
