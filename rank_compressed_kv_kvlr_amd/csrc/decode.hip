@@ -847,12 +847,36 @@ constexpr int kBufNonTemporal = 2;
 __device__ __forceinline__ q43_rsrc_t q43_block_rsrc(const uint8_t* base, int nbytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, nbytes, 0x00020000);
 }
-__device__ __forceinline__ u32x4_t q43_load16(q43_rsrc_t rs, int voff, int soff) {
-  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, kBufNonTemporal));
+// 16 bytes per lane from the block into LDS: lane i's bytes land at lds + 16 i (the LDS
+// address is the wave's base plus the lane's index; the block offset is voff + soff).
+typedef __attribute__((address_space(3))) void lds_void_t;
+__device__ __forceinline__ void q43_dma16(q43_rsrc_t rs, uint8_t* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)lds, 16, voff, soff, 0, kBufNonTemporal);
 }
-__device__ __forceinline__ uint32_t q43_load4(q43_rsrc_t rs, int voff, int soff) {
-  return __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, kBufNonTemporal);
-}
+// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector-memory
+// operations of this wave are in flight, and for nothing else
+constexpr int vmcnt_at_most(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Tiles reach LDS by direct buffer-to-LDS loads. Each wave keeps a ring of kStages
+// stages (a key tile, then a value tile) and has the tiles of its next kStages - 1
+// steps in flight while it computes on the current one. Every tile of a kind takes
+// kLoads load instructions (with two, the first covers up to 64 lanes of 16 bytes and
+// the second the rest, at least one lane), so after a step issues its look-ahead tile,
+// at most kWait loads may still be in flight once the step's own tile has landed.
+template <int RB>
+struct Q43Ring {
+  static constexpr int kTileBytes = kQ43Tile * q43_row_bytes(RB);   // the largest tile of the class
+  static constexpr int kLoads = kTileBytes / 16 > 64 ? 2 : 1;
+  static constexpr int kStage = 2 * kTileBytes;
+  static constexpr int kStages = RB <= 32 ? 8 : RB <= 96 ? 5 : 4;
+  static constexpr int kRingBytes = kWaves * kStages * kStage;
+  static constexpr int kProBytes = 4096 + 80 * RB;                   // query projection: q, q~, partial sums
+  static constexpr int kLdsFloats =
+      (kRingBytes + kProBytes) / 4 > kTailLds ? (kRingBytes + kProBytes) / 4 : kTailLds;
+  static constexpr int kWait = (kStages - 1) * 2 * kLoads;
+  static_assert(kWait < 64, "vmcnt holds 6 bits");
+  static_assert(kLoads == 2 || kTileBytes / 16 <= 64, "one instruction covers 64 lanes");
+};
 
 // EXACT: every KV head has r_k = r_v = RB, so the group structure is known at compile time.
 template <int RB, bool EXACT>
@@ -862,7 +886,9 @@ void decode_split_q43(DecodeParams p) {
   constexpr int GI = RB == 128 ? 6 : (RB - 16) / 16;       // 3-bit groups (bound)
   constexpr int NG = GO + GI;                              // groups from GO on are always 3-bit
   constexpr int QTS = RB;
-  __shared__ __attribute__((aligned(16))) float smem[kTailLds];
+  using Ring = Q43Ring<RB>;
+  constexpr int NS = Ring::kStages, STAGE = Ring::kStage, TB = Ring::kTileBytes;
+  __shared__ __attribute__((aligned(16))) float smem[Ring::kLdsFloats];
 
   const int s = blockIdx.x;
   const int h = blockIdx.y / p.n_head_groups;
@@ -891,35 +917,71 @@ void decode_split_q43(DecodeParams p) {
   const int gov = EXACT ? GO : q43_outlier(rv) >> 4, ngv = EXACT ? NG : rv >> 4;
   const int tbk = kQ43Tile * q43_row_bytes(rk), tbv = kQ43Tile * q43_row_bytes(rv);
   const size_t rows = cap_rows_q43(p.cap);
-  // Buffer resources over this (batch row, KV head) block of each cache; the tile offset
-  // travels in the scalar offset, so per-lane offsets stay fixed across tiles.
+  // Buffer resources over this (batch row, KV head) block of each cache
   const q43_rsrc_t rs_k = q43_block_rsrc(static_cast<const uint8_t*>(p.lat_k) + rows * ((size_t)b * p.Sk + p.ht.sk_pre[h]),
                                          (int)rows / kQ43Tile * tbk);
   const q43_rsrc_t rs_v = q43_block_rsrc(static_cast<const uint8_t*>(p.lat_v) + rows * ((size_t)b * p.Sv + p.ht.sv_pre[h]),
                                          (int)rows / kQ43Tile * tbv);
-  // this lane's offsets: its 8 parameter slots, its 4-bit word, and the two dwords that
-  // hold bytes 3 lane .. 3 lane + 2 of a 3-bit group (its 24-bit field)
-  const int vo_meta = 64 * q4, vo_4 = 4 * lane;
-  const int off_a = (3 * lane) & ~3, off_b = (3 * lane + 2) & ~3, f_shift = 8 * ((3 * lane) & 3);
 
-  // One tile of one kind in registers: the 4 parameter arrays (this lane's 8 slots each)
-  // and, per 16-channel group in channel order, the lane's 4-bit word (wa) or the two
-  // dwords of its 24-bit field (wa, wb). Group g starts at byte 256 + 256 g while g is a
-  // 4-bit group, at 256 + 64 go + 192 g once it is a 3-bit one (go 4-bit groups first).
+  // ---- this wave's tiles: every kWaves-th tile of the split (split starts are
+  // multiples of 64 tokens, so whole tiles), n_w of them; the ring's stage u holds
+  // the wave's tiles u, u + NS, ...
+  uint8_t* const ring = reinterpret_cast<uint8_t*>(smem) + wave * NS * STAGE;
+  const int tile0 = (t_begin >> 5) + wave;
+  const int left = t_end - t_begin - wave * kQ43Tile;
+  const int n_w = left > 0 ? (left + kWaves * kQ43Tile - 1) / (kWaves * kQ43Tile) : 0;
+  // The wave's tile j (past its last tile: the last one again, unused) into ring stage u.
+  // The full 64-lane instructions of both kinds come first, then the partial ones, each
+  // in one branch of its own: the count of instructions a tile takes stays 2 kLoads.
+  const int nk = tbk >> 4, nv = tbv >> 4;   // 16-byte pieces of a tile
+  const int nk0 = Ring::kLoads == 1 ? nk : min(64, nk - 1), nv0 = Ring::kLoads == 1 ? nv : min(64, nv - 1);
+  // The lane limits of the partial instructions pass through an empty asm statement at
+  // each call, so the compiler cannot merge or thread branches with equal conditions
+  // across calls (which would issue an instruction once per lane subset).
+  auto issue = [&](int j, int u) {
+    const int tile = tile0 + kWaves * min(j, n_w - 1);
+    uint8_t* const dk = ring + u * STAGE;
+    uint8_t* const dv = dk + TB;
+    int lk = Ring::kLoads == 1 ? nk : nk - nk0, lv = Ring::kLoads == 1 ? nv : nv - nv0;
+    asm volatile("" : "+s"(lk), "+s"(lv));
+    if (Ring::kLoads == 1) {
+      if (lane < lk) q43_dma16(rs_k, dk, 16 * lane, tile * tbk);
+      if (lane < lv) q43_dma16(rs_v, dv, 16 * lane, tile * tbv);
+    } else {
+      if (lane < nk0) q43_dma16(rs_k, dk, 16 * lane, tile * tbk);
+      if (lane < nv0) q43_dma16(rs_v, dv, 16 * lane, tile * tbv);
+      if (lane < lk) q43_dma16(rs_k, dk + 16 * nk0, 16 * lane, tile * tbk + 16 * nk0);
+      if (lane < lv) q43_dma16(rs_v, dv + 16 * nv0, 16 * lane, tile * tbv + 16 * nv0);
+    }
+  };
+  if (n_w > 0) {
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j) issue(j, j);
+  }
+
+  // this lane's bytes of a stage: its 8 parameter slots, its 4-bit word, and the two
+  // dwords that hold bytes 3 lane .. 3 lane + 2 of a 3-bit group (its 24-bit field).
+  // Group g starts at byte 256 + 256 g while g is a 4-bit group, at 256 + 64 go + 192 g
+  // once it is a 3-bit one (go 4-bit groups first).
+  const int off_a = (3 * lane) & ~3, off_b = (3 * lane + 2) & ~3, f_shift = 8 * ((3 * lane) & 3);
+  const uint8_t* const la_meta = ring + 64 * q4;
+  const uint8_t* const la_4 = ring + 4 * lane;
+  const uint8_t* const la_a = ring + off_a;
+  const uint8_t* const la_b = ring + off_b;
   u32x4_t km[4], vm[4];
   uint32_t kwa[NG], kwb[NG], vwa[NG], vwb[NG];
-  auto load_tile = [&](q43_rsrc_t rs, int so, int go, int ng, u32x4_t* meta, uint32_t* wa, uint32_t* wb) {
+  auto read_tile = [&](int at, int go, int ng, u32x4_t* meta, uint32_t* wa, uint32_t* wb) {
 #pragma unroll
-    for (int P = 0; P < 4; ++P) meta[P] = q43_load16(rs, vo_meta, so + 16 * P);
-    const int so_in = so + kQ43MetaBytes + (kQ43OutGroupBytes - kQ43InGroupBytes) * go;
+    for (int P = 0; P < 4; ++P) meta[P] = *reinterpret_cast<const u32x4_t*>(la_meta + at + 16 * P);
+    const int in = at + kQ43MetaBytes + (kQ43OutGroupBytes - kQ43InGroupBytes) * go;
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       const bool four = g == 0 || (GO == 2 && g == 1 && go == 2);
       if (four) {
-        wa[g] = q43_load4(rs, vo_4, so + kQ43MetaBytes + kQ43OutGroupBytes * g);
+        wa[g] = *reinterpret_cast<const uint32_t*>(la_4 + at + kQ43MetaBytes + kQ43OutGroupBytes * g);
       } else if (g < ng) {
-        wa[g] = q43_load4(rs, off_a, so_in + kQ43InGroupBytes * g);
-        wb[g] = q43_load4(rs, off_b, so_in + kQ43InGroupBytes * g);
+        wa[g] = *reinterpret_cast<const uint32_t*>(la_a + in + kQ43InGroupBytes * g);
+        wb[g] = *reinterpret_cast<const uint32_t*>(la_b + in + kQ43InGroupBytes * g);
       }
     }
   };
@@ -934,17 +996,9 @@ void decode_split_q43(DecodeParams p) {
     return go == 2 ? codes4_to_num(wa[g], eb) : codes3_to_num(field24(wa[g], wb[g], f_shift), m7, e2);
   };
 
-  // Each wave takes every kWaves-th tile of the split. The next tile's loads are issued
-  // unconditionally: past the split's end they re-read the current tile (cached, unused).
-  int t0 = t_begin + wave * kQ43Tile;   // split starts are multiples of 64 tokens: whole tiles
-  if (t0 < t_end) {
-    load_tile(rs_k, t0 / kQ43Tile * tbk, gok, ngk, km, kwa, kwb);
-    load_tile(rs_v, t0 / kQ43Tile * tbv, gov, ngv, vm, vwa, vwb);
-  }
-
   // ---- prologue: q~ (scaled to log2 units) and, per key group, this lane's column as B (hi/lo)
-  float* q_lds = smem;                          // [4][d]
-  float* qt_lds = smem + kHeadsPerWg * 256;     // [4][QTS]
+  float* q_lds = smem + Ring::kRingBytes / 4;  // [4][d], after the ring (its tiles are in flight)
+  float* qt_lds = q_lds + kHeadsPerWg * 256;    // [4][QTS]
   float* qred = qt_lds + kHeadsPerWg * QTS;     // [4 waves][4][QTS]
   project_query<RB>(p, b, h, hq0, gpw, rk, q_lds, qred, qt_lds);
   bf16x4_t qh[NG], ql[NG];
@@ -970,7 +1024,6 @@ void decode_split_q43(DecodeParams p) {
   Qi += __shfl_xor(Qi, 16, 64);
   Qi += __shfl_xor(Qi, 32, 64);
   const float c_o = -128.f * Qo, c_i = -128.f * Qi;
-  __syncthreads();   // LDS is reused below
 
   const half8_t ones = __builtin_bit_cast(half8_t, u32x4_t{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u});
   float m = kNegInf, l = 0.f;
@@ -981,9 +1034,18 @@ void decode_split_q43(DecodeParams p) {
 #pragma unroll
   for (int g = 0; g < NG; ++g) acc[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (; t0 < t_end; t0 += kWaves * kQ43Tile) {
-    const int t_next = t0 + kWaves * kQ43Tile;
-    const int t_ld = t_next < t_end ? t_next : t0;
+  for (int it0 = 0; it0 < n_w; it0 += NS) {
+#pragma unroll
+  for (int u = 0; u < NS; ++u) {
+    const int it = it0 + u;
+    if (it >= n_w) break;
+    const int t0 = (tile0 + kWaves * it) * kQ43Tile;
+    // look ahead NS - 1 tiles, into the stage the previous step used; then wait for this one
+    issue(it + NS - 1, (u + NS - 1) % NS);
+    __builtin_amdgcn_s_waitcnt(vmcnt_at_most(Ring::kWait));
+    asm volatile("" ::: "memory");   // the stage's LDS reads stay after the wait
+    read_tile(u * STAGE, gok, ngk, km, kwa, kwb);
+    read_tile(u * STAGE + TB, gov, ngv, vm, vwa, vwb);
     // ---- scores S^T[token][head], both 16-token blocks; accumulators start at -128 Q
     f32x4_t ao[2] = {{c_o, c_o, c_o, c_o}, {c_o, c_o, c_o, c_o}};
     f32x4_t ai[2] = {{c_i, c_i, c_i, c_i}, {c_i, c_i, c_i, c_i}};
@@ -1023,7 +1085,6 @@ void decode_split_q43(DecodeParams p) {
         for (int i = 0; i < 4; ++i)
           if (t0 + 16 * blk + 4 * q4 + i >= t_end) sc[blk][i] = kNegInf;
     }
-    load_tile(rs_k, t_ld / kQ43Tile * tbk, gok, ngk, km, kwa, kwb);
 
     // ---- online softmax (lane: head n16, tokens 16 blk + 4 q4 + i)
     float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
@@ -1097,7 +1158,7 @@ void decode_split_q43(DecodeParams p) {
     // the B operand of lane (n, q) holds slots 8 q .. 8 q + 7 for column n: its own parameters
     sb_o = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap, __builtin_bit_cast(half8_t, vm[1]), sb_o, 0, 0, 0);
     sb_i = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap, __builtin_bit_cast(half8_t, vm[3]), sb_i, 0, 0, 0);
-    load_tile(rs_v, t_ld / kQ43Tile * tbv, gov, ngv, vm, vwa, vwb);
+  }
   }
 
   BasisPrefetch<RB> pf;
@@ -1105,6 +1166,8 @@ void decode_split_q43(DecodeParams p) {
   // ---- per head: l over the lane groups; rows 0..3 (lanes q4 = 0) hold heads 0..3:
   // o_lat = sum_t w_t (1024 + c_t) - 1024 sum_t w_t + sum_t p_t base_t
   l = sum_over_rows(l);
+  __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));   // this wave's tile loads have landed: the ring is reused
+  __syncthreads();
   float* red = smem;                          // [wave][head][RB]
   float* wm = smem + kWaves * kHeadsPerWg * RB;
   float* wl = wm + kWaves * kHeadsPerWg;
