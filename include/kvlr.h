@@ -110,7 +110,8 @@ typedef enum kvlr_value_mode {
  *               (joint values with bf16 latents: Hq <= 32 and Hkv <= 8)
  *   n_kv_heads  Hkv in [1, 64]; query head i reads KV head i / G
  *   head_dim    d   in [32, 256], a multiple of 32
- *   capacity    T_cap in [1, 2^30]: usable rows per (batch row, KV head)
+ *   capacity    T_cap in [1, 2^30]: usable rows per (batch row, KV head); with
+ *               4/3-bit latents at most 35791392 (a block stays below 2^31 bytes)
  *   r_k, r_v    host arrays [Hkv]: ranks of each KV head (uniform per-layer
  *               ranks repeat one value); 1 <= r <= min(d, 128), a multiple of 16
  *               for bf16 and 4/3-bit latents and of 4 for fp32 latents

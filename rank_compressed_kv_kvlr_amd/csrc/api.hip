@@ -161,6 +161,10 @@ int check_desc(const kvlr_desc* d, HeadTable* ht, int* Rk, int* Rv, int* rank_bo
       d->head_dim < 32 || d->head_dim > 256 || d->head_dim % 32 != 0 || d->capacity > (1 << 30))
     return KVLR_ERR_SHAPE;
   if (d->value_mode != KVLR_VALUES_PER_HEAD && d->value_mode != KVLR_VALUES_JOINT) return KVLR_ERR_ARG;
+  // 4/3-bit blocks are addressed with 32-bit buffer offsets: a (row, head) block of
+  // cap rows (rounded up to 32) at up to 60 bytes each stays below 2^31 bytes
+  if (d->latent_dtype == KVLR_Q43 && (long long)kvlr::cap_rows_q43(d->capacity) * 60 >= (1LL << 31))
+    return KVLR_ERR_SHAPE;
   const bool joint = d->value_mode == KVLR_VALUES_JOINT;
   // the joint bf16 kernel holds at most two 16-query row tiles of four KV heads
   if (joint && d->latent_dtype == KVLR_BF16 && (d->n_q_heads > 32 || d->n_kv_heads > 8)) return KVLR_ERR_SHAPE;

@@ -100,12 +100,14 @@ __device__ __forceinline__ void prefetch_basis(const DecodeParams& p, int h, int
     }
 }
 
-template <int RB>
+// scratch: LDS_FLOATS floats of LDS (at least 4 RB + 17 plus a few basis rows).
+// REC: split records folded per memory round trip.
+template <int RB, int LDS_FLOATS = kTailLds, int REC = 8>
 __device__ __forceinline__ void finish_split(const DecodeParams& p, int b, int h, int hg, int hq0, int gpw,
                                              int rv, float* scratch, const BasisPrefetch<RB>& pf,
                                              const RecLayout& rl, int n_rec) {
   if (!p.fuse) return;
-  int* flag = reinterpret_cast<int*>(scratch + kTailLds - 1);
+  int* flag = reinterpret_cast<int*>(scratch + LDS_FLOATS - 1);
   int* counter = p.counters + ((size_t)b * p.Hkv + h) * p.n_head_groups + hg;
   // Hand-off between workgroups without a release/acquire fence. This relies on
   // gfx950 behaviour that the HIP memory model does not promise at relaxed order:
@@ -131,7 +133,7 @@ __device__ __forceinline__ void finish_split(const DecodeParams& p, int b, int h
   float* olat = scratch;                        // [RB][4] head-minor
   float* p_lds = scratch + 4 * RB;              // P_V rows, padded stride (head_dim > 128)
   const int pst = rv + 4;
-  const int p_rows = min(d, (kTailLds - 4 * RB - 16) / pst);
+  const int p_rows = min(d, (LDS_FLOATS - 4 * RB - 16) / pst);
   const float* P = p.pv + (size_t)d * p.ht.rv_pre[h];
   const int per_row4 = rv / 4;
   auto stage_basis = [&](int r0, int nr) {      // rows [r0, r0 + nr) into LDS
@@ -143,13 +145,14 @@ __device__ __forceinline__ void finish_split(const DecodeParams& p, int b, int h
   };
   if (!p.out_latent && !reg_basis) stage_basis(0, p_rows);   // in flight with the record loads below
 
-  // wave g folds the records of head g in one pass with a running maximum
+  // wave g folds the records of head g with a running maximum, REC records per memory
+  // round trip
   float M = kNegInf, L = 0.f, o0 = 0.f, o1 = 0.f;
   if (g < gpw) {
-    for (int s0 = 0; s0 < n_rec; s0 += 8) {
-      float ms[8], ls[8], v0[8], v1[8];
+    for (int s0 = 0; s0 < n_rec; s0 += REC) {
+      float ms[REC], ls[REC], v0[REC], v1[REC];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < REC; ++u) {
         const bool ok = s0 + u < n_rec;
         const float* r = rec_at(rl, ok ? s0 + u : 0, g);
         ms[u] = ok ? load_rec(r) : kNegInf;
@@ -158,7 +161,7 @@ __device__ __forceinline__ void finish_split(const DecodeParams& p, int b, int h
         v1[u] = (ok && lane + 64 < rv) ? load_rec(r + 66 + lane) : 0.f;
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < REC; ++u) {
         if (ms[u] == kNegInf) continue;   // empty split or beyond n_splits
         const float Mn = fmaxf(M, ms[u]);
         const float a = fast_exp2(M - Mn), f = fast_exp2(ms[u] - Mn);
@@ -468,8 +471,7 @@ __device__ __forceinline__ void bf16_segment(const DecodeParams& p, int b, int h
         sc[blk][i] = valid ? sc[blk][i] : kNegInf;
         mx = fmaxf(mx, sc[blk][i]);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = max_over_rows(mx);
     const float m_new = fmaxf(m, mx);
     const float m_use = (m_new == kNegInf) ? 0.f : m_new;
     const float alpha = q_ok ? fast_exp2(m - m_use) : 1.f;
@@ -531,8 +533,7 @@ __device__ __forceinline__ void bf16_segment(const DecodeParams& p, int b, int h
   BasisPrefetch<RB> pf;
   prefetch_basis<RB>(p, h, rv, pf);
   // ---- workgroup merge of the 4 waves: rows 0..3 of each wave's accumulators (q4 = 0 lanes)
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
+  l = sum_over_rows(l);
   float* red = smem;                          // [wave][head][RB]
   float* wm = smem + kWaves * kHeadsPerWg * RB;
   float* wl = wm + kWaves * kHeadsPerWg;
@@ -822,23 +823,6 @@ __device__ __forceinline__ float half_at(const u32x4_t& v, int k) {   // half fl
 }
 __device__ __forceinline__ half2_t half2_of(uint32_t w) { return __builtin_bit_cast(half2_t, w); }
 
-// Reductions over the lanes n, n + 16, n + 32, n + 48 (the four 16-lane rows of a wave)
-// with gfx950's row swaps: after swapping rows 1 <-> 0 and 3 <-> 2 of two copies of x,
-// the two results hold, lane by lane, x and its partner 16 lanes away; likewise for the
-// 32-lane halves.
-__device__ __forceinline__ float max_over_rows(float x) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_over_rows(float x) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
 // Raw buffer access to one (batch row, KV head) block of a 4/3-bit cache: base and size
 // in a resource (word 3 = 0x00020000: the raw 32-bit data format of gfx9 buffers), a
 // per-lane offset in a VGPR and the tile offset in an SGPR; loads stream (non-temporal).
@@ -870,9 +854,7 @@ struct Q43Ring {
   static constexpr int kStage = 2 * kTileBytes;
   static constexpr int kStages = RB <= 32 ? 8 : RB <= 96 ? 5 : 4;
   static constexpr int kRingBytes = kWaves * kStages * kStage;
-  static constexpr int kProBytes = 4096 + 80 * RB;                   // query projection: q, q~, partial sums
-  static constexpr int kLdsFloats =
-      (kRingBytes + kProBytes) / 4 > kTailLds ? (kRingBytes + kProBytes) / 4 : kTailLds;
+  static constexpr int kProFloats = 1024 + 20 * RB;                  // query projection: q, q~, partial sums
   static constexpr int kWait = (kStages - 1) * 2 * kLoads;
   static_assert(kWait < 64, "vmcnt holds 6 bits");
   static_assert(kLoads == 2 || kTileBytes / 16 <= 64, "one instruction covers 64 lanes");
@@ -888,7 +870,14 @@ void decode_split_q43(DecodeParams p) {
   constexpr int QTS = RB;
   using Ring = Q43Ring<RB>;
   constexpr int NS = Ring::kStages, STAGE = Ring::kStage, TB = Ring::kTileBytes;
-  __shared__ __attribute__((aligned(16))) float smem[Ring::kLdsFloats];
+  constexpr int EPI = Ring::kRingBytes / 4;   // the epilogue reuses the ring once every tile has landed
+  // Two LDS objects: the compiler then knows that the prologue's LDS writes do not
+  // touch the ring that the tile loads write, and does not wait for those loads.
+  __shared__ __attribute__((aligned(16))) float ring_lds[EPI];
+  __shared__ __attribute__((aligned(16))) float pro_lds[Ring::kProFloats];
+  float* const smem = ring_lds;
+  static_assert(EPI >= kWaves * kHeadsPerWg * RB + 2 * kWaves * kHeadsPerWg && EPI >= 4 * RB + 17 + 16 * (RB + 4),
+                "the ring holds the epilogue's partial sums and some basis rows");
 
   const int s = blockIdx.x;
   const int h = blockIdx.y / p.n_head_groups;
@@ -905,7 +894,7 @@ void decode_split_q43(DecodeParams p) {
     write_empty_records(rl, s, gpw, rv);
     BasisPrefetch<RB> pf;
     prefetch_basis<RB>(p, h, rv, pf);
-    finish_split<RB>(p, b, h, hg, hq0, gpw, rv, smem, pf, rl, p.n_splits);
+    finish_split<RB, EPI, 16>(p, b, h, hg, hq0, gpw, rv, smem, pf, rl, p.n_splits);
     return;
   }
 
@@ -926,7 +915,7 @@ void decode_split_q43(DecodeParams p) {
   // ---- this wave's tiles: every kWaves-th tile of the split (split starts are
   // multiples of 64 tokens, so whole tiles), n_w of them; the ring's stage u holds
   // the wave's tiles u, u + NS, ...
-  uint8_t* const ring = reinterpret_cast<uint8_t*>(smem) + wave * NS * STAGE;
+  uint8_t* const ring = reinterpret_cast<uint8_t*>(ring_lds) + wave * NS * STAGE;
   const int tile0 = (t_begin >> 5) + wave;
   const int left = t_end - t_begin - wave * kQ43Tile;
   const int n_w = left > 0 ? (left + kWaves * kQ43Tile - 1) / (kWaves * kQ43Tile) : 0;
@@ -954,10 +943,6 @@ void decode_split_q43(DecodeParams p) {
       if (lane < lv) q43_dma16(rs_v, dv + 16 * nv0, 16 * lane, tile * tbv + 16 * nv0);
     }
   };
-  if (n_w > 0) {
-#pragma unroll
-    for (int j = 0; j < NS - 1; ++j) issue(j, j);
-  }
 
   // this lane's bytes of a stage: its 8 parameter slots, its 4-bit word, and the two
   // dwords that hold bytes 3 lane .. 3 lane + 2 of a 3-bit group (its 24-bit field).
@@ -997,7 +982,7 @@ void decode_split_q43(DecodeParams p) {
   };
 
   // ---- prologue: q~ (scaled to log2 units) and, per key group, this lane's column as B (hi/lo)
-  float* q_lds = smem + Ring::kRingBytes / 4;  // [4][d], after the ring (its tiles are in flight)
+  float* q_lds = pro_lds;                       // [4][d]
   float* qt_lds = q_lds + kHeadsPerWg * 256;    // [4][QTS]
   float* qred = qt_lds + kHeadsPerWg * QTS;     // [4 waves][4][QTS]
   project_query<RB>(p, b, h, hq0, gpw, rk, q_lds, qred, qt_lds);
@@ -1019,11 +1004,16 @@ void decode_split_q43(DecodeParams p) {
       if (four) Qo += seen; else Qi += seen;
     }
   }
-  Qo += __shfl_xor(Qo, 16, 64);
-  Qo += __shfl_xor(Qo, 32, 64);
-  Qi += __shfl_xor(Qi, 16, 64);
-  Qi += __shfl_xor(Qi, 32, 64);
+  Qo = sum_over_rows(Qo);
+  Qi = sum_over_rows(Qi);
   const float c_o = -128.f * Qo, c_i = -128.f * Qi;
+  // The first NS - 1 tiles go out once the prologue is done with memory: the waits of
+  // its loads would cover them, and so would those of its LDS reads (the compiler
+  // orders LDS accesses after direct-to-LDS loads issued under a lane mask).
+  if (n_w > 0) {
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j) issue(j, j);
+  }
 
   const half8_t ones = __builtin_bit_cast(half8_t, u32x4_t{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u});
   float m = kNegInf, l = 0.f;
@@ -1189,7 +1179,7 @@ void decode_split_q43(DecodeParams p) {
   __syncthreads();
   merge_waves_and_store(rl, s, gpw, rv, wm, wl,
                         [&](int w, int g, int j) { return red[(w * kHeadsPerWg + g) * RB + j]; });
-  finish_split<RB>(p, b, h, hg, hq0, gpw, rv, smem, pf, rl, p.n_splits);
+  finish_split<RB, EPI, 16>(p, b, h, hg, hq0, gpw, rv, smem, pf, rl, p.n_splits);
 }
 
 // ---------------------------------------------------------------------------

@@ -19,6 +19,16 @@ __device__ __forceinline__ int thread_id() {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
+// A workgroup barrier for data exchanged through LDS by ds_read/ds_write: the
+// wave's LDS accesses complete (lgkmcnt), then all waves meet. Unlike
+// __syncthreads() it does not wait for outstanding vector-memory loads, so
+// loads issued before it (including direct-to-LDS loads into a region the
+// barrier does not guard) stay in flight. The memory clobber keeps the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // ---------------------------------------------------------------------------
 // shared prologue: q~ = (q P_K) * scale * log2(e) for the workgroup's heads
 // ---------------------------------------------------------------------------
@@ -34,11 +44,18 @@ __device__ __forceinline__ void project_query(const DecodeParams& p, int b, int 
   const int tid = thread_id(), lane = tid & 63, wave = tid >> 6;
   const int d = p.d;
   if (p.qt_in) {   // folded mode: q~ [B][Hq][qt_stride] given in latent space
-    for (int idx = tid; idx < kHeadsPerWg * RB; idx += blockDim.x) {
-      const int g = idx / RB, j = idx - g * RB;
-      qt_lds[idx] = (g < gpw && j < rk) ? p.qt_in[((size_t)b * p.Hq + hq0 + g) * p.qt_stride + j] * p.scale_log2 : 0.f;
+    constexpr int kPer = (kHeadsPerWg * RB + 255) / 256;   // values per thread (256 threads)
+    float v[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int idx = tid + 256 * k, g = idx / RB, j = idx - g * RB;
+      v[k] = (idx < kHeadsPerWg * RB && g < gpw && j < rk)
+                 ? p.qt_in[((size_t)b * p.Hq + hq0 + g) * p.qt_stride + j] * p.scale_log2 : 0.f;
     }
-    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+      if (tid + 256 * k < kHeadsPerWg * RB) qt_lds[tid + 256 * k] = v[k];
+    lds_barrier();
     return;
   }
   constexpr int NH = (RB + 63) / 64;      // 64-column halves of P
@@ -47,21 +64,35 @@ __device__ __forceinline__ void project_query(const DecodeParams& p, int b, int 
   const int isub = lane >> 4, m = lane & 15;
   const int rows_per_wave = d >> 2, rpl = d >> 4;
   float4 pr[RPL];
+  // lanes past the rank load a valid address and mask the value (no divergent branch)
   auto load_half = [&](int hf) {
     const int col = 64 * hf + 4 * m;
+    const bool ok = col < rk;
+    const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int e = 0; e < RPL; ++e) {
       const int i = wave * rows_per_wave + isub + 4 * e;
-      pr[e] = (e < rpl && col < rk) ? *reinterpret_cast<const float4*>(P + (size_t)i * rk + col)
-                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+      if (e < rpl) {
+        const float4 v = *reinterpret_cast<const float4*>(P + (size_t)i * rk + (ok ? col : 0));
+        pr[e] = ok ? v : zero;
+      } else {
+        pr[e] = zero;
+      }
     }
   };
   load_half(0);   // basis loads in flight together with the query rows
-  for (int idx = tid; idx < kHeadsPerWg * d; idx += blockDim.x) {
-    const int g = idx / d, i = idx - g * d;
-    q_lds[idx] = (g < gpw) ? p.q[((size_t)b * p.Hq + hq0 + g) * d + i] : 0.f;
+  float qv[4];     // kHeadsPerWg * d <= 1024 values, 256 threads; invalid ones read row 0 and are masked
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int idx = tid + 256 * k, g = idx / d, i = idx - g * d;
+    const bool ok = idx < kHeadsPerWg * d && g < gpw;
+    const float v = p.q[((size_t)b * p.Hq + hq0) * d + (ok ? g * d + i : 0)];
+    qv[k] = ok ? v : 0.f;
   }
-  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (tid + 256 * k < kHeadsPerWg * d) q_lds[tid + 256 * k] = qv[k];
+  lds_barrier();
 #pragma unroll
   for (int hf = 0; hf < NH; ++hf) {
     const int col = 64 * hf + 4 * m;
@@ -88,12 +119,7 @@ __device__ __forceinline__ void project_query(const DecodeParams& p, int b, int 
 #pragma unroll
     for (int g = 0; g < 4; ++g)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        float v = part[g][jj];
-        v += __shfl_xor(v, 16, 64);
-        v += __shfl_xor(v, 32, 64);
-        part[g][jj] = v;
-      }
+      for (int jj = 0; jj < 4; ++jj) part[g][jj] = sum_over_rows(part[g][jj]);
     if (isub == 0 && col < RB) {
 #pragma unroll
       for (int g = 0; g < 4; ++g)
@@ -101,7 +127,7 @@ __device__ __forceinline__ void project_query(const DecodeParams& p, int b, int 
             make_float4(part[g][0], part[g][1], part[g][2], part[g][3]);
     }
   }
-  __syncthreads();
+  lds_barrier();
   for (int idx = tid; idx < kHeadsPerWg * RB; idx += blockDim.x) {
     const int g = idx / RB, j = idx - g * RB;
     float v = 0.f;
@@ -110,7 +136,7 @@ __device__ __forceinline__ void project_query(const DecodeParams& p, int b, int 
            red[(3 * 4 + g) * RB + j]) * p.scale_log2;
     qt_lds[idx] = v;   // zero rows for heads beyond gpw and channels beyond rk
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // Split records are written and read with agent-scope relaxed atomic

@@ -246,8 +246,7 @@ __global__ __launch_bounds__(256) void decode_split_joint(DecodeParams p) {
         sc[blk][i] = valid ? sc[blk][i] : kNegInf;
         mx = fmaxf(mx, sc[blk][i]);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = max_over_rows(mx);
     const float m_new = fmaxf(m, mx);
     const float m_use = (m_new == kNegInf) ? 0.f : m_new;
     const float alpha = q_ok ? fast_exp2(m - m_use) : 1.f;
@@ -309,8 +308,7 @@ __global__ __launch_bounds__(256) void decode_split_joint(DecodeParams p) {
   // ---- merge the token streams of each row tile: the waves of streams > 0 leave
   // their state in LDS, the stream-0 wave adds it to its own and writes one record
   // per (query head, split). Accumulator rows are query heads 4 q4 + i.
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
+  l = sum_over_rows(l);
   if (q4 == 0) {
     wm[wave * 16 + n16] = m;
     wl[wave * 16 + n16] = l;

@@ -216,6 +216,23 @@ __device__ __forceinline__ float row16_allreduce(float x) {
   return x;
 }
 
+// Reductions over the lanes n, n + 16, n + 32, n + 48 (the four 16-lane rows of a wave)
+// with gfx950's row swaps: after swapping rows 1 <-> 0 and 3 <-> 2 of two copies of x,
+// the two results hold, lane by lane, x and its partner 16 lanes away; likewise for the
+// 32-lane halves.
+__device__ __forceinline__ float max_over_rows(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_over_rows(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // All-reduce over the 64 lanes of a wave (butterfly through ds_swizzle/bpermute).
 template <bool kMax>
 __device__ __forceinline__ float wave_allreduce(float x) {
