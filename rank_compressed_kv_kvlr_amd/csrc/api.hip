@@ -101,11 +101,17 @@ int token_fixed_cost() {
   if (v < 0) return kTokenFixedCost;
   return v > 4096 ? 4096 : v;
 }
-int token_cost(const kvlr_desc* d, int h) { return token_fixed_cost() + d->r_k[h] + d->r_v[h]; }
+// With one segment per workgroup the steps of a segment are bound by memory latency
+// more than by its bytes: a token costs nearly the same at every rank (on ragged
+// per-head ranks 16..96: 14.6 us per 1000 tokens at r_k + r_v = 48, 16.6 at 176).
+constexpr int kTokenFixedCostOneSegment = 896;
+int token_cost(const kvlr_desc* d, int h, bool one_segment = false) {
+  return (one_segment ? kTokenFixedCostOneSegment : token_fixed_cost()) + d->r_k[h] + d->r_v[h];
+}
 
-long long row_cost_of(const kvlr_desc* d) {
+long long row_cost_of(const kvlr_desc* d, bool one_segment = false) {
   long long c = 0;
-  for (int h = 0; h < d->n_kv_heads; ++h) c += token_cost(d, h);
+  for (int h = 0; h < d->n_kv_heads; ++h) c += token_cost(d, h, one_segment);
   return c * head_groups_of(d);
 }
 
@@ -128,6 +134,17 @@ bool balanced_plan(const kvlr_desc* d, int32_t split_tokens) {
 // Workgroups of the balanced plan: one round over the device.
 int balanced_wgs(const kvlr_desc* d, int rank_bound) {
   return compute_units() * resident_wgs_per_cu(d->latent_dtype, rank_bound);
+}
+// The balanced plan's one-segment-per-workgroup form (three workgroups per CU up to
+// rank bound 96), used while the (row, KV head, head group) units are few next to
+// the workgroups: the apportionment needs about two workgroups per unit or more.
+int one_segment_wgs(int rank_bound) { return compute_units() * (rank_bound <= 96 ? 3 : 2); }
+bool one_segment_plan(const kvlr_desc* d, int rank_bound) {
+  const long long units = (long long)d->batch * d->n_kv_heads * head_groups_of(d);
+  return units * 2 <= one_segment_wgs(rank_bound) && d->batch * d->n_kv_heads <= kvlr::kApportionPairs;
+}
+int balanced_grid(const kvlr_desc* d, int rank_bound) {
+  return one_segment_plan(d, rank_bound) ? one_segment_wgs(rank_bound) : balanced_wgs(d, rank_bound);
 }
 
 // Largest key rank and its kernel bound.
@@ -259,7 +276,8 @@ size_t record_bytes_of(const kvlr_desc* d, const HeadTable& ht, int32_t split_to
   const size_t stride = ws_stride_of(ht, d->n_kv_heads);
   size_t bytes = (size_t)d->batch * d->n_q_heads * n_splits * stride * sizeof(float);
   if ((split_tokens == 0 || split_tokens == kSplitBalanced) && supports_balanced(d)) {
-    const size_t slots = (size_t)balanced_wgs(d, rank_bound) + (size_t)d->batch * d->n_kv_heads * head_groups_of(d);
+    size_t slots = (size_t)balanced_wgs(d, rank_bound) + (size_t)d->batch * d->n_kv_heads * head_groups_of(d);
+    if ((size_t)one_segment_wgs(rank_bound) > slots) slots = one_segment_wgs(rank_bound);
     const size_t bal = slots * kvlr::kHeadsPerWg * stride * sizeof(float);
     bytes = bal > bytes ? bal : bytes;
   }
@@ -331,7 +349,7 @@ KVLR_API int kvlr_decode_plan(const kvlr_desc* desc, int32_t split_tokens, int32
   if (balanced_plan(desc, split_tokens)) {   // workgroups of equal shares; no fixed split length
     int rank_bound = 0;
     check_desc(desc, nullptr, nullptr, nullptr, &rank_bound);
-    ns = balanced_wgs(desc, rank_bound);
+    ns = balanced_grid(desc, rank_bound);
     len = 0;
   }
   *n_splits = ns;
@@ -460,10 +478,11 @@ int prepare_decode(const kvlr_desc* desc, const float* q, const float* P_K, cons
   const size_t rec_bytes = record_bytes_of(desc, p->ht, split_tokens, ns, *rank_bound);
   const size_t need = cbytes + rec_bytes + qt_bytes_of(desc);
   p->balanced = single_launch && balanced_plan(desc, split_tokens);
-  p->n_wg = p->balanced ? balanced_wgs(desc, *rank_bound) : 0;
-  p->row_cost = p->balanced ? (int)row_cost_of(desc) : 0;
+  p->apportion = p->balanced && one_segment_plan(desc, *rank_bound);
+  p->n_wg = p->balanced ? balanced_grid(desc, *rank_bound) : 0;
+  p->row_cost = p->balanced ? (int)row_cost_of(desc, p->apportion) : 0;
   for (int h = 0, c = 0; h < desc->n_kv_heads; ++h) {
-    p->ht.cost[h] = token_cost(desc, h);
+    p->ht.cost[h] = token_cost(desc, h, p->apportion);
     p->ht.cost_pre[h] = c;
     c += p->ht.cost[h];
   }

@@ -603,6 +603,92 @@ __device__ __forceinline__ long long shfl_up64(long long x, int d) {
 // device and depends on nothing else, so every run gives the same result.
 constexpr int kBalancedTokens = 128;
 
+// One segment of the balanced plan: a token range of unit (b, h, hg), its record
+// index k among the unit's n_rec records, and the record slot of the unit's first.
+struct Segment {
+  int b, h, hg, t_begin, t_end, k, n_rec;
+  size_t slot;
+};
+
+// The balanced plan with one segment per workgroup (used when the units are few next
+// to the workgroups): unit (b, h, hg) is cut into k(b, h) segments of equal token
+// counts, with k(b, h) = ceil(T_b cost[h] / lam), at most one per kBalancedTokens
+// tokens, and lam the least work per segment (found by bisection) for which all the
+// segments number at most gridDim.x. Workgroup w takes segment w in (b, h, hg, j)
+// order and leaves its record in slot w; the segments of a unit are consecutive, so
+// the unit's records are too, and its last arrival merges them. No workgroup pays for
+// two segments' prologues and tails. Every wave computes the plan with the same float
+// operations from the same lengths, so all workgroups agree on it.
+template <typename LenOf>
+__device__ __forceinline__ bool apportioned_segment(const DecodeParams& p, const LenOf& len_of, Segment& sg) {
+  constexpr int R = kApportionPairs / 64;   // (row, KV head) pairs per lane
+  const int lane = thread_id() & 63, w = blockIdx.x;
+  const int Hkv = p.Hkv, n_hg = p.n_head_groups, n_pairs = p.B * Hkv;
+  float work[R];   // T_b cost[h] of pair i = lane + 64 r
+  float kmax[R];
+  int tlen[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int i = lane + 64 * r;
+    const int bi = i / Hkv, hi = i - bi * Hkv;
+    tlen[r] = i < n_pairs ? (int)len_of(bi) : 0;
+    work[r] = (float)tlen[r] * (float)p.ht.cost[i < n_pairs ? hi : 0];
+    kmax[r] = (float)((tlen[r] + kBalancedTokens - 1) / kBalancedTokens);
+  }
+  auto segs = [&](int r, float inv_lam) { return fminf(ceilf(work[r] * inv_lam), kmax[r]); };
+  // segments of the units of pairs below i_end (wave-uniform; exact below 2^24)
+  const int n_r = (n_pairs + 63) >> 6;   // chunks in use
+  auto count = [&](float inv_lam, int i_end) {
+    float n = 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (r < n_r && lane + 64 * r < i_end) n += segs(r, inv_lam);
+    return sum_over_rows(row16_allreduce<false>(n)) * (float)n_hg;
+  };
+  // the bracket: all the work W over gridDim.x segments is too little per segment; W per
+  // segment gives each non-empty unit one segment (two where rounding lifts its share
+  // past 1), at most gridDim.x in all
+  float wsum = 0.f;
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    if (r < n_r) wsum += work[r];
+  const float W = sum_over_rows(row16_allreduce<false>(wsum)) * (float)n_hg;
+  const float Pf = (float)gridDim.x;
+  float lo = W / Pf, hi = W;
+  for (int it = 0; it < 16; ++it) {   // the ratio hi / lo <= gridDim.x shrinks to its 2^-16 power
+    const float mid = sqrtf(lo * hi);
+    if (count(1.f / mid, n_pairs) <= Pf) hi = mid; else lo = mid;
+  }
+  const float inv_lam = 1.f / hi;
+  if (w >= (int)count(inv_lam, n_pairs)) return false;
+  // the pair holding segment w: the last i with count(i) <= w
+  int ilo = 0, ihi = n_pairs;
+  while (ihi - ilo > 1) {
+    const int mid = (ilo + ihi) >> 1;
+    if ((int)count(inv_lam, mid) <= w) ilo = mid; else ihi = mid;
+  }
+  const int E = (int)count(inv_lam, ilo);
+  float kl = 0.f;
+  int tl = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    if (r == (ilo >> 6)) {
+      kl = segs(r, inv_lam);
+      tl = tlen[r];
+    }
+  const int k = (int)readlane_f(kl, ilo & 63);
+  const long long T = __builtin_amdgcn_readlane(tl, ilo & 63);
+  const int b = ilo / Hkv, h = ilo - b * Hkv;
+  const int off = w - E, hg = off / k, j = off - hg * k;
+  auto tok = [&](int x) {   // start of segment x of the unit, on a kBalancedTokens boundary
+    const long long t = ((long long)x * T / k + kBalancedTokens - 1) / kBalancedTokens * kBalancedTokens;
+    return (int)min(t, T);
+  };
+  sg = Segment{b, h, hg, tok(j), tok(j + 1), j, k, (size_t)(E + hg * k)};
+  return true;
+}
+
+
 template <int RB, int TT>
 __device__ __forceinline__ void decode_balanced(const DecodeParams& p, float* smem) {
   const int tid = thread_id(), lane = tid & 63;
@@ -746,6 +832,37 @@ template <int RB, int TT>
 __global__ __launch_bounds__(256) void decode_balanced_bf16(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) float smem[kTailLds];
   decode_balanced<RB, TT>(p, smem);
+}
+
+// Balanced plan with one segment per workgroup (see apportioned_segment); three
+// workgroups per CU up to rank bound 96.
+template <int RB, int TT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB <= 96 ? 3 : 2)))
+void decode_apportioned_bf16(DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) float smem[kTailLds];
+  const int B = p.B, tid = thread_id();
+  auto len_of = [&](int bi) { return bi < B ? (long long)min(max(p.seq_lens[bi], 0), p.cap) : 0ll; };
+  // every length this workgroup needs is loaded at once (one memory round trip): its
+  // zero-row duty (rows without tokens get zero outputs; B <= gridDim.x / 2 here) and
+  // the plan's pairs
+  const bool zero_duty = (int)blockIdx.x < B;
+  const long long Tz = zero_duty ? len_of(blockIdx.x) : 1;
+  // the segment passes through LDS: its values are then re-read where needed instead of
+  // being held in scalar registers across the segment body (which would spill them)
+  __shared__ Segment st;
+  Segment sg;
+  const bool has = apportioned_segment(p, len_of, sg);
+  if (zero_duty && Tz == 0) {
+    const int n = p.Hq * p.out_stride;
+    float* o = p.out + (size_t)blockIdx.x * n;
+    for (int i = tid; i < n; i += blockDim.x) o[i] = 0.f;
+  }
+  if (!has) return;
+  if (tid == 0) st = sg;
+  __syncthreads();
+  const RecLayout rl{p.ws + st.slot * kHeadsPerWg * p.ws_stride, (size_t)kHeadsPerWg * p.ws_stride,
+                     (size_t)p.ws_stride};
+  bf16_segment<RB, TT>(p, st.b, st.h, st.hg, st.t_begin, st.t_end, rl, st.k, st.n_rec, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -1469,11 +1586,15 @@ hipError_t launch_decode(const DecodeParams& p, int latent_dtype, int rank_bound
   if (latent_bf16) {
     if (p.balanced) {   // one workgroup per share of the balanced plan
       const dim3 grid_b(p.n_wg);
+#define KVLR_BAL_LAUNCH(RB)                                                                   \
+  if (p.apportion) hipLaunchKernelGGL((decode_apportioned_bf16<RB, 32>), grid_b, block, 0, stream, p); \
+  else hipLaunchKernelGGL((decode_balanced_bf16<RB, 32>), grid_b, block, 0, stream, p)
       switch (rank_bound) {   // 32-token steps (64 would leave one wave per SIMD at bound 96)
-        case 32: hipLaunchKernelGGL((decode_balanced_bf16<32, 32>), grid_b, block, 0, stream, p); break;
-        case 64: hipLaunchKernelGGL((decode_balanced_bf16<64, 32>), grid_b, block, 0, stream, p); break;
-        case 96: hipLaunchKernelGGL((decode_balanced_bf16<96, 32>), grid_b, block, 0, stream, p); break;
-        default: hipLaunchKernelGGL((decode_balanced_bf16<128, 32>), grid_b, block, 0, stream, p); break;
+        case 32: KVLR_BAL_LAUNCH(32); break;
+        case 64: KVLR_BAL_LAUNCH(64); break;
+        case 96: KVLR_BAL_LAUNCH(96); break;
+        default: KVLR_BAL_LAUNCH(128); break;
+#undef KVLR_BAL_LAUNCH
       }
     } else if (tile == 32) {
       switch (rank_bound) {

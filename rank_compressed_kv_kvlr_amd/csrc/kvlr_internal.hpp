@@ -14,6 +14,7 @@ constexpr int kMaxRank = 128;     // rank bound of the decode kernels' register 
 constexpr int kHeadsPerWg = 4;    // query heads sharing one KV head handled by one workgroup
 constexpr int kTile = 64;         // tokens per wave iteration of the fp32 decode kernel; splits are multiples of it
 constexpr int kWaves = 4;         // waves per decode workgroup
+constexpr int kApportionPairs = 512;   // balanced plan, one segment per workgroup: at most this many (row, KV head) pairs
 
 // Per-KV-head tables: ranks and prefix sums of ranks (latent and basis offsets).
 struct HeadTable {
@@ -43,6 +44,7 @@ struct DecodeParams {
   float* out;            // single-launch merge: [B][Hq][d]
   int fuse;              // 1: the last split workgroup of a group merges and back-projects
   int balanced;          // bf16 latents: balanced plan, n_wg workgroups with equal shares of the work
+  int apportion;         // balanced plan: one segment per workgroup (see decode_balanced)
   int n_wg;
   int row_cost;          // balanced plan: n_head_groups * sum_h cost[h], work per token of a batch row
   int out_latent;        // 1: write the normalised latent output o_lat [B][Hq][out_stride] (no P_V^T)
