@@ -22,12 +22,13 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # Sources of libkvlr.so with their extra flags. The joint-value decode keeps its
-# MFMA accumulators in ordinary VGPRs (its softmax rescales them between MFMAs).
+# MFMA accumulators in ordinary VGPRs (its softmax rescales them between MFMAs), and
+# so does the compression (its stores convert them straight from VGPRs).
 SOURCES = {
     "api.hip": [],
     "decode.hip": [],
     "decode_joint.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-    "compress.hip": [],
+    "compress.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 
 

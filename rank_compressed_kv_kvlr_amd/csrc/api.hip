@@ -407,6 +407,7 @@ KVLR_API int kvlr_prefill_compress(const kvlr_desc* desc, const void* K, const v
   p.out_q43 = desc->latent_dtype == KVLR_Q43;
   p.joint_v = desc->value_mode == KVLR_VALUES_JOINT;
   p.only_kind = -1;
+  p.n_cu = compute_units();
   return hip_status(kvlr::launch_compress(p, static_cast<hipStream_t>(stream)));
 }
 

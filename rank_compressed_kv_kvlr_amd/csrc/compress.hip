@@ -18,6 +18,11 @@
 // rows), so that each lane ends with 4 consecutive tokens of one latent
 // channel: the decode kernels' value-product operand order, stored as one
 // 8-byte piece.
+// A workgroup owns one token range of one (batch row, KV head, kind); the
+// host sizes the ranges by bytes per token so that workgroups carry about the
+// same work, about eight rounds of resident workgroups in all. Each wave keeps
+// the next 64-row tile in flight (buffer loads) while it multiplies the
+// current one, and stores through a buffer resource with wave-uniform offsets.
 //
 // fp32 inputs, ranks that are not whole 16-channel tiles, 4/3-bit latents and
 // joint value latents use a plain VALU kernel; append uses one workgroup per
@@ -27,10 +32,16 @@
 // are quantised from the fp32 latents of a row by one thread per row; the
 // block-wise Hadamard rotation is already folded into the bases it receives
 // (hadamard_fold below, run once per set of bases).
+#include <algorithm>
+#include <cmath>
+
 #include "kvlr_internal.hpp"
 
 namespace kvlr {
 namespace {
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));   // one v_cvt_pk_bf16_f32 per pair
 
 // ---- 4/3-bit rows --------------------------------------------------------
 __device__ __forceinline__ uint32_t half_bits(_Float16 h) { return (uint32_t)__builtin_bit_cast(uint16_t, h); }
@@ -149,139 +160,292 @@ __global__ __launch_bounds__(256) void hadamard_fold(const float* __restrict__ i
 
 constexpr int kCompressWaves = 4;
 constexpr int kTokensPerWave = 64;        // 4 MFMA column tiles of 16 tokens
-constexpr int kWaveIters = 4;             // tiles per wave per workgroup
-constexpr int kTokensPerWg = kCompressWaves * kTokensPerWave * kWaveIters;   // 1024
+constexpr int kCompressGroup = kCompressWaves * kTokensPerWave;   // 256: token ranges are multiples of this
+constexpr int kCompressRounds = 8;        // workgroups per resident slot in the schedule
 
-// LDS budget for the staged basis: (r/16) * (d/32) * 64 lanes * 16 B * 2 = 4 r d bytes.
-constexpr int kStageBytes = 4 * kMaxRank * 256;   // r <= 128, d <= 256
+// One wave's 64 input rows: lane (n16, q4) holds channels 32 kb + 8 q4 + [0, 8) of
+// token tw0 + 16 nt + n16. Four lanes read 64 contiguous bytes of a row, so two loads
+// complete a 128-byte line. The buffer resource covers the workgroup's rows only:
+// rows past its end read as zeros without a memory access (their results are not
+// stored). The rows are read once: non-temporal loads.
+template <int NKB>
+__device__ __forceinline__ void compress_load(u32x4_t (&x)[4][NKB], __amdgpu_buffer_rsrc_t rs, int row_bytes, int u0,
+                                              int n16, int q4) {
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    // unsigned: offsets of rows past the range may pass 2^31 (they read nothing)
+    const uint32_t off = (uint32_t)(u0 + 16 * nt + n16) * (uint32_t)row_bytes + 16u * q4;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+      x[nt][kb] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(off + 64u * kb), 0, 2));
+  }
+}
 
-// NKB = d / 32: 32-channel input blocks (one MFMA each per 16 tokens).
-template <bool kOutBf16, int NKB>
-__global__ __launch_bounds__(256) void compress_bf16_mfma(CompressParams p) {
-  extern __shared__ __attribute__((aligned(16))) uint4 stage[];   // [mt][kb][lane] hi, then lo
-  const int kind = p.only_kind >= 0 ? p.only_kind : (int)(blockIdx.y & 1);   // 0 keys, 1 values
-  const int h = p.only_kind >= 0 ? (int)blockIdx.y : (int)(blockIdx.y >> 1);
-  const int b = blockIdx.z;
-  const int d = p.d;
-  const int r = kind ? p.ht.rv[h] : p.ht.rk[h];
-  const int r_pre = kind ? p.ht.rv_pre[h] : p.ht.rk_pre[h];
-  const float* P = (kind ? p.pv : p.pk) + (size_t)d * r_pre;
-  const uint16_t* X = static_cast<const uint16_t*>(kind ? p.x_v : p.x_k);
-  const int n_mt = r >> 4, dq = d >> 2;
-  constexpr int n_kb = NKB;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// Where a workgroup's whole tiles store their latents: a buffer resource from the
+// 16-row block (bf16 layouts) or the row (fp32) of its first token, and each lane's
+// byte offset in it, for the paired 32-channel part and for a trailing 16-channel
+// tile (bf16 layouts of ranks that are odd multiples of 16). The rest of an offset is
+// wave-uniform: the tile, the 16-row block and the channel tile (see compress_tile).
+struct LatentStoreMap {
+  __amdgpu_buffer_rsrc_t rs;
+  int lane_pair;
+  int lane_tail;
+};
+
+template <int KIND, bool kOutBf16>
+__device__ __forceinline__ LatentStoreMap latent_store_map(const CompressParams& p, void* lat, size_t lat_base,
+                                                           int r, int t0, int t1, int lane) {
   const int n16 = lane & 15, q4 = lane >> 4;
+  LatentStoreMap m;
+  if (!kOutBf16) {   // [row][r] fp32: lane holds channels 4 q4 .. of token n16
+    m.rs = __builtin_amdgcn_make_buffer_rsrc(static_cast<float*>(lat) + lat_base + (size_t)(p.start + t0) * r, (short)0,
+                                             (t1 - t0) * r * 4, 0x00020000);
+    m.lane_pair = m.lane_tail = 4 * (n16 * r + 4 * q4);
+    return m;
+  }
+  const int r16 = 16 * r;   // elements of a 16-row block
+  m.rs = __builtin_amdgcn_make_buffer_rsrc(
+      static_cast<uint16_t*>(lat) + lat_base + (size_t)((p.start >> 4) + (t0 >> 4)) * r16, (short)0,
+      ((t1 - t0) / 16 + 2) * r16 * 2, 0x00020000);
+  const int s15 = p.start & 15;
+  if (KIND == 0) {   // keys: lane holds 4 channels of token n16 (row (start + n16) mod 16 of its block)
+    const int bl = (s15 + n16) >> 4, n = (s15 + n16) & 15;
+    m.lane_pair = 2 * (bl * r16 + (q4 >> 1) * 128 + n * 8 + 4 * (q4 & 1));
+    m.lane_tail = 2 * (bl * r16 + q4 * 64 + n * 4);
+  } else {           // values: lane holds tokens 4 q4 .. 4 q4 + 3 of channel n16 (start is a multiple of 4)
+    const int bl = (s15 + 4 * q4) >> 4, q = ((s15 + 4 * q4) & 15) >> 2;
+    m.lane_pair = 2 * (bl * r16 + q * 128 + n16 * 8);
+    m.lane_tail = 2 * (bl * r16 + q * 64 + n16 * 4);
+  }
+  return m;
+}
 
-  // ---- stage P^T operands: entry (mt, kb, lane) holds P[q*dq + 8kb + e][16mt + lane%16], e < 8
-  const int n_entries = n_mt * n_kb * 64;
+// Latents of one wave's 64 rows, 16 channels (one A tile) at a time, stored as they
+// are formed. WHOLE: every row is below t_end and (value latents) the first row is a
+// multiple of 4, so every store is a whole piece; those go through the store map with
+// wave-uniform offsets, the others element by element.
+template <int KIND, bool kOutBf16, int NKB, bool WHOLE>
+__device__ __forceinline__ void compress_tile(const CompressParams& p, const u32x4_t (&xin)[4][NKB],
+                                              const uint4* st_hi, const uint4* st_lo, int n_mt, int r, int tw0,
+                                              int t0, int t_end, void* lat, size_t lat_base,
+                                              const LatentStoreMap& sm, int lane) {
+  const int n16 = lane & 15, q4 = lane >> 4;
+  // The rows pass through an empty asm statement, so that the wait for them comes here,
+  // counted exactly (the next tile's loads and earlier stores stay in flight), and not
+  // as a wait for every outstanding access before the channel-tile loop.
+  u32x4_t x[4][NKB];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      x[nt][kb] = xin[nt][kb];
+      asm volatile("" : "+v"(x[nt][kb]));
+    }
+  constexpr bool v_tiled = kOutBf16 && KIND == 1;   // bf16 values: value-product operand order
+  constexpr bool k_tiled = kOutBf16 && KIND == 0;   // bf16 keys: MFMA operand order
+  const int np = r >> 5;                            // paired 32-channel groups of the bf16 layouts
+  const int blk0 = (tw0 - t0) >> 4;                 // 16-row block of the tile in the store map
+  for (int mt = 0; mt < n_mt; ++mt) {
+    f32x4_t acc[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[nt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const int e = (mt * NKB + kb) * 64 + lane;
+      const bf16x8_t ahi = __builtin_bit_cast(bf16x8_t, st_hi[e]);
+      const bf16x8_t alo = __builtin_bit_cast(bf16x8_t, st_lo[e]);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const bf16x8_t xb = __builtin_bit_cast(bf16x8_t, x[nt][kb]);
+        if (v_tiled) {   // transposed product: lane ends with 4 consecutive tokens of one channel
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb, ahi, acc[nt], 0, 0, 0);
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb, alo, acc[nt], 0, 0, 0);
+        } else {
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, xb, acc[nt], 0, 0, 0);
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, xb, acc[nt], 0, 0, 0);
+        }
+      }
+    }
+    if (WHOLE) {
+      // byte offset = lane part + tile/block part + channel-tile part (wave-uniform)
+      const bool tail = kOutBf16 && mt >= 2 * np;
+      const int lane_off = tail ? sm.lane_tail : sm.lane_pair;
+      int uni;   // bytes, for nt = 0
+      if (!kOutBf16)
+        uni = 4 * ((tw0 - t0) * r + 16 * mt);
+      else if (k_tiled)
+        uni = 2 * (blk0 * 16 * r + 256 * mt);
+      else
+        uni = 2 * (blk0 * 16 * r + (tail ? 512 * np : (mt >> 1) * 512 + (mt & 1) * 4));
+      const int nt_step = kOutBf16 ? 2 * 16 * r : 4 * 16 * r;   // 16 rows further
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int soff = __builtin_amdgcn_readfirstlane(uni + nt * nt_step);
+        if (kOutBf16) {
+          const bf16x2_t lo2 = __builtin_convertvector((f32x2_t){acc[nt][0], acc[nt][1]}, bf16x2_t);
+          const bf16x2_t hi2 = __builtin_convertvector((f32x2_t){acc[nt][2], acc[nt][3]}, bf16x2_t);
+          const u32x2_t v = {__builtin_bit_cast(uint32_t, lo2), __builtin_bit_cast(uint32_t, hi2)};
+          __builtin_amdgcn_raw_buffer_store_b64(v, sm.rs, lane_off, soff, 0);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc[nt]), sm.rs, lane_off, soff, 0);
+        }
+      }
+      continue;
+    }
+    if (v_tiled) {
+      // lane holds tokens tw0 + 16nt + 4q4 + i (i < 4) of latent channel 16mt + n16
+      uint16_t* V = static_cast<uint16_t*>(lat) + lat_base;
+      const int j = 16 * mt + n16;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int t = tw0 + 16 * nt + 4 * q4;
+        const int row = p.start + t;
+        if (t + 3 < t_end && (row & 3) == 0) {
+          const uint32_t w0 = (uint32_t)f32_to_bf16_bits(acc[nt][0]) | ((uint32_t)f32_to_bf16_bits(acc[nt][1]) << 16);
+          const uint32_t w1 = (uint32_t)f32_to_bf16_bits(acc[nt][2]) | ((uint32_t)f32_to_bf16_bits(acc[nt][3]) << 16);
+          *reinterpret_cast<uint2*>(V + v_joint_offset(row, j, r)) = make_uint2(w0, w1);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (t + i < t_end) V[v_joint_offset(row + i, j, r)] = f32_to_bf16_bits(acc[nt][i]);
+        }
+      }
+      continue;
+    }
+    // lane holds latent channels 16mt + 4q4 + i (i < 4) of token tw0 + 16nt + n16
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int t = tw0 + 16 * nt + n16;
+      if (t < t_end) {
+        const int j0 = 16 * mt + 4 * q4;   // 4 consecutive channels stay contiguous in both layouts
+        const size_t off = lat_base + (k_tiled ? k_tiled_offset(p.start + t, j0, r) : (size_t)(p.start + t) * r + j0);
+        if (kOutBf16) {
+          const uint32_t w0 = (uint32_t)f32_to_bf16_bits(acc[nt][0]) | ((uint32_t)f32_to_bf16_bits(acc[nt][1]) << 16);
+          const uint32_t w1 = (uint32_t)f32_to_bf16_bits(acc[nt][2]) | ((uint32_t)f32_to_bf16_bits(acc[nt][3]) << 16);
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(lat) + off) = make_uint2(w0, w1);
+        } else {
+          *reinterpret_cast<float4*>(static_cast<float*>(lat) + off) =
+              make_float4(acc[nt][0], acc[nt][1], acc[nt][2], acc[nt][3]);
+        }
+      }
+    }
+  }
+}
+
+// Tokens [t0, t1) of one (batch row, KV head, kind): the basis is staged once, then
+// wave w takes the 64-row tiles t0 + 64 (4k + w).
+template <int KIND, bool kOutBf16, int NKB>
+__device__ __forceinline__ void compress_range(const CompressParams& p, int h, int b, int t0, int t1, uint4* stage) {
+  const int d = 32 * NKB;
+  const int r = KIND ? p.ht.rv[h] : p.ht.rk[h];
+  const int r_pre = KIND ? p.ht.rv_pre[h] : p.ht.rk_pre[h];
+  const float* P = (KIND ? p.pv : p.pk) + (size_t)d * r_pre;
+  const uint16_t* X = static_cast<const uint16_t*>(KIND ? p.x_v : p.x_k);
+  void* lat = KIND ? p.lat_v : p.lat_k;
+  const int n_mt = r >> 4;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: tile counts and loops stay scalar
+  const int n16 = lane & 15, q4 = lane >> 4;
+  const size_t row_stride = (size_t)p.Hkv * d;   // elements between consecutive tokens
+  const int row_bytes = (int)(row_stride * 2);
+  // rows [t0, t1) of this head (the host keeps (t1 - t0) * row_bytes below 2^31)
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(X + ((size_t)b * p.n_tok + t0) * row_stride + (size_t)h * d), (short)0,
+      (t1 - t0) * row_bytes, 0x00020000);
+  const size_t lat_base = (size_t)cap_rows_of(p.cap) * ((size_t)b * (KIND ? p.Sv : p.Sk) +
+                                                      (KIND ? p.ht.sv_pre[h] : p.ht.sk_pre[h]));
+  auto tile_u = [&](int k) { return (k * kCompressWaves + wave) * kTokensPerWave; };   // offset from t0
+  const int span = t1 - t0;
+  const int n_all = span > tile_u(0) ? (span - tile_u(0) + kCompressGroup - 1) / kCompressGroup : 0;
+  const int n_full = span >= tile_u(0) + kTokensPerWave ? (span - tile_u(0) - kTokensPerWave) / kCompressGroup + 1 : 0;
+
+  // the first tile's rows are in flight while the basis is staged
+  u32x4_t xa[4][NKB];
+  compress_load<NKB>(xa, rs, row_bytes, tile_u(0), n16, q4);
+
+  // ---- stage P^T operands: entry (mt, kb, lane) holds P[32kb + 8(lane/16) + e][16mt + lane%16], e < 8,
+  // as a high and a low bf16 part. A thread reads an 8-row x 4-column block of P (8 rows of
+  // 16 bytes, consecutive threads on consecutive columns) and writes the 4 entries it holds.
+  const int n_entries = n_mt * NKB * 64;
   uint4* st_hi = stage;
   uint4* st_lo = stage + n_entries;
-  for (int idx = tid; idx < n_entries; idx += blockDim.x) {
-    const int ln = idx & 63;
-    const int kb = (idx >> 6) % n_kb;
-    const int mt = (idx >> 6) / n_kb;
-    const int col = 16 * mt + (ln & 15);
-    const int row0 = (ln >> 4) * dq + 8 * kb;
-    uint32_t hi[4], lo[4];
+  const int n_cq = r >> 2;              // column quads
+  const int n_units = n_cq * (d >> 3);  // (8-row group, column quad) blocks
+  for (int u = tid; u < n_units; u += 256) {
+    const int cq = u % n_cq, kg = u / n_cq;
+    float4 v[8];
 #pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const float x0 = P[(size_t)(row0 + e) * r + col];
-      const float x1 = P[(size_t)(row0 + e + 1) * r + col];
-      const uint16_t h0 = f32_to_bf16_bits(x0), h1 = f32_to_bf16_bits(x1);
-      const uint16_t l0 = f32_to_bf16_bits(x0 - bf16_bits_to_f32(h0));
-      const uint16_t l1 = f32_to_bf16_bits(x1 - bf16_bits_to_f32(h1));
-      hi[e >> 1] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-      lo[e >> 1] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+    for (int e = 0; e < 8; ++e) v[e] = *reinterpret_cast<const float4*>(P + (size_t)(8 * kg + e) * r + 4 * cq);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = 4 * cq + i;
+      const int idx = ((c >> 4) * NKB + (kg >> 2)) * 64 + (kg & 3) * 16 + (c & 15);
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const float x0 = i == 0 ? v[e].x : i == 1 ? v[e].y : i == 2 ? v[e].z : v[e].w;
+        const float x1 = i == 0 ? v[e + 1].x : i == 1 ? v[e + 1].y : i == 2 ? v[e + 1].z : v[e + 1].w;
+        const uint16_t h0 = f32_to_bf16_bits(x0), h1 = f32_to_bf16_bits(x1);
+        const uint16_t l0 = f32_to_bf16_bits(x0 - bf16_bits_to_f32(h0));
+        const uint16_t l1 = f32_to_bf16_bits(x1 - bf16_bits_to_f32(h1));
+        hi[e >> 1] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        lo[e >> 1] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+      }
+      st_hi[idx] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      st_lo[idx] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
     }
-    st_hi[idx] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-    st_lo[idx] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
   }
   __syncthreads();
 
-  const size_t row_stride = (size_t)p.Hkv * d;   // elements between consecutive tokens
-  const uint16_t* Xb = X + (size_t)b * p.n_tok * row_stride + (size_t)h * d;
-  const size_t lat_base = (size_t)cap_rows_of(p.cap) * ((size_t)b * (kind ? p.Sv : p.Sk) +
-                                                      (kind ? p.ht.sv_pre[h] : p.ht.sk_pre[h]));
-  const bool k_tiled = kOutBf16 && kind == 0;   // bf16 key latents: MFMA operand order
-  const bool v_tiled = kOutBf16 && kind == 1;   // bf16 value latents: value-product operand order
-  const int tok_wg0 = blockIdx.x * kTokensPerWg;
-
-  for (int it = 0; it < kWaveIters; ++it) {
-    const int tw0 = tok_wg0 + (it * kCompressWaves + wave) * kTokensPerWave;
-    if (tw0 >= p.n_tok) break;
-    // input rows: 4 column tiles of 16 tokens, lane covers d/4 channels
-    uint4 xin[4][NKB];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int t = min(tw0 + 16 * nt + n16, p.n_tok - 1);
-      const uint16_t* row = Xb + (size_t)t * row_stride + q4 * dq;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) xin[nt][kb] = *reinterpret_cast<const uint4*>(row + 8 * kb);
-    }
-    for (int mt = 0; mt < n_mt; ++mt) {
-      f32x4_t acc[4];
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) acc[nt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        {
-          const int e = (mt * n_kb + kb) * 64 + lane;
-          const bf16x8_t ahi = __builtin_bit_cast(bf16x8_t, st_hi[e]);
-          const bf16x8_t alo = __builtin_bit_cast(bf16x8_t, st_lo[e]);
-#pragma unroll
-          for (int nt = 0; nt < 4; ++nt) {
-            const bf16x8_t xb = __builtin_bit_cast(bf16x8_t, xin[nt][kb]);
-            if (v_tiled) {   // transposed product: lane ends with 4 consecutive tokens of one channel
-              acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb, ahi, acc[nt], 0, 0, 0);
-              acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb, alo, acc[nt], 0, 0, 0);
-            } else {
-              acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, xb, acc[nt], 0, 0, 0);
-              acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, xb, acc[nt], 0, 0, 0);
-            }
-          }
-        }
-      }
-      if (v_tiled) {
-        // lane holds tokens tw0 + 16nt + 4q4 + i (i < 4) of latent channel 16mt + n16: one
-        // 8-byte piece when the 4 tokens are whole and aligned, single values otherwise
-        uint16_t* V = static_cast<uint16_t*>(p.lat_v) + lat_base;
-        const int j = 16 * mt + n16;
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          const int t = tw0 + 16 * nt + 4 * q4;
-          const int row = p.start + t;
-          if (t + 3 < p.n_tok && (row & 3) == 0) {
-            const uint32_t w0 = (uint32_t)f32_to_bf16_bits(acc[nt][0]) | ((uint32_t)f32_to_bf16_bits(acc[nt][1]) << 16);
-            const uint32_t w1 = (uint32_t)f32_to_bf16_bits(acc[nt][2]) | ((uint32_t)f32_to_bf16_bits(acc[nt][3]) << 16);
-            *reinterpret_cast<uint2*>(V + v_joint_offset(row, j, r)) = make_uint2(w0, w1);
-          } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (t + i < p.n_tok) V[v_joint_offset(row + i, j, r)] = f32_to_bf16_bits(acc[nt][i]);
-          }
-        }
-        continue;
-      }
-      // lane holds latent channels 16mt + 4q4 + i (i < 4) of token tw0 + 16nt + n16
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int t = tw0 + 16 * nt + n16;
-        if (t < p.n_tok) {
-          const int j0 = 16 * mt + 4 * q4;   // 4 consecutive channels stay contiguous in both layouts
-          const size_t off = lat_base + (k_tiled ? k_tiled_offset(p.start + t, j0, r) : (size_t)(p.start + t) * r + j0);
-          if (kOutBf16) {
-            const uint32_t w0 = (uint32_t)f32_to_bf16_bits(acc[nt][0]) | ((uint32_t)f32_to_bf16_bits(acc[nt][1]) << 16);
-            const uint32_t w1 = (uint32_t)f32_to_bf16_bits(acc[nt][2]) | ((uint32_t)f32_to_bf16_bits(acc[nt][3]) << 16);
-            uint16_t* dst = static_cast<uint16_t*>(kind ? p.lat_v : p.lat_k) + off;
-            *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
-          } else {
-            float* dst = static_cast<float*>(kind ? p.lat_v : p.lat_k) + off;
-            *reinterpret_cast<float4*>(dst) = make_float4(acc[nt][0], acc[nt][1], acc[nt][2], acc[nt][3]);
-          }
-        }
-      }
+  const bool aligned = KIND == 0 || !kOutBf16 || (p.start & 3) == 0;   // whole 8-byte value pieces
+  const LatentStoreMap sm = latent_store_map<KIND, kOutBf16>(p, lat, lat_base, r, t0, t1, lane);
+  int k = 0;
+  if (aligned && NKB <= 4) {
+    // whole tiles in pairs: the next tile's rows load while the current one is multiplied
+    // (head_dim <= 128: two tiles of rows fit in registers at two waves per SIMD)
+    u32x4_t xb[4][NKB];
+    for (; k + 1 < n_full; k += 2) {
+      compress_load<NKB>(xb, rs, row_bytes, tile_u(k + 1), n16, q4);
+      compress_tile<KIND, kOutBf16, NKB, true>(p, xa, st_hi, st_lo, n_mt, r, t0 + tile_u(k), t0, t1, lat, lat_base,
+                                               sm, lane);
+      compress_load<NKB>(xa, rs, row_bytes, tile_u(k + 2), n16, q4);
+      compress_tile<KIND, kOutBf16, NKB, true>(p, xb, st_hi, st_lo, n_mt, r, t0 + tile_u(k + 1), t0, t1, lat,
+                                               lat_base, sm, lane);
     }
   }
+  // xa holds tile k; the rest one tile at a time
+  for (; k < n_all; ++k) {
+    if (aligned && k < n_full)
+      compress_tile<KIND, kOutBf16, NKB, true>(p, xa, st_hi, st_lo, n_mt, r, t0 + tile_u(k), t0, t1, lat, lat_base,
+                                               sm, lane);
+    else
+      compress_tile<KIND, kOutBf16, NKB, false>(p, xa, st_hi, st_lo, n_mt, r, t0 + tile_u(k), t0, t1, lat,
+                                                lat_base, sm, lane);
+    if (k + 1 < n_all) compress_load<NKB>(xa, rs, row_bytes, tile_u(k + 1), n16, q4);
+  }
+}
+
+// One workgroup per token range of a (batch row, KV head, kind) segment. Per batch row
+// the segments are ordered values (heads 0..Hkv-1), then keys; segment s has
+// sched_pre[s + 1] - sched_pre[s] workgroups of sched_chunk[s] tokens (the host sizes
+// them so that every workgroup has about the same work and all are resident at once).
+template <bool kOutBf16, int NKB>
+__global__ __launch_bounds__(256) void compress_bf16_mfma(CompressParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint4 stage[];   // [mt][kb][lane] hi, then lo
+  const int b = (int)blockIdx.x / p.sched_row;
+  const int rem = (int)blockIdx.x - b * p.sched_row;
+  int lo = 0, hi = 2 * p.Hkv;   // segment s with sched_pre[s] <= rem < sched_pre[s + 1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (p.sched_pre[mid] <= rem) lo = mid; else hi = mid;
+  }
+  const int s = lo;
+  const int t0 = (rem - p.sched_pre[s]) * p.sched_chunk[s];
+  const int t1 = min(p.n_tok, t0 + p.sched_chunk[s]);
+  if (s < p.Hkv)
+    compress_range<1, kOutBf16, NKB>(p, s, b, t0, t1, stage);
+  else
+    compress_range<0, kOutBf16, NKB>(p, s - p.Hkv, b, t0, t1, stage);
 }
 
 // Plain VALU compression (fp32 inputs, ranks that are not whole 16-channel
@@ -581,6 +745,41 @@ size_t q43_lds(const CompressParams& p, int max_r) {
   return ((size_t)q43_lat_offset(p.d) + (size_t)kValuTile * max_r) * sizeof(float);
 }
 
+// Work of the MFMA compression: per batch row, segments (values of heads 0..Hkv-1, then
+// keys; a kind that this launch does not write has none) get workgroups in proportion to
+// their bytes per token (2 d read, 2 r written, writes counted twice), about `slots` in
+// all, so that workgroups have about the same work; every workgroup takes a whole
+// number of 256-token groups, and at least one.
+void compress_schedule(CompressParams& p, int slots) {
+  const int H = p.Hkv;
+  double w[2 * kMaxKvHeads], total = 0.0;
+  for (int s = 0; s < 2 * H; ++s) {
+    const int kind = s < H ? 1 : 0, h = s < H ? s : s - H;
+    const bool on = p.only_kind < 0 || p.only_kind == kind;
+    w[s] = on ? 2.0 * p.d + 4.0 * (kind ? p.ht.rv[h] : p.ht.rk[h]) : 0.0;
+    total += w[s];
+  }
+  const double per_row = (double)slots / p.B;
+  const int groups = (p.n_tok + kCompressGroup - 1) / kCompressGroup;
+  // the rows of one workgroup stay below 2^31 bytes (32-bit buffer offsets)
+  const long long row_bytes = 2LL * p.Hkv * p.d;
+  const int max_groups = (int)std::max(1LL, ((1LL << 31) - 1) / (row_bytes * kCompressGroup));
+  p.sched_pre[0] = 0;
+  for (int s = 0; s < 2 * H; ++s) {
+    int n = 0, chunk = kCompressGroup;
+    if (w[s] > 0.0) {
+      n = std::min(groups, std::max(1, (int)std::lround(per_row * w[s] / total)));
+      int g = (groups + n - 1) / n;   // groups per workgroup
+      g = std::min(g, max_groups);
+      chunk = g * kCompressGroup;
+      n = (p.n_tok + chunk - 1) / chunk;
+    }
+    p.sched_chunk[s] = chunk;
+    p.sched_pre[s + 1] = p.sched_pre[s] + n;
+  }
+  p.sched_row = p.sched_pre[2 * H];
+}
+
 hipError_t launch_compress(const CompressParams& p_in, hipStream_t stream) {
   if (p_in.n_tok <= 0) return hipSuccess;
   int max_r = 0;
@@ -594,13 +793,10 @@ hipError_t launch_compress(const CompressParams& p_in, hipStream_t stream) {
   const int ykinds = p.joint_v ? 1 : 2;
   if (p.in_bf16 && !p.out_q43 && tiles16) {
     const size_t lds = (size_t)4 * max_r * p.d;   // hi + lo operand tiles
-    const dim3 grid((p.n_tok + kTokensPerWg - 1) / kTokensPerWg, ykinds * p.Hkv, p.B);
-#define KVLR_COMPRESS_CASE(NKB)                                                              \
-  case NKB:                                                                                  \
-    if (p.out_bf16)                                                                          \
-      hipLaunchKernelGGL((compress_bf16_mfma<true, NKB>), grid, dim3(256), lds, stream, p);  \
-    else                                                                                     \
-      hipLaunchKernelGGL((compress_bf16_mfma<false, NKB>), grid, dim3(256), lds, stream, p); \
+    const void* fn = nullptr;
+#define KVLR_COMPRESS_CASE(NKB)                                                                             \
+  case NKB:                                                                                                 \
+    fn = p.out_bf16 ? (const void*)compress_bf16_mfma<true, NKB> : (const void*)compress_bf16_mfma<false, NKB>; \
     break;
     switch (p.d / 32) {
       KVLR_COMPRESS_CASE(1)
@@ -613,6 +809,15 @@ hipError_t launch_compress(const CompressParams& p_in, hipStream_t stream) {
       default: KVLR_COMPRESS_CASE(8)
     }
 #undef KVLR_COMPRESS_CASE
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, lds) != hipSuccess || per_cu < 1) per_cu = 1;
+    // about 8 rounds of resident workgroups: measured faster than one round of long
+    // workgroups (whose waves fall into step) and than finer splits (basis staging)
+    compress_schedule(p, kCompressRounds * per_cu * max(p.n_cu, 1));
+    const dim3 grid((unsigned)(p.B * p.sched_row));
+    void* args[] = {&p};
+    const hipError_t e = hipLaunchKernel(fn, grid, dim3(256), args, lds, stream);
+    if (e != hipSuccess) return e;
   } else if (p.out_q43) {
     const dim3 grid(q43_chunks(p), ykinds * p.Hkv, p.B);
     hipLaunchKernelGGL(compress_q43, grid, dim3(256), q43_lds(p, max_r), stream, p);

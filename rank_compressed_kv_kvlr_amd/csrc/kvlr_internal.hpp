@@ -89,6 +89,13 @@ struct CompressParams {
   int in_bf16, out_bf16, out_q43;
   int only_kind;         // -1: keys and values (grid.y = 2 Hkv); 0 or 1: that kind only (grid.y = Hkv)
   int joint_v;           // values: one latent per token from all heads (grid.y = 1 for the value launch)
+  int n_cu;              // compute units of the device (the MFMA kernel's schedule fills them)
+  // MFMA kernel schedule (set by the launcher): per batch row, segment s (values of head
+  // s for s < Hkv, keys of head s - Hkv) has sched_pre[s + 1] - sched_pre[s] workgroups
+  // of sched_chunk[s] tokens; sched_row workgroups per batch row.
+  int sched_row;
+  int sched_pre[2 * kMaxKvHeads + 1];
+  int sched_chunk[2 * kMaxKvHeads];
   HeadTable ht;
 };
 
