@@ -269,8 +269,9 @@ def measure_long_context(kv, torch, np):
 
 
 def measure_32_layers(kv, torch, np):
-    """llama3_8b_32_layers: 32 back-to-back decodes (one per layer, each with its own bases and
-    ranks), timed per whole step; eager and as one captured HIP graph."""
+    """llama3_8b_32_layers: 32 independent decodes (one per layer, each with its own bases and
+    ranks), timed per whole step: as one kvlr_decode_attn_layers call (2 lanes; also 4) and as
+    one kvlr_decode_attn per layer, each eager and as one captured HIP graph."""
     from synth import LLAMA3_32_LAYERS, host
     print("[bench] workload llama3_8b_32_layers", file=sys.stderr, flush=True)
     cfg = LLAMA3_32_LAYERS
@@ -287,13 +288,25 @@ def measure_32_layers(kv, torch, np):
     def step(k=0):
         for c in layers:
             kv.decode_attn(c["desc"], c["q"], c["pk"], c["pv"], c["lk"], c["lv"], lens, out=c["o"], workspace=c["ws"])
+    entries = [dict(desc=c["desc"], q=c["q"], P_K=c["pk"], P_V=c["pv"], lat_k=c["lk"], lat_v=c["lv"],
+                    seq_lens=lens, out=c["o"], workspace=c["ws"]) for c in layers]
+
+    def one_call(lanes):
+        return lambda k=0: kv.decode_attn_layers(entries, lanes=lanes)
     nbytes = sum(cfg.B * cfg.T * int((c["rk"] + c["rv"]).sum()) * 2 for c in layers)
-    st = with_rates(np, spread(np, event_times(torch, np, step, 7, warmup=2)), nbytes, cfg.B)
-    g = _graph_of(torch, step)
-    gst = spread(np, event_times(torch, np, lambda k: g.replay(), 7, warmup=2))
-    st["graph"] = with_rates(np, gst, nbytes, cfg.B)
+    # the step as one kvlr_decode_attn_layers call over 2 lanes (layers overlap), eager and as a graph
+    st = with_rates(np, spread(np, event_times(torch, np, one_call(2), 7, warmup=2)), nbytes, cfg.B)
+    st["entry"] = "kvlr_decode_attn_layers, 2 lanes"
+    g = _graph_of(torch, one_call(2))
+    st["graph"] = with_rates(np, spread(np, event_times(torch, np, lambda k: g.replay(), 7, warmup=2)), nbytes, cfg.B)
+    st["lanes_4"] = with_rates(np, spread(np, event_times(torch, np, one_call(4), 7, warmup=2)), nbytes, cfg.B)
+    # one kvlr_decode_attn per layer on one stream, eager and as a graph
+    st["per_layer_calls"] = with_rates(np, spread(np, event_times(torch, np, step, 7, warmup=2)), nbytes, cfg.B)
+    g2 = _graph_of(torch, step)
+    st["per_layer_calls"]["graph"] = with_rates(np, spread(np, event_times(torch, np, lambda k: g2.replay(), 7,
+                                                                           warmup=2)), nbytes, cfg.B)
     st["layers"] = cfg.n_layers
-    del layers, g
+    del layers, entries, g, g2
     torch.cuda.empty_cache()
     return st
 

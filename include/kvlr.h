@@ -72,7 +72,7 @@ typedef enum kvlr_status {
                               storage granule (16 for bf16 and 4/3-bit latents, 4 for fp32 latents) */
   KVLR_ERR_DTYPE = -4,     /* unsupported dtype code */
   KVLR_ERR_WORKSPACE = -5, /* workspace NULL or smaller than kvlr_decode_workspace_bytes() */
-  KVLR_ERR_HIP = -6,       /* a kernel launch failed (hipGetLastError) */
+  KVLR_ERR_HIP = -6,       /* a kernel launch, stream or event operation failed */
   KVLR_ERR_ARG = -7,       /* other invalid argument (split_tokens, scale, start, a buffer not
                               16-byte aligned) */
   KVLR_ERR_SCRATCH = -8    /* kvlr_decode_attn_noalloc: the call needs more decode workspace than
@@ -360,6 +360,49 @@ KVLR_API int kvlr_append_decode_attn(const kvlr_desc* desc, const void* k_new, c
                                      const int32_t* pos, const float* q, const float* P_K, const float* P_V,
                                      void* lat_k, void* lat_v, const int32_t* seq_lens, float scale, float* out,
                                      void* workspace, size_t workspace_bytes, int32_t split_tokens, void* stream);
+
+/* Decode attention of several independent layers in one call. Each layer has
+ * its own bases and ranks (StiefAttention technical summary, "Mecanismo
+ * Central" item 4: ranks are allocated layer by layer under one cache budget),
+ * so a model step is one kvlr_decode_attn per layer. The result is that of
+ *   for l in 0 .. n_layers-1: kvlr_decode_attn(layers[l]..., stream);
+ * bit for bit, but the kernels of different layers may run at the same time,
+ * so that one layer's last workgroups overlap the next layers' streaming:
+ * the call forks `lanes` internal streams of the library (created once per
+ * device, default priority) from `stream` with an event, issues layer l on
+ * lane l mod lanes, and joins every lane back into `stream` with events.
+ * Work enqueued on `stream` after the call sees every layer's output; the
+ * pattern can be captured into a HIP graph.
+ *   layers    host array of n_layers kvlr_layer (read during the call only);
+ *             each entry holds the arguments of kvlr_decode_attn for its layer
+ *   n_layers  >= 0; 0 does nothing
+ *   lanes     1 .. KVLR_MAX_LANES; 1 issues every layer on `stream` itself
+ * With lanes > 1 the layers' workspaces must not overlap (KVLR_ERR_ARG
+ * otherwise), and no layer's output may overlap another layer's inputs or
+ * output. Every layer is checked before anything is enqueued: on an error
+ * nothing is launched and the first failing layer's status is returned.
+ * Calls on one device from several host threads take turns to enqueue; while
+ * a call is being captured into a graph, make no other call of this entry
+ * point on that device until the capture ends (the lanes are then part of the
+ * capture). */
+#define KVLR_MAX_LANES 4
+
+typedef struct kvlr_layer {
+  const kvlr_desc* desc;
+  const float* q;
+  const float* P_K;
+  const float* P_V;
+  const void* lat_k;
+  const void* lat_v;
+  const int32_t* seq_lens;
+  float scale;
+  float* out;
+  void* workspace;
+  size_t workspace_bytes;
+  int32_t split_tokens;
+} kvlr_layer;
+
+KVLR_API int kvlr_decode_attn_layers(const kvlr_layer* layers, int32_t n_layers, int32_t lanes, void* stream);
 
 /* kvlr_decode_attn for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.

@@ -38,6 +38,8 @@ __all__ = [
 ]
 
 F32, BF16, Q43 = 0, 1, 2
+# status codes (kvlr_status)
+OK, ERR_NULL, ERR_SHAPE, ERR_RANK, ERR_DTYPE, ERR_WORKSPACE, ERR_HIP, ERR_ARG, ERR_SCRATCH = 0, -1, -2, -3, -4, -5, -6, -7, -8
 VALUES_PER_HEAD, VALUES_JOINT = 0, 1
 SPLIT_BALANCED = -1   # split_tokens asking kvlr_decode_attn for the balanced plan
 STATIC_SCRATCH_BYTES = 16 << 20   # the library's static decode scratch (kvlr_decode_attn_noalloc)
@@ -85,6 +87,17 @@ lib.kvlr_decode_attn_latent.argtypes = [_D, _P, _P, _P, _P, ctypes.c_float, _P, 
 lib.kvlr_append_decode_attn.argtypes = [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P,
                                         ctypes.c_size_t, ctypes.c_int32, _P]
 lib.kvlr_hadamard_bases.argtypes = [_D, _P, _P, _P, _P, _P]
+
+
+class _CLayer(ctypes.Structure):
+    """kvlr_layer (kvlr.h): the arguments of kvlr_decode_attn for one layer."""
+    _fields_ = [("desc", _D), ("q", _P), ("P_K", _P), ("P_V", _P), ("lat_k", _P), ("lat_v", _P),
+                ("seq_lens", _P), ("scale", ctypes.c_float), ("out", _P), ("workspace", _P),
+                ("workspace_bytes", ctypes.c_size_t), ("split_tokens", ctypes.c_int32)]
+
+
+lib.kvlr_decode_attn_layers.argtypes = [ctypes.POINTER(_CLayer), ctypes.c_int32, ctypes.c_int32, _P]
+MAX_LANES = 4   # KVLR_MAX_LANES
 for _f in ("kvlr_cache_elems", "kvlr_decode_workspace_bytes", "kvlr_decode_plan", "kvlr_decode_counter_bytes", "kvlr_prefill_compress",
            "kvlr_append", "kvlr_decode_attn", "kvlr_decode_partials", "kvlr_decode_combine",
            "kvlr_decode_attn_latent", "kvlr_hadamard_bases", "kvlr_append_decode_attn", "kvlr_decode_attn_noalloc"):
@@ -127,6 +140,11 @@ class Desc:
     @property
     def ptr(self):
         return ctypes.byref(self._c)
+
+    @property
+    def pointer(self):
+        """A kvlr_desc* value (for structures that hold one)."""
+        return ctypes.pointer(self._c)
 
     @property
     def G(self):
@@ -351,6 +369,34 @@ def decode_attn(desc: Desc, q, P_K, P_V, lat_k, lat_v, seq_lens, scale: Optional
             ctypes.c_size_t(ws_bytes), split_tokens)
     _check(lib.kvlr_decode_attn(desc.ptr, *args, _stream()), "kvlr_decode_attn")
     return out
+
+
+def decode_attn_layers(layers: Sequence[dict], lanes: int = 2):
+    """kvlr_decode_attn_layers: one decode_attn per entry of `layers` (dicts with the keys
+    desc, q, P_K, P_V, lat_k, lat_v, seq_lens, out, workspace, and optionally scale and
+    split_tokens), whose kernels may overlap across `lanes` streams; returns the outputs."""
+    torch = _torch()
+    arr = (_CLayer * max(len(layers), 1))()
+    keep = []
+    for i, L in enumerate(layers):
+        desc = L["desc"]
+        nq = desc.batch * desc.n_q_heads * desc.head_dim
+        nk, nv = cache_elems(desc)
+        lad = _dtype_of(desc.latent_dtype)
+        ws = L["workspace"]
+        scale = L.get("scale")
+        if scale is None:
+            scale = 1.0 / math.sqrt(desc.head_dim)
+        arr[i] = _CLayer(desc.pointer, _need(L["q"], "q", torch.float32, nq),
+                         _need(L["P_K"], "P_K", torch.float32, _basis_numel(desc, "k")),
+                         _need(L["P_V"], "P_V", torch.float32, _basis_numel(desc, "v")),
+                         _need(L["lat_k"], "lat_k", lad, nk), _need(L["lat_v"], "lat_v", lad, nv),
+                         _need(L["seq_lens"], "seq_lens", torch.int32, desc.batch), scale,
+                         _need(L["out"], "out", torch.float32, nq), _need(ws, "workspace", ws.dtype),
+                         ws.numel() * ws.element_size(), int(L.get("split_tokens", 0)))
+        keep.append(desc)
+    _check(lib.kvlr_decode_attn_layers(arr, len(layers), lanes, _stream()), "kvlr_decode_attn_layers")
+    return [L["out"] for L in layers]
 
 
 def decode_attn_noalloc(desc: Desc, q, P_K, P_V, lat_k, lat_v, seq_lens, scale: Optional[float] = None,

@@ -6,11 +6,14 @@
 #include <math.h>
 #include <stdlib.h>
 
+#include <algorithm>
 #include <atomic>
 #include <initializer_list>
 #include <mutex>
 #include <stdint.h>
 #include <string.h>
+#include <utility>
+#include <vector>
 
 #include "kvlr_internal.hpp"
 
@@ -554,6 +557,66 @@ hipError_t joint_partials(const kvlr_desc* desc, kvlr::DecodeParams p, hipStream
   return kvlr::launch_decode_joint(p, rank_bound_of(rk_max), kJointBlocks, s);
 }
 
+// kvlr_decode_attn's launches for a prepared call: projection, split and merge for
+// joint bf16 values; otherwise one launch, whose last split workgroup of each group
+// merges and back-projects.
+hipError_t launch_decode_attn(const kvlr_desc* desc, kvlr::DecodeParams p, const kvlr::MergeParams& m,
+                              int rank_bound, hipStream_t s) {
+  if (joint_bf16(desc)) {
+    hipError_t e = joint_partials(desc, p, s);
+    if (e == hipSuccess) e = kvlr::launch_merge_heads(m, s);
+    return e;
+  }
+  p.fuse = 1;
+  return kvlr::launch_decode(p, desc->latent_dtype, rank_bound, decode_tile(), s);
+}
+
+// kvlr_decode_attn_layers: one prepared layer, and the library's lanes of a device
+// (streams of default priority and the events that fork and join them), made on
+// first use and kept until the process ends.
+struct PreparedLayer {
+  const kvlr_desc* desc;
+  kvlr::DecodeParams p;
+  kvlr::MergeParams m;
+  int rank_bound;
+};
+struct LaneSet {
+  bool ready = false;
+  hipStream_t s[KVLR_MAX_LANES];
+  hipEvent_t fork;
+  hipEvent_t join[KVLR_MAX_LANES];
+};
+LaneSet g_lanes[kMaxDevices];
+std::mutex g_lane_mu[kMaxDevices];   // held while a call enqueues on the device's lanes
+
+hipError_t lane_set(int dev, LaneSet** out) {
+  LaneSet& ls = g_lanes[dev];
+  if (!ls.ready) {
+    hipError_t e = hipEventCreateWithFlags(&ls.fork, hipEventDisableTiming);
+    for (int i = 0; i < KVLR_MAX_LANES && e == hipSuccess; ++i) {
+      e = hipStreamCreateWithFlags(&ls.s[i], hipStreamNonBlocking);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&ls.join[i], hipEventDisableTiming);
+    }
+    if (e != hipSuccess) return e;   // a later call tries again (what was made stays made)
+    ls.ready = true;
+  }
+  *out = &ls;
+  return hipSuccess;
+}
+
+// Whether two layers' workspaces [workspace, workspace + workspace_bytes) overlap.
+bool workspaces_overlap(const kvlr_layer* layers, int n) {
+  std::vector<std::pair<uintptr_t, uintptr_t>> r((size_t)n);
+  for (int l = 0; l < n; ++l) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(layers[l].workspace);
+    r[(size_t)l] = {a, a + layers[l].workspace_bytes};
+  }
+  std::sort(r.begin(), r.end());
+  for (int l = 1; l < n; ++l)
+    if (r[(size_t)l].first < r[(size_t)l - 1].second) return true;
+  return false;
+}
+
 }  // namespace
 
 extern "C" {
@@ -594,15 +657,53 @@ KVLR_API int kvlr_decode_attn(const kvlr_desc* desc, const float* q, const float
   const int rc = prepare_decode(desc, q, P_K, lat_k, lat_v, seq_lens, scale, P_V, out, true, true, workspace,
                                 workspace_bytes, split_tokens, &p, &m, &rank_bound, true);
   if (rc) return rc;
-  if (joint_bf16(desc)) {   // projection, split and merge launches
-    const hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = joint_partials(desc, p, s);
-    if (e == hipSuccess) e = kvlr::launch_merge_heads(m, s);
-    return hip_status(e);
+  return hip_status(launch_decode_attn(desc, p, m, rank_bound, static_cast<hipStream_t>(stream)));
+}
+
+KVLR_API int kvlr_decode_attn_layers(const kvlr_layer* layers, int32_t n_layers, int32_t lanes, void* stream) {
+  if (n_layers < 0 || lanes < 1 || lanes > KVLR_MAX_LANES) return KVLR_ERR_ARG;
+  if (n_layers == 0) return KVLR_OK;
+  if (!layers) return KVLR_ERR_NULL;
+  // every layer checked (and its parameter blocks formed) before anything is enqueued
+  std::vector<PreparedLayer> prep((size_t)n_layers);
+  for (int l = 0; l < n_layers; ++l) {
+    const kvlr_layer& L = layers[l];
+    PreparedLayer& P = prep[(size_t)l];
+    P.desc = L.desc;
+    const int rc = prepare_decode(L.desc, L.q, L.P_K, L.lat_k, L.lat_v, L.seq_lens, L.scale, L.P_V, L.out, true,
+                                  true, L.workspace, L.workspace_bytes, L.split_tokens, &P.p, &P.m, &P.rank_bound,
+                                  true);
+    if (rc) return rc;
   }
-  p.fuse = 1;   // one launch: the last split workgroup of each group merges and back-projects
-  return hip_status(kvlr::launch_decode(p, desc->latent_dtype, rank_bound, decode_tile(),
-                                        static_cast<hipStream_t>(stream)));
+  if (lanes > 1 && workspaces_overlap(layers, n_layers)) return KVLR_ERR_ARG;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (lanes == 1) {
+    for (const PreparedLayer& P : prep) {
+      const hipError_t e = launch_decode_attn(P.desc, P.p, P.m, P.rank_bound, s);
+      if (e != hipSuccess) return hip_status(e);
+    }
+    return KVLR_OK;
+  }
+  LaneSet* ls = nullptr;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KVLR_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_lane_mu[dev]);
+  if (lane_set(dev, &ls) != hipSuccess) return KVLR_ERR_HIP;
+  // fork, issue round robin, join (the joins are enqueued even after a failed launch,
+  // so that `stream` and a capture in progress stay whole)
+  hipError_t first = hipEventRecord(ls->fork, s);
+  for (int i = 0; i < lanes && first == hipSuccess; ++i) first = hipStreamWaitEvent(ls->s[i], ls->fork, 0);
+  if (first != hipSuccess) return hip_status(first);
+  for (int l = 0; l < n_layers && first == hipSuccess; ++l) {
+    const PreparedLayer& P = prep[(size_t)l];
+    first = launch_decode_attn(P.desc, P.p, P.m, P.rank_bound, ls->s[l % lanes]);
+  }
+  for (int i = 0; i < lanes; ++i) {
+    hipError_t e = hipEventRecord(ls->join[i], ls->s[i]);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, ls->join[i], 0);
+    if (first == hipSuccess) first = e;
+  }
+  return hip_status(first);
 }
 
 KVLR_API int kvlr_decode_attn_latent(const kvlr_desc* desc, const float* q_lat, const void* lat_k,

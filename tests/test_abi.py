@@ -310,3 +310,30 @@ def test_noalloc_entry_checks_on_the_host():
     assert f(small.ptr, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, float("nan"), FAKE, 0, None) == -7
     assert f(small.ptr, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, 100, None) == -7   # split not a multiple of 64
 
+
+
+def test_layers_entry_checks_on_the_host():
+    """kvlr_decode_attn_layers checks every layer, the lane count and (with more than one lane)
+    that the workspaces are disjoint before anything is enqueued."""
+    f = kv.lib.kvlr_decode_attn_layers
+    d = _desc()
+    ws = kv.decode_workspace_bytes(d, 0)
+
+    def layer(desc=d, q=FAKE, workspace=FAKE, workspace_bytes=ws, scale=0.1):
+        return kv._CLayer(desc.pointer, q, FAKE, FAKE, FAKE, FAKE, FAKE, scale, FAKE, workspace, workspace_bytes, 0)
+
+    two = (kv._CLayer * 2)(layer(), layer(workspace=FAKE.value + (1 << 24)))
+    assert f(two, 0, 2, None) == kv.OK                      # nothing to do
+    assert f(None, 0, 2, None) == kv.OK
+    assert f(None, 2, 2, None) == kv.ERR_NULL
+    assert f(two, -1, 2, None) == kv.ERR_ARG
+    assert f(two, 2, 0, None) == kv.ERR_ARG
+    assert f(two, 2, kv.MAX_LANES + 1, None) == kv.ERR_ARG
+    bad = (kv._CLayer * 2)(layer(), layer(q=None))
+    assert f(bad, 2, 2, None) == kv.ERR_NULL                # the failing layer's status
+    nan = (kv._CLayer * 2)(layer(), layer(scale=float("nan")))
+    assert f(nan, 2, 1, None) == kv.ERR_ARG
+    small = (kv._CLayer * 2)(layer(), layer(workspace_bytes=ws - 16))
+    assert f(small, 2, 2, None) == kv.ERR_WORKSPACE
+    shared = (kv._CLayer * 2)(layer(), layer(workspace=FAKE.value + ws // 2 // 256 * 256))
+    assert f(shared, 2, 2, None) == kv.ERR_ARG              # overlapping workspaces on two lanes
