@@ -32,6 +32,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_split_traffic.json")
+COMPRESS_COUNTERS = os.path.join(ROOT, "profiles", "compress_counters.json")
+COMPRESS_SRC = [os.path.join(ROOT, "rank_compressed_kv_kvlr_amd", "csrc", f) for f in ("compress.hip", "kvlr_internal.hpp")]
 # sources of the dominant kernel (decode_split_bf16): the traffic counters belong to these
 DECODE_SRC = [os.path.join(ROOT, "rank_compressed_kv_kvlr_amd", "csrc", f)
               for f in ("decode.hip", "decode_common.hpp", "kvlr_internal.hpp")]
@@ -79,6 +81,19 @@ def load_traffic():
     if t.get("decode_src_sha256_16") != source_hash(DECODE_SRC):
         return None
     return t.get("bytes_per_launch")
+
+
+def compress_counters(workload):
+    """MFMA busy share and HBM bytes of prefill compression on `workload` from rocprofv3 counters
+    (profiles/), valid only for the current compression source."""
+    try:
+        with open(COMPRESS_COUNTERS) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("compress_src_sha256_16") != source_hash(COMPRESS_SRC):
+        return None
+    return t.get("workloads", {}).get(workload)
 
 
 def _build(kv, torch, cfg, layer=0, n_rows=None, chunk=8192):
@@ -233,8 +248,9 @@ def measure_long_context(kv, torch, np):
     st["useful_TFLOPs"] = flops / (st["median_us"] * 1e-6) / 1e12
     st["mfma_useful_frac"] = st["useful_TFLOPs"] / BF16_MFMA_PEAK_TFLOPS
     st["kernel"] = "compress_bf16_mfma"
+    st["counters"] = compress_counters("long_context_128k")
     st["note"] = ("bytes: K and V read (bf16) plus latents written; flops 2 d (r_k + r_v) per token and head; "
-                  "MFMA busy share from counters in profiles/")
+                  "counters: rocprofv3 MFMA busy share and raw EA bytes per call (profiles/)")
     out["prefill"] = st
     del K, V
     ks = [gen.make("k", B, 1, t0=T + s)[:, 0].contiguous() for s in range(S)]
@@ -508,6 +524,7 @@ def main():
                 prefill = with_rates(np, spread(np, pre), nbytes, B * T)
                 prefill["useful_TFLOPs"] = flops / (prefill["median_us"] * 1e-6) / 1e12
                 prefill["mfma_useful_frac"] = prefill["useful_TFLOPs"] / BF16_MFMA_PEAK_TFLOPS
+                prefill["counters"] = compress_counters("llama3_8b_layer_32k")
             del K, V
             replicas.append((lat_k, lat_v))
         torch.cuda.synchronize()
