@@ -883,12 +883,15 @@ void decode_apportioned_bf16(DecodeParams p) {
 //    query head n and applies the tokens' block parameters:
 //      s = step_o acc_o + base_o Q_o + step_i acc_i + base_i Q_i.
 //  - Online softmax per query head in the log2 domain, as in the bf16 kernel.
-//  - Values: o_lat[head][ch] += sum_t w_t (128 + c_t,ch) on
-//    v_mfma_f32_16x16x32_bf16 over the tile's 32 tokens, with w = p step_o or
-//    p step_i (high and low bf16 parts, already the A operand in registers) and
-//    the value codes as B. Two more MFMAs against a B operand of ones give
-//    sum_t w_t (the 128 offset), and each lane keeps sum_t p_t base_t; the
-//    three are combined when the split ends.
+//  - Values: o_lat[head][ch] += sum_t w_t (1024 + c_t,ch) on
+//    v_mfma_f32_16x16x32_f16 over the tile's 32 tokens: a value code enters as
+//    the half float 1024 + c (bits 0x6400 | c, exact), and the weights
+//    w = half(half(p) step_o) or half(half(p) step_i), formed two tokens per
+//    packed multiply, are already the A operand in registers. An MFMA against a
+//    B operand of ones gives sum_t w_t (the 1024 offset), and one against the
+//    tokens' minima gives sum_t p_t base_t; the three are combined when the
+//    split ends. The weights carry half-float precision (11 bits), the scores'
+//    q~ about 16 bits (high and low bf16 parts).
 // Codes are turned into MFMA operands with a handful of bit operations: a
 // 4-bit word splits into its low and high nibbles (blocks 0 and 1) and v_perm
 // interleaves them with the exponent byte 0x43; a 24-bit 3-bit field is
