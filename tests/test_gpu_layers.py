@@ -132,3 +132,32 @@ def test_layers_workspace_overlap_rejected(gpu):
     torch.cuda.synchronize()
     for g, r in zip(got, ref):
         assert torch.equal(g, r)
+
+
+def test_layers_with_joint_and_quantised_caches(gpu):
+    """Layers whose decode takes other launches: joint bf16 values (projection, split and merge
+    kernels, q~ passed through the workspace) and 4/3-bit latents, next to a bf16 layer, over 3
+    lanes; equal to one kvlr_decode_attn per layer bit for bit."""
+    import torch
+    from synth import LLAMA3_LAYER_32K
+    from tests.test_gpu_joint import _joint_case
+    from tests.test_gpu_quant import _q43_case
+    kv = _kv()
+    cfg = LLAMA3_LAYER_32K.scaled(B=2, T=900)
+    lens = torch.from_numpy(host.lengths(cfg)).cuda()
+    q = torch.from_numpy(host.queries(cfg, 0, 0)).cuda()
+    jc = _joint_case(cfg, 128)
+    qc = _q43_case(cfg)
+    bc = build_case(cfg)
+    layers = [(jc["desc"], jc["pk"], jc["pj"], jc["lk"], jc["lv"]), (qc["desc"], qc["pk"], qc["pv"], qc["lk"], qc["lv"]),
+              (bc.desc, bc.pk, bc.pv, bc.lat_k, bc.lat_v)] * 2
+    ref = [kv.decode_attn(d, q, pk, pv, lk, lv, lens) for d, pk, pv, lk, lv in layers]
+    torch.cuda.synchronize()
+    ents = [dict(desc=d, q=q, P_K=pk, P_V=pv, lat_k=lk, lat_v=lv, seq_lens=lens,
+                 out=torch.full((cfg.B, cfg.Hq, cfg.d), float("nan"), device="cuda"), workspace=kv.alloc_workspace(d))
+            for d, pk, pv, lk, lv in layers]
+    got = kv.decode_attn_layers(ents, lanes=3)
+    torch.cuda.synchronize()
+    for i, (g, r) in enumerate(zip(got, ref)):
+        assert torch.equal(g, r), f"layer {i}"
+    say("[layers] joint, 4/3-bit and bf16 layers over 3 lanes equal the one-call results")
