@@ -591,14 +591,27 @@ std::mutex g_lane_mu[kMaxDevices];   // held while a call enqueues on the device
 
 hipError_t lane_set(int dev, LaneSet** out) {
   LaneSet& ls = g_lanes[dev];
-  if (!ls.ready) {
-    hipError_t e = hipEventCreateWithFlags(&ls.fork, hipEventDisableTiming);
-    for (int i = 0; i < KVLR_MAX_LANES && e == hipSuccess; ++i) {
-      e = hipStreamCreateWithFlags(&ls.s[i], hipStreamNonBlocking);
-      if (e == hipSuccess) e = hipEventCreateWithFlags(&ls.join[i], hipEventDisableTiming);
+  if (!ls.ready) {   // all or nothing: on a failure what was made is released, and a later call tries again
+    LaneSet t;
+    int n_streams = 0, n_joins = 0;
+    hipError_t e = hipEventCreateWithFlags(&t.fork, hipEventDisableTiming);
+    const bool forked = e == hipSuccess;
+    while (e == hipSuccess && n_streams < KVLR_MAX_LANES) {
+      e = hipStreamCreateWithFlags(&t.s[n_streams], hipStreamNonBlocking);
+      if (e == hipSuccess) ++n_streams;
     }
-    if (e != hipSuccess) return e;   // a later call tries again (what was made stays made)
-    ls.ready = true;
+    while (e == hipSuccess && n_joins < KVLR_MAX_LANES) {
+      e = hipEventCreateWithFlags(&t.join[n_joins], hipEventDisableTiming);
+      if (e == hipSuccess) ++n_joins;
+    }
+    if (e != hipSuccess) {
+      for (int i = 0; i < n_joins; ++i) (void)hipEventDestroy(t.join[i]);
+      for (int i = 0; i < n_streams; ++i) (void)hipStreamDestroy(t.s[i]);
+      if (forked) (void)hipEventDestroy(t.fork);
+      return e;
+    }
+    t.ready = true;
+    ls = t;
   }
   *out = &ls;
   return hipSuccess;
