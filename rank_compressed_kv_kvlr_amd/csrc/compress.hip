@@ -24,9 +24,9 @@
 // the next 64-row tile in flight (buffer loads) while it multiplies the
 // current one, and stores through a buffer resource with wave-uniform offsets.
 //
-// fp32 inputs, ranks that are not whole 16-channel tiles, 4/3-bit latents and
-// joint value latents use a plain VALU kernel; append uses one workgroup per
-// (batch row, KV head, K or V).
+// fp32 inputs, ranks that are not whole 16-channel tiles and joint value latents
+// use a plain VALU kernel, 4/3-bit latents a VALU kernel of their own
+// (compress_q43); append uses one workgroup per (batch row, KV head, K or V).
 //
 // Mixed 4/3-bit latents (STAR-KV technical summary, "Metodologia" section 3)
 // are quantised from the fp32 latents of a row by one thread per row; the
@@ -428,7 +428,8 @@ __device__ __forceinline__ void compress_range(const CompressParams& p, int h, i
 // One workgroup per token range of a (batch row, KV head, kind) segment. Per batch row
 // the segments are ordered values (heads 0..Hkv-1), then keys; segment s has
 // sched_pre[s + 1] - sched_pre[s] workgroups of sched_chunk[s] tokens (the host sizes
-// them so that every workgroup has about the same work and all are resident at once).
+// them so that workgroups carry about the same work, about eight rounds of resident
+// workgroups in all).
 template <bool kOutBf16, int NKB>
 __global__ __launch_bounds__(256) void compress_bf16_mfma(CompressParams p) {
   extern __shared__ __attribute__((aligned(16))) uint4 stage[];   // [mt][kb][lane] hi, then lo
@@ -449,7 +450,7 @@ __global__ __launch_bounds__(256) void compress_bf16_mfma(CompressParams p) {
 }
 
 // Plain VALU compression (fp32 inputs, ranks that are not whole 16-channel
-// tiles, 4/3-bit latents, joint values): one workgroup per (64-token tile,
+// tiles, joint values): one workgroup per (64-token tile,
 // KV head x {K, V}, batch row); the tile is staged in LDS as fp32 and each
 // thread forms latent channels as fp32 dot products, kept in registers (at
 // most 64 * 128 / 256 = 32 per thread). Joint values
