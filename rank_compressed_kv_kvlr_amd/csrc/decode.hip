@@ -876,8 +876,10 @@ void decode_apportioned_bf16(DecodeParams p) {
 // round robin. A code c enters an MFMA as the bf16 number 128 + c (bits
 // 0x4300 | c, exact).
 //  - Scores, transposed: S^T = K q~^T per 16-token block and group of 16 key
-//    channels (v_mfma_f32_16x16x16_bf16, key codes as A, q~ as B in a high and a
-//    low bf16 part), outlier and inlier groups into separate accumulators that
+//    channels (v_mfma_f32_16x16x32_bf16: the A operand holds the lane's 4 key
+//    codes twice, B the same 4 channels of q~ as high and then low bf16 parts, so
+//    one product covers both parts), outlier and inlier groups into separate
+//    accumulators that
 //    start at -128 Q (Q = sum of q~ over the block, as the MFMA sees it), so
 //    they end as sum_j q~_j c_j. Lane (n, q) then holds tokens 4 q .. 4 q + 3 of
 //    query head n and applies the tokens' block parameters:
@@ -1106,7 +1108,10 @@ void decode_split_q43(DecodeParams p) {
   float* qt_lds = q_lds + kHeadsPerWg * 256;    // [4][QTS]
   float* qred = qt_lds + kHeadsPerWg * QTS;     // [4 waves][4][QTS]
   project_query<RB>(p, b, h, hq0, gpw, rk, q_lds, qred, qt_lds);
-  bf16x4_t qh[NG], ql[NG];
+  // B operand per key group: the lane's 4 channels in high bf16 parts, then the same
+  // channels' low parts; the A operand repeats the 4 codes, so one 16x16x32 product
+  // sums code x (high + low) over the group's 16 channels.
+  bf16x8_t qb[NG];
   float Qo = 0.f, Qi = 0.f;
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
@@ -1118,8 +1123,8 @@ void decode_split_q43(DecodeParams p) {
       const float x = (q_ok && ok) ? qt_lds[n16 * QTS + ch] : 0.f;
       const uint16_t hi = f32_to_bf16_bits(x);
       const uint16_t lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
-      qh[g][i] = (short)hi;
-      ql[g][i] = (short)lo;
+      qb[g][i] = (short)hi;
+      qb[g][4 + i] = (short)lo;
       const float seen = bf16_bits_to_f32(hi) + bf16_bits_to_f32(lo);
       if (four) Qo += seen; else Qi += seen;
     }
@@ -1165,14 +1170,12 @@ void decode_split_q43(DecodeParams p) {
         const u32x4_t kc = group_codes(g, gok, kwa, kwb, kBf16Code);
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
-          const bf16x4_t a = __builtin_bit_cast(bf16x4_t, u32x2_t{kc[2 * blk], kc[2 * blk + 1]});
-          if (g == 0 || (GO == 2 && g == 1 && gok == 2)) {
-            ao[blk] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, qh[g], ao[blk], 0, 0, 0);
-            ao[blk] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ql[g], ao[blk], 0, 0, 0);
-          } else {
-            ai[blk] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, qh[g], ai[blk], 0, 0, 0);
-            ai[blk] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ql[g], ai[blk], 0, 0, 0);
-          }
+          const bf16x8_t a = __builtin_bit_cast(
+              bf16x8_t, u32x4_t{kc[2 * blk], kc[2 * blk + 1], kc[2 * blk], kc[2 * blk + 1]});
+          if (g == 0 || (GO == 2 && g == 1 && gok == 2))
+            ao[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[g], ao[blk], 0, 0, 0);
+          else
+            ai[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[g], ai[blk], 0, 0, 0);
         }
       }
     }
