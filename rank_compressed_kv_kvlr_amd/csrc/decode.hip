@@ -29,22 +29,24 @@
 namespace kvlr {
 namespace {
 
-// Merge of the 4 waves' states into one record per head.
-//   wm, wl: [4 waves][4 heads]; red: per-wave per-lane partial sums laid out by
+// Merge of the waves' states into one record per head.
+//   wm, wl: [NW states][4 heads]; red: per-wave per-lane partial sums laid out by
 //   the caller; value(w, g, j) returns wave w's unnormalised latent sum for
 //   head g, channel j.
-template <typename ValueFn>
+//   NW partial states per head (the 4 waves, or 8 where each wave keeps one per
+//   16-token block).
+template <int NW = kWaves, typename ValueFn>
 __device__ __forceinline__ void merge_waves_and_store(const RecLayout& rl, int k, int gpw, int rv, const float* wm,
                                                       const float* wl, ValueFn value) {
   for (int idx = thread_id(); idx < gpw * rv; idx += blockDim.x) {
     const int g = idx / rv, j = idx - g * rv;
     float M = kNegInf;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wm[w * 4 + g]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, wm[w * 4 + g]);
     float o = 0.f, L = 0.f;
     if (M != kNegInf) {
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
+      for (int w = 0; w < NW; ++w) {
         const float f = fast_exp2(wm[w * 4 + g] - M);   // -inf -> 0
         L = fmaf(f, wl[w * 4 + g], L);
         o = fmaf(f, value(w, g, j), o);
@@ -928,6 +930,15 @@ __device__ __forceinline__ u32x4_t codes3_to_num(uint32_t x, uint32_t m7, uint32
   return o;
 }
 
+// Keys: the same fields with dwords 1 and 3 left at bits 3..5 of each half, i.e. the
+// bf16 numbers 128 + 8 c (exact); the score product scales those slots of q~ by 1/8.
+// m7s = m7 << 3.
+__device__ __forceinline__ u32x4_t codes3_to_num_keys(uint32_t x, uint32_t m7, uint32_t m7s, uint32_t e2) {
+  const uint32_t y = (x & 0xFFFFu) | ((x << 4) & 0xFFFF0000u);   // bits 12..23 to 16..27
+  const uint32_t y6 = y >> 6;
+  return u32x4_t{(y & m7) | e2, (y & m7s) | e2, (y6 & m7) | e2, (y6 & m7s) | e2};
+}
+
 // The lane's 24-bit field of an inlier group: bytes 3 lane .. 3 lane + 2 of the group,
 // from the two dwords that hold them (the same dword when they do not straddle).
 __device__ __forceinline__ uint32_t field24(uint32_t w_a, uint32_t w_b, int shift) {
@@ -939,11 +950,11 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 // A vector element is copied to a scalar before it is bit-cast: clang's __builtin_bit_cast
 // applied straight to an element of an ext_vector_type value reads element 0 whatever
 // the index (found in the ISA of this file; the copy is compiled as intended).
-__device__ __forceinline__ float half_at(const u32x4_t& v, int k) {   // half float k (0..7) of a 16-byte piece
+__device__ __forceinline__ half2_t half2_of(uint32_t w) { return __builtin_bit_cast(half2_t, w); }
+__device__ __forceinline__ float half2_at(const u32x2_t& v, int k) {   // half float k (0..3) of an 8-byte piece
   const uint32_t w = v[k >> 1];
   return (float)__builtin_bit_cast(half2_t, w)[k & 1];
 }
-__device__ __forceinline__ half2_t half2_of(uint32_t w) { return __builtin_bit_cast(half2_t, w); }
 
 // Raw buffer access to one (batch row, KV head) block of a 4/3-bit cache: base and size
 // in a resource (word 3 = 0x00020000: the raw 32-bit data format of gfx9 buffers), a
@@ -998,7 +1009,7 @@ void decode_split_q43(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) float ring_lds[EPI];
   __shared__ __attribute__((aligned(16))) float pro_lds[Ring::kProFloats];
   float* const smem = ring_lds;
-  static_assert(EPI >= kWaves * kHeadsPerWg * RB + 2 * kWaves * kHeadsPerWg && EPI >= 4 * RB + 17 + 16 * (RB + 4),
+  static_assert(EPI >= 2 * kWaves * kHeadsPerWg * (RB + 2) && EPI >= 4 * RB + 17 + 16 * (RB + 4),
                 "the ring holds the epilogue's partial sums and some basis rows");
 
   const int s = blockIdx.x;
@@ -1023,7 +1034,6 @@ void decode_split_q43(DecodeParams p) {
   const int tid = thread_id(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = lane & 15, q4 = lane >> 4;
-  const bool q_ok = n16 < gpw;
   const int gok = EXACT ? GO : q43_outlier(rk) >> 4, ngk = EXACT ? NG : rk >> 4;   // 4-bit and all groups of the keys
   const int gov = EXACT ? GO : q43_outlier(rv) >> 4, ngv = EXACT ? NG : rv >> 4;
   const int tbk = kQ43Tile * q43_row_bytes(rk), tbv = kQ43Tile * q43_row_bytes(rv);
@@ -1066,20 +1076,25 @@ void decode_split_q43(DecodeParams p) {
     }
   };
 
-  // this lane's bytes of a stage: its 8 parameter slots, its 4-bit word, and the two
+  // this lane's bytes of a stage: its parameter slots, its 4-bit word, and the two
   // dwords that hold bytes 3 lane .. 3 lane + 2 of a 3-bit group (its 24-bit field).
   // Group g starts at byte 256 + 256 g while g is a 4-bit group, at 256 + 64 go + 192 g
   // once it is a 3-bit one (go 4-bit groups first).
+  // Score columns: lane column n16 = 4 sb + hd holds query head hd of 16-token block
+  // sb (columns 8..15 stay empty), so each lane scores 4 tokens of one block, and the
+  // scores of a lane are the value product's A operand of the same lane (row n16).
+  const int sb = (n16 >> 2) & 1, hd = n16 & 3;
+  const bool s_ok = n16 < 8 && hd < gpw;
   const int off_a = (3 * lane) & ~3, off_b = (3 * lane + 2) & ~3, f_shift = 8 * ((3 * lane) & 3);
-  const uint8_t* const la_meta = ring + 64 * q4;
+  const uint8_t* const la_meta = ring + 64 * q4;            // the 8 tokens' parameters of lane group q4
+  const uint8_t* const la_own = la_meta + 8 * sb;           // those of this lane's 4 tokens
   const uint8_t* const la_4 = ring + 4 * lane;
   const uint8_t* const la_a = ring + off_a;
   const uint8_t* const la_b = ring + off_b;
-  u32x4_t km[4], vm[4];
+  u32x2_t kp[4], vs[2];   // per lane: keys' step_o, base_o, step_i, base_i; values' step_o, step_i
+  u32x4_t vb[2];          // values' base_o, base_i of all 8 tokens (B operands)
   uint32_t kwa[NG], kwb[NG], vwa[NG], vwb[NG];
-  auto read_tile = [&](int at, int go, int ng, u32x4_t* meta, uint32_t* wa, uint32_t* wb) {
-#pragma unroll
-    for (int P = 0; P < 4; ++P) meta[P] = *reinterpret_cast<const u32x4_t*>(la_meta + at + 16 * P);
+  auto read_codes = [&](int at, int go, int ng, uint32_t* wa, uint32_t* wb) {
     const int in = at + kQ43MetaBytes + (kQ43OutGroupBytes - kQ43InGroupBytes) * go;
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
@@ -1092,27 +1107,48 @@ void decode_split_q43(DecodeParams p) {
       }
     }
   };
+  auto read_tile = [&](int at) {
+#pragma unroll
+    for (int P = 0; P < 4; ++P) kp[P] = *reinterpret_cast<const u32x2_t*>(la_own + at + 16 * P);
+    read_codes(at, gok, ngk, kwa, kwb);
+    const int av = at + TB;
+    vs[0] = *reinterpret_cast<const u32x2_t*>(la_own + av);
+    vs[1] = *reinterpret_cast<const u32x2_t*>(la_own + av + 32);
+    vb[0] = *reinterpret_cast<const u32x4_t*>(la_meta + av + 16);
+    vb[1] = *reinterpret_cast<const u32x4_t*>(la_meta + av + 48);
+    read_codes(av, gov, ngv, vwa, vwb);
+  };
   // operands of group g: 16-bit pairs with exponent bytes eb, block 0 then block 1
   // constants of the 3-bit conversion, held in registers (see codes3_to_num)
-  uint32_t m7 = 0x00070007u, e2_k = kBf16Code & 0xFF00FF00u, e2_v = kF16Code & 0xFF00FF00u;
-  asm volatile("" : "+v"(m7), "+s"(e2_k), "+s"(e2_v));
-  auto group_codes = [&](int g, int go, const uint32_t* wa, const uint32_t* wb, uint32_t eb) -> u32x4_t {
-    const uint32_t e2 = eb == kBf16Code ? e2_k : e2_v;
-    if (g == 0) return codes4_to_num(wa[0], eb);
-    if (g >= GO) return codes3_to_num(field24(wa[g], wb[g], f_shift), m7, e2);
-    return go == 2 ? codes4_to_num(wa[g], eb) : codes3_to_num(field24(wa[g], wb[g], f_shift), m7, e2);
+  uint32_t m7 = 0x00070007u, m7s = 0x00380038u, e2_k = kBf16Code & 0xFF00FF00u, e2_v = kF16Code & 0xFF00FF00u;
+  asm volatile("" : "+v"(m7), "+v"(m7s), "+s"(e2_k), "+s"(e2_v));
+  // key groups (3-bit ones with slots 2, 3 of each block at 128 + 8 c) and value groups
+  auto key_codes = [&](int g) -> u32x4_t {
+    if (g == 0) return codes4_to_num(kwa[0], kBf16Code);
+    if (g >= GO) return codes3_to_num_keys(field24(kwa[g], kwb[g], f_shift), m7, m7s, e2_k);
+    return gok == 2 ? codes4_to_num(kwa[g], kBf16Code)
+                    : codes3_to_num_keys(field24(kwa[g], kwb[g], f_shift), m7, m7s, e2_k);
+  };
+  auto value_codes = [&](int g) -> u32x4_t {
+    if (g == 0) return codes4_to_num(vwa[0], kF16Code);
+    if (g >= GO) return codes3_to_num(field24(vwa[g], vwb[g], f_shift), m7, e2_v);
+    return gov == 2 ? codes4_to_num(vwa[g], kF16Code) : codes3_to_num(field24(vwa[g], vwb[g], f_shift), m7, e2_v);
   };
 
-  // ---- prologue: q~ (scaled to log2 units) and, per key group, this lane's column as B (hi/lo)
+  // ---- prologue: q~ (scaled to log2 units) and, per key group, the B operands of the
+  // score product. The A operand of lane (n, q) holds its 8 codes as they are: token n
+  // of block 0 at channels 4 q .. 4 q + 3 of the group, then token n of block 1. Column
+  // 4 sb + hd takes q~ of head hd at those channels in the slots of block sb and zero in
+  // the others, so it sums block sb only; one product takes the high bf16 parts of q~,
+  // a second the low parts. In 3-bit groups the codes of channels 2 and 3 of each 4
+  // enter as 128 + 8 c, so q~ enters there divided by 8 (exact): the products still sum
+  // c q~, on top of 128 times the sum of the B operands (C below).
   float* q_lds = pro_lds;                       // [4][d]
   float* qt_lds = q_lds + kHeadsPerWg * 256;    // [4][QTS]
   float* qred = qt_lds + kHeadsPerWg * QTS;     // [4 waves][4][QTS]
   project_query<RB>(p, b, h, hq0, gpw, rk, q_lds, qred, qt_lds);
-  // B operand per key group: the lane's 4 channels in high bf16 parts, then the same
-  // channels' low parts; the A operand repeats the 4 codes, so one 16x16x32 product
-  // sums code x (high + low) over the group's 16 channels.
-  bf16x8_t qb[NG];
-  float Qo = 0.f, Qi = 0.f;
+  bf16x8_t qbh[NG], qbl[NG];
+  float Qo = 0.f, Qi = 0.f, Ci = 0.f;   // Q: sums of q~ as the products see it; Ci: of the B operands
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
     const bool four = g < gok;
@@ -1120,18 +1156,30 @@ void decode_split_q43(DecodeParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ch = 16 * g + 4 * q4 + i;   // 4-bit groups first, then 3-bit: channels in order
-      const float x = (q_ok && ok) ? qt_lds[n16 * QTS + ch] : 0.f;
-      const uint16_t hi = f32_to_bf16_bits(x);
-      const uint16_t lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
-      qb[g][i] = (short)hi;
-      qb[g][4 + i] = (short)lo;
+      const float x = (s_ok && ok) ? qt_lds[hd * QTS + ch] : 0.f;
+      const bool eighth = !four && i >= 2;
+      const float xs = eighth ? 0.125f * x : x;
+      const uint16_t hi = f32_to_bf16_bits(xs);
+      const uint16_t lo = f32_to_bf16_bits(xs - bf16_bits_to_f32(hi));
+      qbh[g][i] = sb == 0 ? (short)hi : (short)0;
+      qbh[g][4 + i] = sb == 1 ? (short)hi : (short)0;
+      qbl[g][i] = sb == 0 ? (short)lo : (short)0;
+      qbl[g][4 + i] = sb == 1 ? (short)lo : (short)0;
       const float seen = bf16_bits_to_f32(hi) + bf16_bits_to_f32(lo);
-      if (four) Qo += seen; else Qi += seen;
+      if (four) {
+        Qo += seen;
+      } else {
+        Qi += eighth ? 8.f * seen : seen;
+        Ci += seen;
+      }
     }
   }
   Qo = sum_over_rows(Qo);
   Qi = sum_over_rows(Qi);
-  const float c_o = -128.f * Qo, c_i = -128.f * Qi;
+  Ci = sum_over_rows(Ci);
+  const float c_o = -128.f * Qo, c_i = -128.f * Ci;
+  // A-operand masks of the value product: this lane's weights sit in the slots of its block
+  const uint32_t own_lo = sb == 0 ? ~0u : 0u, own_hi = ~own_lo;
   // The first NS - 1 tiles go out once the prologue is done with memory: the waits of
   // its loads would cover them, and so would those of its LDS reads (the compiler
   // orders LDS accesses after direct-to-LDS loads issued under a lane mask).
@@ -1141,9 +1189,11 @@ void decode_split_q43(DecodeParams p) {
   }
 
   const half8_t ones = __builtin_bit_cast(half8_t, u32x4_t{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u});
+  // running maximum and sum of this lane's score column (head hd, block sb)
   float m = kNegInf, l = 0.f;
-  // value accumulators (rows: query heads 4 q4 + i) and the sums over tokens of w_o, w_i,
-  // p base_o and p base_i (the same rows, every column alike)
+  // value accumulators (rows: score columns 4 q4 + i, i.e. (block, head) pairs; rows
+  // 8..15 stay unused) and the sums over tokens of w_o, w_i, p base_o and p base_i (the
+  // same rows, every column alike)
   f32x4_t acc[NG], sw_o = {0.f, 0.f, 0.f, 0.f}, sw_i = {0.f, 0.f, 0.f, 0.f};
   f32x4_t sb_o = {0.f, 0.f, 0.f, 0.f}, sb_i = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1159,65 +1209,55 @@ void decode_split_q43(DecodeParams p) {
     issue(it + NS - 1, (u + NS - 1) % NS);
     __builtin_amdgcn_s_waitcnt(vmcnt_at_most(Ring::kWait));
     asm volatile("" ::: "memory");   // the stage's LDS reads stay after the wait
-    read_tile(u * STAGE, gok, ngk, km, kwa, kwb);
-    read_tile(u * STAGE + TB, gov, ngv, vm, vwa, vwb);
-    // ---- scores S^T[token][head], both 16-token blocks; accumulators start at -128 Q
-    f32x4_t ao[2] = {{c_o, c_o, c_o, c_o}, {c_o, c_o, c_o, c_o}};
-    f32x4_t ai[2] = {{c_i, c_i, c_i, c_i}, {c_i, c_i, c_i, c_i}};
+    read_tile(u * STAGE);
+    // ---- scores S^T[token][column] of both blocks; accumulators start at -128 Q
+    f32x4_t ao = {c_o, c_o, c_o, c_o}, ai = {c_i, c_i, c_i, c_i};
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       if (g < ngk) {
-        const u32x4_t kc = group_codes(g, gok, kwa, kwb, kBf16Code);
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-          const bf16x8_t a = __builtin_bit_cast(
-              bf16x8_t, u32x4_t{kc[2 * blk], kc[2 * blk + 1], kc[2 * blk], kc[2 * blk + 1]});
-          if (g == 0 || (GO == 2 && g == 1 && gok == 2))
-            ao[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[g], ao[blk], 0, 0, 0);
-          else
-            ai[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[g], ai[blk], 0, 0, 0);
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, key_codes(g));
+        if (g == 0 || (GO == 2 && g == 1 && gok == 2)) {
+          ao = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qbh[g], ao, 0, 0, 0);
+          ao = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qbl[g], ao, 0, 0, 0);
+        } else {
+          ai = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qbh[g], ai, 0, 0, 0);
+          ai = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qbl[g], ai, 0, 0, 0);
         }
       }
     }
     // the keys' block parameters: s = step_o acc_o + base_o Q_o + step_i acc_i + base_i Q_i
+    // (lane: tokens t0 + 16 sb + 4 q4 + i)
     const bool tail = t0 + kQ43Tile > t_end;   // rows past the end may hold any bits
-    float sc[2][4];
+    const int tl = t0 + 16 * sb + 4 * q4;
+    float sc[4];
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int k = 4 * blk + i;
-        sc[blk][i] = fmaf(half_at(km[0], k), ao[blk][i],
-                          fmaf(half_at(km[2], k), ai[blk][i],
-                               fmaf(half_at(km[1], k), Qo, fmaf(half_at(km[3], k), Qi, 0.f))));
-      }
+    for (int i = 0; i < 4; ++i)
+      sc[i] = fmaf(half2_at(kp[0], i), ao[i],
+                   fmaf(half2_at(kp[2], i), ai[i], fmaf(half2_at(kp[1], i), Qo, fmaf(half2_at(kp[3], i), Qi, 0.f))));
     if (__builtin_expect(tail, 0)) {
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (t0 + 16 * blk + 4 * q4 + i >= t_end) sc[blk][i] = kNegInf;
+      for (int i = 0; i < 4; ++i)
+        if (tl + i >= t_end) sc[i] = kNegInf;
     }
 
-    // ---- online softmax (lane: head n16, tokens 16 blk + 4 q4 + i)
-    float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+    // ---- online softmax per score column
+    // in-lane maximum by med3(a, b, +inf) = max(a, b): scores are never NaN here
+    float mx = __builtin_amdgcn_fmed3f(__builtin_amdgcn_fmed3f(sc[0], sc[1], kPosInf),
+                                       __builtin_amdgcn_fmed3f(sc[2], sc[3], kPosInf), kPosInf);
     mx = max_over_rows(mx);
     const float m_new = fmaxf(m, mx);
     const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = q_ok ? fast_exp2(m - m_use) : 1.f;
-    float pr[2][4], ls = 0.f;
+    const float alpha = s_ok ? fast_exp2(m - m_use) : 1.f;
+    float pr[4], ls = 0.f;
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pr[blk][i] = fast_exp2(sc[blk][i] - m_use);   // masked: exp2(-inf) = 0
-        ls += pr[blk][i];
-      }
+    for (int i = 0; i < 4; ++i) {
+      pr[i] = fast_exp2(sc[i] - m_use);   // masked: exp2(-inf) = 0
+      ls += pr[i];
+    }
     l = fmaf(l, alpha, ls);
     m = m_new;
     if (__ballot(alpha != 1.f)) {
-      // accumulator rows are query heads 4 q4 + i; their factors sit in lanes 4 q4 + i
+      // accumulator rows are score columns 4 q4 + i; their factors sit in lanes 4 q4 + i
       float ar[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * q4 + i, 64);
@@ -1232,27 +1272,34 @@ void decode_split_q43(DecodeParams p) {
       }
     }
 
-    // ---- value weights in half floats, two tokens per operation: w = p step, and p base;
-    // lane (n16, q4) holds K slots k = 4 blk + i of head n16, whose parameters are the
-    // halves of its 16-byte pieces. In the last tile the parameters of rows past the end
-    // are zeroed (they may hold any bits).
+    // ---- value weights in half floats, two tokens per operation: w = p step, and p
+    // itself, in the A-operand slots of this lane's block (zero in the other block's).
+    // In the last tile the parameters of rows past the end are zeroed (they may hold
+    // any bits).
     if (tail) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t msk = (tl + 2 * j < t_end ? 0xFFFFu : 0u) | (tl + 2 * j + 1 < t_end ? 0xFFFF0000u : 0u);
+        vs[0][j] &= msk;
+        vs[1][j] &= msk;
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int k = 2 * j, t_k = t0 + 16 * (k >> 2) + 4 * q4 + (k & 3);
         const uint32_t msk = (t_k < t_end ? 0xFFFFu : 0u) | (t_k + 1 < t_end ? 0xFFFF0000u : 0u);
-#pragma unroll
-        for (int P = 0; P < 4; ++P) vm[P][j] &= msk;
+        vb[0][j] &= msk;
+        vb[1][j] &= msk;
       }
     }
-    u32x4_t pw, wo, wi;
+    const half2_t p01 = __builtin_convertvector((float __attribute__((ext_vector_type(2)))){pr[0], pr[1]}, half2_t);
+    const half2_t p23 = __builtin_convertvector((float __attribute__((ext_vector_type(2)))){pr[2], pr[3]}, half2_t);
+    const uint32_t w01 = __builtin_bit_cast(uint32_t, p01), w23 = __builtin_bit_cast(uint32_t, p23);
+    const u32x4_t pw = {w01 & own_lo, w23 & own_lo, w01 & own_hi, w23 & own_hi};
+    u32x4_t wo, wi;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const half2_t pk = __builtin_convertvector(
-          (float __attribute__((ext_vector_type(2)))){pr[j >> 1][2 * (j & 1)], pr[j >> 1][2 * (j & 1) + 1]}, half2_t);
-      pw[j] = __builtin_bit_cast(uint32_t, pk);
-      wo[j] = __builtin_bit_cast(uint32_t, pk * half2_of(vm[0][j]));
-      wi[j] = __builtin_bit_cast(uint32_t, pk * half2_of(vm[2][j]));
+      wo[j] = __builtin_bit_cast(uint32_t, half2_of(pw[j]) * half2_of(vs[0][j & 1]));
+      wi[j] = __builtin_bit_cast(uint32_t, half2_of(pw[j]) * half2_of(vs[1][j & 1]));
     }
     const half8_t awo = __builtin_bit_cast(half8_t, wo), awi = __builtin_bit_cast(half8_t, wi);
     const half8_t ap = __builtin_bit_cast(half8_t, pw);
@@ -1261,7 +1308,7 @@ void decode_split_q43(DecodeParams p) {
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       if (g < ngv) {
-        const half8_t bv = __builtin_bit_cast(half8_t, group_codes(g, gov, vwa, vwb, kF16Code));
+        const half8_t bv = __builtin_bit_cast(half8_t, value_codes(g));
         const bool four = g == 0 || (GO == 2 && g == 1 && gov == 2);
         acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(four ? awo : awi, bv, acc[g], 0, 0, 0);
       }
@@ -1269,39 +1316,42 @@ void decode_split_q43(DecodeParams p) {
     sw_o = __builtin_amdgcn_mfma_f32_16x16x32_f16(awo, ones, sw_o, 0, 0, 0);
     sw_i = __builtin_amdgcn_mfma_f32_16x16x32_f16(awi, ones, sw_i, 0, 0, 0);
     // the B operand of lane (n, q) holds slots 8 q .. 8 q + 7 for column n: its own parameters
-    sb_o = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap, __builtin_bit_cast(half8_t, vm[1]), sb_o, 0, 0, 0);
-    sb_i = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap, __builtin_bit_cast(half8_t, vm[3]), sb_i, 0, 0, 0);
+    sb_o = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap, __builtin_bit_cast(half8_t, vb[0]), sb_o, 0, 0, 0);
+    sb_i = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap, __builtin_bit_cast(half8_t, vb[1]), sb_i, 0, 0, 0);
   }
   }
 
   BasisPrefetch<RB> pf;
   prefetch_basis<RB>(p, h, rv, pf);
-  // ---- per head: l over the lane groups; rows 0..3 (lanes q4 = 0) hold heads 0..3:
+  // ---- per (block, head) state: l over the lane groups; rows 4 q4 + i of lane groups
+  // q4 = 0, 1 hold block q4's heads i:
   // o_lat = sum_t w_t (1024 + c_t) - 1024 sum_t w_t + sum_t p_t base_t
   l = sum_over_rows(l);
   __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));   // this wave's tile loads have landed: the ring is reused
   __syncthreads();
-  float* red = smem;                          // [wave][head][RB]
-  float* wm = smem + kWaves * kHeadsPerWg * RB;
-  float* wl = wm + kWaves * kHeadsPerWg;
-  if (q4 == 0) {
+  constexpr int kStates = 2 * kWaves;          // one per (wave, block)
+  float* red = smem;                          // [state][head][RB]
+  float* wm = smem + kStates * kHeadsPerWg * RB;
+  float* wl = wm + kStates * kHeadsPerWg;
+  if (q4 < 2) {
+    const int st = 2 * wave + q4;
 #pragma unroll
     for (int g = 0; g < NG; ++g)
       if (g < ngv) {
         const bool four = g == 0 || (GO == 2 && g == 1 && gov == 2);
 #pragma unroll
         for (int i = 0; i < kHeadsPerWg; ++i)
-          red[(wave * kHeadsPerWg + i) * RB + 16 * g + n16] =
+          red[(st * kHeadsPerWg + i) * RB + 16 * g + n16] =
               acc[g][i] - 1024.f * (four ? sw_o[i] : sw_i[i]) + (four ? sb_o[i] : sb_i[i]);
       }
-    if (n16 < kHeadsPerWg) {
-      wm[wave * kHeadsPerWg + n16] = m;
-      wl[wave * kHeadsPerWg + n16] = l;
+    if (q4 == 0 && n16 < 8) {
+      wm[(2 * wave + sb) * kHeadsPerWg + hd] = m;
+      wl[(2 * wave + sb) * kHeadsPerWg + hd] = l;
     }
   }
   __syncthreads();
-  merge_waves_and_store(rl, s, gpw, rv, wm, wl,
-                        [&](int w, int g, int j) { return red[(w * kHeadsPerWg + g) * RB + j]; });
+  merge_waves_and_store<kStates>(rl, s, gpw, rv, wm, wl,
+                                 [&](int w, int g, int j) { return red[(w * kHeadsPerWg + g) * RB + j]; });
   finish_split<RB, EPI, 16>(p, b, h, hg, hq0, gpw, rv, smem, pf, rl, p.n_splits);
 }
 

@@ -18,6 +18,7 @@ __device__ __forceinline__ int thread_id() {
 }
 
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kPosInf = __builtin_huge_valf();
 
 // A workgroup barrier for data exchanged through LDS by ds_read/ds_write: the
 // wave's LDS accesses complete (lgkmcnt), then all waves meet. Unlike

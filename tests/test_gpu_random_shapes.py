@@ -177,7 +177,11 @@ def test_random_shape_entry_points_agree(gpu, i):
     # (per-head ranks that differ) the sequences are cut elsewhere: weights round differently
     balanced = kv.decode_plan(desc, split)[1] == 0
     assert err_two <= (2e-5 if balanced else 1e-6), err_two
-    assert err_fold <= (1e-5 if kind.endswith("f32") else 1e-4), err_fold
+    # 4/3-bit values enter the value product with half-float weights: the two entry points
+    # form q~ apart in its last bits, so a weight can round to the neighbouring half float,
+    # up to 2^-10 of it, and in a short row one token can carry most of the output
+    fold_bound = 1e-5 if kind.endswith("f32") else (2.0 ** -10 if kind.endswith("q43") else 1e-4)
+    assert err_fold <= fold_bound, err_fold
 
 
 @pytest.mark.parametrize("i", range(len(KINDS)))
