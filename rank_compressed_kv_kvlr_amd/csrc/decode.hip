@@ -877,21 +877,23 @@ void decode_apportioned_bf16(DecodeParams p) {
 // wave takes one tile per step; the waves of a workgroup take the split's tiles
 // round robin. A code c enters an MFMA as the bf16 number 128 + c (bits
 // 0x4300 | c, exact).
-//  - Scores, transposed: S^T = K q~^T per 16-token block and group of 16 key
-//    channels (v_mfma_f32_16x16x32_bf16: the A operand holds the lane's 4 key
-//    codes twice, B the same 4 channels of q~ as high and then low bf16 parts, so
-//    one product covers both parts), outlier and inlier groups into separate
-//    accumulators that
-//    start at -128 Q (Q = sum of q~ over the block, as the MFMA sees it), so
-//    they end as sum_j q~_j c_j. Lane (n, q) then holds tokens 4 q .. 4 q + 3 of
-//    query head n and applies the tokens' block parameters:
+//  - Scores, transposed: S^T = K q~^T per group of 16 key channels, both 16-token
+//    blocks of the tile in one v_mfma_f32_16x16x32_bf16: the lane's 8 codes are the
+//    A operand as stored, and column 4 sb + hd of the B operand holds q~ of head hd
+//    in the slots of block sb (zeros in the other block's), once with its high and
+//    once with its low bf16 parts. Outlier and inlier groups go into separate
+//    accumulators that start at -128 C (C = sum of the B operands), so they end as
+//    sum_j q~_j c_j. Lane (n < 8, q) then holds tokens 4 q .. 4 q + 3 of block n / 4
+//    for head n % 4 and applies the tokens' block parameters:
 //      s = step_o acc_o + base_o Q_o + step_i acc_i + base_i Q_i.
-//  - Online softmax per query head in the log2 domain, as in the bf16 kernel.
-//  - Values: o_lat[head][ch] += sum_t w_t (1024 + c_t,ch) on
-//    v_mfma_f32_16x16x32_f16 over the tile's 32 tokens: a value code enters as
-//    the half float 1024 + c (bits 0x6400 | c, exact), and the weights
-//    w = half(half(p) step_o) or half(half(p) step_i), formed two tokens per
-//    packed multiply, are already the A operand in registers. An MFMA against a
+//  - Online softmax per (block, head) column in the log2 domain; the workgroup
+//    merge takes 8 states per query head (2 per wave).
+//  - Values: o_lat[row][ch] += sum_t w_t (1024 + c_t,ch) on
+//    v_mfma_f32_16x16x32_f16 over the tile's 32 tokens, rows = the (block, head)
+//    columns of the scores: a value code enters as the half float 1024 + c (bits
+//    0x6400 | c, exact), and the weights w = half(half(p) step_o) or
+//    half(half(p) step_i), formed two tokens per packed multiply in the slots of
+//    the lane's block, are already the A operand in registers. An MFMA against a
 //    B operand of ones gives sum_t w_t (the 1024 offset), and one against the
 //    tokens' minima gives sum_t p_t base_t; the three are combined when the
 //    split ends. The weights carry half-float precision (11 bits), the scores'
@@ -900,7 +902,8 @@ void decode_apportioned_bf16(DecodeParams p) {
 // 4-bit word splits into its low and high nibbles (blocks 0 and 1) and v_perm
 // interleaves them with the exponent byte 0x43; a 24-bit 3-bit field is
 // rotated so that codes e and e + 4 sit 16 bits apart, and each pair is one
-// shift and one AND-OR.
+// AND-OR, after a shift for two of the four pairs (keys keep two pairs at bits 3..5,
+// i.e. 128 + 8 c, and value pairs take one shift each).
 constexpr uint32_t kBf16Code = 0x43434343u;   // bf16 exponent bytes of 128 + c (keys)
 constexpr uint32_t kF16Code = 0x64646464u;    // f16 exponent bytes of 1024 + c (values)
 
