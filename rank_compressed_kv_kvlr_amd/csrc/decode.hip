@@ -619,8 +619,10 @@ struct Segment {
 // segments number at most gridDim.x. Workgroup w takes segment w in (b, h, hg, j)
 // order and leaves its record in slot w; the segments of a unit are consecutive, so
 // the unit's records are too, and its last arrival merges them. No workgroup pays for
-// two segments' prologues and tails. Every wave computes the plan with the same float
-// operations from the same lengths, so all workgroups agree on it.
+// two segments' prologues and tails. Wave 0 of every workgroup computes the plan with
+// the same float operations from the same lengths, so all workgroups agree on it: a
+// geometric bisection for lam inside a bracket that the rounding bound gives, then one
+// prefix sum over the units' segment counts to find the unit that holds segment w.
 template <typename LenOf>
 __device__ __forceinline__ bool apportioned_segment(const DecodeParams& p, const LenOf& len_of, Segment& sg) {
   constexpr int R = kApportionPairs / 64;   // (row, KV head) pairs per lane
@@ -638,46 +640,70 @@ __device__ __forceinline__ bool apportioned_segment(const DecodeParams& p, const
     kmax[r] = (float)((tlen[r] + kBalancedTokens - 1) / kBalancedTokens);
   }
   auto segs = [&](int r, float inv_lam) { return fminf(ceilf(work[r] * inv_lam), kmax[r]); };
-  // segments of the units of pairs below i_end (wave-uniform; exact below 2^24)
   const int n_r = (n_pairs + 63) >> 6;   // chunks in use
-  auto count = [&](float inv_lam, int i_end) {
+  // segments of all the units (wave-uniform; exact below 2^24)
+  auto count = [&](float inv_lam) {
     float n = 0.f;
 #pragma unroll
     for (int r = 0; r < R; ++r)
-      if (r < n_r && lane + 64 * r < i_end) n += segs(r, inv_lam);
+      if (r < n_r) n += segs(r, inv_lam);
     return sum_over_rows(row16_allreduce<false>(n)) * (float)n_hg;
   };
-  // the bracket: all the work W over gridDim.x segments is too little per segment; W per
-  // segment gives each non-empty unit one segment (two where rounding lifts its share
-  // past 1), at most gridDim.x in all
-  float wsum = 0.f;
+  // the bracket: W / P is the least work per segment that could do; every unit rounds
+  // its count up by less than one segment, so the count is below W / lam + U (U: the
+  // non-empty units) and lam = W / (P - U) does when P > U (checked, else lam = W,
+  // one segment per non-empty unit, which does since U <= P / 2 in this form)
+  float wsum = 0.f, nz = 0.f;
 #pragma unroll
   for (int r = 0; r < R; ++r)
-    if (r < n_r) wsum += work[r];
+    if (r < n_r) {
+      wsum += work[r];
+      nz += work[r] > 0.f ? 1.f : 0.f;
+    }
   const float W = sum_over_rows(row16_allreduce<false>(wsum)) * (float)n_hg;
+  const float U = sum_over_rows(row16_allreduce<false>(nz)) * (float)n_hg;
   const float Pf = (float)gridDim.x;
-  float lo = W / Pf, hi = W;
-  for (int it = 0; it < 16; ++it) {   // the ratio hi / lo <= gridDim.x shrinks to its 2^-16 power
+  float lo = W / Pf, hi = Pf > U ? W / (Pf - U) : W;
+  if (count(1.f / hi) > Pf) hi = W;
+  for (int it = 0; it < 16 && hi > 1.0005f * lo; ++it) {   // geometric bisection to 0.05%
     const float mid = sqrtf(lo * hi);
-    if (count(1.f / mid, n_pairs) <= Pf) hi = mid; else lo = mid;
+    if (count(1.f / mid) <= Pf) hi = mid; else lo = mid;
   }
   const float inv_lam = 1.f / hi;
-  if (w >= (int)count(inv_lam, n_pairs)) return false;
-  // the pair holding segment w: the last i with count(i) <= w
-  int ilo = 0, ihi = n_pairs;
-  while (ihi - ilo > 1) {
-    const int mid = (ilo + ihi) >> 1;
-    if ((int)count(inv_lam, mid) <= w) ilo = mid; else ihi = mid;
+  // first segment of every pair: an exclusive prefix sum over the pairs in order
+  float first[R], sk[R];
+  float run = 0.f;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (r < n_r) {
+      sk[r] = lane + 64 * r < n_pairs ? segs(r, inv_lam) : 0.f;
+      float v = sk[r];
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(v, off, 64);
+        if (lane >= off) v += y;
+      }
+      first[r] = (run + v - sk[r]) * (float)n_hg;
+      run += readlane_f(v, 63);
+    }
   }
-  const int E = (int)count(inv_lam, ilo);
-  float kl = 0.f;
+  if (w >= (int)(run * (float)n_hg)) return false;
+  // the pair holding segment w: the last pair whose first segment is at most w
+  int n_le = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    if (r < n_r) n_le += __builtin_popcountll(__ballot(lane + 64 * r < n_pairs && first[r] <= (float)w));
+  const int ilo = n_le - 1;
+  float kl = 0.f, el = 0.f;
   int tl = 0;
 #pragma unroll
   for (int r = 0; r < R; ++r)
     if (r == (ilo >> 6)) {
-      kl = segs(r, inv_lam);
+      kl = sk[r];
+      el = first[r];
       tl = tlen[r];
     }
+  const int E = (int)readlane_f(el, ilo & 63);
   const int k = (int)readlane_f(kl, ilo & 63);
   const long long T = __builtin_amdgcn_readlane(tl, ilo & 63);
   const int b = ilo / Hkv, h = ilo - b * Hkv;
@@ -851,17 +877,25 @@ void decode_apportioned_bf16(DecodeParams p) {
   const long long Tz = zero_duty ? len_of(blockIdx.x) : 1;
   // the segment passes through LDS: its values are then re-read where needed instead of
   // being held in scalar registers across the segment body (which would spill them)
+  // Wave 0 works out the plan; the other waves wait at the barrier (every workgroup
+  // computes the same plan from the same lengths, so one wave of each is enough).
   __shared__ Segment st;
-  Segment sg;
-  const bool has = apportioned_segment(p, len_of, sg);
+  __shared__ int st_has;
+  if (tid < 64) {
+    Segment sg;
+    const bool has = apportioned_segment(p, len_of, sg);
+    if (tid == 0) {
+      st = sg;
+      st_has = has;
+    }
+  }
   if (zero_duty && Tz == 0) {
     const int n = p.Hq * p.out_stride;
     float* o = p.out + (size_t)blockIdx.x * n;
     for (int i = tid; i < n; i += blockDim.x) o[i] = 0.f;
   }
-  if (!has) return;
-  if (tid == 0) st = sg;
   __syncthreads();
+  if (!st_has) return;
   const RecLayout rl{p.ws + st.slot * kHeadsPerWg * p.ws_stride, (size_t)kHeadsPerWg * p.ws_stride,
                      (size_t)p.ws_stride};
   bf16_segment<RB, TT>(p, st.b, st.h, st.hg, st.t_begin, st.t_end, rl, st.k, st.n_rec, smem);

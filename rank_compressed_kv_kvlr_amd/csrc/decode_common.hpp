@@ -65,20 +65,16 @@ __device__ __forceinline__ void project_query(const DecodeParams& p, int b, int 
   const int isub = lane >> 4, m = lane & 15;
   const int rows_per_wave = d >> 2, rpl = d >> 4;
   float4 pr[RPL];
-  // lanes past the rank load a valid address and mask the value (no divergent branch)
+  // lanes past the rank take zeros without a load (their loads are masked off, so a
+  // small rank reads only its own columns)
   auto load_half = [&](int hf) {
     const int col = 64 * hf + 4 * m;
     const bool ok = col < rk;
-    const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int e = 0; e < RPL; ++e) {
       const int i = wave * rows_per_wave + isub + 4 * e;
-      if (e < rpl) {
-        const float4 v = *reinterpret_cast<const float4*>(P + (size_t)i * rk + (ok ? col : 0));
-        pr[e] = ok ? v : zero;
-      } else {
-        pr[e] = zero;
-      }
+      pr[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (e < rpl && ok) pr[e] = *reinterpret_cast<const float4*>(P + (size_t)i * rk + col);
     }
   };
   load_half(0);   // basis loads in flight together with the query rows
@@ -97,6 +93,7 @@ __device__ __forceinline__ void project_query(const DecodeParams& p, int b, int 
 #pragma unroll
   for (int hf = 0; hf < NH; ++hf) {
     const int col = 64 * hf + 4 * m;
+    if (hf > 0 && 64 * hf >= rk) break;   // halves past the rank: nothing to load (red is read below rk only)
     if (hf > 0) load_half(hf);
     float part[4][4];
 #pragma unroll
