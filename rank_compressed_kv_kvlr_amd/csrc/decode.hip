@@ -651,8 +651,9 @@ __device__ __forceinline__ bool apportioned_segment(const DecodeParams& p, const
   };
   // the bracket: W / P is the least work per segment that could do; every unit rounds
   // its count up by less than one segment, so the count is below W / lam + U (U: the
-  // non-empty units) and lam = W / (P - U) does when P > U (checked, else lam = W,
-  // one segment per non-empty unit, which does since U <= P / 2 in this form)
+  // non-empty units) and lam = W / (P - U) does when P > U (checked; else lam = W: one
+  // segment per non-empty unit, two where rounding lifts a share past 1, at most
+  // 2 U <= P in this form)
   float wsum = 0.f, nz = 0.f;
 #pragma unroll
   for (int r = 0; r < R; ++r)
