@@ -83,6 +83,27 @@ def load_traffic():
     return t.get("bytes_per_launch")
 
 
+Q43_COUNTERS = os.path.join(ROOT, "profiles", "decode_split_q43_counters.json")
+# VALU issue rate of the chip: 256 CUs x 4 SIMDs x 2.4 GHz / 4 cycles per wave64 instruction
+VALU_ISSUE_PEAK_PER_US = 256 * 4 * 2400 / 4
+
+
+def q43_alu_roofline(median_us):
+    """The 4/3-bit decode against the VALU issue rate: VALU instructions per launch from the
+    rocprofv3 counters (valid only for the current decode source) over the measured time."""
+    try:
+        with open(Q43_COUNTERS) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("decode_src_sha256_16") != source_hash(DECODE_SRC):
+        return None
+    achieved = t["valu_instr_per_launch"] / median_us
+    return {"bound": "alu", "achieved": achieved, "peak": VALU_ISSUE_PEAK_PER_US,
+            "unit": "VALU wave64 instructions per us", "frac": achieved / VALU_ISSUE_PEAK_PER_US,
+            "valu_instr_per_launch": t["valu_instr_per_launch"], "source": "profiles/decode_split_q43_counters.json"}
+
+
 def compress_counters(workload):
     """MFMA busy share and HBM bytes of prefill compression on `workload` from rocprofv3 counters
     (profiles/), valid only for the current compression source."""
@@ -412,7 +433,8 @@ def measure_q43(kv, torch, np, cfg, gen, q, lens, steps, warmup):
     st = with_rates(np, spread(np, event_times(torch, np, call, steps, warmup)), nbytes, B)
     st.update({"entry": "kvlr_decode_attn on KVLR_Q43 caches", "kernel": "decode_split_q43",
                "region_us_per_call": region_us(torch, call, steps),
-               "bytes_vs_bf16": nbytes / (B * T * int((rk + rv).sum()) * 2)})
+               "bytes_vs_bf16": nbytes / (B * T * int((rk + rv).sum()) * 2),
+               "alu_roofline": q43_alu_roofline(st["median_us"])})
     return st
 
 
